@@ -1,0 +1,7 @@
+"""Float64 CPU oracle of the attention forward pass.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, by the smoke check and by the bench's CPU-baseline leg, never by
+the library. It shares no code with the GPU path.
+"""
+from .attention import (mha_ref, sdpa_brute, sdpa_head, sdpa_ref, sdpa_weights_head,  # noqa: F401
+                        sdpa_weights_ref)

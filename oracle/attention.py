@@ -1,0 +1,146 @@
+"""Plain float64 CPU oracle for scaled dot-product attention and multi-head attention.
+
+TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the bench's CPU-baseline leg may import this module.
+The library's GPU path never imports, links or calls anything here, and this module imports nothing from it.
+
+Every function is the plain definition written out in float64 with NumPy (matmul, exp, max and sum are the only
+library primitives). No blocking, no streaming softmax, no fusion: one head at a time, the full score matrix, then
+the row softmax, then the weighted sum of the values.
+
+Sources (web pages about "Attention Is All You Need"):
+  * "Attention Is All You Need" (lettle.cn translation), section 3.2.1 Scaled Dot-Product Attention, equation
+    Attention(Q,K,V) = softmax(QK^T / sqrt(d_k)) V; section 3.2.2 Multi-Head Attention.
+  * "Transformer：抛弃循环与卷积的序列建模" (jiashun-ye.github.io), sections "Scaled Dot-Product Attention",
+    "Multi-Head Attention" (head_i = Attention(QW_i^Q, KW_i^K, VW_i^V), MultiHead = Concat(head_1..head_h) W^O),
+    "Transformer 中的三种 Attention" (future scores set to -inf before the softmax in decoder self-attention), and
+    the training example's mask matrix M (section "训练样本").
+  * "Transformer 为什么抛弃循环网络" (treecat.cn), sections "一次注意力计算在做什么" and "为什么需要多头注意力".
+
+Readings where the pages leave a step open:
+  * The causal mask sets the score of key j for query i to -inf when j > i (the diagonal is allowed), so those
+    weights are exactly 0. It is defined only for self-attention, where n_q == n_k; `q_index` lets a caller ask for a
+    subset of query rows and still get the mask of their true positions.
+  * Subtracting the row max before exp is an exact identity of the softmax, used only to avoid overflow.
+  * Projections carry no bias (the attention formulas on the pages have none). The row-vector convention X W is used:
+    W_i^Q is the column block i of Wq [d_model, h*d_k]; Concat orders the heads 1..h along the last axis; W^O is
+    [h*d_v, d_model].
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def _as_f64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def _causal_disallowed(n_q, n_k, q_index):
+    """Boolean [n_q, n_k]: True where key j comes after query position i (j > i)."""
+    if q_index is None:
+        if n_q != n_k:
+            raise ValueError("the causal mask is defined for self-attention only (n_q == n_k)")
+        q_index = np.arange(n_q)
+    q_index = np.asarray(q_index)
+    if q_index.shape != (n_q,):
+        raise ValueError("q_index must give one position per query row")
+    return np.arange(n_k)[None, :] > q_index[:, None]
+
+
+def sdpa_weights_head(q, k, causal=False, q_index=None):
+    """Attention weights softmax(q k^T / sqrt(d_k)) of one head. q [n_q, d_k], k [n_k, d_k] -> [n_q, n_k]."""
+    q = _as_f64(q)
+    k = _as_f64(k)
+    if q.ndim != 2 or k.ndim != 2 or q.shape[1] != k.shape[1]:
+        raise ValueError("q [n_q, d_k] and k [n_k, d_k] expected")
+    d_k = q.shape[1]
+    s = (q @ k.T) / math.sqrt(d_k)                       # dot products divided by sqrt(d_k)
+    if causal:
+        s = np.where(_causal_disallowed(s.shape[0], s.shape[1], q_index), -np.inf, s)
+    m = s.max(axis=1, keepdims=True)                     # finite: every row keeps at least its own position
+    e = np.exp(s - m)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def sdpa_head(q, k, v, causal=False, q_index=None):
+    """Output softmax(q k^T / sqrt(d_k)) v of one head. v [n_k, d_v] -> [n_q, d_v]."""
+    v = _as_f64(v)
+    w = sdpa_weights_head(q, k, causal, q_index)
+    if v.ndim != 2 or v.shape[0] != w.shape[1]:
+        raise ValueError("v [n_k, d_v] expected")
+    return w @ v
+
+
+def _per_head(fn, Q, *rest, **kw):
+    Q = _as_f64(Q)
+    lead = Q.shape[:-2]
+    rest = [_as_f64(r) for r in rest]
+    for r in rest:
+        if r.shape[:-2] != lead:
+            raise ValueError("leading (batch, head) dimensions differ")
+    outs = None
+    for idx in np.ndindex(*lead):
+        o = fn(Q[idx], *[r[idx] for r in rest], **kw)
+        if outs is None:
+            outs = np.empty(lead + o.shape, dtype=np.float64)
+        outs[idx] = o
+    return outs
+
+
+def sdpa_weights_ref(Q, K, causal=False, q_index=None):
+    """Attention weights for every leading (batch, head) index. Q [..., n_q, d_k], K [..., n_k, d_k]."""
+    return _per_head(sdpa_weights_head, Q, K, causal=causal, q_index=q_index)
+
+
+def sdpa_ref(Q, K, V, causal=False, q_index=None):
+    """Scaled dot-product attention, head by head. Q [..., n_q, d_k], K [..., n_k, d_k], V [..., n_k, d_v]."""
+    return _per_head(sdpa_head, Q, K, V, causal=causal, q_index=q_index)
+
+
+def mha_ref(Xq, Xkv, Wq, Wk, Wv, Wo, h, causal=False):
+    """Multi-head attention: Concat(head_1..head_h) W^O with head_i = Attention(Xq W_i^Q, Xkv W_i^K, Xkv W_i^V).
+
+    Xq [B, n_q, d_model], Xkv [B, n_k, d_model]; Wq, Wk [d_model, h*d_k]; Wv [d_model, h*d_v]; Wo [h*d_v, d_model].
+    Each head projects from the full d_model-wide input with its own column block of the weight matrices.
+    """
+    Xq, Xkv, Wq, Wk, Wv, Wo = (_as_f64(a) for a in (Xq, Xkv, Wq, Wk, Wv, Wo))
+    if Wq.shape[1] % h or Wv.shape[1] % h:
+        raise ValueError("projection widths must be multiples of h")
+    d_k = Wq.shape[1] // h
+    d_v = Wv.shape[1] // h
+    heads = []
+    for i in range(h):
+        qi = Xq @ Wq[:, i * d_k:(i + 1) * d_k]
+        ki = Xkv @ Wk[:, i * d_k:(i + 1) * d_k]
+        vi = Xkv @ Wv[:, i * d_v:(i + 1) * d_v]
+        heads.append(sdpa_ref(qi[:, None], ki[:, None], vi[:, None], causal=causal)[:, 0])
+    concat = np.concatenate(heads, axis=-1)              # head 1 first, along the feature axis
+    return concat @ Wo
+
+
+def sdpa_brute(q, k, v, causal=False):
+    """Pure-Python literal definition for one small head, with no max shift: weight_ij = e^{s_ij} / sum_j e^{s_ij}.
+
+    q, k, v are nested lists (or arrays) [n][d]. Only for tiny cases with moderate scores (e^s must not overflow).
+    Masked positions (j > i under the causal mask) get weight exactly 0 (e^{-inf} = 0).
+    """
+    q = [[float(x) for x in row] for row in q]
+    k = [[float(x) for x in row] for row in k]
+    v = [[float(x) for x in row] for row in v]
+    d_k = len(q[0])
+    n_k = len(k)
+    if causal and len(q) != n_k:
+        raise ValueError("the causal mask is defined for self-attention only (n_q == n_k)")
+    out = []
+    for i, qi in enumerate(q):
+        e = []
+        for j in range(n_k):
+            if causal and j > i:
+                e.append(0.0)
+                continue
+            s = math.fsum(qi[t] * k[j][t] for t in range(d_k)) / math.sqrt(d_k)
+            e.append(math.exp(s))
+        total = math.fsum(e)
+        out.append([math.fsum(e[j] * v[j][c] for j in range(n_k)) / total for c in range(len(v[0]))])
+    return out

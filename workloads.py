@@ -1,0 +1,119 @@
+"""Seeded synthetic inputs shared by the parity tests, the smoke check and the bench.
+
+This module holds no attention arithmetic. It only draws seeded normal samples, quantises them to the storage
+dtype the GPU path consumes (fp32 or bf16, round-to-nearest-even), and hands both sides the same numbers: the raw
+storage (float32 array or bf16 bit patterns as uint16) for the device, and the exact same values widened to float64
+for the oracle. bf16 and fp32 values are exactly representable in float64, so the comparison measures kernel error,
+not input quantisation.
+
+Shapes follow the base model of "Attention Is All You Need": d_model = 512, h = 8, d_k = d_v = 64 (the
+"Multi-Head Attention" section and the "模型变体与消融实验" base-configuration table of the page
+"Transformer：抛弃循环与卷积的序列建模"). The datasets the pages train on are not used: these seeded normal inputs
+stand in for them.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+# Named workloads. Seeds are fixed so that every run (tests, smoke, bench) sees the same numbers.
+WORKLOADS = {
+    # single-head fp32 attention, Q/K/V ~ N(0,1)
+    "sdpa_f32_b1_h1_n16": dict(kind="sdpa", dtype="f32", B=1, h=1, n_q=16, n_k=16, d_k=64, d_v=64,
+                               causal=False, seed=1001),
+    # encoder self-attention MHA: X ~ N(0,1), W ~ N(0, 1/512)
+    "mha_self_bf16_b32_n128_dm512": dict(kind="mha", dtype="bf16", B=32, h=8, n_q=128, n_k=128, d_model=512,
+                                         d_k=64, d_v=64, causal=False, seed=1002),
+    # decoder masked self-attention
+    "sdpa_causal_bf16_b32_h8_n256": dict(kind="sdpa", dtype="bf16", B=32, h=8, n_q=256, n_k=256, d_k=64, d_v=64,
+                                         causal=True, seed=1003),
+    # encoder-decoder cross-attention, 200 decoder positions against 256 encoder positions
+    "sdpa_cross_bf16_b16_h8_nq200_nk256": dict(kind="sdpa", dtype="bf16", B=16, h=8, n_q=200, n_k=256, d_k=64,
+                                               d_v=64, causal=False, seed=1004),
+    # long-sequence self-attention, unmasked and causal over the same tensors
+    "sdpa_bf16_b4_h8_n4096": dict(kind="sdpa", dtype="bf16", B=4, h=8, n_q=4096, n_k=4096, d_k=64, d_v=64,
+                                  causal=False, seed=1005),
+    "sdpa_causal_bf16_b4_h8_n4096": dict(kind="sdpa", dtype="bf16", B=4, h=8, n_q=4096, n_k=4096, d_k=64, d_v=64,
+                                         causal=True, seed=1005),
+}
+
+
+@dataclass
+class Quantised:
+    """One tensor: `raw` is what the device gets, `f64` is the same values for the oracle."""
+    raw: np.ndarray      # float32 array (dtype "f32") or uint16 bf16 bit patterns (dtype "bf16")
+    f64: np.ndarray      # float64 array of exactly the same values
+    dtype: str
+
+    @property
+    def shape(self):
+        return self.f64.shape
+
+
+def f32_to_bf16_bits(x32: np.ndarray) -> np.ndarray:
+    """Round float32 to bf16 (round to nearest, ties to even) and return the 16-bit patterns."""
+    x32 = np.ascontiguousarray(x32, dtype=np.float32)
+    if not np.all(np.isfinite(x32)):
+        raise ValueError("inputs must be finite")
+    u = x32.view(np.uint32).astype(np.uint64)
+    bias = np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))
+    return ((u + bias) >> np.uint64(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns to float64 (exact)."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def quantise(x: np.ndarray, dtype: str) -> Quantised:
+    """Quantise float64 samples to the storage dtype: float64 -> float32 (RNE) [-> bf16 (RNE)]."""
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    if dtype == "f32":
+        return Quantised(raw=x32, f64=x32.astype(np.float64), dtype="f32")
+    if dtype == "bf16":
+        bits = f32_to_bf16_bits(x32)
+        return Quantised(raw=bits, f64=bf16_bits_to_f64(bits), dtype="bf16")
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def _rng(seed: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def make_sdpa_inputs(B, h, n_q, n_k, d_k, d_v, dtype, seed, scale_q=1.0):
+    """Q [B,h,n_q,d_k], K [B,h,n_k,d_k], V [B,h,n_k,d_v], each ~ N(0,1), drawn in the order Q, K, V."""
+    rng = _rng(seed)
+    q = rng.standard_normal((B, h, n_q, d_k)) * scale_q
+    k = rng.standard_normal((B, h, n_k, d_k))
+    v = rng.standard_normal((B, h, n_k, d_v))
+    return {"Q": quantise(q, dtype), "K": quantise(k, dtype), "V": quantise(v, dtype)}
+
+
+def make_mha_inputs(B, n_q, n_k, d_model, h, d_k, d_v, dtype, seed, cross=False):
+    """X ~ N(0,1) [B,n,d_model]; Wq, Wk [d_model, h*d_k], Wv [d_model, h*d_v], Wo [h*d_v, d_model] ~ N(0, 1/d_model).
+
+    Drawn in the order X (then Xkv when `cross`), Wq, Wk, Wv, Wo. For self-attention Xkv is Xq itself.
+    """
+    rng = _rng(seed)
+    xq = rng.standard_normal((B, n_q, d_model))
+    xkv = rng.standard_normal((B, n_k, d_model)) if cross else None
+    sd = np.sqrt(1.0 / d_model)
+    wq = rng.standard_normal((d_model, h * d_k)) * sd
+    wk = rng.standard_normal((d_model, h * d_k)) * sd
+    wv = rng.standard_normal((d_model, h * d_v)) * sd
+    wo = rng.standard_normal((h * d_v, d_model)) * sd
+    out = {"Xq": quantise(xq, dtype)}
+    out["Xkv"] = quantise(xkv, dtype) if cross else out["Xq"]
+    out.update(Wq=quantise(wq, dtype), Wk=quantise(wk, dtype), Wv=quantise(wv, dtype), Wo=quantise(wo, dtype))
+    return out
+
+
+def make_workload(name: str):
+    """Inputs of a named workload (see WORKLOADS)."""
+    w = WORKLOADS[name]
+    if w["kind"] == "sdpa":
+        return make_sdpa_inputs(w["B"], w["h"], w["n_q"], w["n_k"], w["d_k"], w["d_v"], w["dtype"], w["seed"])
+    return make_mha_inputs(w["B"], w["n_q"], w["n_k"], w["d_model"], w["h"], w["d_k"], w["d_v"], w["dtype"],
+                           w["seed"], cross=w["n_q"] != w["n_k"])
