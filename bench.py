@@ -1,0 +1,165 @@
+"""Benchmark of the attention forward on one MI355X; prints ONE JSON line.
+
+A step is one sdpa_forward call (scores, scale, mask, online softmax, weighted sum of V: the whole fused attention)
+over the long-sequence workload B=4, h=8, n_q=n_k=4096, d_k=d_v=64, bf16, unmasked, with Q/K/V ~ N(0,1) seeded and
+already resident in HBM. Metric: attention TFLOP/s = 4*B*h*n_q*n_k*d_k / time, against the bf16 dense MFMA peak.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "attention TFLOP/s (4·B·h·n_q·n_k·d_k) at h=8,d_k=64; % of bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+PROFILES = ROOT / "profiles"
+
+
+def flops_metric(w):
+    return 4.0 * w["B"] * w["h"] * w["n_q"] * w["n_k"] * w["d_k"]
+
+
+def flops_algorithmic(w):
+    # causal: only the n(n+1)/2 allowed (query, key) pairs do work
+    pairs = w["n_q"] * (w["n_q"] + 1) / 2 if w["causal"] else w["n_q"] * w["n_k"]
+    return 2.0 * w["B"] * w["h"] * pairs * (w["d_k"] + w["d_v"])
+
+
+def hbm_bytes(w):
+    es = 2 if w["dtype"] == "bf16" else 4
+    return es * w["B"] * w["h"] * (w["n_q"] * w["d_k"] + w["n_k"] * (w["d_k"] + w["d_v"]) + w["n_q"] * w["d_v"])
+
+
+def measured_traffic(kernel_prefix: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if one exists for this kernel and workload."""
+    f = PROFILES / f"{kernel_prefix}_{workload}_hbm_traffic.json"
+    if not f.exists():
+        return None
+    try:
+        d = json.loads(f.read_text())
+        return d.get("bytes_per_launch")
+    except Exception:
+        return None
+
+
+def cpu_baseline(w, x, budget_s: float):
+    """Time the float64 oracle on whole heads of the same workload until about `budget_s` seconds are spent."""
+    import numpy as np
+
+    from oracle import sdpa_head
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    Q, K, V = x["Q"].f64, x["K"].f64, x["V"].f64
+    heads = [(b, hh) for b in range(w["B"]) for hh in range(w["h"])]
+    done, t_total = 0, 0.0
+    sdpa_head(Q[0, 0, :64], K[0, 0], V[0, 0], False)  # warm
+    # whole heads, cycling over the workload's heads until the time budget is spent
+    while t_total < budget_s:
+        b, hh = heads[done % len(heads)]
+        t0 = time.perf_counter()
+        o = sdpa_head(Q[b, hh], K[b, hh], V[b, hh], w["causal"])
+        t_total += time.perf_counter() - t0
+        done += 1
+        assert np.isfinite(o).all()
+    per_head = flops_metric(w) / (w["B"] * w["h"])
+    return {"value": per_head * done / t_total / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} head evaluations over the workload's {len(heads)} heads ({w['n_q']}x{w['n_k']} "
+                      f"scores each, float64 NumPy), {t_total:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="sdpa_bf16_b4_h8_n4096")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the attention path here is a single-GPU kernel library "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import transformer_head_scaled_02_amd as m
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    m.load_library()
+    w = workloads.WORKLOADS[args.workload]
+    if w["kind"] != "sdpa":
+        raise SystemExit("bench workload must be an sdpa workload")
+    x = workloads.make_workload(args.workload)
+
+    def dev(q):
+        if q.dtype == "bf16":
+            return torch.from_numpy(q.raw.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(q.raw).cuda()
+
+    q, k, v = dev(x["Q"]), dev(x["K"]), dev(x["V"])
+    out = torch.empty(w["B"], w["h"], w["n_q"], w["d_v"], dtype=q.dtype, device="cuda")
+    mask = "causal" if w["causal"] else "none"
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        m.sdpa_forward(q, k, v, mask=mask, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        m.sdpa_forward(q, k, v, mask=mask, out=out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # parity of the last timed output on sampled rows (float64 oracle, same inputs)
+    from oracle import sdpa_ref
+    got = out.float().cpu().numpy()
+    rows = np.array([0, 1, 127, 128, 2047, w["n_q"] - 1])
+    ref = np.stack([sdpa_ref(x["Q"].f64[b, hh, rows], x["K"].f64[b, hh], x["V"].f64[b, hh], w["causal"], q_index=rows)
+                    for b, hh in ((0, 0), (w["B"] - 1, w["h"] - 1))])
+    err = np.abs(np.stack([got[0, 0, rows], got[-1, -1, rows]]) - ref)
+
+    value = flops_metric(w) / (ms * 1e-3) / 1e12
+    achieved = flops_algorithmic(w) / (ms * 1e-3) / 1e12
+    rec = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w["dtype"], "data": "synthetic (seeded N(0,1) Q/K/V, no dataset)",
+        "config": {"workload": args.workload, "B": w["B"], "h": w["h"], "n_q": w["n_q"], "n_k": w["n_k"],
+                   "d_k": w["d_k"], "d_v": w["d_v"], "mask": mask},
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic("attn_fwd_bf16_d64", args.workload),
+                     "kernel": "attn_fwd_bf16_d64", "algorithmic_hbm_bytes": hbm_bytes(w),
+                     "algorithmic_hbm_GBps": round(hbm_bytes(w) / (ms * 1e-3) / 1e9, 1)},
+        "wall_s_timed_region": round(wall, 4),
+        "parity_last_step": {"max_abs": float(err.max()), "mean_abs": float(err.mean())},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, x, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,97 @@
+/* mi355_attn.h - C ABI of the MI355X (gfx950) scaled dot-product / multi-head attention forward library.
+ *
+ * What is computed (sources are web pages about "Attention Is All You Need"):
+ *   Attention(Q, K, V) = softmax(Q K^T / sqrt(d_k)) V
+ *     - "Attention Is All You Need" (lettle.cn translation), section 3.2.1 Scaled Dot-Product Attention, the
+ *       Attention(Q,K,V) equation: dot products of each query with all keys, each divided by sqrt(d_k), a softmax
+ *       over the keys, and the weighted sum of the values.
+ *   Causal mask: for decoder self-attention the score of key j for query i is set to -inf before the softmax when
+ *   j > i, so its weight is exactly 0; position i sees itself and everything before it.
+ *     - "Transformer：抛弃循环与卷积的序列建模" (jiashun-ye.github.io), section "Transformer 中的三种 Attention", and the
+ *       mask matrix M of its training example (section "训练样本").
+ *   MultiHead(Q, K, V) = Concat(head_1, ..., head_h) W^O,  head_i = Attention(Xq W_i^Q, Xkv W_i^K, Xkv W_i^V)
+ *     - same page, section "Multi-Head Attention"; lettle.cn translation section 3.2.2. Queries come from Xq, keys and
+ *       values from Xkv: Xkv == Xq for self-attention, the encoder output for encoder-decoder attention (section
+ *       "Transformer 中的三种 Attention").
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library never allocates, frees or copies
+ *     caller memory and never synchronises the stream. Work is enqueued on `stream` (a hipStream_t; NULL means the
+ *     default stream) and the call returns before it finishes.
+ *   - Tensors are dense, row-major, in the element type `dtype` (ATTN_F32: IEEE float32; ATTN_BF16: bfloat16 bit
+ *     patterns, accumulation in float32). Every pointer must be 16-byte aligned.
+ *   - A non-zero return is an attn_status. Argument errors are detected before any HIP call, and nothing has been
+ *     enqueued or written when they are returned. ATTN_ERR_HIP means a HIP call (the launch) failed; faults while the
+ *     kernels run show up at the caller's next synchronisation, as for any asynchronous HIP work.
+ *   - attn_last_error() gives a thread-local, human-readable detail for the most recent non-OK return.
+ *   - No C++ exception crosses this interface. The library keeps no state besides that thread-local string.
+ */
+#ifndef MI355_ATTN_H
+#define MI355_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID = 1,     /* null pointer, non-positive size, misaligned pointer, output overlapping an input,
+                               unknown mask kind, workspace too small */
+  ATTN_ERR_UNSUPPORTED = 2, /* valid request this library does not implement: dtype other than F32/BF16, head dims
+                               other than d_k = d_v = 64, causal mask with n_q != n_k, sizes beyond the limits below */
+  ATTN_ERR_HIP = 3          /* a HIP runtime call failed */
+} attn_status;
+
+typedef enum { ATTN_MASK_NONE = 0, ATTN_MASK_CAUSAL = 1 } attn_mask_kind;
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
+
+/* Size limits (ATTN_ERR_UNSUPPORTED beyond them). */
+#define ATTN_MAX_SEQ   (1 << 24) /* n_q, n_k */
+#define ATTN_MAX_HEADS 65536     /* B * h */
+
+/* sdpa_forward: scaled dot-product attention of every (batch, head) pair.
+ *   Q   [B, h, n_q, d_k]   queries
+ *   K   [B, h, n_k, d_k]   keys
+ *   V   [B, h, n_k, d_v]   values
+ *   out [B, h, n_q, d_v]   out[b,h,i,:] = sum_j softmax_j(Q[b,h,i,:] . K[b,h,j,:] / sqrt(d_k)) V[b,h,j,:]
+ *   mask_kind: ATTN_MASK_NONE, or ATTN_MASK_CAUSAL (keys j > i excluded; requires n_q == n_k).
+ *   dtype: ATTN_BF16 (bf16 in/out, float32 scores, softmax and accumulation; the softmax weights are rounded to
+ *          bf16 before they multiply V) or ATTN_F32 (float32 throughout).
+ *   d_k and d_v must both be 64. `out` must not overlap Q, K or V. */
+int sdpa_forward(const void* Q, const void* K, const void* V, int mask_kind, void* out, int dtype,
+                 int64_t B, int64_t h, int64_t n_q, int64_t n_k, int64_t d_k, int64_t d_v, void* stream);
+
+/* mha_forward: multi-head attention with learned projections and no biases.
+ *   Xq  [B, n_q, d_model]  query-side input; Xkv [B, n_k, d_model] key/value-side input (may be the same pointer
+ *                          as Xq for self-attention)
+ *   Wq  [d_model, h*d_k]   column block i (columns i*d_k .. i*d_k+d_k-1) is W_i^Q; Wk likewise is W_i^K
+ *   Wv  [d_model, h*d_v]   column block i is W_i^V
+ *   Wo  [h*d_v, d_model]   output projection W^O; the concat orders head 1..h along its rows' index
+ *   out [B, n_q, d_model]  Concat(head_1..head_h) W^O
+ *   workspace: device scratch of at least mha_workspace_size(...) bytes, 16-byte aligned, owned by the caller; it
+ *              holds the projected Q/K/V (head-major) and the concatenated heads, in `dtype`.
+ *   dtype: ATTN_BF16 only (the projections accumulate in float32 and round to bf16).
+ *   Requirements: d_k = d_v = 64, d_model a positive multiple of 64, causal only with n_q == n_k. `out` must not
+ *   overlap any input or the workspace, and the workspace must not overlap any input. */
+int mha_forward(const void* Xq, const void* Xkv, const void* Wq, const void* Wk, const void* Wv, const void* Wo,
+                int mask_kind, void* out, void* workspace, size_t workspace_bytes, int dtype,
+                int64_t B, int64_t n_q, int64_t n_k, int64_t d_model, int64_t h, int64_t d_k, int64_t d_v,
+                void* stream);
+
+/* Bytes of workspace mha_forward needs for these sizes (0 if the sizes are invalid). */
+size_t mha_workspace_size(int dtype, int64_t B, int64_t n_q, int64_t n_k, int64_t h, int64_t d_k, int64_t d_v);
+
+/* Static string naming an attn_status value. */
+const char* attn_status_string(int status);
+
+/* Thread-local detail of the last non-OK return on this thread ("" if none). Valid until the next call on it. */
+const char* attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MI355_ATTN_H */

@@ -1,0 +1,245 @@
+"""Parity of the HIP path (through the C ABI) with the float64 oracle on the same seeded inputs.
+
+Bars: bf16 max-abs <= 2e-2, mean-abs <= 2e-3 (plus normalised rms <= 1e-2); fp32 1e-5 relative. The five named
+workloads run at full size (the two n=4096 ones on sampled query rows plus two whole heads); ragged shapes sweep
+the tile tails; property tests check what the pages fix exactly (causal zeros, future independence, uniform weights
+for identical keys, permutation equivariance, normalisation).
+"""
+import numpy as np
+import pytest
+import torch
+
+import transformer_head_scaled_02_amd as m
+import workloads
+from oracle import mha_ref, sdpa_ref, sdpa_weights_ref
+from tests._helpers import assert_bf16_parity, assert_f32_parity, errors, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs an MI355X")
+    m.load_library()
+
+
+def _sdpa_case(B, h, n_q, n_k, dtype, causal, seed, scale_q=1.0):
+    x = workloads.make_sdpa_inputs(B, h, n_q, n_k, 64, 64, dtype, seed, scale_q=scale_q)
+    q, k, v = (to_dev(x[n]) for n in "QKV")
+    out = m.sdpa_forward(q, k, v, mask="causal" if causal else "none")
+    torch.cuda.synchronize()
+    return x, to_f64(out)
+
+
+# --- the named workloads ------------------------------------------------------------------------------------------
+
+def test_workload_sdpa_f32_b1_h1_n16():
+    w = workloads.WORKLOADS["sdpa_f32_b1_h1_n16"]
+    x, got = _sdpa_case(w["B"], w["h"], w["n_q"], w["n_k"], "f32", w["causal"], w["seed"])
+    assert_f32_parity(got, sdpa_ref(x["Q"].f64, x["K"].f64, x["V"].f64), "f32 n16")
+
+
+def test_workload_mha_self_bf16_b32_n128():
+    w = workloads.WORKLOADS["mha_self_bf16_b32_n128_dm512"]
+    x = workloads.make_workload("mha_self_bf16_b32_n128_dm512")
+    xq = to_dev(x["Xq"])
+    ws = [to_dev(x[n]) for n in ("Wq", "Wk", "Wv", "Wo")]
+    got = to_f64(m.mha_forward(xq, xq, *ws, h=w["h"]))
+    ref = mha_ref(x["Xq"].f64, x["Xq"].f64, x["Wq"].f64, x["Wk"].f64, x["Wv"].f64, x["Wo"].f64, h=w["h"])
+    assert_bf16_parity(got, ref, "mha n128")
+
+
+@pytest.mark.parametrize("name", ["sdpa_causal_bf16_b32_h8_n256", "sdpa_cross_bf16_b16_h8_nq200_nk256"])
+def test_workload_sdpa_full(name):
+    w = workloads.WORKLOADS[name]
+    x, got = _sdpa_case(w["B"], w["h"], w["n_q"], w["n_k"], "bf16", w["causal"], w["seed"])
+    assert_bf16_parity(got, sdpa_ref(x["Q"].f64, x["K"].f64, x["V"].f64, w["causal"]), name)
+
+
+@pytest.mark.parametrize("name", ["sdpa_bf16_b4_h8_n4096", "sdpa_causal_bf16_b4_h8_n4096"])
+def test_workload_sdpa_n4096_sampled(name):
+    w = workloads.WORKLOADS[name]
+    x, got = _sdpa_case(w["B"], w["h"], w["n_q"], w["n_k"], "bf16", w["causal"], w["seed"])
+    Q, K, V = x["Q"].f64, x["K"].f64, x["V"].f64
+    rng = np.random.Generator(np.random.PCG64(7))
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, 4095], rng.choice(4096, 57, replace=False)]))
+    ref_rows = np.stack([sdpa_ref(Q[b, hh, rows], K[b, hh], V[b, hh], w["causal"], q_index=rows)
+                         for b in range(w["B"]) for hh in range(w["h"])])
+    got_rows = got[:, :, rows].reshape(ref_rows.shape)
+    assert_bf16_parity(got_rows, ref_rows, name + " sampled rows")
+    for b, hh in ((0, 0), (w["B"] - 1, w["h"] - 1)):
+        assert_bf16_parity(got[b, hh], sdpa_ref(Q[b, hh], K[b, hh], V[b, hh], w["causal"]), f"{name} head {b},{hh}")
+
+
+# --- ragged shapes and tile tails --------------------------------------------------------------------------------
+
+BF16_SHAPES = [(1, 1, 1, 1, False), (1, 1, 1, 1, True), (1, 2, 17, 17, True), (2, 1, 63, 65, False),
+               (1, 1, 65, 63, False), (1, 3, 127, 129, False), (2, 2, 129, 129, True), (1, 1, 200, 256, False),
+               (1, 1, 255, 255, True), (1, 1, 257, 257, True), (3, 1, 300, 1, False), (1, 1, 1, 300, False),
+               (1, 1, 520, 520, True), (1, 2, 1000, 777, False), (5, 3, 64, 64, True), (1, 1, 128, 4, False)]
+
+
+@pytest.mark.parametrize("B,h,n_q,n_k,causal", BF16_SHAPES)
+def test_bf16_ragged(B, h, n_q, n_k, causal):
+    x, got = _sdpa_case(B, h, n_q, n_k, "bf16", causal, 2000 + n_q + 7 * n_k)
+    assert_bf16_parity(got, sdpa_ref(x["Q"].f64, x["K"].f64, x["V"].f64, causal), f"{(B, h, n_q, n_k, causal)}")
+
+
+F32_SHAPES = [(1, 1, 16, 16, False), (2, 3, 33, 70, False), (1, 1, 65, 65, True), (1, 2, 130, 130, True),
+              (1, 1, 1, 5, False), (2, 1, 100, 1, False), (1, 1, 300, 300, True)]
+
+
+@pytest.mark.parametrize("B,h,n_q,n_k,causal", F32_SHAPES)
+def test_f32_ragged(B, h, n_q, n_k, causal):
+    x, got = _sdpa_case(B, h, n_q, n_k, "f32", causal, 3000 + n_q + 7 * n_k)
+    assert_f32_parity(got, sdpa_ref(x["Q"].f64, x["K"].f64, x["V"].f64, causal), f"{(B, h, n_q, n_k, causal)}")
+
+
+# --- properties the pages fix -------------------------------------------------------------------------------------
+
+def _dev(a, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to("cuda", torch.bfloat16 if dtype == "bf16" else torch.float32)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_values_all_ones_give_ones(dtype, causal):
+    # weights sum to 1, so V = 1 must give O = 1
+    x = workloads.make_sdpa_inputs(2, 2, 150, 150, 64, 64, dtype, 11)
+    q, k = to_dev(x["Q"]), to_dev(x["K"])
+    v = torch.ones_like(k)
+    o = to_f64(m.sdpa_forward(q, k, v, mask="causal" if causal else "none"))
+    if dtype == "bf16":
+        assert np.all(o == 1.0)
+    else:
+        assert np.abs(o - 1).max() <= 1e-6
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_one_hot_values_expose_the_weights(causal):
+    # V = identity rows: O[i, j] is the weight of key j, so the causal zeros are exact and the pattern is checkable
+    n = 48
+    x = workloads.make_sdpa_inputs(1, 2, n, n, 64, 64, "bf16", 12)
+    v = np.zeros((1, 2, n, 64)); v[:, :, np.arange(n), np.arange(n)] = 1.0
+    o = to_f64(m.sdpa_forward(to_dev(x["Q"]), to_dev(x["K"]), _dev(v, "bf16"), mask="causal" if causal else "none"))
+    w = sdpa_weights_ref(x["Q"].f64, x["K"].f64, causal)
+    assert_bf16_parity(o[..., :n], w, "one-hot weights")
+    assert np.all(o[..., n:] == 0.0)
+    if causal:
+        j, i = np.meshgrid(np.arange(n), np.arange(n))
+        w_gpu = o[..., :n]
+        assert np.all(w_gpu[:, :, j > i] == 0.0)
+        assert np.all(w_gpu[:, :, j <= i] > 0.0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("t", [1, 63, 64, 65, 127, 128, 129, 200])
+def test_causal_future_rows_do_not_matter(dtype, t):
+    # rows i < t depend only on keys/values j <= i: overwriting rows >= t must leave them bitwise unchanged
+    n = 300
+    x = workloads.make_sdpa_inputs(1, 2, n, n, 64, 64, dtype, 13)
+    q, k, v = (to_dev(x[s]) for s in "QKV")
+    o1 = m.sdpa_forward(q, k, v, mask="causal").clone()
+    g = torch.Generator(device="cpu").manual_seed(t)
+    k2, v2 = k.clone(), v.clone()
+    k2[:, :, t:] = (torch.randn(k2[:, :, t:].shape, generator=g) * 4).to(k.dtype).to("cuda")
+    v2[:, :, t:] = (torch.randn(v2[:, :, t:].shape, generator=g) * 4).to(v.dtype).to("cuda")
+    o2 = m.sdpa_forward(q, k2, v2, mask="causal")
+    torch.cuda.synchronize()
+    assert torch.equal(o1[:, :, :t], o2[:, :, :t])
+    assert not torch.equal(o1[:, :, t:], o2[:, :, t:])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_identical_keys_give_mean_of_values(causal):
+    n = 200
+    x = workloads.make_sdpa_inputs(1, 1, n, n, 64, 64, "bf16", 14)
+    k = np.repeat(x["K"].f64[:, :, :1], n, axis=2)
+    o = to_f64(m.sdpa_forward(to_dev(x["Q"]), _dev(k, "bf16"), to_dev(x["V"]), mask="causal" if causal else "none"))
+    vals = x["V"].f64
+    ref = (np.cumsum(vals, 2) / np.arange(1, n + 1)[:, None]) if causal else np.repeat(vals.mean(2, keepdims=True), n, 2)
+    # all weights are exactly 1/count: the only errors are fp32 summation and the final bf16 rounding
+    assert np.all(np.abs(o - ref) <= 2.0**-8 * np.abs(ref) + 1e-5)
+
+
+def test_self_attention_permutation_equivariance():
+    n = 333
+    x = workloads.make_sdpa_inputs(2, 2, n, n, 64, 64, "bf16", 15)
+    q, k, v = (to_dev(x[s]) for s in "QKV")
+    perm = torch.from_numpy(np.random.Generator(np.random.PCG64(5)).permutation(n)).cuda()
+    o = m.sdpa_forward(q, k, v)
+    op = m.sdpa_forward(q[:, :, perm].contiguous(), k[:, :, perm].contiguous(), v[:, :, perm].contiguous())
+    assert_bf16_parity(to_f64(op), to_f64(o[:, :, perm]), "permutation")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_large_scores_stay_finite(dtype):
+    # Q x 30 puts scores far beyond where an unshifted fp32 exp overflows
+    x, got = _sdpa_case(1, 2, 130, 190, dtype, False, 16, scale_q=30.0)
+    ref = sdpa_ref(x["Q"].f64, x["K"].f64, x["V"].f64)
+    (assert_bf16_parity if dtype == "bf16" else assert_f32_parity)(got, ref, "large scores")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_no_writes_outside_the_output(dtype):
+    # guard bands on both sides of `out` must be untouched (tail rows n_q=200 are not a tile multiple)
+    B, h, n_q, n_k = 2, 3, 200, 130
+    x = workloads.make_sdpa_inputs(B, h, n_q, n_k, 64, 64, dtype, 17)
+    q, k, v = (to_dev(x[s]) for s in "QKV")
+    pad = 4096
+    buf = torch.full((pad + B * h * n_q * 64 + pad,), 777.0, dtype=q.dtype, device="cuda")
+    out = buf[pad:pad + B * h * n_q * 64].view(B, h, n_q, 64)
+    m.sdpa_forward(q, k, v, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(buf[:pad] == 777.0) and torch.all(buf[-pad:] == 777.0)
+    ref = sdpa_ref(x["Q"].f64, x["K"].f64, x["V"].f64)
+    (assert_bf16_parity if dtype == "bf16" else assert_f32_parity)(to_f64(out), ref, "guard band")
+
+
+# --- multi-head attention -----------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("B,n_q,n_k,d_model,h,causal,cross", [
+    (2, 50, 77, 512, 8, False, True), (2, 100, 100, 512, 8, True, False), (3, 37, 37, 128, 2, False, False),
+    (1, 64, 64, 64, 1, False, False), (2, 90, 90, 1024, 16, False, False), (4, 129, 260, 256, 4, False, True)])
+def test_mha_shapes(B, n_q, n_k, d_model, h, causal, cross):
+    x = workloads.make_mha_inputs(B, n_q, n_k, d_model, h, 64, 64, "bf16", 21 + n_q, cross=cross)
+    xq, xkv = to_dev(x["Xq"]), to_dev(x["Xkv"])
+    ws = [to_dev(x[n]) for n in ("Wq", "Wk", "Wv", "Wo")]
+    got = to_f64(m.mha_forward(xq, xkv, *ws, h=h, mask="causal" if causal else "none"))
+    ref = mha_ref(x["Xq"].f64, x["Xkv"].f64, x["Wq"].f64, x["Wk"].f64, x["Wv"].f64, x["Wo"].f64, h=h, causal=causal)
+    assert_bf16_parity(got, ref, f"mha {(B, n_q, n_k, d_model, h, causal, cross)}")
+
+
+def test_mha_concat_order_closed_form():
+    # Wq = Wk = 0 -> uniform weights; Wv = I -> head i is the mean of X's column block i; in-order concat gives
+    # mean(X), so out = mean(X) Wo for every row
+    B, n, d_model, h = 2, 40, 512, 8
+    x = workloads.make_mha_inputs(B, n, n, d_model, h, 64, 64, "bf16", 22)
+    xq = to_dev(x["Xq"])
+    z = torch.zeros(d_model, d_model, dtype=torch.bfloat16, device="cuda")
+    eye = torch.eye(d_model, dtype=torch.bfloat16, device="cuda")
+    got = to_f64(m.mha_forward(xq, xq, z, z, eye, to_dev(x["Wo"]), h=h))
+    mean = x["Xq"].f64.mean(1, keepdims=True)
+    # the concat is rounded to bf16 before W^O, as the oracle is not: compare against both orders of rounding
+    ref = np.broadcast_to(mean @ x["Wo"].f64, got.shape)
+    e = errors(got, ref)
+    assert e["max_abs"] <= 2e-2 and e["mean_abs"] <= 2e-3, e
+    wrong = np.broadcast_to(np.concatenate(np.split(mean, h, axis=-1)[::-1], -1) @ x["Wo"].f64, got.shape)
+    assert errors(got, wrong)["mean_abs"] > 1e-2
+
+
+def test_mha_workspace_reuse_and_out_argument():
+    B, n, d_model, h = 2, 70, 512, 8
+    x = workloads.make_mha_inputs(B, n, n, d_model, h, 64, 64, "bf16", 23)
+    xq = to_dev(x["Xq"])
+    ws = [to_dev(x[k]) for k in ("Wq", "Wk", "Wv", "Wo")]
+    need = m.mha_workspace_size(B, n, n, h)
+    work = torch.empty(need, dtype=torch.uint8, device="cuda")
+    out = torch.empty(B, n, d_model, dtype=torch.bfloat16, device="cuda")
+    a = m.mha_forward(xq, xq, *ws, h=h, out=out, workspace=work).clone()
+    b = m.mha_forward(xq, xq, *ws, h=h, out=out, workspace=work)
+    assert torch.equal(a, b)
+    with pytest.raises(m.AttnError):
+        m.mha_forward(xq, xq, *ws, h=h, workspace=work[:need - 16])

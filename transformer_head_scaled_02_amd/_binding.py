@@ -1,0 +1,163 @@
+"""ctypes binding over libmi355_attn.so: argument marshalling only.
+
+Every step of the computation runs in the library's HIP kernels. torch provides the device buffers and the current
+stream; this module checks shapes, dtypes and devices, passes raw pointers, and raises on a non-OK status. If the
+library has not been built, loading fails loudly: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+import torch
+
+LIB_PATH = Path(__file__).resolve().parent / "libmi355_attn.so"
+
+ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
+ATTN_MASK_NONE, ATTN_MASK_CAUSAL = 0, 1
+ATTN_F32, ATTN_BF16 = 0, 1
+
+# every symbol include/mi355_attn.h declares
+EXPORTED = ("sdpa_forward", "mha_forward", "mha_workspace_size", "attn_status_string", "attn_last_error")
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+def load_library(path: Path | str | None = None) -> ctypes.CDLL:
+    """Load libmi355_attn.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = Path(path) if path is not None else LIB_PATH
+    if not p.exists():
+        raise ImportError(f"{p} is missing: build it with `python -m transformer_head_scaled_02_amd.build` "
+                          "(or __graft_entry__.build()); there is no non-HIP fallback")
+    lib = ctypes.CDLL(str(p))
+    i64, vp, ci, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.sdpa_forward.argtypes = [vp, vp, vp, ci, vp, ci, i64, i64, i64, i64, i64, i64, vp]
+    lib.sdpa_forward.restype = ci
+    lib.mha_forward.argtypes = [vp, vp, vp, vp, vp, vp, ci, vp, vp, sz, ci, i64, i64, i64, i64, i64, i64, i64, vp]
+    lib.mha_forward.restype = ci
+    lib.mha_workspace_size.argtypes = [ci, i64, i64, i64, i64, i64, i64]
+    lib.mha_workspace_size.restype = sz
+    lib.attn_status_string.argtypes = [ci]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_last_error.argtypes = []
+    lib.attn_last_error.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != ATTN_OK:
+        lib = load_library()
+        raise AttnError(status, f"{lib.attn_status_string(status).decode()}: {lib.attn_last_error().decode()}")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _mask_code(mask) -> int:
+    if mask in (None, "none", ATTN_MASK_NONE, False):
+        return ATTN_MASK_NONE
+    if mask in ("causal", ATTN_MASK_CAUSAL, True):
+        return ATTN_MASK_CAUSAL
+    raise ValueError(f"mask must be 'none' or 'causal', got {mask!r}")
+
+
+def _dev_tensor(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream_handle(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def sdpa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask="none",
+                 out: torch.Tensor | None = None) -> torch.Tensor:
+    """softmax(q k^T / sqrt(d_k)) v per (batch, head). q [B,h,n_q,64], k/v [B,h,n_k,64] -> [B,h,n_q,64]."""
+    lib = load_library()
+    q, k, v = _dev_tensor(q, "q"), _dev_tensor(k, "k"), _dev_tensor(v, "v")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, h, n, d]")
+    if not (q.dtype == k.dtype == v.dtype) or not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must share dtype and device")
+    B, h, n_q, d_k = q.shape
+    n_k, d_v = k.shape[2], v.shape[3]
+    if k.shape != (B, h, n_k, d_k) or v.shape[:3] != (B, h, n_k):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    if out is None:
+        out = torch.empty((B, h, n_q, d_v), dtype=q.dtype, device=q.device)
+    else:
+        out = _dev_tensor(out, "out")
+        if out.shape != (B, h, n_q, d_v) or out.dtype != q.dtype or out.device != q.device:
+            raise ValueError("out has the wrong shape, dtype or device")
+    _check(lib.sdpa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), _mask_code(mask), out.data_ptr(),
+                            _dtype_code(q), B, h, n_q, n_k, d_k, d_v, _stream_handle(q.device)))
+    return out
+
+
+def mha_workspace_size(B: int, n_q: int, n_k: int, h: int, d_k: int = 64, d_v: int = 64,
+                       dtype: torch.dtype = torch.bfloat16) -> int:
+    lib = load_library()
+    code = ATTN_BF16 if dtype == torch.bfloat16 else ATTN_F32
+    return int(lib.mha_workspace_size(code, B, n_q, n_k, h, d_k, d_v))
+
+
+def mha_forward(xq: torch.Tensor, xkv: torch.Tensor, wq: torch.Tensor, wk: torch.Tensor, wv: torch.Tensor,
+                wo: torch.Tensor, h: int, mask="none", out: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Concat(head_1..head_h) W^O with head_i = Attention(xq W_i^Q, xkv W_i^K, xkv W_i^V); no biases.
+
+    xq [B,n_q,d_model], xkv [B,n_k,d_model] (pass xq again for self-attention), wq/wk [d_model, h*d_k],
+    wv [d_model, h*d_v], wo [h*d_v, d_model] -> [B, n_q, d_model]. `workspace` (uint8, at least
+    mha_workspace_size bytes) may be passed in to avoid an allocation.
+    """
+    lib = load_library()
+    ts = [_dev_tensor(t, n) for t, n in ((xq, "xq"), (xkv, "xkv"), (wq, "wq"), (wk, "wk"), (wv, "wv"), (wo, "wo"))]
+    xq, xkv, wq, wk, wv, wo = ts
+    if len({t.dtype for t in ts}) != 1 or len({t.device for t in ts}) != 1:
+        raise ValueError("all inputs must share dtype and device")
+    if xq.dim() != 3 or xkv.dim() != 3:
+        raise ValueError("xq and xkv must be [B, n, d_model]")
+    B, n_q, d_model = xq.shape
+    n_k = xkv.shape[1]
+    if xkv.shape != (B, n_k, d_model) or wq.shape[0] != d_model or wq.shape[1] % h or wv.shape[1] % h:
+        raise ValueError("shape mismatch")
+    d_k, d_v = wq.shape[1] // h, wv.shape[1] // h
+    if wk.shape != wq.shape or wv.shape[0] != d_model or wo.shape != (h * d_v, d_model):
+        raise ValueError("weight shape mismatch")
+    need = mha_workspace_size(B, n_q, n_k, h, d_k, d_v, xq.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=xq.device)
+    else:
+        workspace = _dev_tensor(workspace, "workspace")
+    if out is None:
+        out = torch.empty((B, n_q, d_model), dtype=xq.dtype, device=xq.device)
+    else:
+        out = _dev_tensor(out, "out")
+        if out.shape != (B, n_q, d_model) or out.dtype != xq.dtype:
+            raise ValueError("out has the wrong shape or dtype")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.mha_forward(xq.data_ptr(), xkv.data_ptr(), wq.data_ptr(), wk.data_ptr(), wv.data_ptr(), wo.data_ptr(),
+                           _mask_code(mask), out.data_ptr(), workspace.data_ptr(), ws_bytes, _dtype_code(xq),
+                           B, n_q, n_k, d_model, h, d_k, d_v, _stream_handle(xq.device)))
+    return out

@@ -1,0 +1,108 @@
+// Scaled dot-product attention forward in fp32 throughout, d_k = d_v = 64, for gfx950.
+//
+// Same mathematics as the bf16 kernel (softmax(Q K^T / sqrt(64)) V per head, optional causal mask; "Attention Is All
+// You Need" (lettle.cn translation), section 3.2.1), but every value stays fp32, including the softmax weights that
+// multiply V. This path serves small fp32 problems, so it is a plain VALU kernel: one thread per query row keeps q and
+// its output accumulator in registers, key/value tiles are staged in LDS and read as wave-wide broadcasts, and the
+// softmax is streamed tile by tile (running max, rescaled running sum).
+#include "device_common.h"
+#include "launch.h"
+
+#include <math.h>
+
+namespace mi355 {
+namespace {
+
+constexpr int kD = 64;
+constexpr int kBQ = 64;   // queries per workgroup (one per thread)
+constexpr int kBK = 32;   // keys per tile
+
+__global__ __launch_bounds__(kBQ) void attn_fwd_f32_d64(AttnArgs a, int n_qblocks, float c) {
+  __shared__ __attribute__((aligned(16))) float Ks[kBK * kD];
+  __shared__ __attribute__((aligned(16))) float Vs[kBK * kD];
+
+  const int tid = threadIdx.x;
+  const int blk = xcd_remap(blockIdx.x, gridDim.x);
+  int qb = blk % n_qblocks;
+  const int bh = blk / n_qblocks;
+  if (a.causal) qb = n_qblocks - 1 - qb;
+  const int b = bh / a.H, hh = bh % a.H;
+  const int n_q = a.n_q, n_k = a.n_k;
+  const float* Qp = static_cast<const float*>(a.Q) + (int64_t)bh * a.q_stride_bh;
+  const float* Kp = static_cast<const float*>(a.K) + (int64_t)bh * a.k_stride_bh;
+  const float* Vp = static_cast<const float*>(a.V) + (int64_t)bh * a.k_stride_bh;
+  float* Op = static_cast<float*>(a.O) + b * a.o_stride_b + hh * a.o_stride_h;
+
+  const int q0 = qb * kBQ;
+  const int qi = q0 + tid;
+  float q[kD], o[kD];
+#pragma unroll
+  for (int d = 0; d < kD; d += 4) {
+    const float4 v = qi < n_q ? *reinterpret_cast<const float4*>(Qp + (int64_t)qi * kD + d) : float4{0, 0, 0, 0};
+    q[d] = v.x; q[d + 1] = v.y; q[d + 2] = v.z; q[d + 3] = v.w;
+    o[d] = o[d + 1] = o[d + 2] = o[d + 3] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+
+  int n_end = n_k;
+  if (a.causal) n_end = min(n_k, q0 + kBQ);  // keys after the block's last query are never needed
+  for (int k0 = 0; k0 < n_end; k0 += kBK) {
+    __syncthreads();
+    // 32 rows x 64 floats per tensor = 512 float4 chunks, 8 per thread; rows past n_k load as zeros
+    for (int ch = tid; ch < kBK * kD / 4; ch += kBQ) {
+      const int r = ch / (kD / 4), col = (ch % (kD / 4)) * 4;
+      const bool ok = k0 + r < n_k;
+      const float4 z = {0, 0, 0, 0};
+      *reinterpret_cast<float4*>(&Ks[r * kD + col]) = ok ? *reinterpret_cast<const float4*>(Kp + (int64_t)(k0 + r) * kD + col) : z;
+      *reinterpret_cast<float4*>(&Vs[r * kD + col]) = ok ? *reinterpret_cast<const float4*>(Vp + (int64_t)(k0 + r) * kD + col) : z;
+    }
+    __syncthreads();
+
+    float s[kBK];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kBK; ++j) {
+      float acc = 0.f;
+#pragma unroll
+      for (int d = 0; d < kD; ++d) acc = fmaf(q[d], Ks[j * kD + d], acc);
+      const int key = k0 + j;
+      if (key >= n_k || (a.causal && key > qi)) acc = -INFINITY;
+      s[j] = acc;
+      mx = fmaxf(mx, acc);
+    }
+    const float m_new = fmaxf(m, mx * c);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = fast_exp2(m - m_use);
+    m = m_new;
+    l *= alpha;
+#pragma unroll
+    for (int d = 0; d < kD; ++d) o[d] *= alpha;
+#pragma unroll
+    for (int j = 0; j < kBK; ++j) {
+      const float p = fast_exp2(fmaf(s[j], c, -m_use));
+      l += p;
+#pragma unroll
+      for (int d = 0; d < kD; ++d) o[d] = fmaf(p, Vs[j * kD + d], o[d]);
+    }
+  }
+  if (qi < n_q) {
+    const float inv = 1.0f / l;
+    float* orow = Op + (int64_t)qi * a.o_stride_row;
+#pragma unroll
+    for (int d = 0; d < kD; d += 4)
+      *reinterpret_cast<float4*>(orow + d) = float4{o[d] * inv, o[d + 1] * inv, o[d + 2] * inv, o[d + 3] * inv};
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd_f32(const AttnArgs& a, hipStream_t stream) {
+  const int n_qblocks = (a.n_q + kBQ - 1) / kBQ;
+  const int64_t nblocks = (int64_t)n_qblocks * a.B * a.H;
+  if (nblocks <= 0 || nblocks > 0x7fffffff) return hipErrorInvalidValue;
+  const float c = (float)(1.4426950408889634 / 8.0);  // log2(e) / sqrt(64)
+  hipLaunchKernelGGL(attn_fwd_f32_d64, dim3((unsigned)nblocks), dim3(kBQ), 0, stream, a, n_qblocks, c);
+  return hipGetLastError();
+}
+
+}  // namespace mi355

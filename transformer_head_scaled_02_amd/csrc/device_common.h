@@ -1,0 +1,58 @@
+// Device helpers shared by the gfx950 kernels: vector types, MFMA wrappers, bf16 packing, cross-lane ops and the
+// XCD-aware workgroup remap.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mi355 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// D(32x32, f32) += A(32x16, bf16) * B(16x32, bf16), one wave.
+// Lane l supplies A[l%32][8*(l/32) + j] and B[8*(l/32) + j][l%32] for j = 0..7; it receives
+// D[8*(r/4) + 4*(l/32) + r%4][l%32] in accumulator register r = 0..15. (Checked against a host matmul on gfx950.)
+__device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Two fp32 values -> two bf16 (round to nearest even), packed low/high.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  bf16x2 r = __builtin_convertvector(v, bf16x2);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// v_permlane32_swap with the same value in both operands: r[0] and r[1] together hold this lane's value and the
+// value of the lane 32 away (lanes < 32: r[0] own, r[1] partner; lanes >= 32: r[0] partner, r[1] own).
+__device__ __forceinline__ float max_with_partner32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_with_partner32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2). Map the hardware block id so that
+// every XCD receives one contiguous range of logical block ids: neighbouring logical blocks (same head, same K/V)
+// then share an L2. A bijection on [0, nblocks).
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+  constexpr int kXcds = 8;
+  const int per = nblocks / kXcds, rem = nblocks % kXcds;
+  const int xcd = bid % kXcds, slot = bid / kXcds;
+  return xcd * per + (xcd < rem ? xcd : rem) + slot;
+}
+
+}  // namespace mi355

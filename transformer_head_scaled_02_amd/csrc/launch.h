@@ -1,0 +1,38 @@
+// Internal (C++) launch interface between the C-ABI host layer and the kernels. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mi355 {
+
+// One attention problem over [B, H] heads of width 64. Q/K/V rows are dense (64 elements); the output row of query i
+// of head (b, h) starts at O + b*o_stride_b + h*o_stride_h + i*o_stride_row (elements), which covers both the
+// [B,h,n_q,64] layout and the concatenated [B,n_q,h*64] layout.
+struct AttnArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  void* O;
+  int B, H, n_q, n_k;
+  int64_t q_stride_bh, k_stride_bh;   // elements between consecutive (b,h) heads of Q and of K/V
+  int64_t o_stride_b, o_stride_h, o_stride_row;
+  int causal;
+};
+
+hipError_t launch_attn_fwd_bf16(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_attn_fwd_f32(const AttnArgs& a, hipStream_t stream);
+
+// C = A[M,K] * W[K,N] in bf16 with fp32 accumulation, up to three independent problems in one launch.
+// Row-major C (ldc = N) when head_seq == 0; otherwise "head-major": column n of row m goes to
+// C[((m / head_seq) * (N / 64) + n / 64) * head_seq + m % head_seq][n % 64], i.e. [B, N/64, head_seq, 64].
+struct GemmProblem {
+  const void* A;
+  const void* W;
+  void* C;
+  int M, N, K;
+  int head_seq;
+};
+hipError_t launch_gemm_bf16(const GemmProblem* probs, int nprobs, hipStream_t stream);
+
+}  // namespace mi355
