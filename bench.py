@@ -39,16 +39,43 @@ def hbm_bytes(w):
     return es * w["B"] * w["h"] * (w["n_q"] * w["d_k"] + w["n_k"] * (w["d_k"] + w["d_v"]) + w["n_q"] * w["d_v"])
 
 
-def measured_traffic(kernel_prefix: str, workload: str):
-    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if one exists for this kernel and workload."""
-    f = PROFILES / f"{kernel_prefix}_{workload}_hbm_traffic.json"
+KERNEL_SOURCES = ("transformer_head_scaled_02_amd/csrc/attn_fwd_bf16.hip",
+                  "transformer_head_scaled_02_amd/csrc/device_common.h")
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        h.update((ROOT / rel).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary for this kernel and workload, or None when
+    there is none or the kernel source has changed since the counters were taken."""
+    f = PROFILES / f"{kernel}_{workload}_hbm_traffic.json"
     if not f.exists():
         return None
     try:
         d = json.loads(f.read_text())
-        return d.get("bytes_per_launch")
     except Exception:
         return None
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("bytes_per_launch")
+
+
+def copy_calibration(nbytes: int = 512 << 20, reps: int = 3):
+    """A plain device-to-device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
 
 
 def cpu_baseline(w, x, budget_s: float):
@@ -87,6 +114,8 @@ def main():
     ap.add_argument("--workload", default="sdpa_bf16_b4_h8_n4096")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain copy of known size (for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the attention path here is a single-GPU kernel library "
@@ -102,6 +131,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     m.load_library()
     w = workloads.WORKLOADS[args.workload]
     if w["kind"] != "sdpa":
@@ -151,6 +183,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic("attn_fwd_bf16_d64", args.workload),
+                     "kernel_source_hash": kernel_source_hash(),
                      "kernel": "attn_fwd_bf16_d64", "algorithmic_hbm_bytes": hbm_bytes(w),
                      "algorithmic_hbm_GBps": round(hbm_bytes(w) / (ms * 1e-3) / 1e9, 1)},
         "wall_s_timed_region": round(wall, 4),

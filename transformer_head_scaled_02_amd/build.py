@@ -21,6 +21,11 @@ HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
     # keep the compiler from emitting packed-fp32 VALU instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the softmax rescales them with VALU ops, which cannot address AGPRs
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
+    # no NaN inputs are supported (they are not valid attention inputs): fmaxf then maps directly onto v_max3_f32
+    # without canonicalising its operands
+    "-fno-honor-nans",
 ]
 
 

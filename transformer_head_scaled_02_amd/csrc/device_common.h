@@ -28,6 +28,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// Two non-negative finite fp32 values -> two bf16, rounded to nearest (ties away from zero) with one integer add each
+// and one byte permute: adding 0x8000 to the bit pattern carries into the kept half exactly when the dropped half is
+// at least half an ulp. (v_cvt_pk_bf16_f32 costs several times more VALU cycles on gfx950.)
+__device__ __forceinline__ uint32_t pack_bf16x2_nonneg(float lo, float hi) {
+  const uint32_t a = __float_as_uint(lo) + 0x8000u, b = __float_as_uint(hi) + 0x8000u;
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);  // bytes 2,3 of a (low half) and of b (high half)
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
@@ -44,6 +52,15 @@ __device__ __forceinline__ float sum_with_partner32(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ds_read_b64_tr_b16: every lane passes the LDS address of 4 consecutive 16-bit elements. Within each group of 16
+// lanes, output lane i receives component j from source lane 4j + i/4, element i%4. (Checked on gfx950.) So if
+// source lane 4j + t of a group points at row (r0 + j), column (c0 + 4t) of a row-major tile, output lane i gets
+// the 4 elements of column c0 + i in rows r0 .. r0+3: a transposed read.
+__device__ __forceinline__ bf16x4 lds_read_tr16x4(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+}
 
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2). Map the hardware block id so that
 // every XCD receives one contiguous range of logical block ids: neighbouring logical blocks (same head, same K/V)
