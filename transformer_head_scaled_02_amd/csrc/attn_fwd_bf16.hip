@@ -7,23 +7,28 @@
 //
 // Design (a workgroup of NW waves owns NW*32 queries of one head; keys are streamed in tiles of 64):
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: a wave's 32 queries sit in the
-//    lane index (lanes l and l+32 both own query l%32), keys in the accumulator registers. The row softmax reduces
-//    over registers plus one v_permlane32_swap, and the fp32 scores packed to bf16 are directly the B operand of the
-//    second product O^T = V^T P^T: the n x n score matrix never leaves registers.
+//    lane index (lanes l and l+32 both own query l%32), keys in the accumulator registers. The fp32 exponentials
+//    packed to bf16 are directly the B operand of the second product O^T = V^T P^T: the n x n score matrix never
+//    leaves registers.
 //  * K and V tiles go HBM -> LDS with global_load_lds_dwordx4 (no register staging, no LDS store instructions) into
 //    a STAGES-deep ring, so a tile's loads have STAGES-1 tiles of compute to land; one barrier per tile. Each wave
 //    issues 16/NW of the 16 one-kilobyte copies of a tile from a scalar tile base and fixed per-lane offsets. Rows
 //    are unpadded (128 B) with an XOR chunk swizzle that keeps the K row reads and the V transpose reads
 //    (ds_read_b64_tr_b16) free of bank conflicts.
-//  * The softmax is VALU-bound on this chip (v_exp_f32 alone costs more SIMD cycles than a tile's MFMAs per
-//    score), so the code minimises VALU instructions: the exponent argument is one v_fmamk_f32, P is packed with
-//    v_cvt_pk_bf16_f32, the row sum is accumulated on the matrix core (v_mfma_f32_16x16x32_bf16 with a 0/1
-//    selector operand) from the very bf16 P that multiplies V, mask-free tiles run mask-free code, and the launch
-//    keeps four waves per SIMD so other waves' MFMAs overlap each wave's VALU work.
-//  * Online softmax in the exp2 domain: p = exp2(s*c - m) with c = log2(e)/sqrt(64). m is a per-row offset raised
-//    only when a tile's row max exceeds it by more than 2^8 (the rescale branch is skipped when no row of the wave
-//    needs it, and the decision is per row, so a row never depends on other rows' keys); p <= 256 is exact enough
-//    in bf16 and the fp32 sums.
+//  * The softmax runs on the VALU, which on this chip is busier than the matrix core at d = 64 (one v_exp_f32 per
+//    score costs about as many SIMD cycles as the score's share of both products), so the steady-state tile spends
+//    only an exp2 and half a v_cvt_pk_bf16_f32 per score:
+//      - the exponent argument s*c - m (c = log2(e)/sqrt(64), m the row's offset) is one v_fmamk_f32 on the fp32
+//        score: the scale is applied to the accumulated score, never to the bf16 inputs, where its rounding would
+//        grow with the size of the scores;
+//      - the row sum of P is accumulated on the matrix core (v_mfma_f32_16x16x32_bf16 with a 0/1 selector operand)
+//        from the very bf16 P that multiplies V, and that per-tile sum also guards the offset: while it stays at
+//        most 2^20 every p of the tile is at most 2^20 and the tile is accepted; otherwise (a rare slow path, and
+//        always on a row's first tile) the row's offset is raised to the tile's row max, the accumulated O and l
+//        are rescaled and the tile's P is recomputed before it touches O. The decision is per row, so a row never
+//        depends on another row's keys.
+//  * The loop is unrolled over the ring so every LDS address is a per-lane base plus an immediate offset, and the
+//    launch keeps four waves per SIMD so other waves' MFMAs overlap each wave's VALU work.
 //  * Key tiles entirely after a wave's last query are skipped (causal), and query blocks run heaviest first.
 #include "device_common.h"
 #include "launch.h"
@@ -31,6 +36,7 @@
 #include <math.h>
 
 #include <type_traits>
+#include <utility>
 
 namespace mi355 {
 namespace {
@@ -38,8 +44,8 @@ namespace {
 constexpr int kD = 64;                      // head width
 constexpr int kBN = 64;                     // keys per tile
 constexpr int kTileElems = kBN * kD;        // one 64 x 64 bf16 tile (K or V), 8 KB
-constexpr float kRescaleThreshold = 8.0f;   // log2 units
-constexpr float kScaleLog2 = (float)(1.4426950408889634 / 8.0);  // log2(e) / sqrt(64); bit pattern 0x3e38aa3b
+constexpr float kScaleLog2 = (float)(1.4426950408889634 / 8.0);  // log2(e) / sqrt(64)
+constexpr float kTileSumLimit = 1048576.0f;  // 2^20: largest accepted per-tile row sum of P
 
 // 16-byte chunk swizzle of tile row r (depends on r mod 16): logical chunk c of row r is stored at chunk c ^ swz(r).
 __device__ __forceinline__ int swz(int r) { return (2 * (r & 3) + ((r >> 2) & 1)) ^ ((r >> 2) & 2); }
@@ -48,9 +54,11 @@ __device__ __forceinline__ int swz(int r) { return (2 * (r & 3) + ((r >> 2) & 1)
 // base + voff(l) and its 16 bytes land at LDS byte address lds + 16*l. Issued as inline assembly with m0 (the LDS
 // destination) set in the same statement, so that the compiler does not treat later LDS reads as possibly reading
 // these bytes (it would then wait for every outstanding global load before the first LDS read of each tile). The
-// kernel orders these copies with explicit vmcnt waits and barriers. Nothing else in this kernel uses m0.
+// kernel orders these copies with explicit vmcnt waits and barriers. Nothing else in this kernel uses m0. An LDS-DMA
+// load needs one wait state after an SALU write of m0 (the s_nop 0, as the compiler emits for its own copies).
 __device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds) : "memory");
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds)
+               : "memory");
 }
 
 template <int N>
@@ -68,14 +76,6 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // the asm-issued tile copies) it would wait for every outstanding global load on every iteration.
 __device__ __forceinline__ void settle(bf16x8& v) { asm volatile("" : "+v"(v)); }
 
-// s * c - m as one VOP2 instruction (v_fmamk_f32 with the literal c): cheaper on the VALU than the VOP3 v_fma_f32
-// the compiler picks for an SGPR-held constant.
-__device__ __forceinline__ float scaled_minus(float s, float neg_m) {
-  float r;
-  asm("v_fmamk_f32 %0, %1, 0x3e38aa3b, %2" : "=v"(r) : "v"(s), "v"(neg_m));
-  return r;
-}
-
 __device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -90,11 +90,32 @@ __device__ __forceinline__ bf16x8 lsum_selector(int lane) {
   return bf16x8{v, v, v, v, v, v, v, v};
 }
 
+// s * c - m, one fused multiply-add. Written as a builtin, not inline assembly: s comes straight from an MFMA, and
+// only instructions the compiler emits itself get the wait states a VALU read of an MFMA result needs.
+__device__ __forceinline__ float scaled_minus(float s, float neg_m) { return __builtin_fmaf(s, kScaleLog2, neg_m); }
+
+// The other lane of this lane's query (lane +- 32) has the flag set.
+__device__ __forceinline__ bool partner32_any(bool x) {
+  const uint32_t v = x ? 1u : 0u;
+  auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return (r[0] | r[1]) != 0u;
+}
+
+template <class F, int... I>
+__device__ __forceinline__ void unroll_impl(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>), in order.
+template <int N, class F>
+__device__ __forceinline__ void unroll(F&& f) {
+  unroll_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 template <int NW, int MINB, int STAGES>
 __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, int n_qblocks) {
   constexpr int kBM = 32 * NW;   // queries per workgroup
   constexpr int kLPW = 16 / NW;  // one-kilobyte tile copies per wave per tile (16 per K+V tile)
-  static_assert(16 % NW == 0, "tile copies split evenly over the waves");
+  static_assert(16 % NW == 0 && kLPW % 2 == 0, "tile copies split evenly, in pairs, over the waves");
   static_assert(STAGES >= 2 && STAGES <= 4, "ring depth");
   __shared__ __attribute__((aligned(16))) uint16_t smem[STAGES * 2 * kTileElems];  // [stage][K | V]
 
@@ -138,19 +159,18 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, i
   const int key_lim = (causal ? min(q, n_k - 1) : n_k - 1) - 4 * g;
 
   // Tile copies: copy gi (0..15) of a tile moves rows 8*(gi%8) .. +7 of K (gi < 8) or V; lane l brings the logical
-  // chunk that belongs at physical chunk l%8 of row 8*(gi%8) + l/8. Rows past n_k read row n_k-1 (their scores are
-  // masked and their weights are zero).
+  // chunk that belongs at physical chunk l%8 of row 8*(gi%8) + l/8. The swizzle repeats every 16 rows, so two
+  // per-lane offsets (rows l/8 and 8 + l/8) serve every copy, the rest of the row offset going into the scalar base.
+  // Rows past n_k read row n_k-1 (their scores are masked and their weights are zero).
   const uint32_t smem_lds = (uint32_t)(uintptr_t)smem;  // LDS byte address of the ring
   const int lrow = lane >> 3;
-  uint32_t ld_voff[kLPW];
-  int ld_row[kLPW];
+  uint32_t ld_voff[2];
 #pragma unroll
-  for (int i = 0; i < kLPW; ++i) {
-    const int gi = wave * kLPW + i;
-    ld_row[i] = 8 * (gi & 7) + lrow;
-    ld_voff[i] = (uint32_t)(ld_row[i] * kD + (((lane & 7) ^ swz(ld_row[i])) << 3)) * 2u;
+  for (int c = 0; c < 2; ++c) {
+    const int row = 8 * c + lrow;
+    ld_voff[c] = (uint32_t)(row * kD + (((lane & 7) ^ swz(row)) << 3)) * 2u;
   }
-  auto issue_tile = [&](int t) {
+  auto issue_tile = [&](int t) __attribute__((always_inline)) {
     const uint32_t stage = smem_lds + (uint32_t)((t % STAGES) * 2 * kTileElems * 2);
     const uint16_t* kt = Kp + (int64_t)t * kBN * kD;
     const uint16_t* vt = Vp + (int64_t)t * kBN * kD;
@@ -158,15 +178,21 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, i
 #pragma unroll
       for (int i = 0; i < kLPW; ++i) {
         const int gi = wave * kLPW + i;
-        lds_dma16(gi < 8 ? kt : vt, ld_voff[i], stage + (gi < 8 ? 0u : kTileElems * 2u) + (uint32_t)(gi & 7) * 1024u);
+        const int c = gi & 7;  // this copy moves rows 8c .. 8c+7
+        lds_dma16((gi < 8 ? kt : vt) + (c >> 1) * 16 * kD, ld_voff[i & 1],
+                  stage + (gi < 8 ? 0u : kTileElems * 2u) + (uint32_t)c * 1024u);
       }
     } else {
+      // Partial tile: from the unshifted tile base, lane offset = row min(row, last_row) with the chunk swizzle of
+      // destination row `row` (the 16-row shift is folded back in, so the 32-bit offset is never negative).
+      const int last_row = n_k - 1 - t * kBN;  // last valid row of this partial tile, >= 0
 #pragma unroll
       for (int i = 0; i < kLPW; ++i) {
         const int gi = wave * kLPW + i;
-        const int r = min(ld_row[i], n_k - 1 - t * kBN);
-        const uint32_t voff = ld_voff[i] + (uint32_t)((r - ld_row[i]) * kD * 2);
-        lds_dma16(gi < 8 ? kt : vt, voff, stage + (gi < 8 ? 0u : kTileElems * 2u) + (uint32_t)(gi & 7) * 1024u);
+        const int c = gi & 7;
+        const int row = 8 * c + lrow;
+        lds_dma16(gi < 8 ? kt : vt, ld_voff[i & 1] + (uint32_t)((min(row, last_row) - (8 * (c & 1) + lrow)) * kD * 2),
+                  stage + (gi < 8 ? 0u : kTileElems * 2u) + (uint32_t)c * 1024u);
       }
     }
   };
@@ -190,83 +216,115 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, i
 
   f32x16 o[2];
   o[0] = o[1] = f32x16{};
-  float m = -INFINITY;
-  f32x4 lacc = f32x4{};
+  float neg_m = 0.f;  // -m, m = the row's exponent offset (log2 units, set by the first tile)
+  float l = 0.f;
 
-  // One tile: S^T = K Q^T, row max and lazy offset raise, P = exp2(s*c - m) packed to bf16, O^T += V^T P^T and the
-  // row sum. Masked tiles give keys past the row's bound the score -inf.
-  auto step = [&](int t, auto masked_tag) {
-    constexpr bool kM = decltype(masked_tag)::value;
-    const uint16_t* stage = smem + (t % STAGES) * 2 * kTileElems;
+  // One tile: S^T = K Q^T, P = exp2(s*c - m) packed to bf16 with its row sums, the offset check, O^T += V^T P^T.
+  // Masked tiles give keys past the row's bound the score -inf. The first tile sets the offset to its row max.
+  auto step = [&](int t, auto stage_c, auto masked_c, auto first_c) __attribute__((always_inline)) {
+    constexpr int kStage = decltype(stage_c)::value;
+    constexpr bool kM = decltype(masked_c)::value;
+    constexpr bool kFirst = decltype(first_c)::value;
+    const uint16_t* stage = smem + kStage * 2 * kTileElems;
     f32x16 s[2];
-    s[0] = s[1] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        s[kb] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(stage + kb * 32 * kD + koff[ks]), qf[ks], s[kb]);
-    // s[kb] register r holds key 32kb + 8(r/4) + 4g + r%4 of the tile
-    if (kM) {
-      const int lim = key_lim - t * kBN;
+    // S^T = K Q^T; s[kb] register r holds key 32kb + 8(r/4) + 4g + r%4 of the tile
+    auto scores = [&]() __attribute__((always_inline)) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
+        s[kb] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(stage + kb * 32 * kD + koff[0]), qf[0], f32x16{});
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = -INFINITY;
-    }
-    float mx[4];
+      for (int ks = 1; ks < 4; ++ks)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) mx[j] = fmaxf(fmaxf(s[0][4 * j], s[0][4 * j + 1]), s[0][4 * j + 2]);
+        for (int kb = 0; kb < 2; ++kb)
+          s[kb] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(stage + kb * 32 * kD + koff[ks]), qf[ks], s[kb]);
+      if (kM) {
+        const int lim = key_lim - t * kBN;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      mx[j] = fmaxf(fmaxf(mx[j], s[0][4 * j + 3]), s[1][4 * j]);
-      mx[j] = fmaxf(fmaxf(mx[j], s[1][4 * j + 1]), s[1][4 * j + 2]);
-      mx[j] = fmaxf(mx[j], s[1][4 * j + 3]);
-    }
-    const float rmax = max_with_partner32(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]))) * kScaleLog2;
-    // Raise a row's offset only when its p would otherwise exceed 2^threshold. The decision is per row (the ballot
-    // only skips the branch when no row needs it).
-    const bool need = rmax > m + kRescaleThreshold;  // implies rmax finite
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      const float alpha = need ? fast_exp2(m - rmax) : 1.f;  // 0 on a row's first tile (m = -inf)
-      m = need ? rmax : m;
-      lacc *= alpha;
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        o[0][r] *= alpha;
-        o[1][r] *= alpha;
+          for (int r = 0; r < 16; ++r)
+            if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = -INFINITY;
       }
-    }
-    const float neg_m = (kM && m == -INFINITY) ? 0.f : -m;  // a fully masked row so far keeps p = 0
+    };
+
     bf16x8 pf[4];
+    f32x4 ts;
+    // P = exp2(s*c - m) in bf16 and the tile's row sum of P
+    auto exponentiate = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const f32x16& sk = s[ks >> 1];
-      const int base = 8 * (ks & 1);
-      uint32_t w[4];
+      for (int ks = 0; ks < 4; ++ks) {
+        const f32x16& sk = s[ks >> 1];
+        const int base = 8 * (ks & 1);
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          w[j] = pack_bf16x2(fast_exp2(scaled_minus(sk[base + 2 * j], neg_m)),
+                             fast_exp2(scaled_minus(sk[base + 2 * j + 1], neg_m)));
+        }
+        pf[ks] = __builtin_bit_cast(bf16x8, (uint4){w[0], w[1], w[2], w[3]});
+      }
+      ts = mfma16x16x32(lsel, pf[0], f32x4{});
+#pragma unroll
+      for (int ks = 1; ks < 4; ++ks) ts = mfma16x16x32(lsel, pf[ks], ts);
+    };
+    // this row's max of s*c over the tile (both lanes of the row)
+    auto row_max = [&]() __attribute__((always_inline)) {
+      float mx[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        w[j] = pack_bf16x2(fast_exp2(scaled_minus(sk[base + 2 * j], neg_m)),
-                           fast_exp2(scaled_minus(sk[base + 2 * j + 1], neg_m)));
-      pf[ks] = __builtin_bit_cast(bf16x8, (uint4){w[0], w[1], w[2], w[3]});
+        mx[j] = fmaxf(fmaxf(fmaxf(s[0][4 * j], s[0][4 * j + 1]), fmaxf(s[0][4 * j + 2], s[0][4 * j + 3])),
+                      fmaxf(fmaxf(s[1][4 * j], s[1][4 * j + 1]), fmaxf(s[1][4 * j + 2], s[1][4 * j + 3])));
+      return max_with_partner32(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]))) * kScaleLog2;
+    };
+
+    scores();
+    if (kFirst) {
+      // the first tile sets the offset to its row max (o and l are still zero: nothing to rescale)
+      neg_m = -row_max();
+      exponentiate();
+    } else {
+      exponentiate();
+      // accepted when 0 <= sum <= limit; as unsigned bit patterns this also rejects inf and NaN (a NaN sum comes
+      // from 0 * inf when another row's p overflowed)
+      bool need = __float_as_uint(ts[0]) > __float_as_uint(kTileSumLimit);
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        // Slow path: S was overwritten by P; recompute it (the tile is still in LDS), raise the offset of the rows
+        // that need it to the tile's row max (never lowering it), rescale O and l, and recompute P. The empty asm
+        // with a memory clobber makes the compiler read the K operands from LDS again instead of keeping all eight
+        // alive across the fast path.
+        asm volatile("" ::: "memory");
+        scores();
+        const float rmax = row_max();
+        need = need || partner32_any(need);  // the same decision for both lanes of a row
+        const float d = need ? fmaxf(rmax + neg_m, 0.f) : 0.f;  // how far m rises
+        const float alpha = fast_exp2(-d);
+        l *= alpha;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          o[0][r] *= alpha;
+          o[1][r] *= alpha;
+        }
+        neg_m -= d;
+        exponentiate();
+      }
     }
+    l += ts[0];
+
     // k-step ks pairs P registers 8(ks%2) .. +7 of key block ks/2 with keys 16ks + 4g + (0..3) and
     // 16ks + 8 + 4g + (0..3): two transpose reads of V rows give the matching V^T operand.
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         const bf16x4 lo = lds_read_tr16x4(stage + ks * 16 * kD + voff[mb][0]);
         const bf16x4 hi = lds_read_tr16x4(stage + ks * 16 * kD + voff[mb][1]);
         o[mb] = mfma32x32x16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pf[ks], o[mb]);
       }
-      lacc = mfma16x16x32(lsel, pf[ks], lacc);
-    }
   };
 
   // Wait until this wave's copies of tile t have landed (tiles after t that were issued may stay in flight), then
   // for every wave's (the barrier), which also frees the stage of tile t-1; then issue tile t + STAGES - 1.
-  auto advance = [&](int t) {
+  auto advance = [&](int t) __attribute__((always_inline)) {
     const int ahead = min(STAGES - 2, nt - 1 - t);  // tiles issued after t
     if (ahead >= 2) wait_vmcnt<2 * kLPW>();
     else if (ahead == 1) wait_vmcnt<kLPW>();
@@ -275,22 +333,40 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, i
     if (t + STAGES - 1 < nt) issue_tile(t + STAGES - 1);
   };
 
+  const std::false_type no;
+  const std::true_type yes;
 #pragma unroll
   for (int t = 0; t < STAGES - 1; ++t)
     if (t < nt) issue_tile(t);
-  int t = 0;
-  for (; t < t_mask; ++t) {
-    advance(t);
-    step(t, std::integral_constant<bool, false>{});
-  }
+  // tile 0 (every wave has at least one tile with a key it may see)
+  advance(0);
+  if (t_mask > 0) step(0, std::integral_constant<int, 0>{}, no, yes);
+  else step(0, std::integral_constant<int, 0>{}, yes, yes);
+  int t = 1;
+  // steady state: groups of STAGES unmasked tiles starting at t = 1 (mod STAGES), so each tile's ring stage is a
+  // compile-time constant
+  for (; t + STAGES <= t_mask; t += STAGES)
+    unroll<STAGES>([&](auto u) __attribute__((always_inline)) {
+      advance(t + u);
+      step(t + u, std::integral_constant<int, (1 + decltype(u)::value) % STAGES>{}, no, no);
+    });
   for (; t < nt; ++t) {
     advance(t);
-    if (t < t_skip) step(t, std::integral_constant<bool, true>{});
+    if (t < t_skip) {
+      const int st = t % STAGES;
+      const bool masked = t >= t_mask;
+      unroll<STAGES>([&](auto u) __attribute__((always_inline)) {
+        if (st == decltype(u)::value) {
+          if (masked) step(t, u, yes, no);
+          else step(t, u, no, no);
+        }
+      });
+    }
   }
 
   // O = O^T / l; lane holds d = 32mb + 8(r/4) + 4g + r%4 of its query.
   if (q < n_q) {
-    const float inv = 1.0f / lacc[0];
+    const float inv = 1.0f / l;
     uint16_t* orow = Op + (int64_t)q * a.o_stride_row;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
