@@ -40,14 +40,18 @@ def hbm_bytes(w):
 
 
 KERNEL_SOURCES = ("transformer_head_scaled_02_amd/csrc/attn_fwd_bf16.hip",
+                  "transformer_head_scaled_02_amd/csrc/attn_tile.h",
                   "transformer_head_scaled_02_amd/csrc/device_common.h")
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel's code: comments and blank lines do not count, so a comment edit keeps the counters."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        h.update((ROOT / rel).read_bytes())
+        text = re.sub(r"//[^\n]*", "", (ROOT / rel).read_text())
+        h.update("\n".join(ln.rstrip() for ln in text.splitlines() if ln.strip()).encode())
     return h.hexdigest()[:16]
 
 

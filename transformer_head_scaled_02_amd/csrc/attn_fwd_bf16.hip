@@ -27,96 +27,27 @@
 //        always on a row's first tile) the row's offset is raised to the tile's row max, the accumulated O and l
 //        are rescaled and the tile's P is recomputed before it touches O. The decision is per row, so a row never
 //        depends on another row's keys.
-//  * The loop is unrolled over the ring so every LDS address is a per-lane base plus an immediate offset, and the
-//    launch keeps four waves per SIMD so other waves' MFMAs overlap each wave's VALU work.
+//  * With H = 2 a wave owns two independent halves of 32 queries: every K and V operand read from LDS feeds two
+//    products, and one half's MFMAs fill the gaps of the other half's softmax chain within the same wave.
+//  * The loop is unrolled over the ring so every LDS address is a per-lane base plus an immediate offset; two
+//    workgroups per CU (two waves per SIMD) let one wave's MFMAs overlap the other's VALU work.
 //  * Key tiles entirely after a wave's last query are skipped (causal), and query blocks run heaviest first.
-#include "device_common.h"
-#include "launch.h"
-
 #include <math.h>
 
-#include <type_traits>
-#include <utility>
+#include "attn_tile.h"
+#include "launch.h"
 
 namespace mi355 {
 namespace {
 
-constexpr int kD = 64;                      // head width
-constexpr int kBN = 64;                     // keys per tile
-constexpr int kTileElems = kBN * kD;        // one 64 x 64 bf16 tile (K or V), 8 KB
-constexpr float kScaleLog2 = (float)(1.4426950408889634 / 8.0);  // log2(e) / sqrt(64)
-constexpr float kTileSumLimit = 1048576.0f;  // 2^20: largest accepted per-tile row sum of P
-
-// 16-byte chunk swizzle of tile row r (depends on r mod 16): logical chunk c of row r is stored at chunk c ^ swz(r).
-__device__ __forceinline__ int swz(int r) { return (2 * (r & 3) + ((r >> 2) & 1)) ^ ((r >> 2) & 2); }
-
-// Global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4, scalar-base form): lane l reads
-// base + voff(l) and its 16 bytes land at LDS byte address lds + 16*l. Issued as inline assembly with m0 (the LDS
-// destination) set in the same statement, so that the compiler does not treat later LDS reads as possibly reading
-// these bytes (it would then wait for every outstanding global load before the first LDS read of each tile). The
-// kernel orders these copies with explicit vmcnt waits and barriers. Nothing else in this kernel uses m0. An LDS-DMA
-// load needs one wait state after an SALU write of m0 (the s_nop 0, as the compiler emits for its own copies).
-__device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds)
-               : "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// This wave's LDS reads are complete, then every wave of the workgroup has arrived. Unlike __syncthreads() it does
-// not wait for outstanding global -> LDS copies (their completion is tracked with explicit vmcnt waits).
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// The Q operands are loaded once, before the tile loop. Passing them through an empty asm statement makes the
-// compiler wait for those loads here, once, instead of at their first use inside the loop, where (not knowing about
-// the asm-issued tile copies) it would wait for every outstanding global load on every iteration.
-__device__ __forceinline__ void settle(bf16x8& v) { asm volatile("" : "+v"(v)); }
-
-__device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-// Row sum on the matrix core: with v_mfma_f32_16x16x32_bf16, lane l supplies B[8(l/16) + j][l%16] from its 8 P
-// values and A[m][8(l/16) + j] from this selector; register i of lane l receives D[4(l/16) + i][l%16]. The selector
-// is 1 where (m/4 + k/8) is even, so D[4(l/16) + i][l%16] sums the P values of the two lanes that hold the keys of
-// query l%32 in the 32x32 layout: every register of every lane gets the sum over this k-step's 16 keys for the lane's
-// own query.
-__device__ __forceinline__ bf16x8 lsum_selector(int lane) {
-  const __bf16 v = ((((lane & 15) >> 2) + (lane >> 4)) & 1) ? (__bf16)0.0f : (__bf16)1.0f;
-  return bf16x8{v, v, v, v, v, v, v, v};
-}
-
-// s * c - m, one fused multiply-add. Written as a builtin, not inline assembly: s comes straight from an MFMA, and
-// only instructions the compiler emits itself get the wait states a VALU read of an MFMA result needs.
-__device__ __forceinline__ float scaled_minus(float s, float neg_m) { return __builtin_fmaf(s, kScaleLog2, neg_m); }
-
-// The other lane of this lane's query (lane +- 32) has the flag set.
-__device__ __forceinline__ bool partner32_any(bool x) {
-  const uint32_t v = x ? 1u : 0u;
-  auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  return (r[0] | r[1]) != 0u;
-}
-
-template <class F, int... I>
-__device__ __forceinline__ void unroll_impl(F& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-// f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>), in order.
-template <int N, class F>
-__device__ __forceinline__ void unroll(F&& f) {
-  unroll_impl(f, std::make_integer_sequence<int, N>{});
-}
-
-template <int NW, int MINB, int STAGES>
+template <int NW, int H, int MINB, int STAGES>
 __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, int n_qblocks) {
-  constexpr int kBM = 32 * NW;   // queries per workgroup
+  constexpr int kQW = 32 * H;    // queries per wave: H independent halves of 32
+  constexpr int kBM = kQW * NW;  // queries per workgroup
   constexpr int kLPW = 16 / NW;  // one-kilobyte tile copies per wave per tile (16 per K+V tile)
   static_assert(16 % NW == 0 && kLPW % 2 == 0, "tile copies split evenly, in pairs, over the waves");
   static_assert(STAGES >= 2 && STAGES <= 4, "ring depth");
+  static_assert(H == 1 || H == 2, "one or two query halves per wave");
   __shared__ __attribute__((aligned(16))) uint16_t smem[STAGES * 2 * kTileElems];  // [stage][K | V]
 
   const int tid = threadIdx.x;
@@ -137,26 +68,33 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, i
   uint16_t* Op = static_cast<uint16_t*>(a.O) + b * a.o_stride_b + hh * a.o_stride_h;
 
   const int q_blk0 = qb * kBM;
-  const int qw0 = q_blk0 + wave * 32;  // first query of this wave
-  const int q = qw0 + li;
+  const int qw0 = q_blk0 + wave * kQW;  // first query of this wave; half h owns queries qw0 + 32h + (0..31)
 
   // Q as the B operand of S^T = K Q^T: lane supplies Q[q][32g + 8ks + j], ks = 0..3 (the same d order as the K
   // operand). Rows at or past n_q are zero.
-  bf16x8 qf[4];
+  bf16x8 qf[H][4];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
-    qf[ks] = q < n_q ? *reinterpret_cast<const bf16x8*>(Qp + (int64_t)q * kD + 32 * g + 8 * ks) : bf16x8{};
+  for (int h = 0; h < H; ++h) {
+    const int q = qw0 + 32 * h + li;
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) settle(qf[ks]);
+    for (int ks = 0; ks < 4; ++ks)
+      qf[h][ks] = q < n_q ? *reinterpret_cast<const bf16x8*>(Qp + (int64_t)q * kD + 32 * g + 8 * ks) : bf16x8{};
+  }
+#pragma unroll
+  for (int h = 0; h < H; ++h)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) settle(qf[h][ks]);
 
   int nt = (n_k + kBN - 1) / kBN;
   if (causal) nt = min(nt, (q_blk0 + kBM - 1) / kBN + 1);
-  // tiles before t_mask need no mask for this wave; tiles from t_skip on lie entirely in this wave's future
+  // tiles before t_mask need no mask for any query of this wave; tiles from t_skip on lie entirely in its future
   const int t_mask = min(causal ? qw0 / kBN : nt, n_k / kBN);
-  const int t_skip = causal ? min(nt, (qw0 + 31) / kBN + 1) : nt;
+  const int t_skip = causal ? min(nt, (qw0 + kQW - 1) / kBN + 1) : nt;
   const int nt_full = n_k / kBN;  // tiles with no row past n_k
   // keys past this bound, counted from the lane's first key 4g of tile 0, are masked
-  const int key_lim = (causal ? min(q, n_k - 1) : n_k - 1) - 4 * g;
+  int key_lim[H];
+#pragma unroll
+  for (int h = 0; h < H; ++h) key_lim[h] = (causal ? min(qw0 + 32 * h + li, n_k - 1) : n_k - 1) - 4 * g;
 
   // Tile copies: copy gi (0..15) of a tile moves rows 8*(gi%8) .. +7 of K (gi < 8) or V; lane l brings the logical
   // chunk that belongs at physical chunk l%8 of row 8*(gi%8) + l/8. The swizzle repeats every 16 rows, so two
@@ -214,112 +152,150 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, i
     }
   const bf16x8 lsel = lsum_selector(lane);
 
-  f32x16 o[2];
-  o[0] = o[1] = f32x16{};
-  float neg_m = 0.f;  // -m, m = the row's exponent offset (log2 units, set by the first tile)
-  float l = 0.f;
+  f32x16 o[H][2];
+  float neg_m[H], l[H];  // -m (m = the row's exponent offset, log2 units, set by the first tile) and the row sum
+#pragma unroll
+  for (int h = 0; h < H; ++h) {
+    o[h][0] = o[h][1] = f32x16{};
+    neg_m[h] = 0.f;
+    l[h] = 0.f;
+  }
 
-  // One tile: S^T = K Q^T, P = exp2(s*c - m) packed to bf16 with its row sums, the offset check, O^T += V^T P^T.
-  // Masked tiles give keys past the row's bound the score -inf. The first tile sets the offset to its row max.
+  // One tile: S^T = K Q^T, P = exp2(s*c - m) packed to bf16 with its row sums, the offset check, O^T += V^T P^T,
+  // for each query half. The K and V operands are read from LDS once and serve every half; while one half's softmax
+  // runs on the VALU, the other half's products keep the matrix core busy. Masked tiles give keys past the row's
+  // bound the score -inf. The first tile sets the offset to its row max.
   auto step = [&](int t, auto stage_c, auto masked_c, auto first_c) __attribute__((always_inline)) {
     constexpr int kStage = decltype(stage_c)::value;
     constexpr bool kM = decltype(masked_c)::value;
     constexpr bool kFirst = decltype(first_c)::value;
     const uint16_t* stage = smem + kStage * 2 * kTileElems;
-    f32x16 s[2];
-    // S^T = K Q^T; s[kb] register r holds key 32kb + 8(r/4) + 4g + r%4 of the tile
-    auto scores = [&]() __attribute__((always_inline)) {
+
+    auto load_k = [&](bf16x8(&ka)[4][2]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        s[kb] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(stage + kb * 32 * kD + koff[0]), qf[0], f32x16{});
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) ka[ks][kb] = *reinterpret_cast<const bf16x8*>(stage + kb * 32 * kD + koff[ks]);
+    };
+    f32x16 s[H][2];
+    // S^T = K Q^T for half h; s[h][kb] register r holds key 32kb + 8(r/4) + 4g + r%4 of the tile
+    auto scores = [&](auto h_c, const bf16x8(&ka)[4][2]) __attribute__((always_inline)) {
+      constexpr int h = decltype(h_c)::value;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s[h][kb] = mfma32x32x16(ka[0][kb], qf[h][0], f32x16{});
 #pragma unroll
       for (int ks = 1; ks < 4; ++ks)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          s[kb] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(stage + kb * 32 * kD + koff[ks]), qf[ks], s[kb]);
+        for (int kb = 0; kb < 2; ++kb) s[h][kb] = mfma32x32x16(ka[ks][kb], qf[h][ks], s[h][kb]);
       if (kM) {
-        const int lim = key_lim - t * kBN;
+        const int lim = key_lim[h] - t * kBN;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = -INFINITY;
+            if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) s[h][kb][r] = -INFINITY;
       }
     };
 
-    bf16x8 pf[4];
-    f32x4 ts;
-    // P = exp2(s*c - m) in bf16 and the tile's row sum of P
-    auto exponentiate = [&]() __attribute__((always_inline)) {
+    bf16x8 pf[H][4];
+    f32x4 ts[H];
+    // P = exp2(s*c - m) in bf16 and the tile's row sum of P, for half h
+    auto exponentiate = [&](auto h_c) __attribute__((always_inline)) {
+      constexpr int h = decltype(h_c)::value;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const f32x16& sk = s[ks >> 1];
+        const f32x16& sk = s[h][ks >> 1];
         const int base = 8 * (ks & 1);
         uint32_t w[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          w[j] = pack_bf16x2(fast_exp2(scaled_minus(sk[base + 2 * j], neg_m)),
-                             fast_exp2(scaled_minus(sk[base + 2 * j + 1], neg_m)));
-        }
-        pf[ks] = __builtin_bit_cast(bf16x8, (uint4){w[0], w[1], w[2], w[3]});
+        for (int j = 0; j < 4; ++j)
+          w[j] = pack_bf16x2(fast_exp2(scaled_minus(sk[base + 2 * j], neg_m[h])),
+                             fast_exp2(scaled_minus(sk[base + 2 * j + 1], neg_m[h])));
+        pf[h][ks] = __builtin_bit_cast(bf16x8, (uint4){w[0], w[1], w[2], w[3]});
       }
-      ts = mfma16x16x32(lsel, pf[0], f32x4{});
+      ts[h] = mfma16x16x32(lsel, pf[h][0], f32x4{});
 #pragma unroll
-      for (int ks = 1; ks < 4; ++ks) ts = mfma16x16x32(lsel, pf[ks], ts);
+      for (int ks = 1; ks < 4; ++ks) ts[h] = mfma16x16x32(lsel, pf[h][ks], ts[h]);
     };
-    // this row's max of s*c over the tile (both lanes of the row)
-    auto row_max = [&]() __attribute__((always_inline)) {
+    // this row's max of s*c over the tile (both lanes of the row), for half h
+    auto row_max = [&](auto h_c) __attribute__((always_inline)) {
+      constexpr int h = decltype(h_c)::value;
       float mx[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        mx[j] = fmaxf(fmaxf(fmaxf(s[0][4 * j], s[0][4 * j + 1]), fmaxf(s[0][4 * j + 2], s[0][4 * j + 3])),
-                      fmaxf(fmaxf(s[1][4 * j], s[1][4 * j + 1]), fmaxf(s[1][4 * j + 2], s[1][4 * j + 3])));
+        mx[j] = fmaxf(fmaxf(fmaxf(s[h][0][4 * j], s[h][0][4 * j + 1]), fmaxf(s[h][0][4 * j + 2], s[h][0][4 * j + 3])),
+                      fmaxf(fmaxf(s[h][1][4 * j], s[h][1][4 * j + 1]), fmaxf(s[h][1][4 * j + 2], s[h][1][4 * j + 3])));
       return max_with_partner32(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]))) * kScaleLog2;
     };
-
-    scores();
-    if (kFirst) {
-      // the first tile sets the offset to its row max (o and l are still zero: nothing to rescale)
-      neg_m = -row_max();
-      exponentiate();
-    } else {
-      exponentiate();
-      // accepted when 0 <= sum <= limit; as unsigned bit patterns this also rejects inf and NaN (a NaN sum comes
-      // from 0 * inf when another row's p overflowed)
-      bool need = __float_as_uint(ts[0]) > __float_as_uint(kTileSumLimit);
-      if (__builtin_amdgcn_ballot_w64(need)) {
-        // Slow path: S was overwritten by P; recompute it (the tile is still in LDS), raise the offset of the rows
-        // that need it to the tile's row max (never lowering it), rescale O and l, and recompute P. The empty asm
-        // with a memory clobber makes the compiler read the K operands from LDS again instead of keeping all eight
-        // alive across the fast path.
-        asm volatile("" ::: "memory");
-        scores();
-        const float rmax = row_max();
-        need = need || partner32_any(need);  // the same decision for both lanes of a row
-        const float d = need ? fmaxf(rmax + neg_m, 0.f) : 0.f;  // how far m rises
-        const float alpha = fast_exp2(-d);
-        l *= alpha;
+    // the softmax of half h, ending with its row sums added to l
+    auto softmax = [&](auto h_c) __attribute__((always_inline)) {
+      constexpr int h = decltype(h_c)::value;
+      if (kFirst) {
+        // the first tile sets the offset to its row max (o and l are still zero: nothing to rescale)
+        neg_m[h] = -row_max(h_c);
+        exponentiate(h_c);
+      } else {
+        exponentiate(h_c);
+        // accepted when 0 <= sum <= limit; as unsigned bit patterns this also rejects inf and NaN (a NaN sum comes
+        // from 0 * inf when another row's p overflowed)
+        const bool need = __float_as_uint(ts[h][0]) > __float_as_uint(kTileSumLimit);
+        if (__builtin_amdgcn_ballot_w64(need)) {
+          // Slow path: S was overwritten by P; recompute it (the tile is still in LDS), raise the offset of the rows
+          // that need it to the tile's row max (never lowering it), rescale O and l, and recompute P. The empty asm
+          // with a memory clobber makes the compiler read the K operands from LDS again instead of keeping them
+          // alive across the fast path.
+          asm volatile("" ::: "memory");
+          {
+            bf16x8 ka[4][2];
+            load_k(ka);
+            scores(h_c, ka);
+          }
+          const float rmax = row_max(h_c);
+          // the same decision for both lanes of a row (computed in every lane: a cross-lane read must not sit
+          // behind a branch on the lane's own flag)
+          const bool partner = partner32_any(need);
+          const bool raise = need || partner;
+          const float d = raise ? fmaxf(rmax + neg_m[h], 0.f) : 0.f;  // how far m rises
+          const float alpha = fast_exp2(-d);
+          l[h] *= alpha;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          o[0][r] *= alpha;
-          o[1][r] *= alpha;
+          for (int r = 0; r < 16; ++r) {
+            o[h][0][r] *= alpha;
+            o[h][1][r] *= alpha;
+          }
+          neg_m[h] -= d;
+          exponentiate(h_c);
         }
-        neg_m -= d;
-        exponentiate();
       }
-    }
-    l += ts[0];
+      l[h] += ts[h][0];
+    };
 
-    // k-step ks pairs P registers 8(ks%2) .. +7 of key block ks/2 with keys 16ks + 4g + (0..3) and
-    // 16ks + 8 + 4g + (0..3): two transpose reads of V rows give the matching V^T operand.
+    {
+      bf16x8 ka[4][2];
+      load_k(ka);
+      unroll<H>([&](auto h_c) __attribute__((always_inline)) { scores(h_c, ka); });
+    }
+    // V^T operands, read once for every half: k-step ks pairs P registers 8(ks%2) .. +7 of key block ks/2 with keys
+    // 16ks + 4g + (0..3) and 16ks + 8 + 4g + (0..3); two transpose reads of V rows give the matching operand.
+    bf16x8 va[4][2];
+    unroll<H>([&](auto h_c) __attribute__((always_inline)) {
+      constexpr int h = decltype(h_c)::value;
+      softmax(h_c);
+      if (h == 0) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+        for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const bf16x4 lo = lds_read_tr16x4(stage + ks * 16 * kD + voff[mb][0]);
-        const bf16x4 hi = lds_read_tr16x4(stage + ks * 16 * kD + voff[mb][1]);
-        o[mb] = mfma32x32x16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pf[ks], o[mb]);
+          for (int mb = 0; mb < 2; ++mb) {
+            const bf16x4 lo = lds_read_tr16x4(stage + ks * 16 * kD + voff[mb][0]);
+            const bf16x4 hi = lds_read_tr16x4(stage + ks * 16 * kD + voff[mb][1]);
+            va[ks][mb] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          }
       }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) o[h][mb] = mfma32x32x16(va[ks][mb], pf[h][ks], o[h][mb]);
+    });
   };
 
   // Wait until this wave's copies of tile t have landed (tiles after t that were issued may stay in flight), then
@@ -338,7 +314,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, i
 #pragma unroll
   for (int t = 0; t < STAGES - 1; ++t)
     if (t < nt) issue_tile(t);
-  // tile 0 (every wave has at least one tile with a key it may see)
+  // tile 0 (every row has at least one key it may see there)
   advance(0);
   if (t_mask > 0) step(0, std::integral_constant<int, 0>{}, no, yes);
   else step(0, std::integral_constant<int, 0>{}, yes, yes);
@@ -365,27 +341,31 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, i
   }
 
   // O = O^T / l; lane holds d = 32mb + 8(r/4) + 4g + r%4 of its query.
-  if (q < n_q) {
-    const float inv = 1.0f / l;
-    uint16_t* orow = Op + (int64_t)q * a.o_stride_row;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+  for (int h = 0; h < H; ++h) {
+    const int q = qw0 + 32 * h + li;
+    if (q < n_q) {
+      const float inv = 1.0f / l[h];
+      uint16_t* orow = Op + (int64_t)q * a.o_stride_row;
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const uint2 w = {pack_bf16x2(o[mb][4 * rg] * inv, o[mb][4 * rg + 1] * inv),
-                         pack_bf16x2(o[mb][4 * rg + 2] * inv, o[mb][4 * rg + 3] * inv)};
-        *reinterpret_cast<uint2*>(orow + 32 * mb + 8 * rg + 4 * g) = w;
-      }
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const uint2 w = {pack_bf16x2(o[h][mb][4 * rg] * inv, o[h][mb][4 * rg + 1] * inv),
+                           pack_bf16x2(o[h][mb][4 * rg + 2] * inv, o[h][mb][4 * rg + 3] * inv)};
+          *reinterpret_cast<uint2*>(orow + 32 * mb + 8 * rg + 4 * g) = w;
+        }
+    }
   }
 }
 
-template <int NW, int MINB, int STAGES>
+template <int NW, int H, int MINB, int STAGES>
 hipError_t launch(const AttnArgs& a, hipStream_t stream) {
-  constexpr int kBM = 32 * NW;
+  constexpr int kBM = 32 * H * NW;
   const int n_qblocks = (a.n_q + kBM - 1) / kBM;
   const int64_t nblocks = (int64_t)n_qblocks * a.B * a.H;
   if (nblocks <= 0 || nblocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((attn_fwd_bf16_d64<NW, MINB, STAGES>), dim3((unsigned)nblocks), dim3(64 * NW), 0, stream, a,
+  hipLaunchKernelGGL((attn_fwd_bf16_d64<NW, H, MINB, STAGES>), dim3((unsigned)nblocks), dim3(64 * NW), 0, stream, a,
                      n_qblocks);
   return hipGetLastError();
 }
@@ -393,10 +373,11 @@ hipError_t launch(const AttnArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, hipStream_t stream) {
-  // Unmasked: 4-wave workgroups (128 queries), four per CU (four waves per SIMD), a 2-tile ring. Causal: the same
-  // workgroups with a 4-tile ring, two per CU, which balanced the triangular work best.
-  if (!a.causal) return launch<4, 4, 2>(a, stream);
-  return launch<4, 2, 4>(a, stream);
+  // Unmasked: 4-wave workgroups of 256 queries (two halves of 32 per wave), two per CU (two waves per SIMD, 256
+  // registers each), a 3-tile ring. Causal: 4-wave workgroups of 128 queries with a 4-tile ring, two per CU, which
+  // balanced the triangular work best.
+  if (!a.causal) return launch<4, 2, 2, 3>(a, stream);
+  return launch<4, 1, 2, 4>(a, stream);
 }
 
 }  // namespace mi355
