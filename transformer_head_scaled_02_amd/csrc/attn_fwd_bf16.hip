@@ -11,9 +11,11 @@
 //    packed to bf16 are directly the B operand of the second product O^T = V^T P^T: the n x n score matrix never
 //    leaves registers.
 //  * K and V tiles go HBM -> LDS with global_load_lds_dwordx4 (no register staging, no LDS store instructions) into
-//    a STAGES-deep ring, so a tile's loads have STAGES-1 tiles of compute to land; one barrier per tile. Each wave
-//    issues 16/NW of the 16 one-kilobyte copies of a tile from a scalar tile base and fixed per-lane offsets. Rows
-//    are unpadded (128 B) with an XOR chunk swizzle that keeps the K row reads and the V transpose reads
+//    a STAGES-deep ring; one barrier per tile, placed before the last half's P V^T product of tile t: it publishes
+//    tile t+1, whose K operands are then read into registers while those products run (so the next tile's score
+//    products never wait on LDS), and it frees tile t's stage for the copy of tile t + STAGES. Each wave issues
+//    16/NW of the 16 one-kilobyte copies of a tile from a scalar tile base and fixed per-lane offsets. Rows are
+//    unpadded (128 B) with an XOR chunk swizzle that keeps the K row reads and the V transpose reads
 //    (ds_read_b64_tr_b16) free of bank conflicts.
 //  * The softmax runs on the VALU, which on this chip is busier than the matrix core at d = 64 (one v_exp_f32 per
 //    score costs about as many SIMD cycles as the score's share of both products), so the steady-state tile spends
@@ -28,9 +30,13 @@
 //        are rescaled and the tile's P is recomputed before it touches O. The decision is per row, so a row never
 //        depends on another row's keys.
 //  * With H = 2 a wave owns two independent halves of 32 queries: every K and V operand read from LDS feeds two
-//    products, and one half's MFMAs fill the gaps of the other half's softmax chain within the same wave.
-//  * The loop is unrolled over the ring so every LDS address is a per-lane base plus an immediate offset; two
-//    workgroups per CU (two waves per SIMD) let one wave's MFMAs overlap the other's VALU work.
+//    products, and one half's MFMAs fill the gaps of the other half's softmax chain within the same wave. This
+//    configuration serves unmasked attention only; its one masked tile (a ragged last tile) runs the halves one after
+//    the other, which needs fewer registers than the interleaved order and keeps the kernel within the
+//    two-waves-per-SIMD budget.
+//  * The steady-state loop is unrolled over the ring so every LDS address is a per-lane base plus an immediate
+//    offset (the few remaining tiles compute their stage at run time); two workgroups per CU (two waves per SIMD)
+//    let one wave's MFMAs overlap the other's VALU work.
 //  * Key tiles entirely after a wave's last query are skipped (causal), and query blocks run heaviest first.
 #include <math.h>
 
@@ -39,6 +45,10 @@
 
 namespace mi355 {
 namespace {
+
+// a ring stage given at compile time (integral_constant) or at run time (int)
+template <class T>
+__device__ __forceinline__ constexpr int stage_index(T s) { return (int)s; }
 
 template <int NW, int H, int MINB, int STAGES>
 __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, int n_qblocks) {
@@ -55,7 +65,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, i
   const int lane = tid & 63;
   const int g = lane >> 5, li = lane & 31;
   const int n_q = a.n_q, n_k = a.n_k;
-  const bool causal = a.causal != 0;
+  const bool causal = H == 1 && a.causal != 0;  // the two-half kernel serves unmasked attention only
 
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
   int qb = blk % n_qblocks;
@@ -124,12 +134,15 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, i
       // Partial tile: from the unshifted tile base, lane offset = row min(row, last_row) with the chunk swizzle of
       // destination row `row` (the 16-row shift is folded back in, so the 32-bit offset is never negative).
       const int last_row = n_k - 1 - t * kBN;  // last valid row of this partial tile, >= 0
+      // (lrow passes through an empty asm so these rare-path rows are computed here, not kept in registers)
+      int lr = lrow;
+      asm volatile("" : "+v"(lr));
 #pragma unroll
       for (int i = 0; i < kLPW; ++i) {
         const int gi = wave * kLPW + i;
         const int c = gi & 7;
-        const int row = 8 * c + lrow;
-        lds_dma16(gi < 8 ? kt : vt, ld_voff[i & 1] + (uint32_t)((min(row, last_row) - (8 * (c & 1) + lrow)) * kD * 2),
+        const int row = 8 * c + lr;
+        lds_dma16(gi < 8 ? kt : vt, ld_voff[i & 1] + (uint32_t)((min(row, last_row) - (8 * (c & 1) + lr)) * kD * 2),
                   stage + (gi < 8 ? 0u : kTileElems * 2u) + (uint32_t)c * 1024u);
       }
     }
@@ -165,11 +178,11 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, i
   // for each query half. The K and V operands are read from LDS once and serve every half; while one half's softmax
   // runs on the VALU, the other half's products keep the matrix core busy. Masked tiles give keys past the row's
   // bound the score -inf. The first tile sets the offset to its row max.
-  auto step = [&](int t, auto stage_c, auto masked_c, auto first_c) __attribute__((always_inline)) {
-    constexpr int kStage = decltype(stage_c)::value;
+  auto step = [&](int t, auto stage_c, auto masked_c, auto first_c, bf16x8(&kreg)[4][2], auto&& mid)
+                  __attribute__((always_inline)) {
     constexpr bool kM = decltype(masked_c)::value;
     constexpr bool kFirst = decltype(first_c)::value;
-    const uint16_t* stage = smem + kStage * 2 * kTileElems;
+    const uint16_t* stage = smem + stage_index(stage_c) * 2 * kTileElems;
 
     auto load_k = [&](bf16x8(&ka)[4][2]) __attribute__((always_inline)) {
 #pragma unroll
@@ -270,16 +283,16 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, i
       l[h] += ts[h][0];
     };
 
-    {
-      bf16x8 ka[4][2];
-      load_k(ka);
-      unroll<H>([&](auto h_c) __attribute__((always_inline)) { scores(h_c, ka); });
-    }
+    // Masked tiles of the two-half kernel (only a ragged last tile: it serves unmasked attention) run the halves one
+    // after the other, which needs fewer registers than the interleaved order.
+    constexpr bool kSeq = kM && H == 2;
+    if (!kSeq) unroll<H>([&](auto h_c) __attribute__((always_inline)) { scores(h_c, kreg); });
     // V^T operands, read once for every half: k-step ks pairs P registers 8(ks%2) .. +7 of key block ks/2 with keys
     // 16ks + 4g + (0..3) and 16ks + 8 + 4g + (0..3); two transpose reads of V rows give the matching operand.
     bf16x8 va[4][2];
     unroll<H>([&](auto h_c) __attribute__((always_inline)) {
       constexpr int h = decltype(h_c)::value;
+      if (kSeq) scores(h_c, kreg);
       softmax(h_c);
       if (h == 0) {
 #pragma unroll
@@ -291,6 +304,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, i
             va[ks][mb] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
           }
       }
+      if (h == H - 1) mid();
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
@@ -298,46 +312,69 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, i
     });
   };
 
-  // Wait until this wave's copies of tile t have landed (tiles after t that were issued may stay in flight), then
-  // for every wave's (the barrier), which also frees the stage of tile t-1; then issue tile t + STAGES - 1.
-  auto advance = [&](int t) __attribute__((always_inline)) {
-    const int ahead = min(STAGES - 2, nt - 1 - t);  // tiles issued after t
+  // K operands of a tile, read from its ring stage
+  auto read_k = [&](const uint16_t* st, bf16x8(&kr)[4][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) kr[ks][kb] = *reinterpret_cast<const bf16x8*>(st + kb * 32 * kD + koff[ks]);
+  };
+  // Between the last half's softmax and its P V^T product of tile t: wait until this wave's copies of tile t+1 have
+  // landed (later tiles may stay in flight), then for every wave's (the barrier, which also certifies that every
+  // wave has read V of tile t and K of every tile up to t+1, so tile t's stage is free), read K of tile t+1 into
+  // registers while the products run, and issue tile t + STAGES into the freed stage.
+  bf16x8 kr[4][2];
+  auto mid = [&](int t, auto next_stage_c) __attribute__((always_inline)) {
+    if (t + 1 >= nt) return;
+    const int ahead = min(STAGES - 2, nt - 2 - t);  // tiles issued after t+1
     if (ahead >= 2) wait_vmcnt<2 * kLPW>();
     else if (ahead == 1) wait_vmcnt<kLPW>();
     else wait_vmcnt<0>();
     lds_barrier();
-    if (t + STAGES - 1 < nt) issue_tile(t + STAGES - 1);
+    read_k(smem + stage_index(next_stage_c) * 2 * kTileElems, kr);
+    if (t + STAGES < nt) issue_tile(t + STAGES);
   };
 
   const std::false_type no;
   const std::true_type yes;
 #pragma unroll
-  for (int t = 0; t < STAGES - 1; ++t)
+  for (int t = 0; t < STAGES; ++t)
     if (t < nt) issue_tile(t);
+  {
+    const int ahead = min(STAGES - 1, nt - 1);
+    if (ahead >= 3) wait_vmcnt<3 * kLPW>();
+    else if (ahead == 2) wait_vmcnt<2 * kLPW>();
+    else if (ahead == 1) wait_vmcnt<kLPW>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    read_k(smem, kr);
+  }
   // tile 0 (every row has at least one key it may see there)
-  advance(0);
-  if (t_mask > 0) step(0, std::integral_constant<int, 0>{}, no, yes);
-  else step(0, std::integral_constant<int, 0>{}, yes, yes);
+  {
+    auto m0 = [&]() __attribute__((always_inline)) { mid(0, std::integral_constant<int, 1 % STAGES>{}); };
+    if (t_mask > 0) step(0, std::integral_constant<int, 0>{}, no, yes, kr, m0);
+    else step(0, std::integral_constant<int, 0>{}, yes, yes, kr, m0);
+  }
   int t = 1;
   // steady state: groups of STAGES unmasked tiles starting at t = 1 (mod STAGES), so each tile's ring stage is a
   // compile-time constant
   for (; t + STAGES <= t_mask; t += STAGES)
     unroll<STAGES>([&](auto u) __attribute__((always_inline)) {
-      advance(t + u);
-      step(t + u, std::integral_constant<int, (1 + decltype(u)::value) % STAGES>{}, no, no);
+      constexpr int kU = decltype(u)::value;
+      auto mu = [&]() __attribute__((always_inline)) {
+        mid(t + kU, std::integral_constant<int, (2 + kU) % STAGES>{});
+      };
+      step(t + kU, std::integral_constant<int, (1 + kU) % STAGES>{}, no, no, kr, mu);
     });
+  // the remaining tiles, with the ring stage computed at run time
+  for (; t < t_mask; ++t) {
+    auto md = [&]() __attribute__((always_inline)) { mid(t, (t + 1) % STAGES); };
+    step(t, t % STAGES, no, no, kr, md);
+  }
   for (; t < nt; ++t) {
-    advance(t);
-    if (t < t_skip) {
-      const int st = t % STAGES;
-      const bool masked = t >= t_mask;
-      unroll<STAGES>([&](auto u) __attribute__((always_inline)) {
-        if (st == decltype(u)::value) {
-          if (masked) step(t, u, yes, no);
-          else step(t, u, no, no);
-        }
-      });
-    }
+    auto md = [&]() __attribute__((always_inline)) { mid(t, (t + 1) % STAGES); };
+    if (t < t_skip) step(t, t % STAGES, yes, no, kr, md);
+    else md();
   }
 
   // O = O^T / l; lane holds d = 32mb + 8(r/4) + 4g + r%4 of its query.
