@@ -117,6 +117,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="sdpa_bf16_b4_h8_n4096")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probes", action="store_true", help="skip the measured-ceiling microbenchmarks")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain copy of known size (for scaling HBM byte counters)")
@@ -193,6 +194,16 @@ def main():
         "wall_s_timed_region": round(wall, 4),
         "parity_last_step": {"max_abs": float(err.max()), "mean_abs": float(err.mean())},
     }
+    if not args.no_probes:
+        # measured ceilings on this chip, taken after the timed region: dense bf16 MFMA throughput with every CU busy
+        # (and the clock it holds under that load), the v_exp_f32 rate and device-to-device copy bandwidth
+        tf, ghz = m.probe_mfma_bf16(iters=20000)
+        rate, ghz_e = m.probe_exp_f32(iters=4000)
+        gbps = m.probe_hbm_copy(nbytes=1 << 30, reps=5)
+        rec["measured_ceilings"] = {"mfma_bf16_tflops": round(tf, 1), "mfma_clock_ghz": round(ghz, 3),
+                                    "exp2_per_clock_per_cu": round(rate, 2), "exp_clock_ghz": round(ghz_e, 3),
+                                    "hbm_copy_GBps": round(gbps, 1)}
+        rec["pct_of_measured_mfma_ceiling"] = round(100 * value / tf, 2)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, x, args.cpu_budget)
     print(json.dumps(rec), flush=True)

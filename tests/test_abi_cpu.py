@@ -8,7 +8,7 @@ import pytest
 
 import transformer_head_scaled_02_amd as m
 
-HEADER = Path(__file__).resolve().parents[1] / "include" / "mi355_attn.h"
+HEADERS = sorted((Path(__file__).resolve().parents[1] / "include").glob("*.h"))
 INVALID, UNSUPPORTED = m.ATTN_ERR_INVALID, m.ATTN_ERR_UNSUPPORTED
 F32, BF16 = m.ATTN_F32, m.ATTN_BF16
 
@@ -16,8 +16,11 @@ pytestmark = pytest.mark.skipif(not m.LIB_PATH.exists(), reason="library not bui
 
 
 def header_functions():
-    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+    names = set()
+    for header in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", header.read_text(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 def test_header_declares_the_binding_names():
@@ -93,3 +96,37 @@ def test_python_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 1, 4, 64)
     with pytest.raises(ValueError):
         m.sdpa_forward(q, q, q)
+
+
+def test_probe_scratch_size_is_positive(lib):
+    assert lib.probe_scratch_size() > 0
+
+
+@pytest.mark.parametrize("case", ["null", "small", "iters0", "iters_big", "misaligned"])
+def test_probes_reject_bad_scratch_before_any_hip_call(lib, case):
+    import ctypes
+    need = lib.probe_scratch_size()
+    scratch, nbytes, iters = A, need, 10
+    if case == "null":
+        scratch = 0
+    elif case == "small":
+        nbytes = need - 1
+    elif case == "iters0":
+        iters = 0
+    elif case == "iters_big":
+        iters = 10**7
+    else:
+        scratch = A + 4
+    x, y = ctypes.c_double(), ctypes.c_double()
+    assert lib.probe_mfma_bf16(scratch, nbytes, iters, None, ctypes.byref(x), ctypes.byref(y)) == INVALID
+    assert lib.probe_exp_f32(scratch, nbytes, iters, None, ctypes.byref(x), ctypes.byref(y)) == INVALID
+
+
+@pytest.mark.parametrize("kw", [dict(src=0), dict(nbytes=0), dict(nbytes=24), dict(reps=0), dict(reps=1001),
+                                dict(dst=A + 16)])
+def test_probe_copy_rejects_bad_arguments(lib, kw):
+    import ctypes
+    args = dict(src=A, dst=A * 1000, nbytes=1 << 20, reps=2)
+    args.update(kw)
+    g = ctypes.c_double()
+    assert lib.probe_hbm_copy(args["src"], args["dst"], args["nbytes"], args["reps"], None, ctypes.byref(g)) == INVALID

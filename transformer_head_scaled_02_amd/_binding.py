@@ -18,7 +18,8 @@ ATTN_MASK_NONE, ATTN_MASK_CAUSAL = 0, 1
 ATTN_F32, ATTN_BF16 = 0, 1
 
 # every symbol include/mi355_attn.h declares
-EXPORTED = ("sdpa_forward", "mha_forward", "mha_workspace_size", "attn_status_string", "attn_last_error")
+EXPORTED = ("sdpa_forward", "mha_forward", "mha_workspace_size", "attn_status_string", "attn_last_error",
+            "probe_scratch_size", "probe_mfma_bf16", "probe_exp_f32", "probe_hbm_copy")
 
 _lib = None
 
@@ -50,6 +51,15 @@ def load_library(path: Path | str | None = None) -> ctypes.CDLL:
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_last_error.argtypes = []
     lib.attn_last_error.restype = ctypes.c_char_p
+    dp = ctypes.POINTER(ctypes.c_double)
+    lib.probe_scratch_size.argtypes = []
+    lib.probe_scratch_size.restype = sz
+    lib.probe_mfma_bf16.argtypes = [vp, sz, i64, vp, dp, dp]
+    lib.probe_mfma_bf16.restype = ci
+    lib.probe_exp_f32.argtypes = [vp, sz, i64, vp, dp, dp]
+    lib.probe_exp_f32.restype = ci
+    lib.probe_hbm_copy.argtypes = [vp, vp, sz, ci, vp, dp]
+    lib.probe_hbm_copy.restype = ci
     if path is None:
         _lib = lib
     return lib
@@ -161,3 +171,41 @@ def mha_forward(xq: torch.Tensor, xkv: torch.Tensor, wq: torch.Tensor, wk: torch
                            _mask_code(mask), out.data_ptr(), workspace.data_ptr(), ws_bytes, _dtype_code(xq),
                            B, n_q, n_k, d_model, h, d_k, d_v, _stream_handle(xq.device)))
     return out
+
+
+def _probe_scratch(device) -> torch.Tensor:
+    lib = load_library()
+    return torch.empty(int(lib.probe_scratch_size()), dtype=torch.uint8, device=device)
+
+
+def probe_mfma_bf16(iters: int = 20000, device="cuda") -> tuple[float, float]:
+    """Dense bf16 MFMA throughput with every CU busy: (TFLOP/s, shader clock in GHz). Synchronises the stream."""
+    lib = load_library()
+    dev = torch.device(device)
+    scratch = _probe_scratch(dev)
+    tf, ghz = ctypes.c_double(), ctypes.c_double()
+    _check(lib.probe_mfma_bf16(scratch.data_ptr(), scratch.numel(), iters, _stream_handle(dev), ctypes.byref(tf),
+                               ctypes.byref(ghz)))
+    return tf.value, ghz.value
+
+
+def probe_exp_f32(iters: int = 4000, device="cuda") -> tuple[float, float]:
+    """v_exp_f32 throughput with every CU busy: (lane results per clock per CU, shader clock in GHz)."""
+    lib = load_library()
+    dev = torch.device(device)
+    scratch = _probe_scratch(dev)
+    rate, ghz = ctypes.c_double(), ctypes.c_double()
+    _check(lib.probe_exp_f32(scratch.data_ptr(), scratch.numel(), iters, _stream_handle(dev), ctypes.byref(rate),
+                             ctypes.byref(ghz)))
+    return rate.value, ghz.value
+
+
+def probe_hbm_copy(nbytes: int = 1 << 30, reps: int = 5, device="cuda") -> float:
+    """Device-to-device copy bandwidth in GB/s (bytes read + written per second). Synchronises the stream."""
+    lib = load_library()
+    dev = torch.device(device)
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    gbps = ctypes.c_double()
+    _check(lib.probe_hbm_copy(src.data_ptr(), dst.data_ptr(), nbytes, reps, _stream_handle(dev), ctypes.byref(gbps)))
+    return gbps.value

@@ -16,16 +16,20 @@
 #define ATTN_EXPORT extern "C" __attribute__((visibility("default")))
 
 namespace {
-
 thread_local char g_err[512] = "";
+}  // namespace
 
-int fail(int code, const char* fmt, ...) {
+int mi355::fail_status(int code, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
   vsnprintf(g_err, sizeof g_err, fmt, ap);
   va_end(ap);
   return code;
 }
+
+namespace {
+
+using mi355::fail_status;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -71,29 +75,29 @@ ATTN_EXPORT const char* attn_last_error(void) { return g_err; }
 
 ATTN_EXPORT int sdpa_forward(const void* Q, const void* K, const void* V, int mask_kind, void* out, int dtype,
                              int64_t B, int64_t h, int64_t n_q, int64_t n_k, int64_t d_k, int64_t d_v, void* stream) {
-  if (!Q || !K || !V || !out) return fail(ATTN_ERR_INVALID, "sdpa_forward: null tensor pointer");
-  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "sdpa_forward: dtype %d", dtype);
+  if (!Q || !K || !V || !out) return fail_status(ATTN_ERR_INVALID, "sdpa_forward: null tensor pointer");
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail_status(ATTN_ERR_UNSUPPORTED, "sdpa_forward: dtype %d", dtype);
   if (mask_kind != ATTN_MASK_NONE && mask_kind != ATTN_MASK_CAUSAL)
-    return fail(ATTN_ERR_INVALID, "sdpa_forward: mask_kind %d", mask_kind);
+    return fail_status(ATTN_ERR_INVALID, "sdpa_forward: mask_kind %d", mask_kind);
   if (B <= 0 || h <= 0 || n_q <= 0 || n_k <= 0 || d_k <= 0 || d_v <= 0)
-    return fail(ATTN_ERR_INVALID, "sdpa_forward: sizes must be positive (B=%lld h=%lld n_q=%lld n_k=%lld d_k=%lld "
+    return fail_status(ATTN_ERR_INVALID, "sdpa_forward: sizes must be positive (B=%lld h=%lld n_q=%lld n_k=%lld d_k=%lld "
                 "d_v=%lld)", (long long)B, (long long)h, (long long)n_q, (long long)n_k, (long long)d_k,
                 (long long)d_v);
   if (d_k != 64 || d_v != 64)
-    return fail(ATTN_ERR_UNSUPPORTED, "sdpa_forward: head dims d_k=%lld d_v=%lld (only 64 is implemented)",
+    return fail_status(ATTN_ERR_UNSUPPORTED, "sdpa_forward: head dims d_k=%lld d_v=%lld (only 64 is implemented)",
                 (long long)d_k, (long long)d_v);
   if (mask_kind == ATTN_MASK_CAUSAL && n_q != n_k)
-    return fail(ATTN_ERR_UNSUPPORTED, "sdpa_forward: causal mask needs n_q == n_k (got %lld, %lld)", (long long)n_q,
+    return fail_status(ATTN_ERR_UNSUPPORTED, "sdpa_forward: causal mask needs n_q == n_k (got %lld, %lld)", (long long)n_q,
                 (long long)n_k);
   if (n_q > ATTN_MAX_SEQ || n_k > ATTN_MAX_SEQ || B > ATTN_MAX_HEADS || h > ATTN_MAX_HEADS ||
       B * h > ATTN_MAX_HEADS || !grid_fits(B, h, n_q))
-    return fail(ATTN_ERR_UNSUPPORTED, "sdpa_forward: sizes beyond the library limits");
+    return fail_status(ATTN_ERR_UNSUPPORTED, "sdpa_forward: sizes beyond the library limits");
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(out))
-    return fail(ATTN_ERR_INVALID, "sdpa_forward: pointers must be 16-byte aligned");
+    return fail_status(ATTN_ERR_INVALID, "sdpa_forward: pointers must be 16-byte aligned");
   const size_t es = dtype == ATTN_BF16 ? 2 : 4;
   const size_t q_bytes = (size_t)B * h * n_q * 64 * es, kv_bytes = (size_t)B * h * n_k * 64 * es;
   if (overlaps(out, q_bytes, Q, q_bytes) || overlaps(out, q_bytes, K, kv_bytes) || overlaps(out, q_bytes, V, kv_bytes))
-    return fail(ATTN_ERR_INVALID, "sdpa_forward: out overlaps an input");
+    return fail_status(ATTN_ERR_INVALID, "sdpa_forward: out overlaps an input");
 
   mi355::AttnArgs a{};
   a.Q = Q; a.K = K; a.V = V; a.O = out;
@@ -106,7 +110,7 @@ ATTN_EXPORT int sdpa_forward(const void* Q, const void* K, const void* V, int ma
   a.causal = mask_kind == ATTN_MASK_CAUSAL;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = dtype == ATTN_BF16 ? mi355::launch_attn_fwd_bf16(a, s) : mi355::launch_attn_fwd_f32(a, s);
-  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "sdpa_forward: launch failed: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail_status(ATTN_ERR_HIP, "sdpa_forward: launch failed: %s", hipGetErrorString(e));
   return ATTN_OK;
 }
 
@@ -122,39 +126,39 @@ ATTN_EXPORT int mha_forward(const void* Xq, const void* Xkv, const void* Wq, con
                             int dtype, int64_t B, int64_t n_q, int64_t n_k, int64_t d_model, int64_t h, int64_t d_k,
                             int64_t d_v, void* stream) {
   if (!Xq || !Xkv || !Wq || !Wk || !Wv || !Wo || !out || !workspace)
-    return fail(ATTN_ERR_INVALID, "mha_forward: null pointer");
-  if (dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "mha_forward: dtype %d (only ATTN_BF16)", dtype);
+    return fail_status(ATTN_ERR_INVALID, "mha_forward: null pointer");
+  if (dtype != ATTN_BF16) return fail_status(ATTN_ERR_UNSUPPORTED, "mha_forward: dtype %d (only ATTN_BF16)", dtype);
   if (mask_kind != ATTN_MASK_NONE && mask_kind != ATTN_MASK_CAUSAL)
-    return fail(ATTN_ERR_INVALID, "mha_forward: mask_kind %d", mask_kind);
+    return fail_status(ATTN_ERR_INVALID, "mha_forward: mask_kind %d", mask_kind);
   if (B <= 0 || n_q <= 0 || n_k <= 0 || d_model <= 0 || h <= 0 || d_k <= 0 || d_v <= 0)
-    return fail(ATTN_ERR_INVALID, "mha_forward: sizes must be positive");
+    return fail_status(ATTN_ERR_INVALID, "mha_forward: sizes must be positive");
   if (d_k != 64 || d_v != 64)
-    return fail(ATTN_ERR_UNSUPPORTED, "mha_forward: head dims d_k=%lld d_v=%lld (only 64 is implemented)",
+    return fail_status(ATTN_ERR_UNSUPPORTED, "mha_forward: head dims d_k=%lld d_v=%lld (only 64 is implemented)",
                 (long long)d_k, (long long)d_v);
-  if (d_model % 64) return fail(ATTN_ERR_UNSUPPORTED, "mha_forward: d_model=%lld is not a multiple of 64",
+  if (d_model % 64) return fail_status(ATTN_ERR_UNSUPPORTED, "mha_forward: d_model=%lld is not a multiple of 64",
                                 (long long)d_model);
   if (mask_kind == ATTN_MASK_CAUSAL && n_q != n_k)
-    return fail(ATTN_ERR_UNSUPPORTED, "mha_forward: causal mask needs n_q == n_k");
+    return fail_status(ATTN_ERR_UNSUPPORTED, "mha_forward: causal mask needs n_q == n_k");
   if (n_q > ATTN_MAX_SEQ || n_k > ATTN_MAX_SEQ || B > ATTN_MAX_HEADS || h > ATTN_MAX_HEADS ||
       B * h > ATTN_MAX_HEADS || d_model > 65536 || B * n_q > 0x7fffffffLL || B * n_k > 0x7fffffffLL ||
       !grid_fits(B, h, n_q))
-    return fail(ATTN_ERR_UNSUPPORTED, "mha_forward: sizes beyond the library limits");
+    return fail_status(ATTN_ERR_UNSUPPORTED, "mha_forward: sizes beyond the library limits");
   const MhaLayout L = mha_layout(B, n_q, n_k, h);
   if (workspace_bytes < L.total)
-    return fail(ATTN_ERR_INVALID, "mha_forward: workspace %zu bytes, need %zu", workspace_bytes, L.total);
+    return fail_status(ATTN_ERR_INVALID, "mha_forward: workspace %zu bytes, need %zu", workspace_bytes, L.total);
   const void* ptrs[] = {Xq, Xkv, Wq, Wk, Wv, Wo, out, workspace};
   for (const void* p : ptrs)
-    if (!aligned16(p)) return fail(ATTN_ERR_INVALID, "mha_forward: pointers must be 16-byte aligned");
+    if (!aligned16(p)) return fail_status(ATTN_ERR_INVALID, "mha_forward: pointers must be 16-byte aligned");
   const size_t xq_b = (size_t)B * n_q * d_model * 2, xkv_b = (size_t)B * n_k * d_model * 2;
   const size_t w_b = (size_t)d_model * h * 64 * 2;
   const void* ins[] = {Xq, Xkv, Wq, Wk, Wv, Wo};
   const size_t in_b[] = {xq_b, xkv_b, w_b, w_b, w_b, w_b};
   for (int i = 0; i < 6; ++i) {
-    if (overlaps(out, xq_b, ins[i], in_b[i])) return fail(ATTN_ERR_INVALID, "mha_forward: out overlaps an input");
+    if (overlaps(out, xq_b, ins[i], in_b[i])) return fail_status(ATTN_ERR_INVALID, "mha_forward: out overlaps an input");
     if (overlaps(workspace, L.total, ins[i], in_b[i]))
-      return fail(ATTN_ERR_INVALID, "mha_forward: workspace overlaps an input");
+      return fail_status(ATTN_ERR_INVALID, "mha_forward: workspace overlaps an input");
   }
-  if (overlaps(out, xq_b, workspace, L.total)) return fail(ATTN_ERR_INVALID, "mha_forward: out overlaps workspace");
+  if (overlaps(out, xq_b, workspace, L.total)) return fail_status(ATTN_ERR_INVALID, "mha_forward: out overlaps workspace");
 
   char* ws = static_cast<char*>(workspace);
   void* Qh = ws + L.q_off;
@@ -171,7 +175,7 @@ ATTN_EXPORT int mha_forward(const void* Xq, const void* Xkv, const void* Wq, con
       {Xkv, Wv, Vh, (int)(B * n_k), hd, (int)d_model, (int)n_k},
   };
   hipError_t e = mi355::launch_gemm_bf16(proj, 3, s);
-  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "mha_forward: projection launch failed: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail_status(ATTN_ERR_HIP, "mha_forward: projection launch failed: %s", hipGetErrorString(e));
 
   // 2. attention per head, output written into the concatenated layout [B, n_q, h*64]
   mi355::AttnArgs a{};
@@ -184,11 +188,11 @@ ATTN_EXPORT int mha_forward(const void* Xq, const void* Xkv, const void* Wq, con
   a.o_stride_row = h * 64;
   a.causal = mask_kind == ATTN_MASK_CAUSAL;
   e = mi355::launch_attn_fwd_bf16(a, s);
-  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "mha_forward: attention launch failed: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail_status(ATTN_ERR_HIP, "mha_forward: attention launch failed: %s", hipGetErrorString(e));
 
   // 3. output projection: out [B*n_q, d_model] = concat [B*n_q, h*64] x Wo [h*64, d_model]
   mi355::GemmProblem outp = {Ch, Wo, out, (int)(B * n_q), (int)d_model, hd, 0};
   e = mi355::launch_gemm_bf16(&outp, 1, s);
-  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "mha_forward: W^O launch failed: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail_status(ATTN_ERR_HIP, "mha_forward: W^O launch failed: %s", hipGetErrorString(e));
   return ATTN_OK;
 }

@@ -35,4 +35,7 @@ struct GemmProblem {
 };
 hipError_t launch_gemm_bf16(const GemmProblem* probs, int nprobs, hipStream_t stream);
 
+// Records a printf-style detail as the calling thread's last error (attn_last_error) and returns `code`.
+int fail_status(int code, const char* fmt, ...);
+
 }  // namespace mi355
