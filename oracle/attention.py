@@ -1,4 +1,4 @@
-"""Plain float64 CPU oracle for scaled dot-product attention and multi-head attention.
+"""Plain float64 CPU oracle for scaled dot-product attention (forward and backward) and multi-head attention.
 
 TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the bench's CPU-baseline leg may import this module.
 The library's GPU path never imports, links or calls anything here, and this module imports nothing from it.
@@ -15,12 +15,20 @@ Sources (web pages about "Attention Is All You Need"):
     "Transformer 中的三种 Attention" (future scores set to -inf before the softmax in decoder self-attention), and
     the training example's mask matrix M (section "训练样本").
   * "Transformer 为什么抛弃循环网络" (treecat.cn), sections "一次注意力计算在做什么" and "为什么需要多头注意力".
+  * Backward pass: "Transformer：抛弃循环与卷积的序列建模", section "训练样本", subsection "反向传播": training
+    carries the loss back through the attention computation by the chain rule to reach the gradients of W^Q, W^K and
+    W^V; the gradients with respect to Q, K and V are the step of that chain that passes through attention.
 
 Readings where the pages leave a step open:
   * The causal mask sets the score of key j for query i to -inf when j > i (the diagonal is allowed), so those
     weights are exactly 0. It is defined only for self-attention, where n_q == n_k; `q_index` lets a caller ask for a
     subset of query rows and still get the mask of their true positions.
   * Subtracting the row max before exp is an exact identity of the softmax, used only to avoid overflow.
+  * The backward pass of attention is the exact derivative of the forward function: given an upstream gradient dO
+    (the derivative of some loss L with respect to O), it returns dL/dQ, dL/dK and dL/dV, i.e. the gradient of
+    L = sum(dO * O) with the forward outputs O treated as a function of Q, K and V.
+  * The row log-sum-exp of the scaled scores, lse_i = log sum_j exp(s_ij) over the keys the row may see, is the
+    statistic a forward pass hands to the backward pass: the weights are then exp(s_ij - lse_i).
   * Projections carry no bias (the attention formulas on the pages have none). The row-vector convention X W is used:
     W_i^Q is the column block i of Wq [d_model, h*d_k]; Concat orders the heads 1..h along the last axis; W^O is
     [h*d_v, d_model].
@@ -144,3 +152,65 @@ def sdpa_brute(q, k, v, causal=False):
         total = math.fsum(e)
         out.append([math.fsum(e[j] * v[j][c] for j in range(n_k)) / total for c in range(len(v[0]))])
     return out
+
+
+def sdpa_lse_head(q, k, causal=False, q_index=None):
+    """Row log-sum-exp of the scaled scores of one head: lse_i = log sum_j exp(q_i . k_j / sqrt(d_k)) over the keys
+    query i may see (natural log). q [n_q, d_k], k [n_k, d_k] -> [n_q]."""
+    q = _as_f64(q)
+    k = _as_f64(k)
+    if q.ndim != 2 or k.ndim != 2 or q.shape[1] != k.shape[1]:
+        raise ValueError("q [n_q, d_k] and k [n_k, d_k] expected")
+    s = (q @ k.T) / math.sqrt(q.shape[1])
+    if causal:
+        s = np.where(_causal_disallowed(s.shape[0], s.shape[1], q_index), -np.inf, s)
+    m = s.max(axis=1)                                    # the max shift again only avoids overflow
+    return m + np.log(np.exp(s - m[:, None]).sum(axis=1))
+
+
+def sdpa_lse_ref(Q, K, causal=False, q_index=None):
+    """Row log-sum-exp for every leading (batch, head) index. Q [..., n_q, d_k], K [..., n_k, d_k] -> [..., n_q]."""
+    return _per_head(lambda q, k, **kw: sdpa_lse_head(q, k, **kw)[:, None], Q, K, causal=causal,
+                     q_index=q_index)[..., 0]
+
+
+def sdpa_backward_head(q, k, v, dout, causal=False, q_index=None):
+    """Gradients (dq, dk, dv) of L = sum(dout * O) for one head, O = softmax(q k^T / sqrt(d_k)) v.
+
+    The chain rule through the three steps of the forward pass, from the output back:
+      * O = W v:        dL/dv = W^T dout and dL/dW = dout v^T;
+      * W_i = softmax(S_i) row by row: the Jacobian of a softmax row is diag(W_i) - W_i^T W_i, so
+                        dL/dS_ij = W_ij (dL/dW_ij - sum_t W_it dL/dW_it);
+      * S = q k^T / sqrt(d_k): dL/dq = (dL/dS) k / sqrt(d_k) and dL/dk = (dL/dS)^T q / sqrt(d_k).
+    Masked scores have W_ij = 0, so their dL/dS_ij is 0 and they pass no gradient.
+    q [n_q, d_k], k [n_k, d_k], v [n_k, d_v], dout [n_q, d_v].
+    """
+    v = _as_f64(v)
+    dout = _as_f64(dout)
+    w = sdpa_weights_head(q, k, causal, q_index)
+    if v.ndim != 2 or v.shape[0] != w.shape[1] or dout.shape != (w.shape[0], v.shape[1]):
+        raise ValueError("v [n_k, d_v] and dout [n_q, d_v] expected")
+    q = _as_f64(q)
+    k = _as_f64(k)
+    d_k = q.shape[1]
+    dv = w.T @ dout
+    dw = dout @ v.T
+    ds = w * (dw - (w * dw).sum(axis=1, keepdims=True))
+    dq = ds @ k / math.sqrt(d_k)
+    dk = ds.T @ q / math.sqrt(d_k)
+    return dq, dk, dv
+
+
+def sdpa_backward_ref(Q, K, V, dO, causal=False):
+    """(dQ, dK, dV) of attention for every leading (batch, head) index, head by head.
+
+    Q [..., n_q, d_k], K [..., n_k, d_k], V [..., n_k, d_v], dO [..., n_q, d_v] -> arrays shaped like Q, K, V.
+    """
+    Q, K, V, dO = (_as_f64(a) for a in (Q, K, V, dO))
+    lead = Q.shape[:-2]
+    if K.shape[:-2] != lead or V.shape[:-2] != lead or dO.shape[:-2] != lead:
+        raise ValueError("leading (batch, head) dimensions differ")
+    dQ, dK, dV = np.empty_like(Q), np.empty_like(K), np.empty_like(V)
+    for idx in np.ndindex(*lead):
+        dQ[idx], dK[idx], dV[idx] = sdpa_backward_head(Q[idx], K[idx], V[idx], dO[idx], causal)
+    return dQ, dK, dV
