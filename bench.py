@@ -1,8 +1,13 @@
-"""Benchmark of the attention forward on one MI355X; prints ONE JSON line.
+"""Benchmark of the attention forward (or backward) on one MI355X; prints ONE JSON line.
 
 A step is one sdpa_forward call (scores, scale, mask, online softmax, weighted sum of V: the whole fused attention)
 over the long-sequence workload B=4, h=8, n_q=n_k=4096, d_k=d_v=64, bf16, unmasked, with Q/K/V ~ N(0,1) seeded and
 already resident in HBM. Metric: attention TFLOP/s = 4*B*h*n_q*n_k*d_k / time, against the bf16 dense MFMA peak.
+
+With a backward workload (--workload sdpa_bwd_bf16_b4_h8_n4096 or sdpa_bwd_causal_bf16_b4_h8_n4096) a step is one
+sdpa_backward call (pre-pass, dK/dV, dQ) on the same tensors plus a seeded upstream gradient, with the forward's
+output and log-sum-exp computed once before the timed region; metric: backward TFLOP/s = 10*B*h*n_q*n_k*d_k / time
+(the five n_q x n_k x 64 products the gradient needs).
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 """
@@ -19,6 +24,7 @@ ROOT = Path(__file__).resolve().parent
 sys.path.insert(0, str(ROOT))
 
 METRIC = "attention TFLOP/s (4·B·h·n_q·n_k·d_k) at h=8,d_k=64; % of bf16 MFMA peak"
+METRIC_BWD = "attention backward TFLOP/s (10·B·h·n_q·n_k·d_k) at h=8,d_k=64; % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
 PROFILES = ROOT / "profiles"
@@ -28,10 +34,29 @@ def flops_metric(w):
     return 4.0 * w["B"] * w["h"] * w["n_q"] * w["n_k"] * w["d_k"]
 
 
-def flops_algorithmic(w):
+def _pairs(w):
     # causal: only the n(n+1)/2 allowed (query, key) pairs do work
-    pairs = w["n_q"] * (w["n_q"] + 1) / 2 if w["causal"] else w["n_q"] * w["n_k"]
-    return 2.0 * w["B"] * w["h"] * pairs * (w["d_k"] + w["d_v"])
+    return w["n_q"] * (w["n_q"] + 1) / 2 if w["causal"] else w["n_q"] * w["n_k"]
+
+
+def flops_algorithmic(w):
+    return 2.0 * w["B"] * w["h"] * _pairs(w) * (w["d_k"] + w["d_v"])
+
+
+def flops_metric_bwd(w):
+    return 10.0 * w["B"] * w["h"] * w["n_q"] * w["n_k"] * w["d_k"]
+
+
+def flops_algorithmic_bwd(w):
+    # S = Q K^T, dP = dO V^T, dV = P^T dO, dQ = dS K, dK = dS^T Q over the allowed pairs
+    return 2.0 * w["B"] * w["h"] * _pairs(w) * (3 * w["d_k"] + 2 * w["d_v"])
+
+
+def hbm_bytes_bwd(w):
+    # read Q, K, V, O, dO (and lse); write dQ, dK, dV
+    es = 2 if w["dtype"] == "bf16" else 4
+    nq, nk = w["n_q"], w["n_k"]
+    return w["B"] * w["h"] * (es * (3 * nq * w["d_k"] + 4 * nk * w["d_k"]) + es * nq * w["d_v"] + 4 * nq)
 
 
 def hbm_bytes(w):
@@ -110,6 +135,89 @@ def cpu_baseline(w, x, budget_s: float):
                       f"scores each, float64 NumPy), {t_total:.1f} s"}
 
 
+def cpu_baseline_bwd(w, x, budget_s: float):
+    """Time the float64 oracle's backward pass on whole heads until about `budget_s` seconds are spent."""
+    import numpy as np
+
+    from oracle import sdpa_backward_head
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    heads = [(b, hh) for b in range(w["B"]) for hh in range(w["h"])]
+    done, t_total = 0, 0.0
+    sdpa_backward_head(x["Q"].f64[0, 0, :64], x["K"].f64[0, 0, :64], x["V"].f64[0, 0, :64], x["dO"].f64[0, 0, :64])
+    while t_total < budget_s:
+        b, hh = heads[done % len(heads)]
+        t0 = time.perf_counter()
+        g = sdpa_backward_head(*(x[n].f64[b, hh] for n in ("Q", "K", "V", "dO")), w["causal"])
+        t_total += time.perf_counter() - t0
+        done += 1
+        assert all(np.isfinite(a).all() for a in g)
+    per_head = flops_metric_bwd(w) / (w["B"] * w["h"])
+    return {"value": per_head * done / t_total / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} head backward evaluations over the workload's {len(heads)} heads ({w['n_q']}x{w['n_k']}"
+                      f" scores each, float64 NumPy), {t_total:.1f} s"}
+
+
+def bench_backward(args, w, x, m, dev):
+    """Time sdpa_backward (three launches per step) on the workload; returns the JSON record."""
+    import numpy as np
+    import torch
+
+    from oracle import sdpa_backward_head
+    q, k, v, do = (dev(x[n]) for n in ("Q", "K", "V", "dO"))
+    mask = "causal" if w["causal"] else "none"
+    out, lse = m.sdpa_forward_lse(q, k, v, mask=mask)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(m.sdpa_backward_workspace_size(w["B"], w["h"], w["n_q"], w["n_k"]), dtype=torch.uint8,
+                     device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        m.sdpa_backward(q, k, v, out, do, lse, mask=mask, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # parity of the last timed step on one whole head (float64 oracle, same inputs)
+    ref = sdpa_backward_head(*(x[n].f64[0, 0] for n in ("Q", "K", "V", "dO")), w["causal"])
+    errs = {}
+    for name, g, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
+        d = np.abs(g[0, 0].float().cpu().numpy().astype(np.float64) - r)
+        errs[name] = {"nrms": float(np.sqrt(np.mean(d * d)) / np.sqrt(np.mean(r * r))),
+                      "max_rel": float(d.max() / np.abs(r).max())}
+
+    value = flops_metric_bwd(w) / (ms * 1e-3) / 1e12
+    achieved = flops_algorithmic_bwd(w) / (ms * 1e-3) / 1e12
+    return {
+        "metric": METRIC_BWD, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w["dtype"], "data": "synthetic (seeded N(0,1) Q/K/V/dO, no dataset)",
+        "config": {"workload": args.workload, "B": w["B"], "h": w["h"], "n_q": w["n_q"], "n_k": w["n_k"],
+                   "d_k": w["d_k"], "d_v": w["d_v"], "mask": mask},
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "sdpa_backward step (attn_bwd_pre + attn_bwd_dkdv_bf16 + attn_bwd_dq_bf16)",
+                     "algorithmic_hbm_bytes": hbm_bytes_bwd(w),
+                     "algorithmic_hbm_GBps": round(hbm_bytes_bwd(w) / (ms * 1e-3) / 1e9, 1)},
+        "wall_s_timed_region": round(wall, 4),
+        "parity_last_step_head0": errs,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -141,14 +249,21 @@ def main():
         return
     m.load_library()
     w = workloads.WORKLOADS[args.workload]
-    if w["kind"] != "sdpa":
-        raise SystemExit("bench workload must be an sdpa workload")
+    if w["kind"] not in ("sdpa", "sdpa_bwd"):
+        raise SystemExit("bench workload must be an sdpa or sdpa_bwd workload")
     x = workloads.make_workload(args.workload)
 
     def dev(q):
         if q.dtype == "bf16":
             return torch.from_numpy(q.raw.view(np.int16)).view(torch.bfloat16).cuda()
         return torch.from_numpy(q.raw).cuda()
+
+    if w["kind"] == "sdpa_bwd":
+        rec = bench_backward(args, w, x, m, dev)
+        if not args.no_cpu_baseline:
+            rec["cpu_baseline"] = cpu_baseline_bwd(w, x, args.cpu_budget)
+        print(json.dumps(rec), flush=True)
+        return
 
     q, k, v = dev(x["Q"]), dev(x["K"]), dev(x["V"])
     out = torch.empty(w["B"], w["h"], w["n_q"], w["d_v"], dtype=q.dtype, device="cuda")

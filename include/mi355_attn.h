@@ -1,4 +1,5 @@
-/* mi355_attn.h - C ABI of the MI355X (gfx950) scaled dot-product / multi-head attention forward library.
+/* mi355_attn.h - C ABI of the MI355X (gfx950) scaled dot-product / multi-head attention library (attention forward
+ * and backward, multi-head attention forward).
  *
  * What is computed (sources are web pages about "Attention Is All You Need"):
  *   Attention(Q, K, V) = softmax(Q K^T / sqrt(d_k)) V
@@ -13,6 +14,9 @@
  *     - same page, section "Multi-Head Attention"; lettle.cn translation section 3.2.2. Queries come from Xq, keys and
  *       values from Xkv: Xkv == Xq for self-attention, the encoder output for encoder-decoder attention (section
  *       "Transformer 中的三种 Attention").
+ *   Backward pass: the gradients of a loss L with respect to Q, K and V given dL/dO, by the chain rule through the
+ *   forward computation (the step of training that carries the loss back through attention).
+ *     - "Transformer：抛弃循环与卷积的序列建模", section "训练样本", subsection "反向传播".
  *
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library never allocates, frees or copies
@@ -63,6 +67,37 @@ typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
  *   d_k and d_v must both be 64. `out` must not overlap Q, K or V. */
 int sdpa_forward(const void* Q, const void* K, const void* V, int mask_kind, void* out, int dtype,
                  int64_t B, int64_t h, int64_t n_q, int64_t n_k, int64_t d_k, int64_t d_v, void* stream);
+
+/* sdpa_forward_lse: sdpa_forward that also writes the row log-sum-exp of the scaled scores,
+ *   lse [B, h, n_q] float32 (natural log): lse[b,h,i] = log sum_j exp(Q[b,h,i,:] . K[b,h,j,:] / sqrt(d_k)) over the
+ *   keys row i may see, so that the weights are exp(score - lse). It is the statistic sdpa_backward needs.
+ *   For ATTN_BF16 the sum is that of the bf16-rounded weights the kernel multiplies V with, so that the weights the
+ *   backward pass recomputes are those of the forward output.
+ *   Other arguments, requirements and errors as sdpa_forward; `lse` must not overlap any other tensor. */
+int sdpa_forward_lse(const void* Q, const void* K, const void* V, int mask_kind, void* out, float* lse, int dtype,
+                     int64_t B, int64_t h, int64_t n_q, int64_t n_k, int64_t d_k, int64_t d_v, void* stream);
+
+/* sdpa_backward: gradients of attention.
+ *   Q, K, V      the forward inputs, as for sdpa_forward
+ *   O   [B, h, n_q, d_v]  the forward output and lse [B, h, n_q] float32 its row log-sum-exp (sdpa_forward_lse with
+ *                         the same Q, K, V and mask_kind)
+ *   dO  [B, h, n_q, d_v]  dL/dO, the upstream gradient
+ *   dQ  [B, h, n_q, d_k], dK [B, h, n_k, d_k], dV [B, h, n_k, d_v]: written with dL/dQ, dL/dK, dL/dV:
+ *       P = exp(Q K^T / sqrt(d_k) - lse) (0 where masked), dV = P^T dO, dP = dO V^T,
+ *       dS = P o (dP - D) with D_i = dO_i . O_i, dQ = dS K / sqrt(d_k), dK = dS^T Q / sqrt(d_k).
+ *   workspace: device scratch of at least sdpa_backward_workspace_size(...) bytes, 16-byte aligned, owned by the
+ *              caller (it holds per-row lse and D between the three launches).
+ *   dtype: ATTN_BF16 (bf16 tensors, float32 accumulation, P and dS rounded to bf16 where they enter the matrix core,
+ *          outputs rounded to nearest even) or ATTN_F32 (float32 throughout). lse is float32 in both.
+ *   Requirements as sdpa_forward (d_k = d_v = 64, causal only with n_q == n_k). dQ, dK, dV and the workspace must not
+ *   overlap each other or any input. Every element of dQ, dK and dV is written (rows no query can see get 0). */
+int sdpa_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse,
+                  int mask_kind, void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes, int dtype,
+                  int64_t B, int64_t h, int64_t n_q, int64_t n_k, int64_t d_k, int64_t d_v, void* stream);
+
+/* Bytes of workspace sdpa_backward needs for these sizes (0 if the sizes are invalid). */
+size_t sdpa_backward_workspace_size(int dtype, int64_t B, int64_t h, int64_t n_q, int64_t n_k, int64_t d_k,
+                                    int64_t d_v);
 
 /* mha_forward: multi-head attention with learned projections and no biases.
  *   Xq  [B, n_q, d_model]  query-side input; Xkv [B, n_k, d_model] key/value-side input (may be the same pointer

@@ -85,6 +85,52 @@ def test_workspace_size(lib):
     assert lib.mha_workspace_size(BF16, 1, 3, 5, 1, 32, 64) == 0
 
 
+def sdpa_lse(lib, Q=A, K=A * 2, V=A * 3, mask=0, out=A * 1000, lse=A * 1100, dtype=BF16, B=1, h=1, n_q=16, n_k=16,
+             d_k=64, d_v=64):
+    return lib.sdpa_forward_lse(Q, K, V, mask, out, lse, dtype, B, h, n_q, n_k, d_k, d_v, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(lse=None), INVALID), (dict(Q=None), INVALID), (dict(lse=A * 1100 + 4), INVALID), (dict(dtype=5), UNSUPPORTED),
+    (dict(mask=1, n_k=17), UNSUPPORTED), (dict(d_k=128), UNSUPPORTED),
+    # lse [1,1,16] float32 = 64 bytes, placed inside out (2 KiB at A*1000) or inside Q
+    (dict(lse=A * 1000 + 256), INVALID), (dict(lse=A + 16), INVALID),
+])
+def test_sdpa_forward_lse_rejects_bad_arguments(lib, kw, code):
+    assert sdpa_lse(lib, **kw) == code
+    assert lib.attn_last_error().decode().startswith("sdpa_forward_lse")
+
+
+def bwd(lib, Q=A, K=A * 2, V=A * 3, O=A * 4, dO=A * 5, lse=A * 6, mask=0, dQ=A * 100, dK=A * 200, dV=A * 300,
+        ws=A * 400, ws_bytes=1 << 20, dtype=BF16, B=1, h=1, n_q=16, n_k=16, d_k=64, d_v=64):
+    return lib.sdpa_backward(Q, K, V, O, dO, lse, mask, dQ, dK, dV, ws, ws_bytes, dtype, B, h, n_q, n_k, d_k, d_v,
+                             None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(O=None), INVALID), (dict(dO=None), INVALID), (dict(lse=None), INVALID), (dict(dQ=None), INVALID),
+    (dict(dK=None), INVALID), (dict(dV=None), INVALID), (dict(ws=None), INVALID), (dict(ws_bytes=1023), INVALID),
+    (dict(B=0), INVALID), (dict(mask=3), INVALID), (dict(dtype=7), UNSUPPORTED), (dict(d_v=32), UNSUPPORTED),
+    (dict(mask=1, n_q=16, n_k=32), UNSUPPORTED), (dict(n_k=1 << 25), UNSUPPORTED), (dict(dK=A * 200 + 8), INVALID),
+    (dict(lse=A * 6 + 4), INVALID),
+    # outputs over inputs, outputs over each other, workspace over an input
+    (dict(dQ=A * 4), INVALID), (dict(dV=A * 200 + 1024), INVALID), (dict(ws=A * 6), INVALID),
+    (dict(dK=A * 400), INVALID),
+])
+def test_sdpa_backward_rejects_bad_arguments(lib, kw, code):
+    assert bwd(lib, **kw) == code
+    assert lib.attn_last_error().decode().startswith("sdpa_backward")
+
+
+def test_backward_workspace_size(lib):
+    # 1 KiB per (batch, head) and 64-row query tile: lse and D of the tile's rows
+    assert lib.sdpa_backward_workspace_size(BF16, 4, 8, 4096, 4096, 64, 64) == 4 * 8 * 64 * 1024
+    assert lib.sdpa_backward_workspace_size(F32, 1, 1, 65, 3, 64, 64) == 2 * 1024
+    assert lib.sdpa_backward_workspace_size(BF16, 1, 1, 16, 16, 32, 64) == 0
+    assert lib.sdpa_backward_workspace_size(5, 1, 1, 16, 16, 64, 64) == 0
+    assert lib.sdpa_backward_workspace_size(BF16, 0, 1, 16, 16, 64, 64) == 0
+
+
 def test_status_strings(lib):
     assert lib.attn_status_string(0) == b"ATTN_OK"
     assert lib.attn_status_string(2) == b"ATTN_ERR_UNSUPPORTED"

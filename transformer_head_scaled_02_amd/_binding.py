@@ -18,8 +18,8 @@ ATTN_MASK_NONE, ATTN_MASK_CAUSAL = 0, 1
 ATTN_F32, ATTN_BF16 = 0, 1
 
 # every symbol include/mi355_attn.h declares
-EXPORTED = ("sdpa_forward", "mha_forward", "mha_workspace_size", "attn_status_string", "attn_last_error",
-            "probe_scratch_size", "probe_mfma_bf16", "probe_exp_f32", "probe_hbm_copy")
+EXPORTED = ("sdpa_forward", "sdpa_forward_lse", "sdpa_backward", "sdpa_backward_workspace_size", "mha_forward",
+            "mha_workspace_size", "attn_status_string", "attn_last_error", "probe_scratch_size", "probe_mfma_bf16", "probe_exp_f32", "probe_hbm_copy")
 
 _lib = None
 
@@ -43,6 +43,13 @@ def load_library(path: Path | str | None = None) -> ctypes.CDLL:
     i64, vp, ci, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     lib.sdpa_forward.argtypes = [vp, vp, vp, ci, vp, ci, i64, i64, i64, i64, i64, i64, vp]
     lib.sdpa_forward.restype = ci
+    lib.sdpa_forward_lse.argtypes = [vp, vp, vp, ci, vp, vp, ci, i64, i64, i64, i64, i64, i64, vp]
+    lib.sdpa_forward_lse.restype = ci
+    lib.sdpa_backward.argtypes = [vp, vp, vp, vp, vp, vp, ci, vp, vp, vp, vp, sz, ci, i64, i64, i64, i64, i64, i64,
+                                  vp]
+    lib.sdpa_backward.restype = ci
+    lib.sdpa_backward_workspace_size.argtypes = [ci, i64, i64, i64, i64, i64, i64]
+    lib.sdpa_backward_workspace_size.restype = sz
     lib.mha_forward.argtypes = [vp, vp, vp, vp, vp, vp, ci, vp, vp, sz, ci, i64, i64, i64, i64, i64, i64, i64, vp]
     lib.mha_forward.restype = ci
     lib.mha_workspace_size.argtypes = [ci, i64, i64, i64, i64, i64, i64]
@@ -123,6 +130,101 @@ def sdpa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask="none",
     _check(lib.sdpa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), _mask_code(mask), out.data_ptr(),
                             _dtype_code(q), B, h, n_q, n_k, d_k, d_v, _stream_handle(q.device)))
     return out
+
+
+def _sdpa_shapes(q, k, v):
+    q, k, v = _dev_tensor(q, "q"), _dev_tensor(k, "k"), _dev_tensor(v, "v")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, h, n, d]")
+    if not (q.dtype == k.dtype == v.dtype) or not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must share dtype and device")
+    B, h, n_q, d_k = q.shape
+    n_k, d_v = k.shape[2], v.shape[3]
+    if k.shape != (B, h, n_k, d_k) or v.shape[:3] != (B, h, n_k):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    return q, k, v, (B, h, n_q, n_k, d_k, d_v)
+
+
+def _out_tensor(t, name, shape, dtype, device):
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    t = _dev_tensor(t, name)
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != device:
+        raise ValueError(f"{name} has the wrong shape, dtype or device")
+    return t
+
+
+def sdpa_forward_lse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask="none", out: torch.Tensor | None = None,
+                     lse: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """sdpa_forward that also returns the row log-sum-exp of the scaled scores, lse [B,h,n_q] float32 (natural log),
+    the statistic sdpa_backward needs."""
+    lib = load_library()
+    q, k, v, (B, h, n_q, n_k, d_k, d_v) = _sdpa_shapes(q, k, v)
+    out = _out_tensor(out, "out", (B, h, n_q, d_v), q.dtype, q.device)
+    lse = _out_tensor(lse, "lse", (B, h, n_q), torch.float32, q.device)
+    _check(lib.sdpa_forward_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), _mask_code(mask), out.data_ptr(),
+                                lse.data_ptr(), _dtype_code(q), B, h, n_q, n_k, d_k, d_v, _stream_handle(q.device)))
+    return out, lse
+
+
+def sdpa_backward_workspace_size(B: int, h: int, n_q: int, n_k: int, d_k: int = 64, d_v: int = 64,
+                                 dtype: torch.dtype = torch.bfloat16) -> int:
+    lib = load_library()
+    code = ATTN_BF16 if dtype == torch.bfloat16 else ATTN_F32
+    return int(lib.sdpa_backward_workspace_size(code, B, h, n_q, n_k, d_k, d_v))
+
+
+def sdpa_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, dout: torch.Tensor,
+                  lse: torch.Tensor, mask="none", dq: torch.Tensor | None = None, dk: torch.Tensor | None = None,
+                  dv: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """Gradients (dq, dk, dv) of attention given the forward's output `out`, its `lse` (from sdpa_forward_lse) and
+    the upstream gradient `dout` [B,h,n_q,64]. `workspace` (uint8, at least sdpa_backward_workspace_size bytes) may
+    be passed in to avoid an allocation."""
+    lib = load_library()
+    q, k, v, (B, h, n_q, n_k, d_k, d_v) = _sdpa_shapes(q, k, v)
+    out, dout, lse = _dev_tensor(out, "out"), _dev_tensor(dout, "dout"), _dev_tensor(lse, "lse")
+    for t, name in ((out, "out"), (dout, "dout")):
+        if tuple(t.shape) != (B, h, n_q, d_v) or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{name} must be [B, h, n_q, d_v] like the forward output")
+    if tuple(lse.shape) != (B, h, n_q) or lse.dtype != torch.float32 or lse.device != q.device:
+        raise ValueError("lse must be float32 [B, h, n_q]")
+    dq = _out_tensor(dq, "dq", q.shape, q.dtype, q.device)
+    dk = _out_tensor(dk, "dk", k.shape, q.dtype, q.device)
+    dv = _out_tensor(dv, "dv", v.shape, q.dtype, q.device)
+    need = sdpa_backward_workspace_size(B, h, n_q, n_k, d_k, d_v, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    else:
+        workspace = _dev_tensor(workspace, "workspace")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.sdpa_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+                             lse.data_ptr(), _mask_code(mask), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                             workspace.data_ptr(), ws_bytes, _dtype_code(q), B, h, n_q, n_k, d_k, d_v,
+                             _stream_handle(q.device)))
+    return dq, dk, dv
+
+
+class SDPAFunction(torch.autograd.Function):
+    """torch.autograd wrapper: forward = sdpa_forward_lse, backward = sdpa_backward (both in the HIP library)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, mask="none"):
+        q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+        out, lse = sdpa_forward_lse(q, k, v, mask)
+        ctx.save_for_backward(q, k, v, out, lse)
+        ctx.mask = mask
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, out, lse = ctx.saved_tensors
+        dq, dk, dv = sdpa_backward(q, k, v, out, dout.contiguous(), lse, ctx.mask)
+        return dq, dk, dv, None
+
+
+def attention(q, k, v, mask="none"):
+    """Differentiable attention on the HIP library: softmax(q k^T / sqrt(d_k)) v with gradients for q, k and v."""
+    return SDPAFunction.apply(q, k, v, mask)
 
 
 def mha_workspace_size(B: int, n_q: int, n_k: int, h: int, d_k: int = 64, d_v: int = 64,

@@ -1,6 +1,8 @@
 // C-ABI host layer: argument validation, workspace carving and kernel dispatch on the caller's stream.
 //
-// sdpa_forward -> one fused attention launch (bf16 MFMA kernel or fp32 VALU kernel).
+// sdpa_forward -> one fused attention launch (bf16 MFMA kernel or fp32 VALU kernel); sdpa_forward_lse also writes
+//                 the row log-sum-exp.
+// sdpa_backward -> three launches: the per-row pre-pass (D = dO . O and lse into the workspace), dK/dV, dQ.
 // mha_forward  -> Q/K/V projections (one grouped GEMM launch writing per-head layout into the workspace), the fused
 //                 attention writing the concatenated heads, and the W^O GEMM into `out`: three launches, no host sync.
 // Every argument error is returned before the first HIP call; nothing is enqueued in that case.
@@ -31,6 +33,7 @@ namespace {
 
 using mi355::fail_status;
 
+// (a null pointer counts as aligned: optional arguments are checked for null by the caller)
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // byte ranges [a, a+na) and [b, b+nb) intersect
@@ -43,6 +46,8 @@ constexpr size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Largest grid any attention launch would use for these sizes (64 queries per workgroup is the smallest block).
 bool grid_fits(int64_t B, int64_t h, int64_t n_q) { return ((n_q + 63) / 64) * B * h <= 0x7fffffffLL; }
+// The backward launches use blocks of as few as 32 rows of either side.
+bool grid_fits32(int64_t B, int64_t h, int64_t n) { return ((n + 31) / 32) * B * h <= 0x7fffffffLL; }
 
 struct MhaLayout {
   size_t q_off, k_off, v_off, c_off, total;
@@ -73,31 +78,47 @@ ATTN_EXPORT const char* attn_status_string(int status) {
 
 ATTN_EXPORT const char* attn_last_error(void) { return g_err; }
 
-ATTN_EXPORT int sdpa_forward(const void* Q, const void* K, const void* V, int mask_kind, void* out, int dtype,
-                             int64_t B, int64_t h, int64_t n_q, int64_t n_k, int64_t d_k, int64_t d_v, void* stream) {
-  if (!Q || !K || !V || !out) return fail_status(ATTN_ERR_INVALID, "sdpa_forward: null tensor pointer");
-  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail_status(ATTN_ERR_UNSUPPORTED, "sdpa_forward: dtype %d", dtype);
+namespace {
+
+// Shared checks of sdpa_forward / sdpa_forward_lse / sdpa_backward on the tensor sizes; 0 when they pass.
+int check_sdpa_sizes(const char* fn, int dtype, int mask_kind, int64_t B, int64_t h, int64_t n_q, int64_t n_k,
+                     int64_t d_k, int64_t d_v, bool backward) {
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail_status(ATTN_ERR_UNSUPPORTED, "%s: dtype %d", fn, dtype);
   if (mask_kind != ATTN_MASK_NONE && mask_kind != ATTN_MASK_CAUSAL)
-    return fail_status(ATTN_ERR_INVALID, "sdpa_forward: mask_kind %d", mask_kind);
+    return fail_status(ATTN_ERR_INVALID, "%s: mask_kind %d", fn, mask_kind);
   if (B <= 0 || h <= 0 || n_q <= 0 || n_k <= 0 || d_k <= 0 || d_v <= 0)
-    return fail_status(ATTN_ERR_INVALID, "sdpa_forward: sizes must be positive (B=%lld h=%lld n_q=%lld n_k=%lld d_k=%lld "
-                "d_v=%lld)", (long long)B, (long long)h, (long long)n_q, (long long)n_k, (long long)d_k,
-                (long long)d_v);
+    return fail_status(ATTN_ERR_INVALID, "%s: sizes must be positive (B=%lld h=%lld n_q=%lld n_k=%lld d_k=%lld "
+                       "d_v=%lld)", fn, (long long)B, (long long)h, (long long)n_q, (long long)n_k, (long long)d_k,
+                       (long long)d_v);
   if (d_k != 64 || d_v != 64)
-    return fail_status(ATTN_ERR_UNSUPPORTED, "sdpa_forward: head dims d_k=%lld d_v=%lld (only 64 is implemented)",
-                (long long)d_k, (long long)d_v);
+    return fail_status(ATTN_ERR_UNSUPPORTED, "%s: head dims d_k=%lld d_v=%lld (only 64 is implemented)", fn,
+                       (long long)d_k, (long long)d_v);
   if (mask_kind == ATTN_MASK_CAUSAL && n_q != n_k)
-    return fail_status(ATTN_ERR_UNSUPPORTED, "sdpa_forward: causal mask needs n_q == n_k (got %lld, %lld)", (long long)n_q,
-                (long long)n_k);
+    return fail_status(ATTN_ERR_UNSUPPORTED, "%s: causal mask needs n_q == n_k (got %lld, %lld)", fn,
+                       (long long)n_q, (long long)n_k);
   if (n_q > ATTN_MAX_SEQ || n_k > ATTN_MAX_SEQ || B > ATTN_MAX_HEADS || h > ATTN_MAX_HEADS ||
-      B * h > ATTN_MAX_HEADS || !grid_fits(B, h, n_q))
-    return fail_status(ATTN_ERR_UNSUPPORTED, "sdpa_forward: sizes beyond the library limits");
-  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(out))
-    return fail_status(ATTN_ERR_INVALID, "sdpa_forward: pointers must be 16-byte aligned");
+      B * h > ATTN_MAX_HEADS || !grid_fits(B, h, n_q) ||
+      (backward && (!grid_fits32(B, h, n_q) || !grid_fits32(B, h, n_k))))
+    return fail_status(ATTN_ERR_UNSUPPORTED, "%s: sizes beyond the library limits", fn);
+  return ATTN_OK;
+}
+
+int sdpa_forward_impl(const char* fn, const void* Q, const void* K, const void* V, int mask_kind, void* out,
+                      float* lse, int dtype, int64_t B, int64_t h, int64_t n_q, int64_t n_k, int64_t d_k, int64_t d_v,
+                      void* stream) {
+  if (int st = check_sdpa_sizes(fn, dtype, mask_kind, B, h, n_q, n_k, d_k, d_v, false)) return st;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(out) || !aligned16(lse))
+    return fail_status(ATTN_ERR_INVALID, "%s: pointers must be 16-byte aligned", fn);
   const size_t es = dtype == ATTN_BF16 ? 2 : 4;
   const size_t q_bytes = (size_t)B * h * n_q * 64 * es, kv_bytes = (size_t)B * h * n_k * 64 * es;
   if (overlaps(out, q_bytes, Q, q_bytes) || overlaps(out, q_bytes, K, kv_bytes) || overlaps(out, q_bytes, V, kv_bytes))
-    return fail_status(ATTN_ERR_INVALID, "sdpa_forward: out overlaps an input");
+    return fail_status(ATTN_ERR_INVALID, "%s: out overlaps an input", fn);
+  if (lse) {
+    const size_t lse_bytes = (size_t)B * h * n_q * 4;
+    if (overlaps(lse, lse_bytes, Q, q_bytes) || overlaps(lse, lse_bytes, K, kv_bytes) ||
+        overlaps(lse, lse_bytes, V, kv_bytes) || overlaps(lse, lse_bytes, out, q_bytes))
+      return fail_status(ATTN_ERR_INVALID, "%s: lse overlaps another tensor", fn);
+  }
 
   mi355::AttnArgs a{};
   a.Q = Q; a.K = K; a.V = V; a.O = out;
@@ -108,9 +129,81 @@ ATTN_EXPORT int sdpa_forward(const void* Q, const void* K, const void* V, int ma
   a.o_stride_h = n_q * 64;
   a.o_stride_row = 64;
   a.causal = mask_kind == ATTN_MASK_CAUSAL;
+  a.lse = lse;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = dtype == ATTN_BF16 ? mi355::launch_attn_fwd_bf16(a, s) : mi355::launch_attn_fwd_f32(a, s);
-  if (e != hipSuccess) return fail_status(ATTN_ERR_HIP, "sdpa_forward: launch failed: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail_status(ATTN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ATTN_OK;
+}
+
+size_t bwd_workspace_bytes(int64_t B, int64_t h, int64_t n_q) {
+  return (size_t)B * h * ((n_q + 63) / 64) * mi355::kAuxFloatsPerTile * sizeof(float);
+}
+
+}  // namespace
+
+ATTN_EXPORT int sdpa_forward(const void* Q, const void* K, const void* V, int mask_kind, void* out, int dtype,
+                             int64_t B, int64_t h, int64_t n_q, int64_t n_k, int64_t d_k, int64_t d_v, void* stream) {
+  if (!Q || !K || !V || !out) return fail_status(ATTN_ERR_INVALID, "sdpa_forward: null tensor pointer");
+  return sdpa_forward_impl("sdpa_forward", Q, K, V, mask_kind, out, nullptr, dtype, B, h, n_q, n_k, d_k, d_v, stream);
+}
+
+ATTN_EXPORT int sdpa_forward_lse(const void* Q, const void* K, const void* V, int mask_kind, void* out, float* lse,
+                                 int dtype, int64_t B, int64_t h, int64_t n_q, int64_t n_k, int64_t d_k, int64_t d_v,
+                                 void* stream) {
+  if (!Q || !K || !V || !out || !lse) return fail_status(ATTN_ERR_INVALID, "sdpa_forward_lse: null tensor pointer");
+  return sdpa_forward_impl("sdpa_forward_lse", Q, K, V, mask_kind, out, lse, dtype, B, h, n_q, n_k, d_k, d_v,
+                           stream);
+}
+
+ATTN_EXPORT size_t sdpa_backward_workspace_size(int dtype, int64_t B, int64_t h, int64_t n_q, int64_t n_k,
+                                                int64_t d_k, int64_t d_v) {
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return 0;
+  if (B <= 0 || h <= 0 || n_q <= 0 || n_k <= 0 || d_k != 64 || d_v != 64) return 0;
+  if (n_q > ATTN_MAX_SEQ || n_k > ATTN_MAX_SEQ || B > ATTN_MAX_HEADS || h > ATTN_MAX_HEADS || B * h > ATTN_MAX_HEADS)
+    return 0;
+  return bwd_workspace_bytes(B, h, n_q);
+}
+
+ATTN_EXPORT int sdpa_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                              const float* lse, int mask_kind, void* dQ, void* dK, void* dV, void* workspace,
+                              size_t workspace_bytes, int dtype, int64_t B, int64_t h, int64_t n_q, int64_t n_k,
+                              int64_t d_k, int64_t d_v, void* stream) {
+  static const char* fn = "sdpa_backward";
+  if (!Q || !K || !V || !O || !dO || !lse || !dQ || !dK || !dV || !workspace)
+    return fail_status(ATTN_ERR_INVALID, "%s: null pointer", fn);
+  if (int st = check_sdpa_sizes(fn, dtype, mask_kind, B, h, n_q, n_k, d_k, d_v, true)) return st;
+  const size_t need = bwd_workspace_bytes(B, h, n_q);
+  if (workspace_bytes < need)
+    return fail_status(ATTN_ERR_INVALID, "%s: workspace %zu bytes, need %zu", fn, workspace_bytes, need);
+  const void* ptrs[] = {Q, K, V, O, dO, lse, dQ, dK, dV, workspace};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail_status(ATTN_ERR_INVALID, "%s: pointers must be 16-byte aligned", fn);
+  const size_t es = dtype == ATTN_BF16 ? 2 : 4;
+  const size_t q_b = (size_t)B * h * n_q * 64 * es, kv_b = (size_t)B * h * n_k * 64 * es;
+  const size_t lse_b = (size_t)B * h * n_q * 4;
+  const void* ins[] = {Q, K, V, O, dO, lse};
+  const size_t in_b[] = {q_b, kv_b, kv_b, q_b, q_b, lse_b};
+  void* outs[] = {dQ, dK, dV, workspace};
+  const size_t out_b[] = {q_b, kv_b, kv_b, need};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outs[i], out_b[i], ins[j], in_b[j]))
+        return fail_status(ATTN_ERR_INVALID, "%s: an output or the workspace overlaps an input", fn);
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], out_b[i], outs[j], out_b[j]))
+        return fail_status(ATTN_ERR_INVALID, "%s: outputs and workspace must not overlap", fn);
+  }
+
+  mi355::BwdArgs a{};
+  a.Q = Q; a.K = K; a.V = V; a.O = O; a.dO = dO; a.lse = lse;
+  a.aux = static_cast<float*>(workspace);
+  a.dQ = dQ; a.dK = dK; a.dV = dV;
+  a.B = (int)B; a.H = (int)h; a.n_q = (int)n_q; a.n_k = (int)n_k;
+  a.causal = mask_kind == ATTN_MASK_CAUSAL;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = dtype == ATTN_BF16 ? mi355::launch_attn_bwd_bf16(a, s) : mi355::launch_attn_bwd_f32(a, s);
+  if (e != hipSuccess) return fail_status(ATTN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ATTN_OK;
 }
 

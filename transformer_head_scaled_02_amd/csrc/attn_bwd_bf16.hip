@@ -1,0 +1,479 @@
+// Backward pass of scaled dot-product attention, bf16 in/out, d_k = d_v = 64, for gfx950 (MI355X).
+//
+// The forward pass is O = P V with P = softmax(Q K^T / sqrt(64)) row by row ("Attention Is All You Need", lettle.cn
+// translation, section 3.2.1, equation Attention(Q,K,V)); training carries the loss back through it by the chain
+// rule ("Transformer：抛弃循环与卷积的序列建模", jiashun-ye.github.io, section "训练样本", subsection "反向传播").
+// Given Q, K, V, the forward output O, the forward's row log-sum-exp lse and the upstream gradient dO:
+//   P  = exp(Q K^T / 8 - lse)            (recomputed tile by tile from the saved lse, never stored)
+//   dV = P^T dO,   dP = dO V^T,   dS = P o (dP - D) with D_i = dO_i . O_i = sum_j P_ij dP_ij,
+//   dQ = dS K / 8,   dK = dS^T Q / 8.
+// Masked weights (causal: key after query) are exactly 0 and pass no gradient. fp32 accumulation throughout; P and
+// dS are rounded to bf16 where they enter the matrix core; outputs are rounded to bf16 (nearest even).
+//
+// Three launches:
+//  1. attn_bwd_pre: D = dO . O per query row (fp32) and log2(e) * lse, written to the workspace in 64-row tiles;
+//     rows past n_q get lse = +inf and D = 0, so their recomputed weights are exactly 0 wherever they are read.
+//  2. attn_bwd_dkdv: a workgroup of NW waves owns NW*32 keys of one head; each wave keeps the K and V rows of its 32
+//     keys in registers as MFMA B operands. 64-row query tiles (Q rows, dO rows and the tile's lse/D, 17 KB) stream
+//     through a 3-stage LDS ring by global_load_lds_dwordx4. Per tile and 32-row half, S = Q K^T and dP = dO V^T
+//     come out of v_mfma_f32_32x32x16_bf16 with the wave's keys in the lane index and queries in the accumulator
+//     registers; P and dS are formed on the VALU and packed to bf16, which is directly the B operand of
+//     dV^T += dO^T P and dK^T += Q^T dS, whose A operands are transposed LDS reads (ds_read_b64_tr_b16) of the dO
+//     and Q tiles. Four products per tile, no cross-wave reduction, no atomics.
+//  3. attn_bwd_dq: a workgroup of NW waves owns NW*32 queries; each wave keeps its Q and dO rows in registers as B
+//     operands and its rows' lse and D in lanes. K/V tiles stream through the ring; per tile S^T = K Q^T and
+//     dP^T = V dO^T (keys in registers, queries in lanes), dS^T on the VALU packed to bf16 as the B operand of
+//     dQ^T += K^T dS^T, whose A operand is a transposed read of the K tile. Three products per tile.
+// Splitting dQ from dK/dV costs one recomputation of S and dP (seven products per score instead of five) but needs
+// neither atomics nor a transpose of dS, and every output is written once, deterministically.
+// Causal: query tiles wholly before a wave's keys (dK/dV) and key tiles wholly after a wave's queries (dQ) are
+// skipped; the tiles that straddle the diagonal set the future scores to -inf before the exponential.
+#include <math.h>
+
+#include "attn_tile.h"
+#include "launch.h"
+
+namespace mi355 {
+namespace {
+
+constexpr int kStages = 3;                                  // LDS ring depth (tiles)
+constexpr int kAuxElems = kAuxFloatsPerTile * 2;            // one tile's lse/D block in 16-bit LDS elements (1 KB)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kInvSqrtD = 0.125f;                         // 1 / sqrt(64), exact
+
+// LDS element offset of lane (li, g)'s operand row read in k-step ks: row li of a 32-row block, logical 16-byte
+// chunk 4g + ks (the d order every product here uses: k-step ks holds d = 8(4g + ks) .. +7 of lane group g).
+__device__ __forceinline__ int row_off(int li, int g, int ks) { return li * kD + (((4 * g + ks) ^ swz(li)) << 3); }
+
+// Offsets of the two transposed reads that give the A operand of a product contracting over the 64 rows of an LDS
+// tile: for output rows 32mb + (0..31) (tile columns) and k-step ks, lane l needs tile rows 16ks + 4g + (0..3) and
+// 16ks + 8 + 4g + (0..3) of column 32mb + l%32, which is the k order of a 32x32 accumulator's registers 8(ks%2) ..
+// +7 read as a B operand.
+__device__ __forceinline__ int tr_off(int lane, int mb, int hi) {
+  const int g = lane >> 5, jj = (lane & 15) >> 2;
+  const int row = 4 * g + jj + 8 * hi;
+  const int lchunk = 4 * mb + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  return row * kD + ((lchunk ^ swz(row)) << 3) + 4 * (lane & 1);
+}
+__device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, int ks, const int (&off)[2][2], int mb) {
+  const bf16x4 lo = lds_read_tr16x4(tile + ks * 16 * kD + off[mb][0]);
+  const bf16x4 hi = lds_read_tr16x4(tile + ks * 16 * kD + off[mb][1]);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ void settle_f(float& v) { asm volatile("" : "+v"(v)); }
+
+// Copies of one ring stage: 64 rows of tensor `ta` (first 8 KB of the stage) and of `tb` (next 8 KB), each wave
+// moving 16/NW of the 16 one-kilobyte pieces; rows at or past `rows_left` read row rows_left-1 instead. Copy gi
+// moves rows 8(gi%8) .. +7; lane l brings the logical chunk that belongs at physical chunk l%8 of row 8(gi%8) + l/8
+// (the XOR swizzle of swz()). Two per-lane offsets (rows l/8 and 8 + l/8, which carry the swizzle of every row
+// congruent to them mod 16) serve every copy; the rest of the row offset goes into the scalar base.
+template <int NW>
+__device__ __forceinline__ void issue_rows(const uint16_t* ta, const uint16_t* tb, int rows_left, uint32_t stage,
+                                           int wave, int lrow, const uint32_t (&ld_voff)[2]) {
+  constexpr int kLPW = 16 / NW;
+  if (rows_left >= kBN) {
+#pragma unroll
+    for (int i = 0; i < kLPW; ++i) {
+      const int gi = wave * kLPW + i;
+      const int c = gi & 7;
+      lds_dma16((gi < 8 ? ta : tb) + (c >> 1) * 16 * kD, ld_voff[c & 1],
+                stage + (gi < 8 ? 0u : kTileElems * 2u) + (uint32_t)c * 1024u);
+    }
+  } else {
+    // from the unshifted tile base: lane offset = row min(row, last) with the swizzle of destination row `row` (the
+    // 16-row shift is folded back in, so the 32-bit offset stays non-negative)
+    const int last = rows_left - 1;
+    int lr = lrow;
+    asm volatile("" : "+v"(lr));  // computed here, on this rare path, rather than kept live in registers
+#pragma unroll
+    for (int i = 0; i < kLPW; ++i) {
+      const int gi = wave * kLPW + i;
+      const int c = gi & 7;
+      const int row = 8 * c + lr;
+      lds_dma16(gi < 8 ? ta : tb, ld_voff[c & 1] + (uint32_t)((min(row, last) - (8 * (c & 1) + lr)) * kD * 2),
+                stage + (gi < 8 ? 0u : kTileElems * 2u) + (uint32_t)c * 1024u);
+    }
+  }
+}
+
+// D_i = dO_i . O_i and log2(e) * lse_i for one 64-row query tile of one head; 4 threads per row.
+template <class T>
+__global__ __launch_bounds__(256) void attn_bwd_pre(BwdArgs a, int n_tiles) {
+  const int bh = blockIdx.x / n_tiles, t = blockIdx.x % n_tiles;
+  const int r = threadIdx.x >> 2, part = threadIdx.x & 3;
+  const int n_q = a.n_q;
+  const int row = t * kBN + r;
+  float dot = 0.f;
+  if (row < n_q) {
+    const int64_t base = ((int64_t)bh * n_q + row) * kD + 16 * part;
+    if constexpr (sizeof(T) == 2) {
+      const uint4* o = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.O) + base);
+      const uint4* d = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.dO) + base);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const uint4 ov = o[c], dv = d[c];
+        const uint32_t ow[4] = {ov.x, ov.y, ov.z, ov.w}, dw[4] = {dv.x, dv.y, dv.z, dv.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          dot = fmaf(__uint_as_float(ow[j] << 16), __uint_as_float(dw[j] << 16), dot);
+          dot = fmaf(__uint_as_float(ow[j] & 0xffff0000u), __uint_as_float(dw[j] & 0xffff0000u), dot);
+        }
+      }
+    } else {
+      const float4* o = reinterpret_cast<const float4*>(static_cast<const float*>(a.O) + base);
+      const float4* d = reinterpret_cast<const float4*>(static_cast<const float*>(a.dO) + base);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float4 ov = o[c], dv = d[c];
+        dot = fmaf(ov.x, dv.x, dot);
+        dot = fmaf(ov.y, dv.y, dot);
+        dot = fmaf(ov.z, dv.z, dot);
+        dot = fmaf(ov.w, dv.w, dot);
+      }
+    }
+  }
+  dot += __shfl_xor(dot, 1);
+  dot += __shfl_xor(dot, 2);
+  float* at = a.aux + ((int64_t)bh * n_tiles + t) * kAuxFloatsPerTile;
+  if (part == 0) at[r] = row < n_q ? a.lse[(int64_t)bh * n_q + row] * kLog2e : INFINITY;
+  else if (part == 1) at[kBN + r] = row < n_q ? dot : 0.f;
+  else at[2 * kBN + (part - 2) * kBN + r] = 0.f;
+}
+
+// dK and dV: see the file comment (launch 2).
+template <int NW>
+__global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16(BwdArgs a, int n_kblocks) {
+  constexpr int kBK = 32 * NW;                    // keys per workgroup
+  constexpr int kLPW = 16 / NW;                   // Q/dO copies per wave per tile (wave 0 also copies lse/D)
+  constexpr int kStageElems = 2 * kTileElems + kAuxElems;
+  static_assert(16 % NW == 0, "tile copies split evenly over the waves");
+  __shared__ __attribute__((aligned(16))) uint16_t smem[kStages * kStageElems];  // [stage][Q | dO | lse, D]
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int g = lane >> 5, li = lane & 31;
+  const int n_q = a.n_q, n_k = a.n_k;
+  const bool causal = a.causal != 0;
+  const int n_tiles = (n_q + kBN - 1) / kBN;
+
+  const int blk = xcd_remap(blockIdx.x, gridDim.x);
+  const int kb = blk % n_kblocks, bh = blk / n_kblocks;
+  const uint16_t* Qp = static_cast<const uint16_t*>(a.Q) + (int64_t)bh * n_q * kD;
+  const uint16_t* dOp = static_cast<const uint16_t*>(a.dO) + (int64_t)bh * n_q * kD;
+  const uint16_t* Kp = static_cast<const uint16_t*>(a.K) + (int64_t)bh * n_k * kD;
+  const uint16_t* Vp = static_cast<const uint16_t*>(a.V) + (int64_t)bh * n_k * kD;
+  const float* auxp = a.aux + (int64_t)bh * n_tiles * kAuxFloatsPerTile;
+
+  const int k_blk0 = kb * kBK;
+  const int kw0 = k_blk0 + 32 * wave;  // this wave's keys: kw0 .. kw0+31; lane's key kw0 + li
+  const int key = kw0 + li;
+
+  // K and V rows as B operands of S = Q K^T and dP = dO V^T: lane supplies row `key`, d = 8(4g + ks) .. +7.
+  bf16x8 kf[4], vf[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int64_t off = (int64_t)key * kD + 8 * (4 * g + ks);
+    kf[ks] = key < n_k ? *reinterpret_cast<const bf16x8*>(Kp + off) : bf16x8{};
+    vf[ks] = key < n_k ? *reinterpret_cast<const bf16x8*>(Vp + off) : bf16x8{};
+  }
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    settle(kf[ks]);
+    settle(vf[ks]);
+  }
+
+  // Query tiles: causal work starts at the tile holding the workgroup's first key. Per wave, tiles before t_first
+  // hold only rows before all its keys (all weights 0) and tiles from t_nomask on only rows at or after all of them.
+  const int t0 = causal ? k_blk0 / kBN : 0;
+  const int t_first = causal ? kw0 / kBN : 0;
+  const int t_nomask = causal ? (kw0 + 31) / kBN + 1 : 0;
+
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)smem;
+  const int lrow = lane >> 3;
+  uint32_t ld_voff[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int row = 8 * c + lrow;
+    ld_voff[c] = (uint32_t)(row * kD + (((lane & 7) ^ swz(row)) << 3)) * 2u;
+  }
+  auto issue = [&](int t) __attribute__((always_inline)) {
+    const uint32_t stage = smem_lds + (uint32_t)(((t - t0) % kStages) * kStageElems * 2);
+    issue_rows<NW>(Qp + (int64_t)t * kBN * kD, dOp + (int64_t)t * kBN * kD, n_q - t * kBN, stage, wave, lrow,
+                   ld_voff);
+    if (wave == 0) lds_dma16(auxp + (int64_t)t * kAuxFloatsPerTile, (uint32_t)lane * 16u, stage + kTileElems * 4u);
+  };
+
+  int roff[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) roff[ks] = row_off(li, g, ks);
+  int toff[2][2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) toff[mb][hi] = tr_off(lane, mb, hi);
+
+  f32x16 dv[2], dk[2];
+  dv[0] = dv[1] = dk[0] = dk[1] = f32x16{};
+
+  const int nt = n_tiles;
+  issue(t0);
+  if (t0 + 1 < nt) issue(t0 + 1);
+  for (int t = t0; t < nt; ++t) {
+    // wait for this wave's copies of tile t (tile t+1's may stay in flight), then for every wave's
+    if (t + 1 < nt) {
+      if (wave == 0) wait_vmcnt<kLPW + 1>();
+      else wait_vmcnt<kLPW>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    lds_barrier();  // also: every wave is done with tile t-1, whose stage tile t+2 now takes
+    if (t + 2 < nt) issue(t + 2);
+    if (t < t_first) continue;
+    const bool masked = t < t_nomask;
+    const uint16_t* st = smem + ((t - t0) % kStages) * kStageElems;
+    const float* aux = reinterpret_cast<const float*>(st + 2 * kTileElems);
+
+    bf16x8 pp[4], ps[4];  // P and dS in bf16, B operands for k-steps (16 query rows) 0..3 of the tile
+#pragma unroll
+    for (int mq = 0; mq < 2; ++mq) {
+      f32x16 s = {}, dp = {};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        s = mfma32x32x16(*reinterpret_cast<const bf16x8*>(st + mq * 32 * kD + roff[ks]), kf[ks], s);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        dp = mfma32x32x16(*reinterpret_cast<const bf16x8*>(st + kTileElems + mq * 32 * kD + roff[ks]), vf[ks], dp);
+      // register r holds query row 32mq + 8(r/4) + 4g + r%4 of the tile: its lse and D come in fours
+      f32x4 lq[4], dq[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lq[i] = *reinterpret_cast<const f32x4*>(aux + 32 * mq + 8 * i + 4 * g);
+        dq[i] = *reinterpret_cast<const f32x4*>(aux + kBN + 32 * mq + 8 * i + 4 * g);
+      }
+      float p[16], ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float sv = s[r];
+        if (masked && key > t * kBN + 32 * mq + 8 * (r >> 2) + 4 * g + (r & 3)) sv = -INFINITY;
+        p[r] = fast_exp2(__builtin_fmaf(sv, kScaleLog2, -lq[r >> 2][r & 3]));
+        ds[r] = p[r] * (dp[r] - dq[r >> 2][r & 3]);
+      }
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        uint32_t wp[4], wd[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          wp[j] = pack_bf16x2(p[8 * hf + 2 * j], p[8 * hf + 2 * j + 1]);
+          wd[j] = pack_bf16x2(ds[8 * hf + 2 * j], ds[8 * hf + 2 * j + 1]);
+        }
+        pp[2 * mq + hf] = __builtin_bit_cast(bf16x8, (uint4){wp[0], wp[1], wp[2], wp[3]});
+        ps[2 * mq + hf] = __builtin_bit_cast(bf16x8, (uint4){wd[0], wd[1], wd[2], wd[3]});
+      }
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS, contracting over the tile's 64 query rows
+#pragma unroll
+    for (int kq = 0; kq < 4; ++kq)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        dv[mb] = mfma32x32x16(tr_operand(st + kTileElems, kq, toff, mb), pp[kq], dv[mb]);
+        dk[mb] = mfma32x32x16(tr_operand(st, kq, toff, mb), ps[kq], dk[mb]);
+      }
+  }
+
+  // lane holds d = 32mb + 8(r/4) + 4g + r%4 of its key's dV and dK rows
+  if (key < n_k) {
+    uint16_t* dvrow = static_cast<uint16_t*>(a.dV) + ((int64_t)bh * n_k + key) * kD;
+    uint16_t* dkrow = static_cast<uint16_t*>(a.dK) + ((int64_t)bh * n_k + key) * kD;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int d = 32 * mb + 8 * rg + 4 * g;
+        const uint2 wv = {pack_bf16x2(dv[mb][4 * rg], dv[mb][4 * rg + 1]),
+                          pack_bf16x2(dv[mb][4 * rg + 2], dv[mb][4 * rg + 3])};
+        const uint2 wk = {pack_bf16x2(dk[mb][4 * rg] * kInvSqrtD, dk[mb][4 * rg + 1] * kInvSqrtD),
+                          pack_bf16x2(dk[mb][4 * rg + 2] * kInvSqrtD, dk[mb][4 * rg + 3] * kInvSqrtD)};
+        *reinterpret_cast<uint2*>(dvrow + d) = wv;
+        *reinterpret_cast<uint2*>(dkrow + d) = wk;
+      }
+  }
+}
+
+// dQ: see the file comment (launch 3).
+template <int NW>
+__global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dq_bf16(BwdArgs a, int n_qblocks) {
+  constexpr int kBM = 32 * NW;  // queries per workgroup
+  static_assert(16 % NW == 0, "tile copies split evenly over the waves");
+  __shared__ __attribute__((aligned(16))) uint16_t smem[kStages * 2 * kTileElems];  // [stage][K | V]
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int g = lane >> 5, li = lane & 31;
+  const int n_q = a.n_q, n_k = a.n_k;
+  const bool causal = a.causal != 0;
+  const int n_tiles_q = (n_q + kBN - 1) / kBN;
+
+  const int blk = xcd_remap(blockIdx.x, gridDim.x);
+  int qb = blk % n_qblocks;
+  const int bh = blk / n_qblocks;
+  if (causal) qb = n_qblocks - 1 - qb;  // heaviest query blocks first
+  const uint16_t* Qp = static_cast<const uint16_t*>(a.Q) + (int64_t)bh * n_q * kD;
+  const uint16_t* dOp = static_cast<const uint16_t*>(a.dO) + (int64_t)bh * n_q * kD;
+  const uint16_t* Kp = static_cast<const uint16_t*>(a.K) + (int64_t)bh * n_k * kD;
+  const uint16_t* Vp = static_cast<const uint16_t*>(a.V) + (int64_t)bh * n_k * kD;
+  const float* auxp = a.aux + (int64_t)bh * n_tiles_q * kAuxFloatsPerTile;
+
+  const int q_blk0 = qb * kBM;
+  const int qw0 = q_blk0 + 32 * wave;
+  const int q = qw0 + li;
+
+  // Q and dO rows as B operands of S^T = K Q^T and dP^T = V dO^T (d = 8(4g + ks) .. +7); zero past n_q
+  bf16x8 qf[4], df[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int64_t off = (int64_t)q * kD + 8 * (4 * g + ks);
+    qf[ks] = q < n_q ? *reinterpret_cast<const bf16x8*>(Qp + off) : bf16x8{};
+    df[ks] = q < n_q ? *reinterpret_cast<const bf16x8*>(dOp + off) : bf16x8{};
+  }
+  float lse2 = INFINITY, dq_d = 0.f;  // rows past n_q: weights 0
+  if (q < n_q) {
+    const float* at = auxp + (int64_t)(q / kBN) * kAuxFloatsPerTile;
+    lse2 = at[q % kBN];
+    dq_d = at[kBN + q % kBN];
+  }
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    settle(qf[ks]);
+    settle(df[ks]);
+  }
+  settle_f(lse2);
+  settle_f(dq_d);
+
+  int nt = (n_k + kBN - 1) / kBN;
+  if (causal) nt = min(nt, (q_blk0 + kBM - 1) / kBN + 1);
+  // tiles before t_mask need no mask for any query of this wave; tiles from t_skip on lie entirely in its future
+  const int t_mask = min(causal ? qw0 / kBN : nt, n_k / kBN);
+  const int t_skip = causal ? min(nt, (qw0 + 31) / kBN + 1) : nt;
+  const int key_lim = (causal ? min(q, n_k - 1) : n_k - 1) - 4 * g;  // keys past it (from the lane's first) masked
+
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)smem;
+  const int lrow = lane >> 3;
+  uint32_t ld_voff[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int row = 8 * c + lrow;
+    ld_voff[c] = (uint32_t)(row * kD + (((lane & 7) ^ swz(row)) << 3)) * 2u;
+  }
+  auto issue = [&](int t) __attribute__((always_inline)) {
+    const uint32_t stage = smem_lds + (uint32_t)((t % kStages) * 2 * kTileElems * 2);
+    issue_rows<NW>(Kp + (int64_t)t * kBN * kD, Vp + (int64_t)t * kBN * kD, n_k - t * kBN, stage, wave, lrow, ld_voff);
+  };
+
+  int roff[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) roff[ks] = row_off(li, g, ks);
+  int toff[2][2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) toff[mb][hi] = tr_off(lane, mb, hi);
+
+  f32x16 dq[2];
+  dq[0] = dq[1] = f32x16{};
+
+  constexpr int kLPW = 16 / NW;
+  issue(0);
+  if (1 < nt) issue(1);
+  for (int t = 0; t < nt; ++t) {
+    if (t + 1 < nt) wait_vmcnt<kLPW>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    if (t + 2 < nt) issue(t + 2);
+    if (t >= t_skip) continue;
+    const bool masked = t >= t_mask;
+    const uint16_t* st = smem + (t % kStages) * 2 * kTileElems;
+
+    // S^T and dP^T: register r of block kb holds key 32kb + 8(r/4) + 4g + r%4 of the tile, query = lane's
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = dp[kb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        s[kb] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(st + kb * 32 * kD + roff[ks]), qf[ks], s[kb]);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        dp[kb] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(st + kTileElems + kb * 32 * kD + roff[ks]), df[ks],
+                              dp[kb]);
+    }
+    if (masked) {
+      const int lim = key_lim - t * kBN;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = -INFINITY;
+    }
+    // dS^T in bf16, B operand of k-step ks: registers 8(ks%2) .. +7 of key block ks/2
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int kb = ks >> 1, base = 8 * (ks & 1);
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float p0 = fast_exp2(__builtin_fmaf(s[kb][base + 2 * j], kScaleLog2, -lse2));
+        const float p1 = fast_exp2(__builtin_fmaf(s[kb][base + 2 * j + 1], kScaleLog2, -lse2));
+        w[j] = pack_bf16x2(p0 * (dp[kb][base + 2 * j] - dq_d), p1 * (dp[kb][base + 2 * j + 1] - dq_d));
+      }
+      const bf16x8 pds = __builtin_bit_cast(bf16x8, (uint4){w[0], w[1], w[2], w[3]});
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) dq[mb] = mfma32x32x16(tr_operand(st, ks, toff, mb), pds, dq[mb]);
+    }
+  }
+
+  // dQ = dQ^T / 8; lane holds d = 32mb + 8(r/4) + 4g + r%4 of its query
+  if (q < n_q) {
+    uint16_t* row = static_cast<uint16_t*>(a.dQ) + ((int64_t)bh * n_q + q) * kD;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const uint2 w = {pack_bf16x2(dq[mb][4 * rg] * kInvSqrtD, dq[mb][4 * rg + 1] * kInvSqrtD),
+                         pack_bf16x2(dq[mb][4 * rg + 2] * kInvSqrtD, dq[mb][4 * rg + 3] * kInvSqrtD)};
+        *reinterpret_cast<uint2*>(row + 32 * mb + 8 * rg + 4 * g) = w;
+      }
+  }
+}
+
+bool grid_ok(int64_t n) { return n > 0 && n <= 0x7fffffff; }
+
+}  // namespace
+
+hipError_t launch_attn_bwd_pre(const BwdArgs& a, bool f32, hipStream_t stream) {
+  const int n_tiles = (a.n_q + kBN - 1) / kBN;
+  const int64_t nb = (int64_t)n_tiles * a.B * a.H;
+  if (!grid_ok(nb)) return hipErrorInvalidValue;
+  if (f32) hipLaunchKernelGGL(attn_bwd_pre<float>, dim3((unsigned)nb), dim3(256), 0, stream, a, n_tiles);
+  else hipLaunchKernelGGL(attn_bwd_pre<uint16_t>, dim3((unsigned)nb), dim3(256), 0, stream, a, n_tiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
+  constexpr int NW = 4;
+  const int n_kblocks = (a.n_k + 32 * NW - 1) / (32 * NW);
+  const int n_qblocks = (a.n_q + 32 * NW - 1) / (32 * NW);
+  const int64_t nb_kv = (int64_t)n_kblocks * a.B * a.H, nb_q = (int64_t)n_qblocks * a.B * a.H;
+  if (!grid_ok(nb_kv) || !grid_ok(nb_q)) return hipErrorInvalidValue;
+  hipError_t e = launch_attn_bwd_pre(a, false, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_bwd_dkdv_bf16<NW>), dim3((unsigned)nb_kv), dim3(64 * NW), 0, stream, a, n_kblocks);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_bwd_dq_bf16<NW>), dim3((unsigned)nb_q), dim3(64 * NW), 0, stream, a, n_qblocks);
+  return hipGetLastError();
+}
+
+}  // namespace mi355

@@ -1,0 +1,169 @@
+// Backward pass of scaled dot-product attention in fp32 throughout, d_k = d_v = 64, for gfx950.
+//
+// Same mathematics as the bf16 backward (the chain rule through O = P V, the row softmax and S = Q K^T / sqrt(64):
+// "Transformer：抛弃循环与卷积的序列建模", section "训练样本", subsection "反向传播"; forward definition "Attention Is
+// All You Need", lettle.cn translation, section 3.2.1), with every value in fp32, P and dS included. This path serves
+// small fp32 problems, so it is plain VALU code: two threads per row, each holding one 32-wide half of the row's
+// vectors, partial dot products combined with one lane exchange; the other side's rows are staged in LDS in tiles of
+// 32 and read as broadcasts. The per-row lse and D come from the shared pre-pass (workspace tiles of 64 rows).
+#include <math.h>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace mi355 {
+namespace {
+
+constexpr int kD = 64;
+constexpr int kHalf = 32;
+constexpr int kRows = 32;  // rows per workgroup (two threads each) and per staged tile
+constexpr float kC = (float)(1.4426950408889634 / 8.0);  // log2(e) / sqrt(64)
+constexpr float kInvSqrtD = 0.125f;
+
+// lse2 (= log2(e) * lse) and D of query row i of head bh, from the workspace tiles
+__device__ __forceinline__ float2 aux_row(const float* aux, int n_tiles, int bh, int i) {
+  const float* at = aux + ((int64_t)bh * n_tiles + i / 64) * kAuxFloatsPerTile;
+  return float2{at[i % 64], at[64 + i % 64]};
+}
+
+// dK and dV: a workgroup owns 32 keys; query rows stream through LDS.
+__global__ __launch_bounds__(2 * kRows) void attn_bwd_dkdv_f32(BwdArgs a) {
+  __shared__ float Qs[kRows][kD], dOs[kRows][kD], Ls[kRows], Ds[kRows];
+  const int tid = threadIdx.x, h = tid & 1;
+  const int n_q = a.n_q, n_k = a.n_k, n_tiles = (n_q + 63) / 64;
+  const int nkb = (n_k + kRows - 1) / kRows;
+  const int bh = blockIdx.x / nkb, k0 = (blockIdx.x % nkb) * kRows;
+  const int key = k0 + (tid >> 1);
+  const float* Qp = static_cast<const float*>(a.Q) + (int64_t)bh * n_q * kD;
+  const float* dOp = static_cast<const float*>(a.dO) + (int64_t)bh * n_q * kD;
+  const float* Kp = static_cast<const float*>(a.K) + (int64_t)bh * n_k * kD;
+  const float* Vp = static_cast<const float*>(a.V) + (int64_t)bh * n_k * kD;
+
+  float k[kHalf], v[kHalf], dk[kHalf], dv[kHalf];
+#pragma unroll
+  for (int d = 0; d < kHalf; ++d) {
+    k[d] = key < n_k ? Kp[(int64_t)key * kD + kHalf * h + d] : 0.f;
+    v[d] = key < n_k ? Vp[(int64_t)key * kD + kHalf * h + d] : 0.f;
+    dk[d] = dv[d] = 0.f;
+  }
+  // causal: rows before k0 see none of these keys
+  for (int q0 = a.causal ? k0 : 0; q0 < n_q; q0 += kRows) {
+    __syncthreads();
+    for (int e = tid; e < kRows * kD; e += 2 * kRows) {
+      const int r = e / kD, c = e % kD;
+      const bool ok = q0 + r < n_q;
+      Qs[r][c] = ok ? Qp[(int64_t)(q0 + r) * kD + c] : 0.f;
+      dOs[r][c] = ok ? dOp[(int64_t)(q0 + r) * kD + c] : 0.f;
+    }
+    if (tid < kRows) {
+      const bool ok = q0 + tid < n_q;
+      const float2 ld = ok ? aux_row(a.aux, n_tiles, bh, q0 + tid) : float2{INFINITY, 0.f};
+      Ls[tid] = ld.x;
+      Ds[tid] = ld.y;
+    }
+    __syncthreads();
+    for (int i = 0; i < kRows; ++i) {
+      float s = 0.f, dp = 0.f;
+#pragma unroll
+      for (int d = 0; d < kHalf; ++d) {
+        s = fmaf(k[d], Qs[i][kHalf * h + d], s);
+        dp = fmaf(v[d], dOs[i][kHalf * h + d], dp);
+      }
+      s += __shfl_xor(s, 1);
+      dp += __shfl_xor(dp, 1);
+      const int row = q0 + i;
+      float p = fast_exp2(fmaf(s, kC, -Ls[i]));  // 0 for rows past n_q (lse = +inf)
+      if (a.causal && key > row) p = 0.f;
+      const float ds = p * (dp - Ds[i]);
+#pragma unroll
+      for (int d = 0; d < kHalf; ++d) {
+        dv[d] = fmaf(p, dOs[i][kHalf * h + d], dv[d]);
+        dk[d] = fmaf(ds, Qs[i][kHalf * h + d], dk[d]);
+      }
+    }
+  }
+  if (key < n_k) {
+    float* dkr = static_cast<float*>(a.dK) + ((int64_t)bh * n_k + key) * kD + kHalf * h;
+    float* dvr = static_cast<float*>(a.dV) + ((int64_t)bh * n_k + key) * kD + kHalf * h;
+#pragma unroll
+    for (int d = 0; d < kHalf; d += 4) {
+      *reinterpret_cast<float4*>(dvr + d) = float4{dv[d], dv[d + 1], dv[d + 2], dv[d + 3]};
+      *reinterpret_cast<float4*>(dkr + d) =
+          float4{dk[d] * kInvSqrtD, dk[d + 1] * kInvSqrtD, dk[d + 2] * kInvSqrtD, dk[d + 3] * kInvSqrtD};
+    }
+  }
+}
+
+// dQ: a workgroup owns 32 queries; key/value rows stream through LDS.
+__global__ __launch_bounds__(2 * kRows) void attn_bwd_dq_f32(BwdArgs a) {
+  __shared__ float Ks[kRows][kD], Vs[kRows][kD];
+  const int tid = threadIdx.x, h = tid & 1;
+  const int n_q = a.n_q, n_k = a.n_k, n_tiles = (n_q + 63) / 64;
+  const int nqb = (n_q + kRows - 1) / kRows;
+  const int bh = blockIdx.x / nqb, qb0 = (blockIdx.x % nqb) * kRows;
+  const int qi = qb0 + (tid >> 1);
+  const float* Qp = static_cast<const float*>(a.Q) + (int64_t)bh * n_q * kD;
+  const float* dOp = static_cast<const float*>(a.dO) + (int64_t)bh * n_q * kD;
+  const float* Kp = static_cast<const float*>(a.K) + (int64_t)bh * n_k * kD;
+  const float* Vp = static_cast<const float*>(a.V) + (int64_t)bh * n_k * kD;
+
+  float q[kHalf], o[kHalf], dq[kHalf];
+#pragma unroll
+  for (int d = 0; d < kHalf; ++d) {
+    q[d] = qi < n_q ? Qp[(int64_t)qi * kD + kHalf * h + d] : 0.f;
+    o[d] = qi < n_q ? dOp[(int64_t)qi * kD + kHalf * h + d] : 0.f;
+    dq[d] = 0.f;
+  }
+  const float2 ld = qi < n_q ? aux_row(a.aux, n_tiles, bh, qi) : float2{INFINITY, 0.f};
+  const int k_end = a.causal ? min(n_k, qb0 + kRows) : n_k;  // keys after the block's last query are never needed
+  for (int k0 = 0; k0 < k_end; k0 += kRows) {
+    __syncthreads();
+    for (int e = tid; e < kRows * kD; e += 2 * kRows) {
+      const int r = e / kD, c = e % kD;
+      const bool ok = k0 + r < n_k;
+      Ks[r][c] = ok ? Kp[(int64_t)(k0 + r) * kD + c] : 0.f;
+      Vs[r][c] = ok ? Vp[(int64_t)(k0 + r) * kD + c] : 0.f;
+    }
+    __syncthreads();
+    for (int j = 0; j < kRows; ++j) {
+      float s = 0.f, dp = 0.f;
+#pragma unroll
+      for (int d = 0; d < kHalf; ++d) {
+        s = fmaf(q[d], Ks[j][kHalf * h + d], s);
+        dp = fmaf(o[d], Vs[j][kHalf * h + d], dp);
+      }
+      s += __shfl_xor(s, 1);
+      dp += __shfl_xor(dp, 1);
+      const int key = k0 + j;
+      float p = fast_exp2(fmaf(s, kC, -ld.x));
+      if (key >= n_k || (a.causal && key > qi)) p = 0.f;
+      const float ds = p * (dp - ld.y);
+#pragma unroll
+      for (int d = 0; d < kHalf; ++d) dq[d] = fmaf(ds, Ks[j][kHalf * h + d], dq[d]);
+    }
+  }
+  if (qi < n_q) {
+    float* r = static_cast<float*>(a.dQ) + ((int64_t)bh * n_q + qi) * kD + kHalf * h;
+#pragma unroll
+    for (int d = 0; d < kHalf; d += 4)
+      *reinterpret_cast<float4*>(r + d) =
+          float4{dq[d] * kInvSqrtD, dq[d + 1] * kInvSqrtD, dq[d + 2] * kInvSqrtD, dq[d + 3] * kInvSqrtD};
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd_f32(const BwdArgs& a, hipStream_t stream) {
+  const int64_t nb_kv = (int64_t)((a.n_k + kRows - 1) / kRows) * a.B * a.H;
+  const int64_t nb_q = (int64_t)((a.n_q + kRows - 1) / kRows) * a.B * a.H;
+  if (nb_kv <= 0 || nb_kv > 0x7fffffff || nb_q <= 0 || nb_q > 0x7fffffff) return hipErrorInvalidValue;
+  hipError_t e = launch_attn_bwd_pre(a, true, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_bwd_dkdv_f32, dim3((unsigned)nb_kv), dim3(2 * kRows), 0, stream, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_bwd_dq_f32, dim3((unsigned)nb_q), dim3(2 * kRows), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace mi355

@@ -383,6 +383,8 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, i
     const int q = qw0 + 32 * h + li;
     if (q < n_q) {
       const float inv = 1.0f / l[h];
+      // row log-sum-exp of the scaled scores, natural log: log2(sum_j exp2(s_j c)) = m + log2(l)
+      if (a.lse != nullptr && g == 0) a.lse[(int64_t)bh * n_q + q] = (__builtin_amdgcn_logf(l[h]) - neg_m[h]) * kLn2;
       uint16_t* orow = Op + (int64_t)q * a.o_stride_row;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)

@@ -87,6 +87,8 @@ __global__ __launch_bounds__(kBQ) void attn_fwd_f32_d64(AttnArgs a, int n_qblock
   }
   if (qi < n_q) {
     const float inv = 1.0f / l;
+    // row log-sum-exp of the scaled scores, natural log: log2(sum_j exp2(s_j c)) = m + log2(l)
+    if (a.lse != nullptr) a.lse[(int64_t)bh * n_q + qi] = (m + __builtin_amdgcn_logf(l)) * 0.6931471805599453f;
     float* orow = Op + (int64_t)qi * a.o_stride_row;
 #pragma unroll
     for (int d = 0; d < kD; d += 4)

@@ -15,6 +15,7 @@ constexpr int kD = 64;                      // head width
 constexpr int kBN = 64;                     // keys per tile
 constexpr int kTileElems = kBN * kD;        // one 64 x 64 bf16 tile (K or V), 8 KB
 constexpr float kScaleLog2 = (float)(1.4426950408889634 / 8.0);  // log2(e) / sqrt(64)
+constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kTileSumLimit = 1048576.0f;  // 2^20: largest accepted per-tile row sum of P
 
 // 16-byte chunk swizzle of tile row r (depends on r mod 16): logical chunk c of row r is stored at chunk c ^ swz(r).

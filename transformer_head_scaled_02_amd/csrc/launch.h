@@ -18,10 +18,33 @@ struct AttnArgs {
   int64_t q_stride_bh, k_stride_bh;   // elements between consecutive (b,h) heads of Q and of K/V
   int64_t o_stride_b, o_stride_h, o_stride_row;
   int causal;
+  float* lse;  // optional (nullptr: not written): row log-sum-exp of query i of head bh at lse[bh*n_q + i]
 };
 
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attn_fwd_f32(const AttnArgs& a, hipStream_t stream);
+
+// Backward pass of attention over [B, H] heads of width 64, every tensor dense [B, H, n, 64] in the element type.
+// `aux` is the workspace: per head and per 64-row query tile, 256 floats = [log2(e)*lse of the 64 rows | D of the 64
+// rows | 128 zeros], where D_i = dO_i . O_i; rows past n_q hold lse = +inf and D = 0 (their weights come out 0).
+struct BwdArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const void* O;
+  const void* dO;
+  const float* lse;  // [B, H, n_q], natural log
+  float* aux;
+  void* dQ;
+  void* dK;
+  void* dV;
+  int B, H, n_q, n_k;
+  int causal;
+};
+constexpr int kAuxFloatsPerTile = 256;
+hipError_t launch_attn_bwd_pre(const BwdArgs& a, bool f32, hipStream_t stream);  // fills `aux`
+hipError_t launch_attn_bwd_bf16(const BwdArgs& a, hipStream_t stream);  // pre-pass, dK/dV, dQ
+hipError_t launch_attn_bwd_f32(const BwdArgs& a, hipStream_t stream);
 
 // C = A[M,K] * W[K,N] in bf16 with fp32 accumulation, up to three independent problems in one launch.
 // Row-major C (ldc = N) when head_seq == 0; otherwise "head-major": column n of row m goes to

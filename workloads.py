@@ -36,6 +36,11 @@ WORKLOADS = {
                                   causal=False, seed=1005),
     "sdpa_causal_bf16_b4_h8_n4096": dict(kind="sdpa", dtype="bf16", B=4, h=8, n_q=4096, n_k=4096, d_k=64, d_v=64,
                                          causal=True, seed=1005),
+    # backward pass (dQ, dK, dV) of the long-sequence attention: the same Q, K, V and an upstream gradient ~ N(0,1)
+    "sdpa_bwd_bf16_b4_h8_n4096": dict(kind="sdpa_bwd", dtype="bf16", B=4, h=8, n_q=4096, n_k=4096, d_k=64, d_v=64,
+                                      causal=False, seed=1005),
+    "sdpa_bwd_causal_bf16_b4_h8_n4096": dict(kind="sdpa_bwd", dtype="bf16", B=4, h=8, n_q=4096, n_k=4096, d_k=64,
+                                             d_v=64, causal=True, seed=1005),
 }
 
 
@@ -82,13 +87,17 @@ def _rng(seed: int) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(seed))
 
 
-def make_sdpa_inputs(B, h, n_q, n_k, d_k, d_v, dtype, seed, scale_q=1.0):
-    """Q [B,h,n_q,d_k], K [B,h,n_k,d_k], V [B,h,n_k,d_v], each ~ N(0,1), drawn in the order Q, K, V."""
+def make_sdpa_inputs(B, h, n_q, n_k, d_k, d_v, dtype, seed, scale_q=1.0, dout=False):
+    """Q [B,h,n_q,d_k], K [B,h,n_k,d_k], V [B,h,n_k,d_v], each ~ N(0,1), drawn in the order Q, K, V; with `dout`
+    also an upstream gradient dO [B,h,n_q,d_v] ~ N(0,1), drawn after V (Q, K, V are the same with or without it)."""
     rng = _rng(seed)
     q = rng.standard_normal((B, h, n_q, d_k)) * scale_q
     k = rng.standard_normal((B, h, n_k, d_k))
     v = rng.standard_normal((B, h, n_k, d_v))
-    return {"Q": quantise(q, dtype), "K": quantise(k, dtype), "V": quantise(v, dtype)}
+    out = {"Q": quantise(q, dtype), "K": quantise(k, dtype), "V": quantise(v, dtype)}
+    if dout:
+        out["dO"] = quantise(rng.standard_normal((B, h, n_q, d_v)), dtype)
+    return out
 
 
 def make_mha_inputs(B, n_q, n_k, d_model, h, d_k, d_v, dtype, seed, cross=False):
@@ -113,7 +122,8 @@ def make_mha_inputs(B, n_q, n_k, d_model, h, d_k, d_v, dtype, seed, cross=False)
 def make_workload(name: str):
     """Inputs of a named workload (see WORKLOADS)."""
     w = WORKLOADS[name]
-    if w["kind"] == "sdpa":
-        return make_sdpa_inputs(w["B"], w["h"], w["n_q"], w["n_k"], w["d_k"], w["d_v"], w["dtype"], w["seed"])
+    if w["kind"] in ("sdpa", "sdpa_bwd"):
+        return make_sdpa_inputs(w["B"], w["h"], w["n_q"], w["n_k"], w["d_k"], w["d_v"], w["dtype"], w["seed"],
+                                dout=w["kind"] == "sdpa_bwd")
     return make_mha_inputs(w["B"], w["n_q"], w["n_k"], w["d_model"], w["h"], w["d_k"], w["d_v"], w["dtype"],
                            w["seed"], cross=w["n_q"] != w["n_k"])
