@@ -27,6 +27,12 @@ Readings where the pages leave a step open:
   * The backward pass of attention is the exact derivative of the forward function: given an upstream gradient dO
     (the derivative of some loss L with respect to O), it returns dL/dQ, dL/dK and dL/dV, i.e. the gradient of
     L = sum(dO * O) with the forward outputs O treated as a function of Q, K and V.
+  * Key padding ("Transformer：抛弃循环与卷积的序列建模", section "训练样本", subsection "反向传播": <PAD> positions
+    added to fill a batch of different-length sequences are excluded by a padding mask; section "训练配置",
+    "训练数据与 Batching": batches group sequences of similar length). With per-sequence valid key counts kv_len[b],
+    keys j >= kv_len[b] of batch b get score -inf (weight exactly 0), like masked future keys. A row left with no key
+    it may see (kv_len[b] = 0) has no softmax; its output is read as 0, its log-sum-exp as -inf, and it passes no
+    gradient.
   * The row log-sum-exp of the scaled scores, lse_i = log sum_j exp(s_ij) over the keys the row may see, is the
     statistic a forward pass hands to the backward pass: the weights are then exp(s_ij - lse_i).
   * Projections carry no bias (the attention formulas on the pages have none). The row-vector convention X W is used:
@@ -56,25 +62,35 @@ def _causal_disallowed(n_q, n_k, q_index):
     return np.arange(n_k)[None, :] > q_index[:, None]
 
 
-def sdpa_weights_head(q, k, causal=False, q_index=None):
-    """Attention weights softmax(q k^T / sqrt(d_k)) of one head. q [n_q, d_k], k [n_k, d_k] -> [n_q, n_k]."""
+def _masked_scores(q, k, causal, q_index, n_valid):
+    """Scaled scores q k^T / sqrt(d_k) of one head with -inf where the key may not be seen (after the query under the
+    causal mask, or at or past n_valid)."""
     q = _as_f64(q)
     k = _as_f64(k)
     if q.ndim != 2 or k.ndim != 2 or q.shape[1] != k.shape[1]:
         raise ValueError("q [n_q, d_k] and k [n_k, d_k] expected")
-    d_k = q.shape[1]
-    s = (q @ k.T) / math.sqrt(d_k)                       # dot products divided by sqrt(d_k)
+    s = (q @ k.T) / math.sqrt(q.shape[1])                # dot products divided by sqrt(d_k)
     if causal:
         s = np.where(_causal_disallowed(s.shape[0], s.shape[1], q_index), -np.inf, s)
-    m = s.max(axis=1, keepdims=True)                     # finite: every row keeps at least its own position
+    if n_valid is not None:
+        s[:, max(int(n_valid), 0):] = -np.inf            # padding keys
+    return s
+
+
+def sdpa_weights_head(q, k, causal=False, q_index=None, n_valid=None):
+    """Attention weights softmax(q k^T / sqrt(d_k)) of one head. q [n_q, d_k], k [n_k, d_k] -> [n_q, n_k].
+    `n_valid`: only keys 0 .. n_valid-1 are real (the rest are padding); a row with no key to see gets weights 0."""
+    s = _masked_scores(q, k, causal, q_index, n_valid)
+    empty = np.isneginf(s).all(axis=1, keepdims=True)    # only possible with padding
+    m = np.where(empty, 0.0, s.max(axis=1, keepdims=True))
     e = np.exp(s - m)
-    return e / e.sum(axis=1, keepdims=True)
+    return np.where(empty, 0.0, e / np.where(empty, 1.0, e.sum(axis=1, keepdims=True)))
 
 
-def sdpa_head(q, k, v, causal=False, q_index=None):
+def sdpa_head(q, k, v, causal=False, q_index=None, n_valid=None):
     """Output softmax(q k^T / sqrt(d_k)) v of one head. v [n_k, d_v] -> [n_q, d_v]."""
     v = _as_f64(v)
-    w = sdpa_weights_head(q, k, causal, q_index)
+    w = sdpa_weights_head(q, k, causal, q_index, n_valid)
     if v.ndim != 2 or v.shape[0] != w.shape[1]:
         raise ValueError("v [n_k, d_v] expected")
     return w @ v
@@ -96,13 +112,38 @@ def _per_head(fn, Q, *rest, **kw):
     return outs
 
 
-def sdpa_weights_ref(Q, K, causal=False, q_index=None):
-    """Attention weights for every leading (batch, head) index. Q [..., n_q, d_k], K [..., n_k, d_k]."""
+def _per_batch_head(fn, kv_len, Q, *rest, **kw):
+    """fn over [B, h, ...] tensors with the padding length of batch b passed as n_valid."""
+    Q = _as_f64(Q)
+    if Q.ndim != 4:
+        raise ValueError("kv_len needs [B, h, n, d] tensors")
+    kv_len = np.asarray(kv_len)
+    if kv_len.shape != (Q.shape[0],):
+        raise ValueError("kv_len must give one length per batch entry")
+    rest = [_as_f64(r) for r in rest]
+    outs = None
+    for b in range(Q.shape[0]):
+        for hh in range(Q.shape[1]):
+            o = fn(Q[b, hh], *[r[b, hh] for r in rest], n_valid=int(kv_len[b]), **kw)
+            if outs is None:
+                outs = np.empty(Q.shape[:2] + np.shape(o), dtype=np.float64)
+            outs[b, hh] = o
+    return outs
+
+
+def sdpa_weights_ref(Q, K, causal=False, q_index=None, kv_len=None):
+    """Attention weights for every leading (batch, head) index. Q [..., n_q, d_k], K [..., n_k, d_k].
+    `kv_len` [B] (with [B, h, n, d] tensors): keys j >= kv_len[b] of batch b are padding."""
+    if kv_len is not None:
+        return _per_batch_head(sdpa_weights_head, kv_len, Q, K, causal=causal, q_index=q_index)
     return _per_head(sdpa_weights_head, Q, K, causal=causal, q_index=q_index)
 
 
-def sdpa_ref(Q, K, V, causal=False, q_index=None):
-    """Scaled dot-product attention, head by head. Q [..., n_q, d_k], K [..., n_k, d_k], V [..., n_k, d_v]."""
+def sdpa_ref(Q, K, V, causal=False, q_index=None, kv_len=None):
+    """Scaled dot-product attention, head by head. Q [..., n_q, d_k], K [..., n_k, d_k], V [..., n_k, d_v].
+    `kv_len` [B] (with [B, h, n, d] tensors): keys j >= kv_len[b] of batch b are padding."""
+    if kv_len is not None:
+        return _per_batch_head(sdpa_head, kv_len, Q, K, V, causal=causal, q_index=q_index)
     return _per_head(sdpa_head, Q, K, V, causal=causal, q_index=q_index)
 
 
@@ -154,27 +195,25 @@ def sdpa_brute(q, k, v, causal=False):
     return out
 
 
-def sdpa_lse_head(q, k, causal=False, q_index=None):
+def sdpa_lse_head(q, k, causal=False, q_index=None, n_valid=None):
     """Row log-sum-exp of the scaled scores of one head: lse_i = log sum_j exp(q_i . k_j / sqrt(d_k)) over the keys
-    query i may see (natural log). q [n_q, d_k], k [n_k, d_k] -> [n_q]."""
-    q = _as_f64(q)
-    k = _as_f64(k)
-    if q.ndim != 2 or k.ndim != 2 or q.shape[1] != k.shape[1]:
-        raise ValueError("q [n_q, d_k] and k [n_k, d_k] expected")
-    s = (q @ k.T) / math.sqrt(q.shape[1])
-    if causal:
-        s = np.where(_causal_disallowed(s.shape[0], s.shape[1], q_index), -np.inf, s)
-    m = s.max(axis=1)                                    # the max shift again only avoids overflow
-    return m + np.log(np.exp(s - m[:, None]).sum(axis=1))
+    query i may see (natural log; -inf for a row with none). q [n_q, d_k], k [n_k, d_k] -> [n_q]."""
+    s = _masked_scores(q, k, causal, q_index, n_valid)
+    empty = np.isneginf(s).all(axis=1)
+    m = np.where(empty, 0.0, s.max(axis=1))              # the max shift again only avoids overflow
+    with np.errstate(divide="ignore"):
+        return np.where(empty, -np.inf, m + np.log(np.exp(s - m[:, None]).sum(axis=1)))
 
 
-def sdpa_lse_ref(Q, K, causal=False, q_index=None):
+def sdpa_lse_ref(Q, K, causal=False, q_index=None, kv_len=None):
     """Row log-sum-exp for every leading (batch, head) index. Q [..., n_q, d_k], K [..., n_k, d_k] -> [..., n_q]."""
-    return _per_head(lambda q, k, **kw: sdpa_lse_head(q, k, **kw)[:, None], Q, K, causal=causal,
-                     q_index=q_index)[..., 0]
+    fn = lambda q, k, **kw: sdpa_lse_head(q, k, **kw)[:, None]  # noqa: E731
+    if kv_len is not None:
+        return _per_batch_head(fn, kv_len, Q, K, causal=causal, q_index=q_index)[..., 0]
+    return _per_head(fn, Q, K, causal=causal, q_index=q_index)[..., 0]
 
 
-def sdpa_backward_head(q, k, v, dout, causal=False, q_index=None):
+def sdpa_backward_head(q, k, v, dout, causal=False, q_index=None, n_valid=None):
     """Gradients (dq, dk, dv) of L = sum(dout * O) for one head, O = softmax(q k^T / sqrt(d_k)) v.
 
     The chain rule through the three steps of the forward pass, from the output back:
@@ -187,7 +226,7 @@ def sdpa_backward_head(q, k, v, dout, causal=False, q_index=None):
     """
     v = _as_f64(v)
     dout = _as_f64(dout)
-    w = sdpa_weights_head(q, k, causal, q_index)
+    w = sdpa_weights_head(q, k, causal, q_index, n_valid)
     if v.ndim != 2 or v.shape[0] != w.shape[1] or dout.shape != (w.shape[0], v.shape[1]):
         raise ValueError("v [n_k, d_v] and dout [n_q, d_v] expected")
     q = _as_f64(q)
@@ -201,16 +240,20 @@ def sdpa_backward_head(q, k, v, dout, causal=False, q_index=None):
     return dq, dk, dv
 
 
-def sdpa_backward_ref(Q, K, V, dO, causal=False):
+def sdpa_backward_ref(Q, K, V, dO, causal=False, kv_len=None):
     """(dQ, dK, dV) of attention for every leading (batch, head) index, head by head.
 
     Q [..., n_q, d_k], K [..., n_k, d_k], V [..., n_k, d_v], dO [..., n_q, d_v] -> arrays shaped like Q, K, V.
+    `kv_len` [B] (with [B, h, n, d] tensors): keys j >= kv_len[b] of batch b are padding (their gradients are 0).
     """
     Q, K, V, dO = (_as_f64(a) for a in (Q, K, V, dO))
     lead = Q.shape[:-2]
     if K.shape[:-2] != lead or V.shape[:-2] != lead or dO.shape[:-2] != lead:
         raise ValueError("leading (batch, head) dimensions differ")
+    if kv_len is not None and (len(lead) != 2 or np.shape(kv_len) != (lead[0],)):
+        raise ValueError("kv_len needs [B, h, n, d] tensors and one length per batch entry")
     dQ, dK, dV = np.empty_like(Q), np.empty_like(K), np.empty_like(V)
     for idx in np.ndindex(*lead):
-        dQ[idx], dK[idx], dV[idx] = sdpa_backward_head(Q[idx], K[idx], V[idx], dO[idx], causal)
+        n_valid = None if kv_len is None else int(kv_len[idx[0]])
+        dQ[idx], dK[idx], dV[idx] = sdpa_backward_head(Q[idx], K[idx], V[idx], dO[idx], causal, n_valid=n_valid)
     return dQ, dK, dV
