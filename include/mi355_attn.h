@@ -77,10 +77,26 @@ int sdpa_forward(const void* Q, const void* K, const void* V, int mask_kind, voi
 int sdpa_forward_lse(const void* Q, const void* K, const void* V, int mask_kind, void* out, float* lse, int dtype,
                      int64_t B, int64_t h, int64_t n_q, int64_t n_k, int64_t d_k, int64_t d_v, void* stream);
 
+/* sdpa_forward_padded: sdpa_forward with a key padding mask, for batches of sequences of different lengths padded to
+ * n_k ("Transformer：抛弃循环与卷积的序列建模", section "训练样本": <PAD> positions that fill a batch are excluded by
+ * a padding mask; section "训练配置": batches group sequences of similar length).
+ *   kv_len [B] int32, device: batch entry b has min(max(kv_len[b], 0), n_k) real keys; keys j >= kv_len[b] get weight
+ *          exactly 0, their K and V rows are never read (any contents, NaN included, are fine) and key tiles wholly
+ *          past the length cost nothing. A row left with no key (kv_len[b] <= 0) gets output 0 (and lse -inf).
+ *          Query rows are not masked: every row's output is computed over its batch entry's real keys.
+ *   lse: optional (NULL: not written); as for sdpa_forward_lse.
+ *   Combined with ATTN_MASK_CAUSAL, query i sees keys j <= i with j < kv_len[b].
+ *   Other arguments, requirements and errors as sdpa_forward_lse; kv_len must not overlap out or lse. */
+int sdpa_forward_padded(const void* Q, const void* K, const void* V, const int32_t* kv_len, int mask_kind, void* out,
+                        float* lse, int dtype, int64_t B, int64_t h, int64_t n_q, int64_t n_k, int64_t d_k,
+                        int64_t d_v, void* stream);
+
 /* sdpa_backward: gradients of attention.
  *   Q, K, V      the forward inputs, as for sdpa_forward
- *   O   [B, h, n_q, d_v]  the forward output and lse [B, h, n_q] float32 its row log-sum-exp (sdpa_forward_lse with
- *                         the same Q, K, V and mask_kind)
+ *   O   [B, h, n_q, d_v]  the forward output and lse [B, h, n_q] float32 its row log-sum-exp (sdpa_forward_lse, or
+ *                         sdpa_forward_padded with the same kv_len, on the same Q, K, V and mask_kind)
+ *   kv_len [B] int32 or NULL: the key padding of the forward pass (NULL: none); gradients of padding keys' K and V
+ *          rows are written as 0, and rows that saw no key pass no gradient
  *   dO  [B, h, n_q, d_v]  dL/dO, the upstream gradient
  *   dQ  [B, h, n_q, d_k], dK [B, h, n_k, d_k], dV [B, h, n_k, d_v]: written with dL/dQ, dL/dK, dL/dV:
  *       P = exp(Q K^T / sqrt(d_k) - lse) (0 where masked), dV = P^T dO, dP = dO V^T,
@@ -90,10 +106,11 @@ int sdpa_forward_lse(const void* Q, const void* K, const void* V, int mask_kind,
  *   dtype: ATTN_BF16 (bf16 tensors, float32 accumulation, P and dS rounded to bf16 where they enter the matrix core,
  *          outputs rounded to nearest even) or ATTN_F32 (float32 throughout). lse is float32 in both.
  *   Requirements as sdpa_forward (d_k = d_v = 64, causal only with n_q == n_k). dQ, dK, dV and the workspace must not
- *   overlap each other or any input. Every element of dQ, dK and dV is written (rows no query can see get 0). */
+ *   overlap each other or any input. Every element of dQ, dK and dV is written. */
 int sdpa_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse,
-                  int mask_kind, void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes, int dtype,
-                  int64_t B, int64_t h, int64_t n_q, int64_t n_k, int64_t d_k, int64_t d_v, void* stream);
+                  const int32_t* kv_len, int mask_kind, void* dQ, void* dK, void* dV, void* workspace,
+                  size_t workspace_bytes, int dtype, int64_t B, int64_t h, int64_t n_q, int64_t n_k, int64_t d_k,
+                  int64_t d_v, void* stream);
 
 /* Bytes of workspace sdpa_backward needs for these sizes (0 if the sizes are invalid). */
 size_t sdpa_backward_workspace_size(int dtype, int64_t B, int64_t h, int64_t n_q, int64_t n_k, int64_t d_k,

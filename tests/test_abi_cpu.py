@@ -101,10 +101,10 @@ def test_sdpa_forward_lse_rejects_bad_arguments(lib, kw, code):
     assert lib.attn_last_error().decode().startswith("sdpa_forward_lse")
 
 
-def bwd(lib, Q=A, K=A * 2, V=A * 3, O=A * 4, dO=A * 5, lse=A * 6, mask=0, dQ=A * 100, dK=A * 200, dV=A * 300,
-        ws=A * 400, ws_bytes=1 << 20, dtype=BF16, B=1, h=1, n_q=16, n_k=16, d_k=64, d_v=64):
-    return lib.sdpa_backward(Q, K, V, O, dO, lse, mask, dQ, dK, dV, ws, ws_bytes, dtype, B, h, n_q, n_k, d_k, d_v,
-                             None)
+def bwd(lib, Q=A, K=A * 2, V=A * 3, O=A * 4, dO=A * 5, lse=A * 6, kv_len=None, mask=0, dQ=A * 100, dK=A * 200,
+        dV=A * 300, ws=A * 400, ws_bytes=1 << 20, dtype=BF16, B=1, h=1, n_q=16, n_k=16, d_k=64, d_v=64):
+    return lib.sdpa_backward(Q, K, V, O, dO, lse, kv_len, mask, dQ, dK, dV, ws, ws_bytes, dtype, B, h, n_q, n_k, d_k,
+                             d_v, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -115,11 +115,27 @@ def bwd(lib, Q=A, K=A * 2, V=A * 3, O=A * 4, dO=A * 5, lse=A * 6, mask=0, dQ=A *
     (dict(lse=A * 6 + 4), INVALID),
     # outputs over inputs, outputs over each other, workspace over an input
     (dict(dQ=A * 4), INVALID), (dict(dV=A * 200 + 1024), INVALID), (dict(ws=A * 6), INVALID),
-    (dict(dK=A * 400), INVALID),
+    (dict(dK=A * 400), INVALID), (dict(kv_len=A * 7 + 4), INVALID), (dict(kv_len=A * 100 + 64), INVALID),
 ])
 def test_sdpa_backward_rejects_bad_arguments(lib, kw, code):
     assert bwd(lib, **kw) == code
     assert lib.attn_last_error().decode().startswith("sdpa_backward")
+
+
+def padded(lib, Q=A, K=A * 2, V=A * 3, kv_len=A * 4, mask=0, out=A * 1000, lse=None, dtype=BF16, B=1, h=1, n_q=16,
+           n_k=16, d_k=64, d_v=64):
+    return lib.sdpa_forward_padded(Q, K, V, kv_len, mask, out, lse, dtype, B, h, n_q, n_k, d_k, d_v, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kv_len=None), INVALID), (dict(out=None), INVALID), (dict(kv_len=A * 4 + 4), INVALID),
+    (dict(kv_len=A * 1000 + 16), INVALID), (dict(lse=A * 1100, kv_len=A * 1100 + 32), INVALID),
+    (dict(dtype=9), UNSUPPORTED), (dict(mask=1, n_k=20), UNSUPPORTED), (dict(d_v=16), UNSUPPORTED),
+    (dict(B=-1), INVALID), (dict(lse=A * 1000 + 256), INVALID),
+])
+def test_sdpa_forward_padded_rejects_bad_arguments(lib, kw, code):
+    assert padded(lib, **kw) == code
+    assert lib.attn_last_error().decode().startswith("sdpa_forward_padded")
 
 
 def test_backward_workspace_size(lib):

@@ -18,7 +18,7 @@ ATTN_MASK_NONE, ATTN_MASK_CAUSAL = 0, 1
 ATTN_F32, ATTN_BF16 = 0, 1
 
 # every symbol include/mi355_attn.h declares
-EXPORTED = ("sdpa_forward", "sdpa_forward_lse", "sdpa_backward", "sdpa_backward_workspace_size", "mha_forward",
+EXPORTED = ("sdpa_forward", "sdpa_forward_lse", "sdpa_forward_padded", "sdpa_backward", "sdpa_backward_workspace_size", "mha_forward",
             "mha_workspace_size", "attn_status_string", "attn_last_error", "probe_scratch_size", "probe_mfma_bf16", "probe_exp_f32", "probe_hbm_copy")
 
 _lib = None
@@ -45,7 +45,9 @@ def load_library(path: Path | str | None = None) -> ctypes.CDLL:
     lib.sdpa_forward.restype = ci
     lib.sdpa_forward_lse.argtypes = [vp, vp, vp, ci, vp, vp, ci, i64, i64, i64, i64, i64, i64, vp]
     lib.sdpa_forward_lse.restype = ci
-    lib.sdpa_backward.argtypes = [vp, vp, vp, vp, vp, vp, ci, vp, vp, vp, vp, sz, ci, i64, i64, i64, i64, i64, i64,
+    lib.sdpa_forward_padded.argtypes = [vp, vp, vp, vp, ci, vp, vp, ci, i64, i64, i64, i64, i64, i64, vp]
+    lib.sdpa_forward_padded.restype = ci
+    lib.sdpa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, vp, vp, vp, vp, sz, ci, i64, i64, i64, i64, i64, i64,
                                   vp]
     lib.sdpa_backward.restype = ci
     lib.sdpa_backward_workspace_size.argtypes = [ci, i64, i64, i64, i64, i64, i64]
@@ -167,6 +169,30 @@ def sdpa_forward_lse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask="no
     return out, lse
 
 
+def _kv_len_tensor(kv_len, B, device):
+    kv_len = _dev_tensor(kv_len, "kv_len")
+    if tuple(kv_len.shape) != (B,) or kv_len.dtype != torch.int32 or kv_len.device != device:
+        raise ValueError("kv_len must be an int32 GPU tensor [B] on the inputs' device")
+    return kv_len
+
+
+def sdpa_forward_padded(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_len: torch.Tensor, mask="none",
+                        out: torch.Tensor | None = None, lse: torch.Tensor | None = None, return_lse: bool = False):
+    """Attention with a key padding mask: keys j >= kv_len[b] of batch entry b (int32 [B] on the GPU) get weight 0;
+    rows with no real key give 0. Returns out, or (out, lse) with return_lse (or when `lse` is passed)."""
+    lib = load_library()
+    q, k, v, (B, h, n_q, n_k, d_k, d_v) = _sdpa_shapes(q, k, v)
+    kv_len = _kv_len_tensor(kv_len, B, q.device)
+    out = _out_tensor(out, "out", (B, h, n_q, d_v), q.dtype, q.device)
+    want_lse = return_lse or lse is not None
+    if want_lse:
+        lse = _out_tensor(lse, "lse", (B, h, n_q), torch.float32, q.device)
+    _check(lib.sdpa_forward_padded(q.data_ptr(), k.data_ptr(), v.data_ptr(), kv_len.data_ptr(), _mask_code(mask),
+                                   out.data_ptr(), lse.data_ptr() if want_lse else None, _dtype_code(q), B, h, n_q,
+                                   n_k, d_k, d_v, _stream_handle(q.device)))
+    return (out, lse) if want_lse else out
+
+
 def sdpa_backward_workspace_size(B: int, h: int, n_q: int, n_k: int, d_k: int = 64, d_v: int = 64,
                                  dtype: torch.dtype = torch.bfloat16) -> int:
     lib = load_library()
@@ -176,10 +202,11 @@ def sdpa_backward_workspace_size(B: int, h: int, n_q: int, n_k: int, d_k: int = 
 
 def sdpa_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, dout: torch.Tensor,
                   lse: torch.Tensor, mask="none", dq: torch.Tensor | None = None, dk: torch.Tensor | None = None,
-                  dv: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
-    """Gradients (dq, dk, dv) of attention given the forward's output `out`, its `lse` (from sdpa_forward_lse) and
-    the upstream gradient `dout` [B,h,n_q,64]. `workspace` (uint8, at least sdpa_backward_workspace_size bytes) may
-    be passed in to avoid an allocation."""
+                  dv: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                  kv_len: torch.Tensor | None = None):
+    """Gradients (dq, dk, dv) of attention given the forward's output `out`, its `lse` (from sdpa_forward_lse, or
+    sdpa_forward_padded with the same `kv_len`) and the upstream gradient `dout` [B,h,n_q,64]. `workspace` (uint8,
+    at least sdpa_backward_workspace_size bytes) may be passed in to avoid an allocation."""
     lib = load_library()
     q, k, v, (B, h, n_q, n_k, d_k, d_v) = _sdpa_shapes(q, k, v)
     out, dout, lse = _dev_tensor(out, "out"), _dev_tensor(dout, "dout"), _dev_tensor(lse, "lse")
@@ -197,34 +224,40 @@ def sdpa_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.
     else:
         workspace = _dev_tensor(workspace, "workspace")
     ws_bytes = workspace.numel() * workspace.element_size()
+    kv_ptr = _kv_len_tensor(kv_len, B, q.device).data_ptr() if kv_len is not None else None
     _check(lib.sdpa_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
-                             lse.data_ptr(), _mask_code(mask), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                             lse.data_ptr(), kv_ptr, _mask_code(mask), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                              workspace.data_ptr(), ws_bytes, _dtype_code(q), B, h, n_q, n_k, d_k, d_v,
                              _stream_handle(q.device)))
     return dq, dk, dv
 
 
 class SDPAFunction(torch.autograd.Function):
-    """torch.autograd wrapper: forward = sdpa_forward_lse, backward = sdpa_backward (both in the HIP library)."""
+    """torch.autograd wrapper: forward = sdpa_forward_lse (sdpa_forward_padded with kv_len), backward = sdpa_backward
+    (all in the HIP library)."""
 
     @staticmethod
-    def forward(ctx, q, k, v, mask="none"):
+    def forward(ctx, q, k, v, mask="none", kv_len=None):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
-        out, lse = sdpa_forward_lse(q, k, v, mask)
+        if kv_len is None:
+            out, lse = sdpa_forward_lse(q, k, v, mask)
+        else:
+            out, lse = sdpa_forward_padded(q, k, v, kv_len, mask, return_lse=True)
         ctx.save_for_backward(q, k, v, out, lse)
-        ctx.mask = mask
+        ctx.mask, ctx.kv_len = mask, kv_len
         return out
 
     @staticmethod
     def backward(ctx, dout):
         q, k, v, out, lse = ctx.saved_tensors
-        dq, dk, dv = sdpa_backward(q, k, v, out, dout.contiguous(), lse, ctx.mask)
-        return dq, dk, dv, None
+        dq, dk, dv = sdpa_backward(q, k, v, out, dout.contiguous(), lse, ctx.mask, kv_len=ctx.kv_len)
+        return dq, dk, dv, None, None
 
 
-def attention(q, k, v, mask="none"):
-    """Differentiable attention on the HIP library: softmax(q k^T / sqrt(d_k)) v with gradients for q, k and v."""
-    return SDPAFunction.apply(q, k, v, mask)
+def attention(q, k, v, mask="none", kv_len=None):
+    """Differentiable attention on the HIP library: softmax(q k^T / sqrt(d_k)) v with gradients for q, k and v;
+    `kv_len` (int32 [B] on the GPU) adds the key padding mask."""
+    return SDPAFunction.apply(q, k, v, mask, kv_len)
 
 
 def mha_workspace_size(B: int, n_q: int, n_k: int, h: int, d_k: int = 64, d_v: int = 64,

@@ -2,6 +2,7 @@
 //
 // sdpa_forward -> one fused attention launch (bf16 MFMA kernel or fp32 VALU kernel); sdpa_forward_lse also writes
 //                 the row log-sum-exp.
+// sdpa_forward_padded -> the same launch with per-batch key counts (key padding mask).
 // sdpa_backward -> three launches: the per-row pre-pass (D = dO . O and lse into the workspace), dK/dV, dQ.
 // mha_forward  -> Q/K/V projections (one grouped GEMM launch writing per-head layout into the workspace), the fused
 //                 attention writing the concatenated heads, and the W^O GEMM into `out`: three launches, no host sync.
@@ -103,11 +104,11 @@ int check_sdpa_sizes(const char* fn, int dtype, int mask_kind, int64_t B, int64_
   return ATTN_OK;
 }
 
-int sdpa_forward_impl(const char* fn, const void* Q, const void* K, const void* V, int mask_kind, void* out,
-                      float* lse, int dtype, int64_t B, int64_t h, int64_t n_q, int64_t n_k, int64_t d_k, int64_t d_v,
-                      void* stream) {
+int sdpa_forward_impl(const char* fn, const void* Q, const void* K, const void* V, const int32_t* kv_len,
+                      int mask_kind, void* out, float* lse, int dtype, int64_t B, int64_t h, int64_t n_q, int64_t n_k,
+                      int64_t d_k, int64_t d_v, void* stream) {
   if (int st = check_sdpa_sizes(fn, dtype, mask_kind, B, h, n_q, n_k, d_k, d_v, false)) return st;
-  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(out) || !aligned16(lse))
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(out) || !aligned16(lse) || !aligned16(kv_len))
     return fail_status(ATTN_ERR_INVALID, "%s: pointers must be 16-byte aligned", fn);
   const size_t es = dtype == ATTN_BF16 ? 2 : 4;
   const size_t q_bytes = (size_t)B * h * n_q * 64 * es, kv_bytes = (size_t)B * h * n_k * 64 * es;
@@ -118,6 +119,11 @@ int sdpa_forward_impl(const char* fn, const void* Q, const void* K, const void* 
     if (overlaps(lse, lse_bytes, Q, q_bytes) || overlaps(lse, lse_bytes, K, kv_bytes) ||
         overlaps(lse, lse_bytes, V, kv_bytes) || overlaps(lse, lse_bytes, out, q_bytes))
       return fail_status(ATTN_ERR_INVALID, "%s: lse overlaps another tensor", fn);
+  }
+  if (kv_len) {
+    const size_t len_bytes = (size_t)B * 4;
+    if (overlaps(kv_len, len_bytes, out, q_bytes) || (lse && overlaps(kv_len, len_bytes, lse, (size_t)B * h * n_q * 4)))
+      return fail_status(ATTN_ERR_INVALID, "%s: kv_len overlaps an output", fn);
   }
 
   mi355::AttnArgs a{};
@@ -130,6 +136,7 @@ int sdpa_forward_impl(const char* fn, const void* Q, const void* K, const void* 
   a.o_stride_row = 64;
   a.causal = mask_kind == ATTN_MASK_CAUSAL;
   a.lse = lse;
+  a.kv_len = kv_len;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = dtype == ATTN_BF16 ? mi355::launch_attn_fwd_bf16(a, s) : mi355::launch_attn_fwd_f32(a, s);
   if (e != hipSuccess) return fail_status(ATTN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
@@ -145,14 +152,24 @@ size_t bwd_workspace_bytes(int64_t B, int64_t h, int64_t n_q) {
 ATTN_EXPORT int sdpa_forward(const void* Q, const void* K, const void* V, int mask_kind, void* out, int dtype,
                              int64_t B, int64_t h, int64_t n_q, int64_t n_k, int64_t d_k, int64_t d_v, void* stream) {
   if (!Q || !K || !V || !out) return fail_status(ATTN_ERR_INVALID, "sdpa_forward: null tensor pointer");
-  return sdpa_forward_impl("sdpa_forward", Q, K, V, mask_kind, out, nullptr, dtype, B, h, n_q, n_k, d_k, d_v, stream);
+  return sdpa_forward_impl("sdpa_forward", Q, K, V, nullptr, mask_kind, out, nullptr, dtype, B, h, n_q, n_k, d_k, d_v,
+                           stream);
+}
+
+ATTN_EXPORT int sdpa_forward_padded(const void* Q, const void* K, const void* V, const int32_t* kv_len, int mask_kind,
+                                    void* out, float* lse, int dtype, int64_t B, int64_t h, int64_t n_q, int64_t n_k,
+                                    int64_t d_k, int64_t d_v, void* stream) {
+  if (!Q || !K || !V || !kv_len || !out)
+    return fail_status(ATTN_ERR_INVALID, "sdpa_forward_padded: null tensor pointer");
+  return sdpa_forward_impl("sdpa_forward_padded", Q, K, V, kv_len, mask_kind, out, lse, dtype, B, h, n_q, n_k, d_k, d_v,
+                           stream);
 }
 
 ATTN_EXPORT int sdpa_forward_lse(const void* Q, const void* K, const void* V, int mask_kind, void* out, float* lse,
                                  int dtype, int64_t B, int64_t h, int64_t n_q, int64_t n_k, int64_t d_k, int64_t d_v,
                                  void* stream) {
   if (!Q || !K || !V || !out || !lse) return fail_status(ATTN_ERR_INVALID, "sdpa_forward_lse: null tensor pointer");
-  return sdpa_forward_impl("sdpa_forward_lse", Q, K, V, mask_kind, out, lse, dtype, B, h, n_q, n_k, d_k, d_v,
+  return sdpa_forward_impl("sdpa_forward_lse", Q, K, V, nullptr, mask_kind, out, lse, dtype, B, h, n_q, n_k, d_k, d_v,
                            stream);
 }
 
@@ -166,7 +183,8 @@ ATTN_EXPORT size_t sdpa_backward_workspace_size(int dtype, int64_t B, int64_t h,
 }
 
 ATTN_EXPORT int sdpa_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
-                              const float* lse, int mask_kind, void* dQ, void* dK, void* dV, void* workspace,
+                              const float* lse, const int32_t* kv_len, int mask_kind, void* dQ, void* dK, void* dV,
+                              void* workspace,
                               size_t workspace_bytes, int dtype, int64_t B, int64_t h, int64_t n_q, int64_t n_k,
                               int64_t d_k, int64_t d_v, void* stream) {
   static const char* fn = "sdpa_backward";
@@ -176,18 +194,18 @@ ATTN_EXPORT int sdpa_backward(const void* Q, const void* K, const void* V, const
   const size_t need = bwd_workspace_bytes(B, h, n_q);
   if (workspace_bytes < need)
     return fail_status(ATTN_ERR_INVALID, "%s: workspace %zu bytes, need %zu", fn, workspace_bytes, need);
-  const void* ptrs[] = {Q, K, V, O, dO, lse, dQ, dK, dV, workspace};
+  const void* ptrs[] = {Q, K, V, O, dO, lse, dQ, dK, dV, workspace, kv_len};
   for (const void* p : ptrs)
     if (!aligned16(p)) return fail_status(ATTN_ERR_INVALID, "%s: pointers must be 16-byte aligned", fn);
   const size_t es = dtype == ATTN_BF16 ? 2 : 4;
   const size_t q_b = (size_t)B * h * n_q * 64 * es, kv_b = (size_t)B * h * n_k * 64 * es;
   const size_t lse_b = (size_t)B * h * n_q * 4;
-  const void* ins[] = {Q, K, V, O, dO, lse};
-  const size_t in_b[] = {q_b, kv_b, kv_b, q_b, q_b, lse_b};
+  const void* ins[] = {Q, K, V, O, dO, lse, kv_len};
+  const size_t in_b[] = {q_b, kv_b, kv_b, q_b, q_b, lse_b, kv_len ? (size_t)B * 4 : 0};
   void* outs[] = {dQ, dK, dV, workspace};
   const size_t out_b[] = {q_b, kv_b, kv_b, need};
   for (int i = 0; i < 4; ++i) {
-    for (int j = 0; j < 6; ++j)
+    for (int j = 0; j < 7; ++j)
       if (overlaps(outs[i], out_b[i], ins[j], in_b[j]))
         return fail_status(ATTN_ERR_INVALID, "%s: an output or the workspace overlaps an input", fn);
     for (int j = i + 1; j < 4; ++j)
@@ -201,6 +219,7 @@ ATTN_EXPORT int sdpa_backward(const void* Q, const void* K, const void* V, const
   a.dQ = dQ; a.dK = dK; a.dV = dV;
   a.B = (int)B; a.H = (int)h; a.n_q = (int)n_q; a.n_k = (int)n_k;
   a.causal = mask_kind == ATTN_MASK_CAUSAL;
+  a.kv_len = kv_len;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = dtype == ATTN_BF16 ? mi355::launch_attn_bwd_bf16(a, s) : mi355::launch_attn_bwd_f32(a, s);
   if (e != hipSuccess) return fail_status(ATTN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));

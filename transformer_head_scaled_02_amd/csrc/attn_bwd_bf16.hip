@@ -36,7 +36,6 @@
 namespace mi355 {
 namespace {
 
-constexpr int kStages = 3;                                  // LDS ring depth (tiles)
 constexpr int kAuxElems = kAuxFloatsPerTile * 2;            // one tile's lse/D block in 16-bit LDS elements (1 KB)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kInvSqrtD = 0.125f;                         // 1 / sqrt(64), exact
@@ -97,6 +96,15 @@ __device__ __forceinline__ void issue_rows(const uint16_t* ta, const uint16_t* t
   }
 }
 
+// Wait until at most `ahead` tiles of this wave's copies (kPer vector-memory operations each) are still in flight.
+template <int kPer, int kStages>
+__device__ __forceinline__ void wait_copies(int ahead) {
+  static_assert(kStages >= 2 && kStages <= 4 && kPer * (kStages - 2) < 64, "ring depth");
+  if (kStages >= 4 && ahead >= 2) wait_vmcnt<(kStages >= 4 ? 2 * kPer : 0)>();
+  else if (kStages >= 3 && ahead >= 1) wait_vmcnt<(kStages >= 3 ? kPer : 0)>();
+  else wait_vmcnt<0>();
+}
+
 // D_i = dO_i . O_i and log2(e) * lse_i for one 64-row query tile of one head; 4 threads per row.
 template <class T>
 __global__ __launch_bounds__(256) void attn_bwd_pre(BwdArgs a, int n_tiles) {
@@ -136,13 +144,17 @@ __global__ __launch_bounds__(256) void attn_bwd_pre(BwdArgs a, int n_tiles) {
   dot += __shfl_xor(dot, 1);
   dot += __shfl_xor(dot, 2);
   float* at = a.aux + ((int64_t)bh * n_tiles + t) * kAuxFloatsPerTile;
-  if (part == 0) at[r] = row < n_q ? a.lse[(int64_t)bh * n_q + row] * kLog2e : INFINITY;
+  if (part == 0) {
+    // +inf for padding rows and for rows that saw no key (lse = -inf): their weights come out exactly 0
+    const float lse = row < n_q ? a.lse[(int64_t)bh * n_q + row] : -INFINITY;
+    at[r] = lse == -INFINITY ? INFINITY : lse * kLog2e;
+  }
   else if (part == 1) at[kBN + r] = row < n_q ? dot : 0.f;
   else at[2 * kBN + (part - 2) * kBN + r] = 0.f;
 }
 
 // dK and dV: see the file comment (launch 2).
-template <int NW>
+template <int NW, int kStages>
 __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16(BwdArgs a, int n_kblocks) {
   constexpr int kBK = 32 * NW;                    // keys per workgroup
   constexpr int kLPW = 16 / NW;                   // Q/dO copies per wave per tile (wave 0 also copies lse/D)
@@ -160,6 +172,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16(BwdArgs a, int 
 
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
   const int kb = blk % n_kblocks, bh = blk / n_kblocks;
+  const int n_real = real_keys(a.kv_len, bh / a.H, n_k);  // keys from n_real on are padding: gradient 0
   const uint16_t* Qp = static_cast<const uint16_t*>(a.Q) + (int64_t)bh * n_q * kD;
   const uint16_t* dOp = static_cast<const uint16_t*>(a.dO) + (int64_t)bh * n_q * kD;
   const uint16_t* Kp = static_cast<const uint16_t*>(a.K) + (int64_t)bh * n_k * kD;
@@ -169,14 +182,15 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16(BwdArgs a, int 
   const int k_blk0 = kb * kBK;
   const int kw0 = k_blk0 + 32 * wave;  // this wave's keys: kw0 .. kw0+31; lane's key kw0 + li
   const int key = kw0 + li;
+  const bool wave_real = kw0 < n_real;  // (uniform) the wave has at least one real key
 
   // K and V rows as B operands of S = Q K^T and dP = dO V^T: lane supplies row `key`, d = 8(4g + ks) .. +7.
   bf16x8 kf[4], vf[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     const int64_t off = (int64_t)key * kD + 8 * (4 * g + ks);
-    kf[ks] = key < n_k ? *reinterpret_cast<const bf16x8*>(Kp + off) : bf16x8{};
-    vf[ks] = key < n_k ? *reinterpret_cast<const bf16x8*>(Vp + off) : bf16x8{};
+    kf[ks] = key < n_real ? *reinterpret_cast<const bf16x8*>(Kp + off) : bf16x8{};
+    vf[ks] = key < n_real ? *reinterpret_cast<const bf16x8*>(Vp + off) : bf16x8{};
   }
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
@@ -217,20 +231,19 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16(BwdArgs a, int 
   f32x16 dv[2], dk[2];
   dv[0] = dv[1] = dk[0] = dk[1] = f32x16{};
 
-  const int nt = n_tiles;
-  issue(t0);
-  if (t0 + 1 < nt) issue(t0 + 1);
+  // a workgroup of padding keys only writes zeros
+  const int nt = k_blk0 < n_real ? n_tiles : 0;
+#pragma unroll
+  for (int i = 0; i < kStages - 1; ++i)
+    if (t0 + i < nt) issue(t0 + i);
   for (int t = t0; t < nt; ++t) {
-    // wait for this wave's copies of tile t (tile t+1's may stay in flight), then for every wave's
-    if (t + 1 < nt) {
-      if (wave == 0) wait_vmcnt<kLPW + 1>();
-      else wait_vmcnt<kLPW>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    lds_barrier();  // also: every wave is done with tile t-1, whose stage tile t+2 now takes
-    if (t + 2 < nt) issue(t + 2);
-    if (t < t_first) continue;
+    // wait for this wave's copies of tile t (the later tiles' may stay in flight), then for every wave's
+    const int ahead = min(kStages - 2, nt - 1 - t);
+    if (wave == 0) wait_copies<kLPW + 1, kStages>(ahead);
+    else wait_copies<kLPW, kStages>(ahead);
+    lds_barrier();  // also: every wave is done with tile t-1, whose stage tile t + kStages - 1 now takes
+    if (t + kStages - 1 < nt) issue(t + kStages - 1);
+    if (t < t_first || !wave_real) continue;
     const bool masked = t < t_nomask;
     const uint16_t* st = smem + ((t - t0) % kStages) * kStageElems;
     const float* aux = reinterpret_cast<const float*>(st + 2 * kTileElems);
@@ -282,7 +295,11 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16(BwdArgs a, int 
       }
   }
 
-  // lane holds d = 32mb + 8(r/4) + 4g + r%4 of its key's dV and dK rows
+  // lane holds d = 32mb + 8(r/4) + 4g + r%4 of its key's dV and dK rows; padding keys get 0
+  if (key >= n_real) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) dv[mb] = dk[mb] = f32x16{};
+  }
   if (key < n_k) {
     uint16_t* dvrow = static_cast<uint16_t*>(a.dV) + ((int64_t)bh * n_k + key) * kD;
     uint16_t* dkrow = static_cast<uint16_t*>(a.dK) + ((int64_t)bh * n_k + key) * kD;
@@ -302,7 +319,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16(BwdArgs a, int 
 }
 
 // dQ: see the file comment (launch 3).
-template <int NW>
+template <int NW, int kStages>
 __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dq_bf16(BwdArgs a, int n_qblocks) {
   constexpr int kBM = 32 * NW;  // queries per workgroup
   static_assert(16 % NW == 0, "tile copies split evenly over the waves");
@@ -312,18 +329,19 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dq_bf16(BwdArgs a, int n_
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int g = lane >> 5, li = lane & 31;
-  const int n_q = a.n_q, n_k = a.n_k;
   const bool causal = a.causal != 0;
+  const int n_q = a.n_q;
   const int n_tiles_q = (n_q + kBN - 1) / kBN;
 
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
   int qb = blk % n_qblocks;
   const int bh = blk / n_qblocks;
   if (causal) qb = n_qblocks - 1 - qb;  // heaviest query blocks first
+  const int n_k = real_keys(a.kv_len, bh / a.H, a.n_k);  // keys from n_k on (padding) are never read
   const uint16_t* Qp = static_cast<const uint16_t*>(a.Q) + (int64_t)bh * n_q * kD;
   const uint16_t* dOp = static_cast<const uint16_t*>(a.dO) + (int64_t)bh * n_q * kD;
-  const uint16_t* Kp = static_cast<const uint16_t*>(a.K) + (int64_t)bh * n_k * kD;
-  const uint16_t* Vp = static_cast<const uint16_t*>(a.V) + (int64_t)bh * n_k * kD;
+  const uint16_t* Kp = static_cast<const uint16_t*>(a.K) + (int64_t)bh * a.n_k * kD;
+  const uint16_t* Vp = static_cast<const uint16_t*>(a.V) + (int64_t)bh * a.n_k * kD;
   const float* auxp = a.aux + (int64_t)bh * n_tiles_q * kAuxFloatsPerTile;
 
   const int q_blk0 = qb * kBM;
@@ -385,13 +403,13 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dq_bf16(BwdArgs a, int n_
   dq[0] = dq[1] = f32x16{};
 
   constexpr int kLPW = 16 / NW;
-  issue(0);
-  if (1 < nt) issue(1);
+#pragma unroll
+  for (int i = 0; i < kStages - 1; ++i)
+    if (i < nt) issue(i);
   for (int t = 0; t < nt; ++t) {
-    if (t + 1 < nt) wait_vmcnt<kLPW>();
-    else wait_vmcnt<0>();
+    wait_copies<kLPW, kStages>(min(kStages - 2, nt - 1 - t));
     lds_barrier();
-    if (t + 2 < nt) issue(t + 2);
+    if (t + kStages - 1 < nt) issue(t + kStages - 1);
     if (t >= t_skip) continue;
     const bool masked = t >= t_mask;
     const uint16_t* st = smem + (t % kStages) * 2 * kTileElems;
@@ -462,17 +480,17 @@ hipError_t launch_attn_bwd_pre(const BwdArgs& a, bool f32, hipStream_t stream) {
 }
 
 hipError_t launch_attn_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
-  constexpr int NW = 4;
+  constexpr int NW = 4, kStagesKV = 3, kStagesQ = 3;
   const int n_kblocks = (a.n_k + 32 * NW - 1) / (32 * NW);
   const int n_qblocks = (a.n_q + 32 * NW - 1) / (32 * NW);
   const int64_t nb_kv = (int64_t)n_kblocks * a.B * a.H, nb_q = (int64_t)n_qblocks * a.B * a.H;
   if (!grid_ok(nb_kv) || !grid_ok(nb_q)) return hipErrorInvalidValue;
   hipError_t e = launch_attn_bwd_pre(a, false, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_bwd_dkdv_bf16<NW>), dim3((unsigned)nb_kv), dim3(64 * NW), 0, stream, a, n_kblocks);
+  hipLaunchKernelGGL((attn_bwd_dkdv_bf16<NW, kStagesKV>), dim3((unsigned)nb_kv), dim3(64 * NW), 0, stream, a, n_kblocks);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_bwd_dq_bf16<NW>), dim3((unsigned)nb_q), dim3(64 * NW), 0, stream, a, n_qblocks);
+  hipLaunchKernelGGL((attn_bwd_dq_bf16<NW, kStagesQ>), dim3((unsigned)nb_q), dim3(64 * NW), 0, stream, a, n_qblocks);
   return hipGetLastError();
 }
 

@@ -34,6 +34,7 @@ __global__ __launch_bounds__(2 * kRows) void attn_bwd_dkdv_f32(BwdArgs a) {
   const int nkb = (n_k + kRows - 1) / kRows;
   const int bh = blockIdx.x / nkb, k0 = (blockIdx.x % nkb) * kRows;
   const int key = k0 + (tid >> 1);
+  const int n_real = real_keys(a.kv_len, bh / a.H, n_k);  // keys from n_real on are padding: gradient 0
   const float* Qp = static_cast<const float*>(a.Q) + (int64_t)bh * n_q * kD;
   const float* dOp = static_cast<const float*>(a.dO) + (int64_t)bh * n_q * kD;
   const float* Kp = static_cast<const float*>(a.K) + (int64_t)bh * n_k * kD;
@@ -42,12 +43,12 @@ __global__ __launch_bounds__(2 * kRows) void attn_bwd_dkdv_f32(BwdArgs a) {
   float k[kHalf], v[kHalf], dk[kHalf], dv[kHalf];
 #pragma unroll
   for (int d = 0; d < kHalf; ++d) {
-    k[d] = key < n_k ? Kp[(int64_t)key * kD + kHalf * h + d] : 0.f;
-    v[d] = key < n_k ? Vp[(int64_t)key * kD + kHalf * h + d] : 0.f;
+    k[d] = key < n_real ? Kp[(int64_t)key * kD + kHalf * h + d] : 0.f;
+    v[d] = key < n_real ? Vp[(int64_t)key * kD + kHalf * h + d] : 0.f;
     dk[d] = dv[d] = 0.f;
   }
-  // causal: rows before k0 see none of these keys
-  for (int q0 = a.causal ? k0 : 0; q0 < n_q; q0 += kRows) {
+  // causal: rows before k0 see none of these keys; a workgroup of padding keys only writes zeros
+  for (int q0 = a.causal ? k0 : 0; q0 < (k0 < n_real ? n_q : 0); q0 += kRows) {
     __syncthreads();
     for (int e = tid; e < kRows * kD; e += 2 * kRows) {
       const int r = e / kD, c = e % kD;
@@ -72,8 +73,8 @@ __global__ __launch_bounds__(2 * kRows) void attn_bwd_dkdv_f32(BwdArgs a) {
       s += __shfl_xor(s, 1);
       dp += __shfl_xor(dp, 1);
       const int row = q0 + i;
-      float p = fast_exp2(fmaf(s, kC, -Ls[i]));  // 0 for rows past n_q (lse = +inf)
-      if (a.causal && key > row) p = 0.f;
+      float p = fast_exp2(fmaf(s, kC, -Ls[i]));  // 0 for rows past n_q and rows that saw no key (lse2 = +inf)
+      if ((a.causal && key > row) || key >= n_real) p = 0.f;
       const float ds = p * (dp - Ds[i]);
 #pragma unroll
       for (int d = 0; d < kHalf; ++d) {
@@ -102,6 +103,7 @@ __global__ __launch_bounds__(2 * kRows) void attn_bwd_dq_f32(BwdArgs a) {
   const int nqb = (n_q + kRows - 1) / kRows;
   const int bh = blockIdx.x / nqb, qb0 = (blockIdx.x % nqb) * kRows;
   const int qi = qb0 + (tid >> 1);
+  const int n_real = real_keys(a.kv_len, bh / a.H, n_k);  // keys from n_real on (padding) are never read
   const float* Qp = static_cast<const float*>(a.Q) + (int64_t)bh * n_q * kD;
   const float* dOp = static_cast<const float*>(a.dO) + (int64_t)bh * n_q * kD;
   const float* Kp = static_cast<const float*>(a.K) + (int64_t)bh * n_k * kD;
@@ -115,12 +117,12 @@ __global__ __launch_bounds__(2 * kRows) void attn_bwd_dq_f32(BwdArgs a) {
     dq[d] = 0.f;
   }
   const float2 ld = qi < n_q ? aux_row(a.aux, n_tiles, bh, qi) : float2{INFINITY, 0.f};
-  const int k_end = a.causal ? min(n_k, qb0 + kRows) : n_k;  // keys after the block's last query are never needed
+  const int k_end = a.causal ? min(n_real, qb0 + kRows) : n_real;  // keys after the last query are never needed
   for (int k0 = 0; k0 < k_end; k0 += kRows) {
     __syncthreads();
     for (int e = tid; e < kRows * kD; e += 2 * kRows) {
       const int r = e / kD, c = e % kD;
-      const bool ok = k0 + r < n_k;
+      const bool ok = k0 + r < n_real;
       Ks[r][c] = ok ? Kp[(int64_t)(k0 + r) * kD + c] : 0.f;
       Vs[r][c] = ok ? Vp[(int64_t)(k0 + r) * kD + c] : 0.f;
     }
@@ -136,7 +138,7 @@ __global__ __launch_bounds__(2 * kRows) void attn_bwd_dq_f32(BwdArgs a) {
       dp += __shfl_xor(dp, 1);
       const int key = k0 + j;
       float p = fast_exp2(fmaf(s, kC, -ld.x));
-      if (key >= n_k || (a.causal && key > qi)) p = 0.f;
+      if (key >= n_real || (a.causal && key > qi)) p = 0.f;
       const float ds = p * (dp - ld.y);
 #pragma unroll
       for (int d = 0; d < kHalf; ++d) dq[d] = fmaf(ds, Ks[j][kHalf * h + d], dq[d]);

@@ -64,7 +64,6 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, i
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int g = lane >> 5, li = lane & 31;
-  const int n_q = a.n_q, n_k = a.n_k;
   const bool causal = H == 1 && a.causal != 0;  // the two-half kernel serves unmasked attention only
 
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
@@ -72,6 +71,8 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, i
   const int bh = blk / n_qblocks;
   if (causal) qb = n_qblocks - 1 - qb;  // heaviest query blocks first
   const int b = bh / a.H, hh = bh % a.H;
+  const int n_q = a.n_q;
+  const int n_k = real_keys(a.kv_len, b, a.n_k);  // keys from n_k on (padding) are never read
   const uint16_t* Qp = static_cast<const uint16_t*>(a.Q) + (int64_t)bh * a.q_stride_bh;
   const uint16_t* Kp = static_cast<const uint16_t*>(a.K) + (int64_t)bh * a.k_stride_bh;
   const uint16_t* Vp = static_cast<const uint16_t*>(a.V) + (int64_t)bh * a.k_stride_bh;
@@ -337,44 +338,46 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, i
 
   const std::false_type no;
   const std::true_type yes;
+  if (nt > 0) {  // (no real key: every row's output is 0)
 #pragma unroll
-  for (int t = 0; t < STAGES; ++t)
-    if (t < nt) issue_tile(t);
-  {
-    const int ahead = min(STAGES - 1, nt - 1);
-    if (ahead >= 3) wait_vmcnt<3 * kLPW>();
-    else if (ahead == 2) wait_vmcnt<2 * kLPW>();
-    else if (ahead == 1) wait_vmcnt<kLPW>();
-    else wait_vmcnt<0>();
-    lds_barrier();
-    read_k(smem, kr);
-  }
-  // tile 0 (every row has at least one key it may see there)
-  {
-    auto m0 = [&]() __attribute__((always_inline)) { mid(0, std::integral_constant<int, 1 % STAGES>{}); };
-    if (t_mask > 0) step(0, std::integral_constant<int, 0>{}, no, yes, kr, m0);
-    else step(0, std::integral_constant<int, 0>{}, yes, yes, kr, m0);
-  }
-  int t = 1;
-  // steady state: groups of STAGES unmasked tiles starting at t = 1 (mod STAGES), so each tile's ring stage is a
-  // compile-time constant
-  for (; t + STAGES <= t_mask; t += STAGES)
-    unroll<STAGES>([&](auto u) __attribute__((always_inline)) {
-      constexpr int kU = decltype(u)::value;
-      auto mu = [&]() __attribute__((always_inline)) {
-        mid(t + kU, std::integral_constant<int, (2 + kU) % STAGES>{});
-      };
-      step(t + kU, std::integral_constant<int, (1 + kU) % STAGES>{}, no, no, kr, mu);
-    });
-  // the remaining tiles, with the ring stage computed at run time
-  for (; t < t_mask; ++t) {
-    auto md = [&]() __attribute__((always_inline)) { mid(t, (t + 1) % STAGES); };
-    step(t, t % STAGES, no, no, kr, md);
-  }
-  for (; t < nt; ++t) {
-    auto md = [&]() __attribute__((always_inline)) { mid(t, (t + 1) % STAGES); };
-    if (t < t_skip) step(t, t % STAGES, yes, no, kr, md);
-    else md();
+    for (int t = 0; t < STAGES; ++t)
+      if (t < nt) issue_tile(t);
+    {
+      const int ahead = min(STAGES - 1, nt - 1);
+      if (ahead >= 3) wait_vmcnt<3 * kLPW>();
+      else if (ahead == 2) wait_vmcnt<2 * kLPW>();
+      else if (ahead == 1) wait_vmcnt<kLPW>();
+      else wait_vmcnt<0>();
+      lds_barrier();
+      read_k(smem, kr);
+    }
+    // tile 0 (every row has at least one key it may see there)
+    {
+      auto m0 = [&]() __attribute__((always_inline)) { mid(0, std::integral_constant<int, 1 % STAGES>{}); };
+      if (t_mask > 0) step(0, std::integral_constant<int, 0>{}, no, yes, kr, m0);
+      else step(0, std::integral_constant<int, 0>{}, yes, yes, kr, m0);
+    }
+    int t = 1;
+    // steady state: groups of STAGES unmasked tiles starting at t = 1 (mod STAGES), so each tile's ring stage is a
+    // compile-time constant
+    for (; t + STAGES <= t_mask; t += STAGES)
+      unroll<STAGES>([&](auto u) __attribute__((always_inline)) {
+        constexpr int kU = decltype(u)::value;
+        auto mu = [&]() __attribute__((always_inline)) {
+          mid(t + kU, std::integral_constant<int, (2 + kU) % STAGES>{});
+        };
+        step(t + kU, std::integral_constant<int, (1 + kU) % STAGES>{}, no, no, kr, mu);
+      });
+    // the remaining tiles, with the ring stage computed at run time
+    for (; t < t_mask; ++t) {
+      auto md = [&]() __attribute__((always_inline)) { mid(t, (t + 1) % STAGES); };
+      step(t, t % STAGES, no, no, kr, md);
+    }
+    for (; t < nt; ++t) {
+      auto md = [&]() __attribute__((always_inline)) { mid(t, (t + 1) % STAGES); };
+      if (t < t_skip) step(t, t % STAGES, yes, no, kr, md);
+      else md();
+    }
   }
 
   // O = O^T / l; lane holds d = 32mb + 8(r/4) + 4g + r%4 of its query.
@@ -382,9 +385,11 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, i
   for (int h = 0; h < H; ++h) {
     const int q = qw0 + 32 * h + li;
     if (q < n_q) {
-      const float inv = 1.0f / l[h];
+      const bool seen = l[h] > 0.f;  // false only for a row with no real key (all padding): output 0, lse -inf
+      const float inv = seen ? 1.0f / l[h] : 0.f;
       // row log-sum-exp of the scaled scores, natural log: log2(sum_j exp2(s_j c)) = m + log2(l)
-      if (a.lse != nullptr && g == 0) a.lse[(int64_t)bh * n_q + q] = (__builtin_amdgcn_logf(l[h]) - neg_m[h]) * kLn2;
+      if (a.lse != nullptr && g == 0)
+        a.lse[(int64_t)bh * n_q + q] = seen ? (__builtin_amdgcn_logf(l[h]) - neg_m[h]) * kLn2 : -INFINITY;
       uint16_t* orow = Op + (int64_t)q * a.o_stride_row;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)

@@ -27,7 +27,7 @@ __global__ __launch_bounds__(kBQ) void attn_fwd_f32_d64(AttnArgs a, int n_qblock
   const int bh = blk / n_qblocks;
   if (a.causal) qb = n_qblocks - 1 - qb;
   const int b = bh / a.H, hh = bh % a.H;
-  const int n_q = a.n_q, n_k = a.n_k;
+  const int n_q = a.n_q, n_k = real_keys(a.kv_len, b, a.n_k);  // keys from n_k on (padding) are never read
   const float* Qp = static_cast<const float*>(a.Q) + (int64_t)bh * a.q_stride_bh;
   const float* Kp = static_cast<const float*>(a.K) + (int64_t)bh * a.k_stride_bh;
   const float* Vp = static_cast<const float*>(a.V) + (int64_t)bh * a.k_stride_bh;
@@ -86,9 +86,11 @@ __global__ __launch_bounds__(kBQ) void attn_fwd_f32_d64(AttnArgs a, int n_qblock
     }
   }
   if (qi < n_q) {
-    const float inv = 1.0f / l;
+    const bool seen = l > 0.f;  // false only for a row with no real key (all padding): output 0, lse -inf
+    const float inv = seen ? 1.0f / l : 0.f;
     // row log-sum-exp of the scaled scores, natural log: log2(sum_j exp2(s_j c)) = m + log2(l)
-    if (a.lse != nullptr) a.lse[(int64_t)bh * n_q + qi] = (m + __builtin_amdgcn_logf(l)) * 0.6931471805599453f;
+    if (a.lse != nullptr)
+      a.lse[(int64_t)bh * n_q + qi] = seen ? (m + __builtin_amdgcn_logf(l)) * 0.6931471805599453f : -INFINITY;
     float* orow = Op + (int64_t)qi * a.o_stride_row;
 #pragma unroll
     for (int d = 0; d < kD; d += 4)

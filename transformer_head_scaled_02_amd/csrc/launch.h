@@ -19,6 +19,9 @@ struct AttnArgs {
   int64_t o_stride_b, o_stride_h, o_stride_row;
   int causal;
   float* lse;  // optional (nullptr: not written): row log-sum-exp of query i of head bh at lse[bh*n_q + i]
+  // optional (nullptr: none) key padding: batch entry b has min(max(kv_len[b], 0), n_k) real keys; later keys get
+  // weight 0 and are never read; a row with no key to see gets output 0 and lse -inf
+  const int* kv_len;
 };
 
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, hipStream_t stream);
@@ -40,8 +43,14 @@ struct BwdArgs {
   void* dV;
   int B, H, n_q, n_k;
   int causal;
+  const int* kv_len;  // optional key padding, as in AttnArgs; dK and dV rows of padding keys are written as 0
 };
 constexpr int kAuxFloatsPerTile = 256;
+
+// Real keys of batch entry b: n_k, or the clamped padding length.
+__device__ __forceinline__ int real_keys(const int* kv_len, int b, int n_k) {
+  return kv_len == nullptr ? n_k : min(max(kv_len[b], 0), n_k);
+}
 hipError_t launch_attn_bwd_pre(const BwdArgs& a, bool f32, hipStream_t stream);  // fills `aux`
 hipError_t launch_attn_bwd_bf16(const BwdArgs& a, hipStream_t stream);  // pre-pass, dK/dV, dQ
 hipError_t launch_attn_bwd_f32(const BwdArgs& a, hipStream_t stream);
