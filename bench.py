@@ -9,6 +9,9 @@ sdpa_backward call (pre-pass, dK/dV, dQ) on the same tensors plus a seeded upstr
 output and log-sum-exp computed once before the timed region; metric: backward TFLOP/s = 10*B*h*n_q*n_k*d_k / time
 (the five n_q x n_k x 64 products the gradient needs).
 
+With --workload sdpa_padded_bf16_b4_h8_n4096 a step is one sdpa_forward_padded call on the same tensors treated as a
+length bucket (real key counts per batch entry in the workload); metric: TFLOP/s over the real (query, key) pairs.
+
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 """
 from __future__ import annotations
@@ -24,6 +27,7 @@ ROOT = Path(__file__).resolve().parent
 sys.path.insert(0, str(ROOT))
 
 METRIC = "attention TFLOP/s (4·B·h·n_q·n_k·d_k) at h=8,d_k=64; % of bf16 MFMA peak"
+METRIC_PADDED = "attention TFLOP/s over real keys (4·h·n_q·Σ_b kv_len[b]·d_k) at h=8,d_k=64; % of bf16 MFMA peak"
 METRIC_BWD = "attention backward TFLOP/s (10·B·h·n_q·n_k·d_k) at h=8,d_k=64; % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
@@ -41,6 +45,11 @@ def _pairs(w):
 
 def flops_algorithmic(w):
     return 2.0 * w["B"] * w["h"] * _pairs(w) * (w["d_k"] + w["d_v"])
+
+
+def flops_padded(w):
+    # only (query, real key) pairs: 4 * h * n_q * sum_b kv_len[b] * d_k
+    return 4.0 * w["h"] * w["n_q"] * sum(min(max(L, 0), w["n_k"]) for L in w["kv_len"]) * w["d_k"]
 
 
 def flops_metric_bwd(w):
@@ -218,6 +227,51 @@ def bench_backward(args, w, x, m, dev):
     }
 
 
+def bench_padded(args, w, x, m, dev):
+    """Time sdpa_forward_padded on a length-bucketed batch; returns the JSON record."""
+    import numpy as np
+    import torch
+
+    from oracle import sdpa_ref
+    q, k, v = dev(x["Q"]), dev(x["K"]), dev(x["V"])
+    lens = torch.tensor(w["kv_len"], dtype=torch.int32, device="cuda")
+    out = torch.empty(w["B"], w["h"], w["n_q"], w["d_v"], dtype=q.dtype, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        m.sdpa_forward_padded(q, k, v, lens, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        m.sdpa_forward_padded(q, k, v, lens, out=out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    got = out.float().cpu().numpy()
+    rows = np.array([0, 1, 127, 128, 2047, w["n_q"] - 1])
+    errs = []
+    for b in range(w["B"]):
+        L = w["kv_len"][b]
+        ref = sdpa_ref(x["Q"].f64[b, 0, rows], x["K"].f64[b, 0, :L], x["V"].f64[b, 0, :L], q_index=rows)
+        errs.append(np.abs(got[b, 0, rows] - ref))
+    err = np.stack(errs)
+    value = flops_padded(w) / (ms * 1e-3) / 1e12
+    return {
+        "metric": METRIC_PADDED, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w["dtype"], "data": "synthetic (seeded N(0,1) Q/K/V, no dataset)",
+        "config": {"workload": args.workload, "B": w["B"], "h": w["h"], "n_q": w["n_q"], "n_k": w["n_k"],
+                   "d_k": w["d_k"], "d_v": w["d_v"], "mask": "none", "kv_len": w["kv_len"]},
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(value, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(value / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": "attn_fwd_bf16_d64"},
+        "wall_s_timed_region": round(wall, 4),
+        "parity_last_step": {"max_abs": float(err.max()), "mean_abs": float(err.mean())},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -249,8 +303,8 @@ def main():
         return
     m.load_library()
     w = workloads.WORKLOADS[args.workload]
-    if w["kind"] not in ("sdpa", "sdpa_bwd"):
-        raise SystemExit("bench workload must be an sdpa or sdpa_bwd workload")
+    if w["kind"] not in ("sdpa", "sdpa_bwd", "sdpa_padded"):
+        raise SystemExit("bench workload must be an sdpa, sdpa_bwd or sdpa_padded workload")
     x = workloads.make_workload(args.workload)
 
     def dev(q):
@@ -258,6 +312,9 @@ def main():
             return torch.from_numpy(q.raw.view(np.int16)).view(torch.bfloat16).cuda()
         return torch.from_numpy(q.raw).cuda()
 
+    if w["kind"] == "sdpa_padded":
+        print(json.dumps(bench_padded(args, w, x, m, dev)), flush=True)
+        return
     if w["kind"] == "sdpa_bwd":
         rec = bench_backward(args, w, x, m, dev)
         if not args.no_cpu_baseline:

@@ -68,9 +68,9 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, i
 
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
   int qb = blk % n_qblocks;
-  const int bh = blk / n_qblocks;
+  int bh;
+  const int b = head_of_slot(blk / n_qblocks, a.B, a.H, bh), hh = bh - b * a.H;
   if (causal) qb = n_qblocks - 1 - qb;  // heaviest query blocks first
-  const int b = bh / a.H, hh = bh % a.H;
   const int n_q = a.n_q;
   const int n_k = real_keys(a.kv_len, b, a.n_k);  // keys from n_k on (padding) are never read
   const uint16_t* Qp = static_cast<const uint16_t*>(a.Q) + (int64_t)bh * a.q_stride_bh;

@@ -72,4 +72,14 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   return xcd * per + (xcd < rem ? xcd : rem) + slot;
 }
 
+// Head of a workgroup's slot: slots are decoded batch-minor (slot % B is the batch entry), so that the contiguous
+// slot range xcd_remap gives each XCD spans every batch entry. Heads are independent, so this costs nothing when
+// every entry does the same work, and it keeps the XCDs evenly loaded when entries differ (key padding). Returns the
+// batch entry; `bh` receives the head's index b*H + h into the [B, H, ...] tensors.
+__device__ __forceinline__ int head_of_slot(int slot, int B, int H, int& bh) {
+  const int b = slot % B;
+  bh = b * H + slot / B;
+  return b;
+}
+
 }  // namespace mi355

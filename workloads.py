@@ -36,6 +36,10 @@ WORKLOADS = {
                                   causal=False, seed=1005),
     "sdpa_causal_bf16_b4_h8_n4096": dict(kind="sdpa", dtype="bf16", B=4, h=8, n_q=4096, n_k=4096, d_k=64, d_v=64,
                                          causal=True, seed=1005),
+    # key padding: the long-sequence tensors as one length bucket of a length-grouped batch, each entry padded to 4096
+    # (real key counts per entry in kv_len)
+    "sdpa_padded_bf16_b4_h8_n4096": dict(kind="sdpa_padded", dtype="bf16", B=4, h=8, n_q=4096, n_k=4096, d_k=64,
+                                         d_v=64, causal=False, seed=1005, kv_len=[4096, 3700, 3300, 3100]),
     # backward pass (dQ, dK, dV) of the long-sequence attention: the same Q, K, V and an upstream gradient ~ N(0,1)
     "sdpa_bwd_bf16_b4_h8_n4096": dict(kind="sdpa_bwd", dtype="bf16", B=4, h=8, n_q=4096, n_k=4096, d_k=64, d_v=64,
                                       causal=False, seed=1005),
@@ -122,7 +126,7 @@ def make_mha_inputs(B, n_q, n_k, d_model, h, d_k, d_v, dtype, seed, cross=False)
 def make_workload(name: str):
     """Inputs of a named workload (see WORKLOADS)."""
     w = WORKLOADS[name]
-    if w["kind"] in ("sdpa", "sdpa_bwd"):
+    if w["kind"] in ("sdpa", "sdpa_bwd", "sdpa_padded"):
         return make_sdpa_inputs(w["B"], w["h"], w["n_q"], w["n_k"], w["d_k"], w["d_v"], w["dtype"], w["seed"],
                                 dout=w["kind"] == "sdpa_bwd")
     return make_mha_inputs(w["B"], w["n_q"], w["n_k"], w["d_model"], w["h"], w["d_k"], w["d_v"], w["dtype"],
