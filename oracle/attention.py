@@ -147,11 +147,12 @@ def sdpa_ref(Q, K, V, causal=False, q_index=None, kv_len=None):
     return _per_head(sdpa_head, Q, K, V, causal=causal, q_index=q_index)
 
 
-def mha_ref(Xq, Xkv, Wq, Wk, Wv, Wo, h, causal=False):
+def mha_ref(Xq, Xkv, Wq, Wk, Wv, Wo, h, causal=False, kv_len=None):
     """Multi-head attention: Concat(head_1..head_h) W^O with head_i = Attention(Xq W_i^Q, Xkv W_i^K, Xkv W_i^V).
 
     Xq [B, n_q, d_model], Xkv [B, n_k, d_model]; Wq, Wk [d_model, h*d_k]; Wv [d_model, h*d_v]; Wo [h*d_v, d_model].
     Each head projects from the full d_model-wide input with its own column block of the weight matrices.
+    `kv_len` [B]: keys (positions of Xkv) at or past kv_len[b] are padding.
     """
     Xq, Xkv, Wq, Wk, Wv, Wo = (_as_f64(a) for a in (Xq, Xkv, Wq, Wk, Wv, Wo))
     if Wq.shape[1] % h or Wv.shape[1] % h:
@@ -163,7 +164,7 @@ def mha_ref(Xq, Xkv, Wq, Wk, Wv, Wo, h, causal=False):
         qi = Xq @ Wq[:, i * d_k:(i + 1) * d_k]
         ki = Xkv @ Wk[:, i * d_k:(i + 1) * d_k]
         vi = Xkv @ Wv[:, i * d_v:(i + 1) * d_v]
-        heads.append(sdpa_ref(qi[:, None], ki[:, None], vi[:, None], causal=causal)[:, 0])
+        heads.append(sdpa_ref(qi[:, None], ki[:, None], vi[:, None], causal=causal, kv_len=kv_len)[:, 0])
     concat = np.concatenate(heads, axis=-1)              # head 1 first, along the feature axis
     return concat @ Wo
 
@@ -257,3 +258,33 @@ def sdpa_backward_ref(Q, K, V, dO, causal=False, kv_len=None):
         n_valid = None if kv_len is None else int(kv_len[idx[0]])
         dQ[idx], dK[idx], dV[idx] = sdpa_backward_head(Q[idx], K[idx], V[idx], dO[idx], causal, n_valid=n_valid)
     return dQ, dK, dV
+
+
+def layer_norm_ref(x, gamma, beta, eps):
+    """LayerNorm over the last axis: (x - mean) / sqrt(var + eps) * gamma + beta, with the biased variance (the mean of
+    the squared deviations). The pages name the operation; its form, the learnable gamma/beta and eps are the usual
+    definition (eps is an argument)."""
+    x = _as_f64(x)
+    mu = x.mean(axis=-1, keepdims=True)
+    var = np.square(x - mu).mean(axis=-1, keepdims=True)
+    return (x - mu) / np.sqrt(var + eps) * _as_f64(gamma) + _as_f64(beta)
+
+
+def ffn_ref(x, W1, b1, W2, b2):
+    """Position-wise feed-forward network FFN(x) = max(0, x W1 + b1) W2 + b2, the same weights at every position
+    ("Transformer：抛弃循环与卷积的序列建模", section "FFN")."""
+    return np.maximum(0.0, _as_f64(x) @ _as_f64(W1) + _as_f64(b1)) @ _as_f64(W2) + _as_f64(b2)
+
+
+def encoder_layer_ref(X, Wq, Wk, Wv, Wo, g1, be1, W1, b1, W2, b2, g2, be2, h, eps, causal=False, kv_len=None):
+    """One encoder layer in the pages' post-norm form: each sub-layer's output is LayerNorm(x + Sublayer(x))
+    ("Transformer：抛弃循环与卷积的序列建模", section "Residual Connection 与 LayerNorm"; lettle.cn translation,
+    section 3.1): H1 = LayerNorm(X + MultiHead(X, X, X)), Y = LayerNorm(H1 + FFN(H1)).
+
+    X [B, n, d_model]; attention weights as mha_ref (no bias); W1 [d_model, d_ff], b1 [d_ff], W2 [d_ff, d_model],
+    b2 [d_model]; g1/be1, g2/be2 [d_model] the two LayerNorms' scale and shift. `causal` turns the self-attention
+    into the decoder's masked self-attention; `kv_len` [B] marks padding keys.
+    """
+    X = _as_f64(X)
+    h1 = layer_norm_ref(X + mha_ref(X, X, Wq, Wk, Wv, Wo, h, causal, kv_len), g1, be1, eps)
+    return layer_norm_ref(h1 + ffn_ref(h1, W1, b1, W2, b2), g2, be2, eps)
