@@ -1,5 +1,5 @@
 /* mi355_attn.h - C ABI of the MI355X (gfx950) scaled dot-product / multi-head attention library (attention forward
- * and backward, multi-head attention forward).
+ * and backward, multi-head attention forward, the encoder layer around it).
  *
  * What is computed (sources are web pages about "Attention Is All You Need"):
  *   Attention(Q, K, V) = softmax(Q K^T / sqrt(d_k)) V
@@ -135,6 +135,33 @@ int mha_forward(const void* Xq, const void* Xkv, const void* Wq, const void* Wk,
 
 /* Bytes of workspace mha_forward needs for these sizes (0 if the sizes are invalid). */
 size_t mha_workspace_size(int dtype, int64_t B, int64_t n_q, int64_t n_k, int64_t h, int64_t d_k, int64_t d_v);
+
+/* encoder_layer_forward: one Transformer encoder layer in the pages' post-norm form (each sub-layer's output is
+ * LayerNorm(x + Sublayer(x)): "Attention Is All You Need", lettle.cn translation, section 3.1; "Transformer：抛弃循环与
+ * 卷积的序列建模", sections "FFN" and "Residual Connection 与 LayerNorm"):
+ *     H1  = LayerNorm_1(X + MultiHead(X, X, X))            (MultiHead as mha_forward: no biases)
+ *     out = LayerNorm_2(H1 + max(0, H1 W1 + b1) W2 + b2)   (the position-wise FFN)
+ *   X   [B, n, d_model]; Wq, Wk, Wv, Wo [d_model, d_model] (head i = column block i, as mha_forward)
+ *   W1  [d_model, d_ff], b1 [d_ff], W2 [d_ff, d_model], b2 [d_model]
+ *   ln1_gamma, ln1_beta, ln2_gamma, ln2_beta [d_model]: LayerNorm(r) = (r - mean) / sqrt(var + eps) * gamma + beta
+ *       over the d_model features of each position, var the biased variance (mean squared deviation), eps >= 0
+ *   kv_len [B] int32 or NULL: key padding of the self-attention, as sdpa_forward_padded (NULL: none)
+ *   mask_kind: ATTN_MASK_NONE (encoder) or ATTN_MASK_CAUSAL (masked self-attention, a decoder-only layer)
+ *   out [B, n, d_model]
+ *   workspace: at least encoder_layer_workspace_size(...) bytes, 16-byte aligned (per-head Q/K/V, the concatenated
+ *              heads, the residual sums, H1 and the FFN hidden activations, all bf16).
+ *   dtype: ATTN_BF16 only: every tensor above is bf16; products accumulate in float32, the LayerNorm statistics are
+ *          float32, and every intermediate listed for the workspace is rounded to bf16.
+ *   Requirements: d_model = 64 h <= 1024, d_ff a positive multiple of 64. `out` must not overlap any input or the
+ *   workspace; the workspace must not overlap any input. */
+int encoder_layer_forward(const void* X, const int32_t* kv_len, const void* Wq, const void* Wk, const void* Wv,
+                          const void* Wo, const void* ln1_gamma, const void* ln1_beta, const void* W1, const void* b1,
+                          const void* W2, const void* b2, const void* ln2_gamma, const void* ln2_beta, float eps,
+                          int mask_kind, void* out, void* workspace, size_t workspace_bytes, int dtype, int64_t B,
+                          int64_t n, int64_t d_model, int64_t h, int64_t d_ff, void* stream);
+
+/* Bytes of workspace encoder_layer_forward needs for these sizes (0 if the sizes are invalid). */
+size_t encoder_layer_workspace_size(int dtype, int64_t B, int64_t n, int64_t d_model, int64_t h, int64_t d_ff);
 
 /* Static string naming an attn_status value. */
 const char* attn_status_string(int status);

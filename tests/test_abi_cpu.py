@@ -138,6 +138,37 @@ def test_sdpa_forward_padded_rejects_bad_arguments(lib, kw, code):
     assert lib.attn_last_error().decode().startswith("sdpa_forward_padded")
 
 
+def enc(lib, X=A, kv_len=None, W=A * 10, ln=A * 20, W1=A * 30, b1=A * 40, W2=A * 50, b2=A * 60, eps=1e-5, mask=0,
+        out=A * 1000, ws=A * 2000, ws_bytes=1 << 30, dtype=BF16, B=1, n=16, d_model=512, h=8, d_ff=2048):
+    return lib.encoder_layer_forward(X, kv_len, W, W + 1 << 20, W + 2 << 20, W + 3 << 20, ln, ln + 4096, W1, b1, W2,
+                                     b2, ln + 8192, ln + 12288, eps, mask, out, ws, ws_bytes, dtype, B, n, d_model, h,
+                                     d_ff, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(X=None), INVALID), (dict(W1=None), INVALID), (dict(out=None), INVALID), (dict(ws=None), INVALID),
+    (dict(dtype=F32), UNSUPPORTED), (dict(mask=4), INVALID), (dict(eps=-1.0), INVALID),
+    (dict(eps=float("nan")), INVALID), (dict(d_model=512, h=4), UNSUPPORTED), (dict(d_ff=100), UNSUPPORTED),
+    (dict(d_model=2048, h=32), UNSUPPORTED), (dict(n=0), INVALID), (dict(ws_bytes=1000), INVALID),
+    (dict(b1=A * 40 + 2), INVALID), (dict(kv_len=A * 70 + 4), INVALID),
+    # out [1,16,512] bf16 = 16 KiB over X; the workspace over W1
+    (dict(out=A + 4096), INVALID), (dict(ws=A * 30), INVALID),
+])
+def test_encoder_layer_rejects_bad_arguments(lib, kw, code):
+    assert enc(lib, **kw) == code
+    assert lib.attn_last_error().decode().startswith("encoder_layer_forward")
+
+
+def test_encoder_layer_workspace_size(lib):
+    B, n, dm, h, ff = 32, 128, 512, 8, 2048
+    act = B * n * dm * 2
+    # Q, K, V, the concat, the residual sums and H1 (six [B, n, d_model] regions) plus the FFN hidden [B, n, d_ff]
+    assert lib.encoder_layer_workspace_size(BF16, B, n, dm, h, ff) == 6 * act + B * n * ff * 2
+    assert lib.encoder_layer_workspace_size(F32, B, n, dm, h, ff) == 0
+    assert lib.encoder_layer_workspace_size(BF16, B, n, dm, 4, ff) == 0
+    assert lib.encoder_layer_workspace_size(BF16, B, n, dm, h, 100) == 0
+
+
 def test_backward_workspace_size(lib):
     # 1 KiB per (batch, head) and 64-row query tile: lse and D of the tile's rows
     assert lib.sdpa_backward_workspace_size(BF16, 4, 8, 4096, 4096, 64, 64) == 4 * 8 * 64 * 1024

@@ -19,6 +19,7 @@ ATTN_F32, ATTN_BF16 = 0, 1
 
 # every symbol include/mi355_attn.h declares
 EXPORTED = ("sdpa_forward", "sdpa_forward_lse", "sdpa_forward_padded", "sdpa_backward", "sdpa_backward_workspace_size", "mha_forward",
+            "encoder_layer_forward", "encoder_layer_workspace_size",
             "mha_workspace_size", "attn_status_string", "attn_last_error", "probe_scratch_size", "probe_mfma_bf16", "probe_exp_f32", "probe_hbm_copy")
 
 _lib = None
@@ -56,6 +57,10 @@ def load_library(path: Path | str | None = None) -> ctypes.CDLL:
     lib.mha_forward.restype = ci
     lib.mha_workspace_size.argtypes = [ci, i64, i64, i64, i64, i64, i64]
     lib.mha_workspace_size.restype = sz
+    lib.encoder_layer_forward.argtypes = [vp] * 14 + [ctypes.c_float, ci, vp, vp, sz, ci, i64, i64, i64, i64, i64, vp]
+    lib.encoder_layer_forward.restype = ci
+    lib.encoder_layer_workspace_size.argtypes = [ci, i64, i64, i64, i64, i64]
+    lib.encoder_layer_workspace_size.restype = sz
     lib.attn_status_string.argtypes = [ci]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_last_error.argtypes = []
@@ -305,6 +310,46 @@ def mha_forward(xq: torch.Tensor, xkv: torch.Tensor, wq: torch.Tensor, wk: torch
     _check(lib.mha_forward(xq.data_ptr(), xkv.data_ptr(), wq.data_ptr(), wk.data_ptr(), wv.data_ptr(), wo.data_ptr(),
                            _mask_code(mask), out.data_ptr(), workspace.data_ptr(), ws_bytes, _dtype_code(xq),
                            B, n_q, n_k, d_model, h, d_k, d_v, _stream_handle(xq.device)))
+    return out
+
+
+def encoder_layer_workspace_size(B: int, n: int, d_model: int, h: int, d_ff: int) -> int:
+    return int(load_library().encoder_layer_workspace_size(ATTN_BF16, B, n, d_model, h, d_ff))
+
+
+def encoder_layer_forward(x, wq, wk, wv, wo, ln1_gamma, ln1_beta, w1, b1, w2, b2, ln2_gamma, ln2_beta, h: int,
+                          eps: float = 1e-5, mask="none", kv_len=None, out=None, workspace=None) -> torch.Tensor:
+    """LayerNorm_2(H1 + FFN(H1)) with H1 = LayerNorm_1(x + MultiHead(x, x, x)); bf16 tensors (see
+    include/mi355_attn.h): x [B,n,d_model], wq..wo [d_model,d_model], w1 [d_model,d_ff], b1 [d_ff],
+    w2 [d_ff,d_model], b2 and the LayerNorm parameters [d_model]; kv_len (int32 [B]) adds key padding."""
+    lib = load_library()
+    named = (("x", x), ("wq", wq), ("wk", wk), ("wv", wv), ("wo", wo), ("ln1_gamma", ln1_gamma),
+             ("ln1_beta", ln1_beta), ("w1", w1), ("b1", b1), ("w2", w2), ("b2", b2), ("ln2_gamma", ln2_gamma),
+             ("ln2_beta", ln2_beta))
+    ts = [_dev_tensor(t, nm) for nm, t in named]
+    if any(t.dtype != torch.bfloat16 for t in ts) or len({t.device for t in ts}) != 1:
+        raise ValueError("all tensors must be bfloat16 on one device")
+    x = ts[0]
+    if x.dim() != 3:
+        raise ValueError("x must be [B, n, d_model]")
+    B, n, d_model = x.shape
+    d_ff = w1.shape[1] if w1.dim() == 2 else -1
+    shapes = [(d_model, d_model)] * 4 + [(d_model,)] * 2 + [(d_model, d_ff), (d_ff,), (d_ff, d_model), (d_model,),
+                                                            (d_model,), (d_model,)]
+    for (nm, _), t, shp in zip(named[1:], ts[1:], shapes):
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{nm} must be {shp}, got {tuple(t.shape)}")
+    kv_ptr = _kv_len_tensor(kv_len, B, x.device).data_ptr() if kv_len is not None else None
+    out = _out_tensor(out, "out", (B, n, d_model), x.dtype, x.device)
+    need = encoder_layer_workspace_size(B, n, d_model, h, d_ff)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    else:
+        workspace = _dev_tensor(workspace, "workspace")
+    p = [t.data_ptr() for t in ts]
+    _check(lib.encoder_layer_forward(p[0], kv_ptr, *p[1:], float(eps), _mask_code(mask), out.data_ptr(),
+                                     workspace.data_ptr(), workspace.numel() * workspace.element_size(), ATTN_BF16,
+                                     B, n, d_model, h, d_ff, _stream_handle(x.device)))
     return out
 
 

@@ -2,6 +2,8 @@
 //
 // sdpa_forward -> one fused attention launch (bf16 MFMA kernel or fp32 VALU kernel); sdpa_forward_lse also writes
 //                 the row log-sum-exp.
+// encoder_layer_forward -> projections, attention, W^O + residual, LayerNorm, FFN W1 + bias + ReLU, FFN W2 + bias +
+//                 residual, LayerNorm: seven launches, no host sync.
 // sdpa_forward_padded -> the same launch with per-batch key counts (key padding mask).
 // sdpa_backward -> three launches: the per-row pre-pass (D = dO . O and lse into the workspace), dK/dV, dQ.
 // mha_forward  -> Q/K/V projections (one grouped GEMM launch writing per-head layout into the workspace), the fused
@@ -9,9 +11,11 @@
 // Every argument error is returned before the first HIP call; nothing is enqueued in that case.
 #include <hip/hip_runtime.h>
 
+#include <math.h>
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <string.h>
 
 #include "../../include/mi355_attn.h"
 #include "launch.h"
@@ -63,6 +67,40 @@ MhaLayout mha_layout(int64_t B, int64_t n_q, int64_t n_k, int64_t h) {
   L.c_off = round_up(L.v_off + kv, 256);
   L.total = round_up(L.c_off + q, 256);
   return L;
+}
+
+// x is finite and >= 0 (checked on the bit pattern: the library is built assuming no NaN in arithmetic, so a float
+// comparison could be folded away)
+bool finite_nonneg(float x) {
+  uint32_t b;
+  memcpy(&b, &x, sizeof b);
+  if ((b & 0x7f800000u) == 0x7f800000u) return false;  // inf or NaN
+  return (b >> 31) == 0 || b == 0x80000000u;             // positive, +0 or -0
+}
+
+struct EncLayout {
+  size_t q_off, k_off, v_off, c_off, r_off, h_off, f_off, total;
+};
+
+// Workspace of encoder_layer_forward: per-head Q/K/V, the concatenated heads, the residual sums (R1, then R2), H1
+// and the FFN hidden activations, each region 256-byte aligned.
+EncLayout enc_layout(int64_t B, int64_t n, int64_t d_model, int64_t d_ff) {
+  const size_t act = (size_t)B * n * d_model * 2;
+  EncLayout L;
+  L.q_off = 0;
+  L.k_off = round_up(L.q_off + act, 256);
+  L.v_off = round_up(L.k_off + act, 256);
+  L.c_off = round_up(L.v_off + act, 256);
+  L.r_off = round_up(L.c_off + act, 256);
+  L.h_off = round_up(L.r_off + act, 256);
+  L.f_off = round_up(L.h_off + act, 256);
+  L.total = round_up(L.f_off + (size_t)B * n * d_ff * 2, 256);
+  return L;
+}
+
+bool enc_sizes_ok(int64_t B, int64_t n, int64_t d_model, int64_t h, int64_t d_ff) {
+  return B > 0 && n > 0 && h > 0 && d_model == h * 64 && d_model <= 1024 && d_ff > 0 && d_ff % 64 == 0 &&
+         d_ff <= 65536 && n <= ATTN_MAX_SEQ && B * h <= ATTN_MAX_HEADS && B * n <= 0x7fffffffLL && grid_fits(B, h, n);
 }
 
 }  // namespace
@@ -306,5 +344,91 @@ ATTN_EXPORT int mha_forward(const void* Xq, const void* Xkv, const void* Wq, con
   mi355::GemmProblem outp = {Ch, Wo, out, (int)(B * n_q), (int)d_model, hd, 0};
   e = mi355::launch_gemm_bf16(&outp, 1, s);
   if (e != hipSuccess) return fail_status(ATTN_ERR_HIP, "mha_forward: W^O launch failed: %s", hipGetErrorString(e));
+  return ATTN_OK;
+}
+
+ATTN_EXPORT size_t encoder_layer_workspace_size(int dtype, int64_t B, int64_t n, int64_t d_model, int64_t h,
+                                                int64_t d_ff) {
+  if (dtype != ATTN_BF16 || !enc_sizes_ok(B, n, d_model, h, d_ff)) return 0;
+  return enc_layout(B, n, d_model, d_ff).total;
+}
+
+ATTN_EXPORT int encoder_layer_forward(const void* X, const int32_t* kv_len, const void* Wq, const void* Wk,
+                                      const void* Wv, const void* Wo, const void* ln1_gamma, const void* ln1_beta,
+                                      const void* W1, const void* b1, const void* W2, const void* b2,
+                                      const void* ln2_gamma, const void* ln2_beta, float eps, int mask_kind, void* out,
+                                      void* workspace, size_t workspace_bytes, int dtype, int64_t B, int64_t n,
+                                      int64_t d_model, int64_t h, int64_t d_ff, void* stream) {
+  static const char* fn = "encoder_layer_forward";
+  const void* ins[] = {X, Wq, Wk, Wv, Wo, ln1_gamma, ln1_beta, W1, b1, W2, b2, ln2_gamma, ln2_beta};
+  for (const void* p : ins)
+    if (!p) return fail_status(ATTN_ERR_INVALID, "%s: null pointer", fn);
+  if (!out || !workspace) return fail_status(ATTN_ERR_INVALID, "%s: null pointer", fn);
+  if (dtype != ATTN_BF16) return fail_status(ATTN_ERR_UNSUPPORTED, "%s: dtype %d (only ATTN_BF16)", fn, dtype);
+  if (mask_kind != ATTN_MASK_NONE && mask_kind != ATTN_MASK_CAUSAL)
+    return fail_status(ATTN_ERR_INVALID, "%s: mask_kind %d", fn, mask_kind);
+  if (B <= 0 || n <= 0 || d_model <= 0 || h <= 0 || d_ff <= 0)
+    return fail_status(ATTN_ERR_INVALID, "%s: sizes must be positive", fn);
+  if (!finite_nonneg(eps)) return fail_status(ATTN_ERR_INVALID, "%s: eps must be finite and >= 0", fn);
+  if (!enc_sizes_ok(B, n, d_model, h, d_ff))
+    return fail_status(ATTN_ERR_UNSUPPORTED, "%s: needs d_model = 64 h <= 1024 and d_ff a multiple of 64 (got "
+                       "d_model=%lld h=%lld d_ff=%lld), sizes within the library limits", fn, (long long)d_model,
+                       (long long)h, (long long)d_ff);
+  const EncLayout L = enc_layout(B, n, d_model, d_ff);
+  if (workspace_bytes < L.total)
+    return fail_status(ATTN_ERR_INVALID, "%s: workspace %zu bytes, need %zu", fn, workspace_bytes, L.total);
+  for (const void* p : ins)
+    if (!aligned16(p)) return fail_status(ATTN_ERR_INVALID, "%s: pointers must be 16-byte aligned", fn);
+  if (!aligned16(out) || !aligned16(workspace) || !aligned16(kv_len))
+    return fail_status(ATTN_ERR_INVALID, "%s: pointers must be 16-byte aligned", fn);
+  const size_t act_b = (size_t)B * n * d_model * 2, wsq = (size_t)d_model * d_model * 2;
+  const size_t vec_b = (size_t)d_model * 2;
+  const size_t in_b[] = {act_b, wsq, wsq, wsq, wsq, vec_b, vec_b, (size_t)d_model * d_ff * 2, (size_t)d_ff * 2,
+                         (size_t)d_ff * d_model * 2, vec_b, vec_b, vec_b};
+  for (int i = 0; i < 13; ++i) {
+    if (overlaps(out, act_b, ins[i], in_b[i])) return fail_status(ATTN_ERR_INVALID, "%s: out overlaps an input", fn);
+    if (overlaps(workspace, L.total, ins[i], in_b[i]))
+      return fail_status(ATTN_ERR_INVALID, "%s: workspace overlaps an input", fn);
+  }
+  if (kv_len && (overlaps(kv_len, (size_t)B * 4, out, act_b) || overlaps(kv_len, (size_t)B * 4, workspace, L.total)))
+    return fail_status(ATTN_ERR_INVALID, "%s: kv_len overlaps an output or the workspace", fn);
+  if (overlaps(out, act_b, workspace, L.total)) return fail_status(ATTN_ERR_INVALID, "%s: out overlaps workspace", fn);
+
+  char* ws = static_cast<char*>(workspace);
+  void *Qh = ws + L.q_off, *Kh = ws + L.k_off, *Vh = ws + L.v_off, *Ch = ws + L.c_off;
+  void *R = ws + L.r_off, *H1 = ws + L.h_off, *F = ws + L.f_off;
+  const int M = (int)(B * n), dm = (int)d_model, ff = (int)d_ff;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+#define ENC_STEP(call, what)                                                                          \
+  e = (call);                                                                                        \
+  if (e != hipSuccess) return fail_status(ATTN_ERR_HIP, "%s: %s launch failed: %s", fn, what, hipGetErrorString(e));
+
+  // 1. Q/K/V projections into the per-head layout, 2. attention into the concatenated heads
+  mi355::GemmProblem proj[3] = {{X, Wq, Qh, M, dm, dm, (int)n}, {X, Wk, Kh, M, dm, dm, (int)n},
+                                {X, Wv, Vh, M, dm, dm, (int)n}};
+  ENC_STEP(mi355::launch_gemm_bf16(proj, 3, s), "projection");
+  mi355::AttnArgs a{};
+  a.Q = Qh; a.K = Kh; a.V = Vh; a.O = Ch;
+  a.B = (int)B; a.H = (int)h; a.n_q = (int)n; a.n_k = (int)n;
+  a.q_stride_bh = n * 64;
+  a.k_stride_bh = n * 64;
+  a.o_stride_b = n * h * 64;
+  a.o_stride_h = 64;
+  a.o_stride_row = h * 64;
+  a.causal = mask_kind == ATTN_MASK_CAUSAL;
+  a.kv_len = kv_len;
+  ENC_STEP(mi355::launch_attn_fwd_bf16(a, s), "attention");
+  // 3. R1 = X + Concat W^O (residual in the GEMM epilogue), H1 = LayerNorm(R1)
+  mi355::GemmProblem wo = {Ch, Wo, R, M, dm, dm, 0, nullptr, X, 0};
+  ENC_STEP(mi355::launch_gemm_bf16(&wo, 1, s), "W^O");
+  ENC_STEP(mi355::launch_layer_norm_bf16(R, ln1_gamma, ln1_beta, H1, M, dm, eps, s), "LayerNorm 1");
+  // 4. F = max(0, H1 W1 + b1), R2 = H1 + F W2 + b2 (bias, ReLU and residual in the GEMM epilogues), out = LayerNorm(R2)
+  mi355::GemmProblem f1 = {H1, W1, F, M, ff, dm, 0, b1, nullptr, 1};
+  ENC_STEP(mi355::launch_gemm_bf16(&f1, 1, s), "FFN W1");
+  mi355::GemmProblem f2 = {F, W2, R, M, dm, ff, 0, b2, H1, 0};
+  ENC_STEP(mi355::launch_gemm_bf16(&f2, 1, s), "FFN W2");
+  ENC_STEP(mi355::launch_layer_norm_bf16(R, ln2_gamma, ln2_beta, out, M, dm, eps, s), "LayerNorm 2");
+#undef ENC_STEP
   return ATTN_OK;
 }

@@ -8,7 +8,10 @@
 // A tiles are staged row-major in LDS; W tiles (k-major in memory) are transposed on the way into LDS so that both
 // MFMA operands are 16-byte LDS reads. Up to three independent problems share one launch (the Q, K and V projections).
 // The "head-major" epilogue writes column block n/64 of row (b, i) straight to [b][n/64][i][n%64], which is the
-// per-head layout the attention kernel reads, so no separate reshape pass exists.
+// per-head layout the attention kernel reads, so no separate reshape pass exists. The row-major epilogue can add a
+// bias, apply ReLU and add a residual before the rounding to bf16: the position-wise FFN max(0, x W1 + b1) W2 + b2 and
+// the residual connection x + Sublayer(x) of the encoder layer ("Transformer：抛弃循环与卷积的序列建模", sections
+// "FFN" and "Residual Connection 与 LayerNorm") then cost no extra pass over memory.
 #include "device_common.h"
 #include "launch.h"
 
@@ -94,28 +97,104 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_mfma(GemmBatch batch) {
 
   // accumulator register r: row m0 + 32*wave + 8(r/4) + 4g + r%4, column n0 + 32nb + li
   uint16_t* C = static_cast<uint16_t*>(P.C);
+  const uint16_t* bias = static_cast<const uint16_t*>(P.bias);
+  const uint16_t* res = static_cast<const uint16_t*>(P.residual);
   const int hs = P.head_seq;
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const f32x16& acc = nb ? acc1 : acc0;
     const int n = n0 + 32 * nb + li;
+    const float bn = bias != nullptr ? bf16_bits_to_f32(bias[n]) : 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int mm = m0 + 32 * wave + 8 * (r >> 2) + 4 * g + (r & 3);
       if (mm >= M) continue;
       int64_t off;
+      float v = acc[r];
       if (hs == 0) {
         off = (int64_t)mm * N + n;
+        v += bn;
+        if (P.relu) v = fmaxf(v, 0.f);
+        if (res != nullptr) v += bf16_bits_to_f32(res[off]);
       } else {
         const int bb = mm / hs, i = mm % hs;
         off = (((int64_t)bb * (N / 64) + n / 64) * hs + i) * 64 + (n & 63);
       }
-      C[off] = (uint16_t)(pack_bf16x2(acc[r], 0.f) & 0xffffu);
+      C[off] = (uint16_t)(pack_bf16x2(v, 0.f) & 0xffffu);
     }
   }
 }
 
+// LayerNorm of rows of D bf16 values, one wave per row: each lane takes 16-byte chunks l and l + 64; the mean and then
+// the mean squared deviation are reduced across the wave in fp32 (two passes over registers, no cancellation).
+__global__ __launch_bounds__(256) void layer_norm_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma,
+                                                      const uint16_t* __restrict__ beta, uint16_t* __restrict__ y,
+                                                      int M, int D, float eps) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= M) return;  // (uniform per wave)
+  const int nchunk = D / 8;
+  const uint16_t* xr = x + (int64_t)row * D;
+  float v[2][8];
+  float sum = 0.f;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int ch = lane + 64 * c;
+    uint4 w = {0u, 0u, 0u, 0u};
+    if (ch < nchunk) w = *reinterpret_cast<const uint4*>(xr + 8 * ch);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[c][2 * j] = __uint_as_float(ws[j] << 16);
+      v[c][2 * j + 1] = __uint_as_float(ws[j] & 0xffff0000u);
+      sum += v[c][2 * j] + v[c][2 * j + 1];
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
+  const float mean = sum / (float)D;
+  float sq = 0.f;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    if (lane + 64 * c >= nchunk) continue;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float d = v[c][j] - mean;
+      sq = fmaf(d, d, sq);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) sq += __shfl_xor(sq, o);
+  const float rstd = 1.0f / sqrtf(sq / (float)D + eps);
+  uint16_t* yr = y + (int64_t)row * D;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int ch = lane + 64 * c;
+    if (ch >= nchunk) continue;
+    const uint4 gw = *reinterpret_cast<const uint4*>(gamma + 8 * ch);
+    const uint4 bw = *reinterpret_cast<const uint4*>(beta + 8 * ch);
+    const uint32_t gs[4] = {gw.x, gw.y, gw.z, gw.w}, bs[4] = {bw.x, bw.y, bw.z, bw.w};
+    uint32_t out[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float y0 = fmaf((v[c][2 * j] - mean) * rstd, __uint_as_float(gs[j] << 16), __uint_as_float(bs[j] << 16));
+      const float y1 = fmaf((v[c][2 * j + 1] - mean) * rstd, __uint_as_float(gs[j] & 0xffff0000u),
+                            __uint_as_float(bs[j] & 0xffff0000u));
+      out[j] = pack_bf16x2(y0, y1);
+    }
+    *reinterpret_cast<uint4*>(yr + 8 * ch) = uint4{out[0], out[1], out[2], out[3]};
+  }
+}
+
 }  // namespace
+
+hipError_t launch_layer_norm_bf16(const void* x, const void* gamma, const void* beta, void* y, int M, int D, float eps,
+                                  hipStream_t stream) {
+  if (M <= 0 || D <= 0 || D % 64 || D > 1024) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(layer_norm_bf16, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(gamma),
+                     static_cast<const uint16_t*>(beta), static_cast<uint16_t*>(y), M, D, eps);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm_bf16(const GemmProblem* probs, int nprobs, hipStream_t stream) {
   if (nprobs < 1 || nprobs > kMaxProbs) return hipErrorInvalidValue;

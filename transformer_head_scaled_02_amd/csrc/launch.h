@@ -58,14 +58,24 @@ hipError_t launch_attn_bwd_f32(const BwdArgs& a, hipStream_t stream);
 // C = A[M,K] * W[K,N] in bf16 with fp32 accumulation, up to three independent problems in one launch.
 // Row-major C (ldc = N) when head_seq == 0; otherwise "head-major": column n of row m goes to
 // C[((m / head_seq) * (N / 64) + n / 64) * head_seq + m % head_seq][n % 64], i.e. [B, N/64, head_seq, 64].
+// Optional row-major epilogue (head_seq == 0 only): v = acc + bias[n]; if relu: v = max(v, 0); v += residual[m][n];
+// then rounded to bf16. bias [N] and residual [M, N] are bf16; nullptr skips the step.
 struct GemmProblem {
   const void* A;
   const void* W;
   void* C;
   int M, N, K;
   int head_seq;
+  const void* bias;
+  const void* residual;
+  int relu;
 };
 hipError_t launch_gemm_bf16(const GemmProblem* probs, int nprobs, hipStream_t stream);
+
+// y = LayerNorm(x) * gamma + beta over rows of D bf16 values (fp32 statistics, biased variance), M rows;
+// D a multiple of 64, at most 1024; gamma, beta bf16 [D].
+hipError_t launch_layer_norm_bf16(const void* x, const void* gamma, const void* beta, void* y, int M, int D, float eps,
+                                  hipStream_t stream);
 
 // Records a printf-style detail as the calling thread's last error (attn_last_error) and returns `code`.
 int fail_status(int code, const char* fmt, ...);

@@ -40,6 +40,9 @@ WORKLOADS = {
     # (real key counts per entry in kv_len)
     "sdpa_padded_bf16_b4_h8_n4096": dict(kind="sdpa_padded", dtype="bf16", B=4, h=8, n_q=4096, n_k=4096, d_k=64,
                                          d_v=64, causal=False, seed=1005, kv_len=[4096, 3700, 3300, 3100]),
+    # one encoder layer (self-attention, FFN 512 -> 2048 -> 512, two post-norm LayerNorms) at the MHA shape above
+    "encoder_layer_bf16_b32_n128_dm512": dict(kind="encoder", dtype="bf16", B=32, h=8, n_q=128, n_k=128, d_model=512,
+                                              d_ff=2048, d_k=64, d_v=64, causal=False, seed=1006, eps=1e-5),
     # backward pass (dQ, dK, dV) of the long-sequence attention: the same Q, K, V and an upstream gradient ~ N(0,1)
     "sdpa_bwd_bf16_b4_h8_n4096": dict(kind="sdpa_bwd", dtype="bf16", B=4, h=8, n_q=4096, n_k=4096, d_k=64, d_v=64,
                                       causal=False, seed=1005),
@@ -123,11 +126,33 @@ def make_mha_inputs(B, n_q, n_k, d_model, h, d_k, d_v, dtype, seed, cross=False)
     return out
 
 
+def make_encoder_inputs(B, n, d_model, h, d_ff, dtype, seed):
+    """One encoder layer's inputs, drawn in this order: X ~ N(0,1) [B,n,d_model]; Wq, Wk, Wv, Wo ~ N(0, 1/d_model)
+    [d_model,d_model]; W1 ~ N(0, 1/d_model) [d_model,d_ff]; b1 ~ N(0, 0.1^2) [d_ff]; W2 ~ N(0, 1/d_ff) [d_ff,d_model];
+    b2 ~ N(0, 0.1^2); LayerNorm scales 1 + N(0, 0.1^2) and shifts N(0, 0.1^2) [d_model] (ln1_gamma, ln1_beta,
+    ln2_gamma, ln2_beta). The pages give no initialisation; these keep every sub-layer's output of order 1."""
+    rng = _rng(seed)
+    out = {"X": quantise(rng.standard_normal((B, n, d_model)), dtype)}
+    sd = np.sqrt(1.0 / d_model)
+    for name in ("Wq", "Wk", "Wv", "Wo"):
+        out[name] = quantise(rng.standard_normal((d_model, d_model)) * sd, dtype)
+    out["W1"] = quantise(rng.standard_normal((d_model, d_ff)) * sd, dtype)
+    out["b1"] = quantise(rng.standard_normal(d_ff) * 0.1, dtype)
+    out["W2"] = quantise(rng.standard_normal((d_ff, d_model)) * np.sqrt(1.0 / d_ff), dtype)
+    out["b2"] = quantise(rng.standard_normal(d_model) * 0.1, dtype)
+    for name in ("ln1_gamma", "ln1_beta", "ln2_gamma", "ln2_beta"):
+        base = 1.0 if name.endswith("gamma") else 0.0
+        out[name] = quantise(base + rng.standard_normal(d_model) * 0.1, dtype)
+    return out
+
+
 def make_workload(name: str):
     """Inputs of a named workload (see WORKLOADS)."""
     w = WORKLOADS[name]
     if w["kind"] in ("sdpa", "sdpa_bwd", "sdpa_padded"):
         return make_sdpa_inputs(w["B"], w["h"], w["n_q"], w["n_k"], w["d_k"], w["d_v"], w["dtype"], w["seed"],
                                 dout=w["kind"] == "sdpa_bwd")
+    if w["kind"] == "encoder":
+        return make_encoder_inputs(w["B"], w["n_q"], w["d_model"], w["h"], w["d_ff"], w["dtype"], w["seed"])
     return make_mha_inputs(w["B"], w["n_q"], w["n_k"], w["d_model"], w["h"], w["d_k"], w["d_v"], w["dtype"],
                            w["seed"], cross=w["n_q"] != w["n_k"])
