@@ -1,26 +1,34 @@
-// bf16 GEMM C = A W with fp32 accumulation on gfx950 MFMA, for the multi-head attention projections.
+// bf16 GEMM C = A W with fp32 accumulation on gfx950 MFMA, for the multi-head attention projections and the FFN.
 //
 // Q_i = Xq W_i^Q, K_i = Xkv W_i^K, V_i = Xkv W_i^V for all heads at once (W_i is the column block i of the packed
 // [d_model, h*64] matrix), and Concat(head_1..head_h) W^O: "Transformer：抛弃循环与卷积的序列建模"
 // (jiashun-ye.github.io), section "Multi-Head Attention"; no bias appears in these formulas.
 //
-// Tile 128 x 64 x 64 per workgroup of 4 waves; each wave owns 32 rows x 64 columns (two 32x32 MFMA accumulators).
-// A tiles are staged row-major in LDS; W tiles (k-major in memory) are transposed on the way into LDS so that both
-// MFMA operands are 16-byte LDS reads. Up to three independent problems share one launch (the Q, K and V projections).
+// A workgroup of 4 waves computes a 128 x 128 tile of C, each wave a 64 x 64 quarter as 2 x 2 blocks of
+// v_mfma_f32_32x32x16_bf16. The product is formed transposed, C^T = W^T A^T: the MFMA's first operand is a 32-column
+// strip of W read from LDS with ds_read_b64_tr_b16 (8 consecutive k of one column per lane, the operand layout W's
+// row-major [K, N] storage does not give directly), its second a 32-row strip of A read row-wise, and each lane ends
+// up with 4 consecutive columns of one row of C, stored 8 bytes at a time. A (128 x 64) and W (64 x 128) k-tiles go
+// HBM -> LDS by global_load_lds_dwordx4 into a two-stage ring (64 KB: two workgroups per CU), as four 64 x 64
+// sub-tiles with 128-byte rows and the XOR chunk swizzle of attn_tile.h, which keeps both the row reads and the
+// transposed reads free of bank conflicts. Up to three independent problems share one launch (the Q, K and V
+// projections).
 // The "head-major" epilogue writes column block n/64 of row (b, i) straight to [b][n/64][i][n%64], which is the
 // per-head layout the attention kernel reads, so no separate reshape pass exists. The row-major epilogue can add a
 // bias, apply ReLU and add a residual before the rounding to bf16: the position-wise FFN max(0, x W1 + b1) W2 + b2 and
 // the residual connection x + Sublayer(x) of the encoder layer ("Transformer：抛弃循环与卷积的序列建模", sections
 // "FFN" and "Residual Connection 与 LayerNorm") then cost no extra pass over memory.
-#include "device_common.h"
+#include "attn_tile.h"
 #include "launch.h"
 
 namespace mi355 {
 namespace {
 
-constexpr int kBM = 128, kBN = 64, kBK = 64;
-constexpr int kLds = 72;  // LDS row stride (bf16 elements)
+constexpr int kTM = 128, kTN = 128, kTK = 64;  // workgroup tile of C and k-tile
 constexpr int kThreads = 256;
+constexpr int kStagesG = 2;
+constexpr int kSub = 64 * 64;                  // one 64 x 64 bf16 sub-tile, rows of 128 bytes (8 KB)
+constexpr int kStageElemsG = 4 * kSub;         // [A rows 0-63 | A rows 64-127 | W cols 0-63 | W cols 64-127]
 constexpr int kMaxProbs = 3;
 
 struct GemmBatch {
@@ -30,9 +38,8 @@ struct GemmBatch {
   int nprobs;
 };
 
-__global__ __launch_bounds__(kThreads) void gemm_bf16_mfma(GemmBatch batch) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[kBM * kLds];
-  __shared__ __attribute__((aligned(16))) uint16_t Wt[kBN * kLds];
+__global__ __launch_bounds__(kThreads, 2) void gemm_bf16_mfma(GemmBatch batch) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[kStagesG * kStageElemsG];
 
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
   int pi = 0;
@@ -40,88 +47,159 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_mfma(GemmBatch batch) {
   const GemmProblem& P = batch.p[pi];
   const int local = blk - batch.tile_start[pi];
   const int tm = local / batch.tiles_n[pi], tn = local % batch.tiles_n[pi];
-  const int m0 = tm * kBM, n0 = tn * kBN;
+  const int m0 = tm * kTM, n0 = tn * kTN;
   const int M = P.M, N = P.N, K = P.K;
   const uint16_t* A = static_cast<const uint16_t*>(P.A);
   const uint16_t* W = static_cast<const uint16_t*>(P.W);
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, li = lane & 31;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, g = lane >> 5, li = lane & 31;
+  const int rows_left = M - m0;            // rows of A (and C) in this tile, >= 1
+  const bool half_n = n0 + 64 >= N;        // only the first 64 columns exist (N is a multiple of 64)
 
-  // loaders: A chunk c = tid + 256i -> row c/8, cols 8*(c%8); W rows k0 + 2*(tid/8) (+1), cols n0 + 8*(tid%8)
-  uint4 ar[4], wr0, wr1;
-  const int wkp = tid >> 3, wnc = (tid & 7) * 8;
-  auto gload = [&](int k0) {
-    const uint4 z = {0u, 0u, 0u, 0u};
+  // Copies: wave w issues copies 8w .. 8w+7 of a stage; copies 0-15 bring A rows 8c .. 8c+7, copies 16-31 W rows
+  // (k) 8c .. 8c+7 of sub-tile c/8. Lane l brings the logical chunk that belongs at physical chunk l%8 of row l/8 of
+  // its eight rows; the two per-lane offsets (first or second eight rows of a 16-row swizzle period) serve all copies.
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)smem;
+  const int lr = lane >> 3;
+  uint32_t a_voff[2], w_voff[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + kThreads * i, r = c >> 3, col = (c & 7) * 8;
-      ar[i] = (m0 + r < M) ? *reinterpret_cast<const uint4*>(A + (int64_t)(m0 + r) * K + k0 + col) : z;
-    }
-    wr0 = *reinterpret_cast<const uint4*>(W + (int64_t)(k0 + 2 * wkp) * N + n0 + wnc);
-    wr1 = *reinterpret_cast<const uint4*>(W + (int64_t)(k0 + 2 * wkp + 1) * N + n0 + wnc);
-  };
-  auto lds_store = [&]() {
+  for (int c = 0; c < 2; ++c) {
+    const uint32_t chunk = (uint32_t)(((lane & 7) ^ swz(8 * c + lr)) << 4);
+    a_voff[c] = (uint32_t)(lr * K * 2) + chunk;
+    w_voff[c] = (uint32_t)(lr * N * 2) + chunk;
+  }
+  auto issue = [&](int t) __attribute__((always_inline)) {
+    const int k0 = t * kTK;
+    const uint32_t stage = smem_lds + (uint32_t)((t % kStagesG) * kStageElemsG * 2);
+    if (wave < 2) {
+      // A: copies 8 * wave + i move rows 8gi .. 8gi+7 of the tile
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + kThreads * i, r = c >> 3, col = (c & 7) * 8;
-      *reinterpret_cast<uint4*>(&As[r * kLds + col]) = ar[i];
-    }
-    const uint32_t wa[4] = {wr0.x, wr0.y, wr0.z, wr0.w};
-    const uint32_t wb[4] = {wr1.x, wr1.y, wr1.z, wr1.w};
+      for (int i = 0; i < 8; ++i) {
+        const int gi = 8 * wave + i;
+        const uint32_t dst = stage + (uint32_t)(gi >> 3) * kSub * 2u + (uint32_t)(gi & 7) * 1024u;
+        if (rows_left >= kTM) {
+          lds_dma16(A + (int64_t)(m0 + 8 * gi) * K + k0, a_voff[gi & 1], dst);
+        } else {
+          // rows past M read row M-1 (their results are not stored); offsets from the unshifted tile base
+          int l8 = lr;
+          asm volatile("" : "+v"(l8));
+          const int row = 8 * gi + l8;
+          const uint32_t chunk = (uint32_t)(((lane & 7) ^ swz(row)) << 4);
+          lds_dma16(A + (int64_t)m0 * K + k0, (uint32_t)(min(row, rows_left - 1) * K * 2) + chunk, dst);
+        }
+      }
+    } else {
+      // W: copies move k-rows 8c .. 8c+7 of sub-tile s (columns n0 + 64s ..); a missing second half re-reads the
+      // first (its results are not stored)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t lo = (e & 1) ? (wa[e >> 1] >> 16) : (wa[e >> 1] & 0xffffu);
-      const uint32_t hi = (e & 1) ? (wb[e >> 1] & 0xffff0000u) : (wb[e >> 1] << 16);
-      *reinterpret_cast<uint32_t*>(&Wt[(wnc + e) * kLds + 2 * wkp]) = lo | hi;
+      for (int i = 0; i < 8; ++i) {
+        const int gi = 8 * (wave - 2) + i, sub = gi >> 3, c = gi & 7;
+        const int src_sub = half_n ? 0 : sub;
+        const uint32_t dst = stage + (uint32_t)(2 + sub) * kSub * 2u + (uint32_t)c * 1024u;
+        lds_dma16(W + (int64_t)(k0 + 8 * c) * N + n0 + 64 * src_sub, w_voff[c & 1], dst);
+      }
     }
   };
 
-  f32x16 acc0 = {}, acc1 = {};
-  const uint16_t* arow = &As[(32 * wave + li) * kLds + 8 * g];
-  const uint16_t* brow = &Wt[li * kLds + 8 * g];
-  gload(0);
-  for (int k0 = 0; k0 < K; k0 += kBK) {
-    __syncthreads();
-    lds_store();
-    __syncthreads();
-    if (k0 + kBK < K) gload(k0 + kBK);
+  // Operand offsets. Second operand (A^T, 16 k x 32 rows of A): lane reads row 32mb + li of its A sub-tile, k =
+  // 16ks + 8g .. +7 (logical chunk 2ks + g). First operand (W^T, 32 columns x 16 k): two transposed reads give column
+  // 32nb + l%32 of its W sub-tile at k-rows 16ks + 8g + (0..3) and 16ks + 8g + 4 + (0..3); within each 16-lane group
+  // source lane 4j + t addresses row r0 + j, columns c0 + 4t .. +3.
+  int aoff[4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(arow + 16 * kk);
-      const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(brow + 16 * kk);
-      const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(brow + 32 * kLds + 16 * kk);
-      acc0 = mfma32x32x16(a, b0, acc0);
-      acc1 = mfma32x32x16(a, b1, acc1);
+  for (int ks = 0; ks < 4; ++ks) aoff[ks] = li * kD + (((2 * ks + g) ^ swz(li)) << 3);
+  int toff[2][2];
+  {
+    const int jj = (lane & 15) >> 2;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi) {
+        const int row = 8 * g + jj + 4 * hi;
+        const int lchunk = 4 * nb + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+        toff[nb][hi] = row * kD + ((lchunk ^ swz(row)) << 3) + 4 * (lane & 1);
+      }
+  }
+
+  f32x16 acc[2][2];  // [nb][mb]: register r = C[row 32mb + li][column 32nb + 8(r/4) + 4g + r%4] of this wave's quarter
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) acc[nb][0] = acc[nb][1] = f32x16{};
+
+  const int nk = K / kTK;
+  issue(0);
+  for (int t = 0; t < nk; ++t) {
+    wait_vmcnt<0>();  // this wave's copies of k-tile t
+    lds_barrier();    // everyone's copies of t; everyone is done with t-1, whose stage t+1 now takes
+    if (t + 1 < nk) issue(t + 1);
+    const uint16_t* st = smem + (t % kStagesG) * kStageElemsG;
+    const uint16_t* As = st + (wave >> 1) * kSub;
+    const uint16_t* Ws = st + (2 + (wave & 1)) * kSub;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8 bo[2], ao[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) bo[mb] = *reinterpret_cast<const bf16x8*>(As + mb * 32 * kD + aoff[ks]);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const bf16x4 lo = lds_read_tr16x4(Ws + ks * 16 * kD + toff[nb][0]);
+        const bf16x4 hi = lds_read_tr16x4(Ws + ks * 16 * kD + toff[nb][1]);
+        ao[nb] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = mfma32x32x16(ao[nb], bo[mb], acc[nb][mb]);
     }
   }
 
-  // accumulator register r: row m0 + 32*wave + 8(r/4) + 4g + r%4, column n0 + 32nb + li
+  // Epilogue: lane writes columns n .. n+3 of row m for each (nb, mb, r/4).
+  const int mw = m0 + 64 * (wave >> 1), nw = n0 + 64 * (wave & 1);
+  if (nw >= N) return;  // (uniform) the missing half of a 64-column-wide problem
   uint16_t* C = static_cast<uint16_t*>(P.C);
   const uint16_t* bias = static_cast<const uint16_t*>(P.bias);
   const uint16_t* res = static_cast<const uint16_t*>(P.residual);
   const int hs = P.head_seq;
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const f32x16& acc = nb ? acc1 : acc0;
-    const int n = n0 + 32 * nb + li;
-    const float bn = bias != nullptr ? bf16_bits_to_f32(bias[n]) : 0.f;
+  for (int mb = 0; mb < 2; ++mb) {
+    const int m = mw + 32 * mb + li;
+    if (m >= M) continue;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int mm = m0 + 32 * wave + 8 * (r >> 2) + 4 * g + (r & 3);
-      if (mm >= M) continue;
-      int64_t off;
-      float v = acc[r];
-      if (hs == 0) {
-        off = (int64_t)mm * N + n;
-        v += bn;
-        if (P.relu) v = fmaxf(v, 0.f);
-        if (res != nullptr) v += bf16_bits_to_f32(res[off]);
-      } else {
-        const int bb = mm / hs, i = mm % hs;
-        off = (((int64_t)bb * (N / 64) + n / 64) * hs + i) * 64 + (n & 63);
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int n = nw + 32 * nb + 8 * rg + 4 * g;
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = acc[nb][mb][4 * rg + i];
+        int64_t off;
+        if (hs == 0) {
+          off = (int64_t)m * N + n;
+          if (bias != nullptr) {
+            const uint2 bw = *reinterpret_cast<const uint2*>(bias + n);
+            v[0] += __uint_as_float(bw.x << 16);
+            v[1] += __uint_as_float(bw.x & 0xffff0000u);
+            v[2] += __uint_as_float(bw.y << 16);
+            v[3] += __uint_as_float(bw.y & 0xffff0000u);
+          }
+          if (P.relu) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = fmaxf(v[i], 0.f);
+          }
+          if (res != nullptr) {
+            const uint2 rw = *reinterpret_cast<const uint2*>(res + off);
+            v[0] += __uint_as_float(rw.x << 16);
+            v[1] += __uint_as_float(rw.x & 0xffff0000u);
+            v[2] += __uint_as_float(rw.y << 16);
+            v[3] += __uint_as_float(rw.y & 0xffff0000u);
+          }
+        } else {
+          const int bb = m / hs, i = m % hs;
+          off = (((int64_t)bb * (N / 64) + n / 64) * hs + i) * 64 + (n & 63);
+        }
+        *reinterpret_cast<uint2*>(C + off) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
       }
-      C[off] = (uint16_t)(pack_bf16x2(v, 0.f) & 0xffffu);
-    }
   }
 }
 
@@ -203,11 +281,12 @@ hipError_t launch_gemm_bf16(const GemmProblem* probs, int nprobs, hipStream_t st
   int64_t total = 0;
   for (int i = 0; i < nprobs; ++i) {
     const GemmProblem& p = probs[i];
-    if (p.M <= 0 || p.N <= 0 || p.K <= 0 || p.N % kBN || p.K % kBK) return hipErrorInvalidValue;
+    if (p.M <= 0 || p.N <= 0 || p.K <= 0 || p.N % 64 || p.K % kTK) return hipErrorInvalidValue;
+    if ((int64_t)8 * p.K * 2 > 0xffffffffLL || (int64_t)8 * p.N * 2 > 0xffffffffLL) return hipErrorInvalidValue;
     batch.p[i] = p;
-    batch.tiles_n[i] = p.N / kBN;
+    batch.tiles_n[i] = (p.N + kTN - 1) / kTN;
     batch.tile_start[i] = (int)total;
-    total += (int64_t)((p.M + kBM - 1) / kBM) * batch.tiles_n[i];
+    total += (int64_t)((p.M + kTM - 1) / kTM) * batch.tiles_n[i];
     if (total > 0x7fffffff) return hipErrorInvalidValue;
   }
   batch.tile_start[nprobs] = (int)total;
