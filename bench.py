@@ -12,6 +12,8 @@ output and log-sum-exp computed once before the timed region; metric: backward T
 With --workload sdpa_padded_bf16_b4_h8_n4096 a step is one sdpa_forward_padded call on the same tensors treated as a
 length bucket (real key counts per batch entry in the workload); metric: TFLOP/s over the real (query, key) pairs.
 
+With --workload mha_self_bf16_b32_n128_dm512 a step is one mha_forward (B=32, n=128, d_model=512, h=8); metric:
+TFLOP/s over its products (projections, attention, W^O).
 With --workload encoder_layer_bf16_b32_n128_dm512 a step is one encoder_layer_forward (B=32, n=128, d_model=512,
 h=8, d_ff=2048); metric: TFLOP/s over the layer's products, with tokens/s beside it.
 
@@ -32,6 +34,7 @@ sys.path.insert(0, str(ROOT))
 METRIC = "attention TFLOP/s (4·B·h·n_q·n_k·d_k) at h=8,d_k=64; % of bf16 MFMA peak"
 METRIC_PADDED = "attention TFLOP/s over real keys (4·h·n_q·Σ_b kv_len[b]·d_k) at h=8,d_k=64; % of bf16 MFMA peak"
 METRIC_ENC = "encoder layer TFLOP/s (projections, attention, W^O, FFN) at d_model=512,h=8,d_ff=2048; % of bf16 MFMA peak"
+METRIC_MHA = "multi-head attention TFLOP/s (Q/K/V projections + attention + W^O) at d_model=512,h=8; % of bf16 MFMA peak"
 METRIC_BWD = "attention backward TFLOP/s (10·B·h·n_q·n_k·d_k) at h=8,d_k=64; % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
@@ -60,6 +63,12 @@ def flops_encoder(w):
     """Products of one encoder layer: Q/K/V and W^O projections, attention (4 n^2 d per head), FFN (two GEMMs)."""
     M, d, ff = w["B"] * w["n_q"], w["d_model"], w["d_ff"]
     return 2.0 * M * d * 3 * d + 4.0 * w["B"] * w["h"] * w["n_q"] * w["n_k"] * 64 + 2.0 * M * d * d + 4.0 * M * d * ff
+
+
+def flops_mha(w):
+    """Products of mha_forward: Q/K/V projections, attention (4 n_q n_k 64 per head), W^O."""
+    Mq, Mk, d = w["B"] * w["n_q"], w["B"] * w["n_k"], w["d_model"]
+    return 2.0 * Mq * d * d + 4.0 * Mk * d * d + 4.0 * w["B"] * w["h"] * w["n_q"] * w["n_k"] * 64 + 2.0 * Mq * d * d
 
 
 def flops_metric_bwd(w):
@@ -282,6 +291,52 @@ def bench_padded(args, w, x, m, dev):
     }
 
 
+def bench_mha(args, w, x, m, dev):
+    """Time mha_forward (three launches per step: projections, attention, W^O); returns the JSON record."""
+    import numpy as np
+    import torch
+
+    from oracle import mha_ref
+    xq = dev(x["Xq"])
+    ws_t = [dev(x[nm]) for nm in ("Wq", "Wk", "Wv", "Wo")]
+    out = torch.empty_like(xq)
+    work = torch.empty(m.mha_workspace_size(w["B"], w["n_q"], w["n_k"], w["h"]), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        m.mha_forward(xq, xq, *ws_t, h=w["h"], out=out, workspace=work)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    ref = mha_ref(x["Xq"].f64[:2], x["Xq"].f64[:2], *(x[nm].f64 for nm in ("Wq", "Wk", "Wv", "Wo")), h=w["h"])
+    d = np.abs(out[:2].float().cpu().numpy() - ref)
+    value = flops_mha(w) / (ms * 1e-3) / 1e12
+    return {
+        "metric": METRIC_MHA, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w["dtype"], "data": "synthetic (seeded inputs and weights, no dataset)",
+        "config": {"workload": args.workload, "B": w["B"], "n": w["n_q"], "d_model": w["d_model"], "h": w["h"],
+                   "mask": "none"},
+        "tokens_per_s": round(w["B"] * w["n_q"] / (ms * 1e-3), 1),
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(value, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(value / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "mha_forward step (3 launches)"},
+        "wall_s_timed_region": round(wall, 4),
+        "parity_last_step_first2": {"max_abs": float(d.max()), "mean_abs": float(d.mean())},
+    }
+
+
 def bench_encoder(args, w, x, m, dev):
     """Time encoder_layer_forward (seven launches per step); returns the JSON record."""
     import numpy as np
@@ -362,8 +417,8 @@ def main():
         return
     m.load_library()
     w = workloads.WORKLOADS[args.workload]
-    if w["kind"] not in ("sdpa", "sdpa_bwd", "sdpa_padded", "encoder"):
-        raise SystemExit("bench workload must be an sdpa, sdpa_bwd, sdpa_padded or encoder workload")
+    if w["kind"] not in ("sdpa", "sdpa_bwd", "sdpa_padded", "encoder", "mha"):
+        raise SystemExit("unknown bench workload kind")
     x = workloads.make_workload(args.workload)
 
     def dev(q):
@@ -371,6 +426,9 @@ def main():
             return torch.from_numpy(q.raw.view(np.int16)).view(torch.bfloat16).cuda()
         return torch.from_numpy(q.raw).cuda()
 
+    if w["kind"] == "mha":
+        print(json.dumps(bench_mha(args, w, x, m, dev)), flush=True)
+        return
     if w["kind"] == "encoder":
         print(json.dumps(bench_encoder(args, w, x, m, dev)), flush=True)
         return

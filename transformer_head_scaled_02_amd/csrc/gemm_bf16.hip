@@ -26,10 +26,10 @@ namespace {
 
 constexpr int kTM = 128, kTN = 128, kTK = 64;  // workgroup tile of C and k-tile
 constexpr int kThreads = 256;
-constexpr int kStagesG = 2;
 constexpr int kSub = 64 * 64;                  // one 64 x 64 bf16 sub-tile, rows of 128 bytes (8 KB)
 constexpr int kStageElemsG = 4 * kSub;         // [A rows 0-63 | A rows 64-127 | W cols 0-63 | W cols 64-127]
 constexpr int kMaxProbs = 3;
+constexpr int kGemmStages = 2;  // ring depth of the launch
 
 struct GemmBatch {
   GemmProblem p[kMaxProbs];
@@ -38,7 +38,8 @@ struct GemmBatch {
   int nprobs;
 };
 
-__global__ __launch_bounds__(kThreads, 2) void gemm_bf16_mfma(GemmBatch batch) {
+template <int kStagesG>
+__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_mfma(GemmBatch batch) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[kStagesG * kStageElemsG];
 
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
@@ -128,11 +129,18 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bf16_mfma(GemmBatch batch) {
   for (int nb = 0; nb < 2; ++nb) acc[nb][0] = acc[nb][1] = f32x16{};
 
   const int nk = K / kTK;
-  issue(0);
+#pragma unroll
+  for (int i = 0; i < kStagesG - 1; ++i)
+    if (i < nk) issue(i);
   for (int t = 0; t < nk; ++t) {
-    wait_vmcnt<0>();  // this wave's copies of k-tile t
-    lds_barrier();    // everyone's copies of t; everyone is done with t-1, whose stage t+1 now takes
-    if (t + 1 < nk) issue(t + 1);
+    // this wave's copies of k-tile t (8 per tile; the later tiles' may stay in flight), then everyone's; everyone is
+    // also done with t-1, whose stage tile t + kStagesG - 1 now takes
+    const int ahead = min(kStagesG - 2, nk - 1 - t);
+    if (kStagesG >= 4 && ahead >= 2) wait_vmcnt<(kStagesG >= 4 ? 16 : 0)>();
+    else if (kStagesG >= 3 && ahead >= 1) wait_vmcnt<(kStagesG >= 3 ? 8 : 0)>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    if (t + kStagesG - 1 < nk) issue(t + kStagesG - 1);
     const uint16_t* st = smem + (t % kStagesG) * kStageElemsG;
     const uint16_t* As = st + (wave >> 1) * kSub;
     const uint16_t* Ws = st + (2 + (wave & 1)) * kSub;
@@ -290,7 +298,7 @@ hipError_t launch_gemm_bf16(const GemmProblem* probs, int nprobs, hipStream_t st
     if (total > 0x7fffffff) return hipErrorInvalidValue;
   }
   batch.tile_start[nprobs] = (int)total;
-  hipLaunchKernelGGL(gemm_bf16_mfma, dim3((unsigned)total), dim3(kThreads), 0, stream, batch);
+  hipLaunchKernelGGL(gemm_bf16_mfma<kGemmStages>, dim3((unsigned)total), dim3(kThreads), 0, stream, batch);
   return hipGetLastError();
 }
 
