@@ -24,10 +24,10 @@
 namespace mi355 {
 namespace {
 
-constexpr int kTM = 128, kTN = 128, kTK = 64;  // workgroup tile of C and k-tile
+constexpr int kTN = 128, kTK = 64;             // workgroup tile columns and k-tile (rows: TM = 128 or 64)
 constexpr int kThreads = 256;
 constexpr int kSub = 64 * 64;                  // one 64 x 64 bf16 sub-tile, rows of 128 bytes (8 KB)
-constexpr int kStageElemsG = 4 * kSub;         // [A rows 0-63 | A rows 64-127 | W cols 0-63 | W cols 64-127]
+// a stage: [A rows 0..TM-1 (TM/64 sub-tiles) | W cols 0-63 | W cols 64-127]
 constexpr int kMaxProbs = 3;
 constexpr int kGemmStages = 2;  // ring depth of the launch
 
@@ -38,8 +38,12 @@ struct GemmBatch {
   int nprobs;
 };
 
-template <int kStagesG>
+template <int kStagesG, int TM>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_mfma(GemmBatch batch) {
+  constexpr int kStageElemsG = (TM / 64 + 2) * kSub;
+  constexpr int MB = TM / 64;          // 32-row blocks per wave
+  constexpr int kACopies = TM / 8;     // one-kilobyte copies of A rows per stage (W: 16)
+  constexpr int kCPW = (kACopies + 16) / 4;  // copies per wave
   __shared__ __attribute__((aligned(16))) uint16_t smem[kStagesG * kStageElemsG];
 
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
@@ -48,7 +52,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_mfma(GemmBatch batch) {
   const GemmProblem& P = batch.p[pi];
   const int local = blk - batch.tile_start[pi];
   const int tm = local / batch.tiles_n[pi], tn = local % batch.tiles_n[pi];
-  const int m0 = tm * kTM, n0 = tn * kTN;
+  const int m0 = tm * TM, n0 = tn * kTN;
   const int M = P.M, N = P.N, K = P.K;
   const uint16_t* A = static_cast<const uint16_t*>(P.A);
   const uint16_t* W = static_cast<const uint16_t*>(P.W);
@@ -74,13 +78,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_mfma(GemmBatch batch) {
   auto issue = [&](int t) __attribute__((always_inline)) {
     const int k0 = t * kTK;
     const uint32_t stage = smem_lds + (uint32_t)((t % kStagesG) * kStageElemsG * 2);
-    if (wave < 2) {
-      // A: copies 8 * wave + i move rows 8gi .. 8gi+7 of the tile
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int gi = 8 * wave + i;
+    for (int i = 0; i < kCPW; ++i) {
+      const int gi = kCPW * wave + i;  // (uniform)
+      if (gi < kACopies) {
+        // A rows 8gi .. 8gi+7 of the tile
         const uint32_t dst = stage + (uint32_t)(gi >> 3) * kSub * 2u + (uint32_t)(gi & 7) * 1024u;
-        if (rows_left >= kTM) {
+        if (rows_left >= TM) {
           lds_dma16(A + (int64_t)(m0 + 8 * gi) * K + k0, a_voff[gi & 1], dst);
         } else {
           // rows past M read row M-1 (their results are not stored); offsets from the unshifted tile base
@@ -90,15 +94,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_mfma(GemmBatch batch) {
           const uint32_t chunk = (uint32_t)(((lane & 7) ^ swz(row)) << 4);
           lds_dma16(A + (int64_t)m0 * K + k0, (uint32_t)(min(row, rows_left - 1) * K * 2) + chunk, dst);
         }
-      }
-    } else {
-      // W: copies move k-rows 8c .. 8c+7 of sub-tile s (columns n0 + 64s ..); a missing second half re-reads the
-      // first (its results are not stored)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int gi = 8 * (wave - 2) + i, sub = gi >> 3, c = gi & 7;
+      } else {
+        // W k-rows 8c .. 8c+7 of sub-tile s (columns n0 + 64s ..); a missing second half re-reads the first (its
+        // results are not stored)
+        const int gw = gi - kACopies, sub = gw >> 3, c = gw & 7;
         const int src_sub = half_n ? 0 : sub;
-        const uint32_t dst = stage + (uint32_t)(2 + sub) * kSub * 2u + (uint32_t)c * 1024u;
+        const uint32_t dst = stage + (uint32_t)(MB + sub) * kSub * 2u + (uint32_t)c * 1024u;
         lds_dma16(W + (int64_t)(k0 + 8 * c) * N + n0 + 64 * src_sub, w_voff[c & 1], dst);
       }
     }
@@ -124,9 +125,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_mfma(GemmBatch batch) {
       }
   }
 
-  f32x16 acc[2][2];  // [nb][mb]: register r = C[row 32mb + li][column 32nb + 8(r/4) + 4g + r%4] of this wave's quarter
+  f32x16 acc[2][MB];  // [nb][mb]: register r = C[row 32mb + li][column 32nb + 8(r/4) + 4g + r%4] of this wave's part
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) acc[nb][0] = acc[nb][1] = f32x16{};
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = f32x16{};
 
   const int nk = K / kTK;
 #pragma unroll
@@ -136,19 +139,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_mfma(GemmBatch batch) {
     // this wave's copies of k-tile t (8 per tile; the later tiles' may stay in flight), then everyone's; everyone is
     // also done with t-1, whose stage tile t + kStagesG - 1 now takes
     const int ahead = min(kStagesG - 2, nk - 1 - t);
-    if (kStagesG >= 4 && ahead >= 2) wait_vmcnt<(kStagesG >= 4 ? 16 : 0)>();
-    else if (kStagesG >= 3 && ahead >= 1) wait_vmcnt<(kStagesG >= 3 ? 8 : 0)>();
+    if (kStagesG >= 4 && ahead >= 2) wait_vmcnt<(kStagesG >= 4 ? 2 * kCPW : 0)>();
+    else if (kStagesG >= 3 && ahead >= 1) wait_vmcnt<(kStagesG >= 3 ? kCPW : 0)>();
     else wait_vmcnt<0>();
     lds_barrier();
     if (t + kStagesG - 1 < nk) issue(t + kStagesG - 1);
     const uint16_t* st = smem + (t % kStagesG) * kStageElemsG;
-    const uint16_t* As = st + (wave >> 1) * kSub;
-    const uint16_t* Ws = st + (2 + (wave & 1)) * kSub;
+    const uint16_t* As = st + (wave >> 1) * (TM / 2) * kD;  // this wave's TM/2 rows of A
+    const uint16_t* Ws = st + (MB + (wave & 1)) * kSub;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      bf16x8 bo[2], ao[2];
+      bf16x8 bo[MB], ao[2];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) bo[mb] = *reinterpret_cast<const bf16x8*>(As + mb * 32 * kD + aoff[ks]);
+      for (int mb = 0; mb < MB; ++mb) bo[mb] = *reinterpret_cast<const bf16x8*>(As + mb * 32 * kD + aoff[ks]);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         const bf16x4 lo = lds_read_tr16x4(Ws + ks * 16 * kD + toff[nb][0]);
@@ -158,19 +161,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_mfma(GemmBatch batch) {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = mfma32x32x16(ao[nb], bo[mb], acc[nb][mb]);
+        for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = mfma32x32x16(ao[nb], bo[mb], acc[nb][mb]);
     }
   }
 
   // Epilogue: lane writes columns n .. n+3 of row m for each (nb, mb, r/4).
-  const int mw = m0 + 64 * (wave >> 1), nw = n0 + 64 * (wave & 1);
+  const int mw = m0 + (TM / 2) * (wave >> 1), nw = n0 + 64 * (wave & 1);
   if (nw >= N) return;  // (uniform) the missing half of a 64-column-wide problem
   uint16_t* C = static_cast<uint16_t*>(P.C);
   const uint16_t* bias = static_cast<const uint16_t*>(P.bias);
   const uint16_t* res = static_cast<const uint16_t*>(P.residual);
   const int hs = P.head_seq;
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
+  for (int mb = 0; mb < MB; ++mb) {
     const int m = mw + 32 * mb + li;
     if (m >= M) continue;
 #pragma unroll
@@ -284,6 +287,11 @@ hipError_t launch_layer_norm_bf16(const void* x, const void* gamma, const void* 
 
 hipError_t launch_gemm_bf16(const GemmProblem* probs, int nprobs, hipStream_t stream) {
   if (nprobs < 1 || nprobs > kMaxProbs) return hipErrorInvalidValue;
+  // 128-row tiles when they already give at least two workgroups per CU, else 64-row tiles (twice the workgroups)
+  int64_t tiles128 = 0;
+  for (int i = 0; i < nprobs; ++i)
+    tiles128 += (int64_t)((probs[i].M + 127) / 128) * ((probs[i].N + kTN - 1) / kTN);
+  const int tm = tiles128 >= 512 ? 128 : 64;
   GemmBatch batch{};
   batch.nprobs = nprobs;
   int64_t total = 0;
@@ -294,11 +302,14 @@ hipError_t launch_gemm_bf16(const GemmProblem* probs, int nprobs, hipStream_t st
     batch.p[i] = p;
     batch.tiles_n[i] = (p.N + kTN - 1) / kTN;
     batch.tile_start[i] = (int)total;
-    total += (int64_t)((p.M + kTM - 1) / kTM) * batch.tiles_n[i];
+    total += (int64_t)((p.M + tm - 1) / tm) * batch.tiles_n[i];
     if (total > 0x7fffffff) return hipErrorInvalidValue;
   }
   batch.tile_start[nprobs] = (int)total;
-  hipLaunchKernelGGL(gemm_bf16_mfma<kGemmStages>, dim3((unsigned)total), dim3(kThreads), 0, stream, batch);
+  if (tm == 128)
+    hipLaunchKernelGGL((gemm_bf16_mfma<kGemmStages, 128>), dim3((unsigned)total), dim3(kThreads), 0, stream, batch);
+  else
+    hipLaunchKernelGGL((gemm_bf16_mfma<kGemmStages, 64>), dim3((unsigned)total), dim3(kThreads), 0, stream, batch);
   return hipGetLastError();
 }
 
