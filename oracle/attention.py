@@ -33,6 +33,10 @@ Readings where the pages leave a step open:
     keys j >= kv_len[b] of batch b get score -inf (weight exactly 0), like masked future keys. A row left with no key
     it may see (kv_len[b] = 0) has no softmax; its output is read as 0, its log-sum-exp as -inf, and it passes no
     gradient.
+  * Restricted self-attention ("Transformer：抛弃循环与卷积的序列建模", section "Self-Attention的优势": each position
+    attends only to a neighbourhood of size r, cost O(rnd); section "总结": proposed for very long sequences). Read as
+    a band centred on the query: with radius w, query i sees keys j with |i - j| <= w (r = 2w + 1), positions shared
+    between queries and keys as in self-attention; with the causal mask as well, keys i - w .. i.
   * The row log-sum-exp of the scaled scores, lse_i = log sum_j exp(s_ij) over the keys the row may see, is the
     statistic a forward pass hands to the backward pass: the weights are then exp(s_ij - lse_i).
   * Projections carry no bias (the attention formulas on the pages have none). The row-vector convention X W is used:
@@ -62,9 +66,18 @@ def _causal_disallowed(n_q, n_k, q_index):
     return np.arange(n_k)[None, :] > q_index[:, None]
 
 
-def _masked_scores(q, k, causal, q_index, n_valid):
+def _window_disallowed(n_q, n_k, q_index, window):
+    """Boolean [n_q, n_k]: True where key j lies farther than `window` positions from query position i."""
+    if q_index is None:
+        if n_q != n_k:
+            raise ValueError("the restricted (windowed) mask is defined for self-attention only (n_q == n_k)")
+        q_index = np.arange(n_q)
+    return np.abs(np.arange(n_k)[None, :] - np.asarray(q_index)[:, None]) > window
+
+
+def _masked_scores(q, k, causal, q_index, n_valid, window=None):
     """Scaled scores q k^T / sqrt(d_k) of one head with -inf where the key may not be seen (after the query under the
-    causal mask, or at or past n_valid)."""
+    causal mask, at or past n_valid, or farther than `window` positions from the query)."""
     q = _as_f64(q)
     k = _as_f64(k)
     if q.ndim != 2 or k.ndim != 2 or q.shape[1] != k.shape[1]:
@@ -74,23 +87,26 @@ def _masked_scores(q, k, causal, q_index, n_valid):
         s = np.where(_causal_disallowed(s.shape[0], s.shape[1], q_index), -np.inf, s)
     if n_valid is not None:
         s[:, max(int(n_valid), 0):] = -np.inf            # padding keys
+    if window is not None:
+        s = np.where(_window_disallowed(s.shape[0], s.shape[1], q_index, window), -np.inf, s)
     return s
 
 
-def sdpa_weights_head(q, k, causal=False, q_index=None, n_valid=None):
+def sdpa_weights_head(q, k, causal=False, q_index=None, n_valid=None, window=None):
     """Attention weights softmax(q k^T / sqrt(d_k)) of one head. q [n_q, d_k], k [n_k, d_k] -> [n_q, n_k].
-    `n_valid`: only keys 0 .. n_valid-1 are real (the rest are padding); a row with no key to see gets weights 0."""
-    s = _masked_scores(q, k, causal, q_index, n_valid)
+    `n_valid`: only keys 0 .. n_valid-1 are real (the rest are padding); a row with no key to see gets weights 0.
+    `window`: radius of the restricted self-attention (keys farther from the query are not seen)."""
+    s = _masked_scores(q, k, causal, q_index, n_valid, window)
     empty = np.isneginf(s).all(axis=1, keepdims=True)    # only possible with padding
     m = np.where(empty, 0.0, s.max(axis=1, keepdims=True))
     e = np.exp(s - m)
     return np.where(empty, 0.0, e / np.where(empty, 1.0, e.sum(axis=1, keepdims=True)))
 
 
-def sdpa_head(q, k, v, causal=False, q_index=None, n_valid=None):
+def sdpa_head(q, k, v, causal=False, q_index=None, n_valid=None, window=None):
     """Output softmax(q k^T / sqrt(d_k)) v of one head. v [n_k, d_v] -> [n_q, d_v]."""
     v = _as_f64(v)
-    w = sdpa_weights_head(q, k, causal, q_index, n_valid)
+    w = sdpa_weights_head(q, k, causal, q_index, n_valid, window)
     if v.ndim != 2 or v.shape[0] != w.shape[1]:
         raise ValueError("v [n_k, d_v] expected")
     return w @ v
@@ -131,20 +147,22 @@ def _per_batch_head(fn, kv_len, Q, *rest, **kw):
     return outs
 
 
-def sdpa_weights_ref(Q, K, causal=False, q_index=None, kv_len=None):
+def sdpa_weights_ref(Q, K, causal=False, q_index=None, kv_len=None, window=None):
     """Attention weights for every leading (batch, head) index. Q [..., n_q, d_k], K [..., n_k, d_k].
-    `kv_len` [B] (with [B, h, n, d] tensors): keys j >= kv_len[b] of batch b are padding."""
+    `kv_len` [B] (with [B, h, n, d] tensors): keys j >= kv_len[b] of batch b are padding; `window`: radius of the
+    restricted self-attention."""
     if kv_len is not None:
-        return _per_batch_head(sdpa_weights_head, kv_len, Q, K, causal=causal, q_index=q_index)
-    return _per_head(sdpa_weights_head, Q, K, causal=causal, q_index=q_index)
+        return _per_batch_head(sdpa_weights_head, kv_len, Q, K, causal=causal, q_index=q_index, window=window)
+    return _per_head(sdpa_weights_head, Q, K, causal=causal, q_index=q_index, window=window)
 
 
-def sdpa_ref(Q, K, V, causal=False, q_index=None, kv_len=None):
+def sdpa_ref(Q, K, V, causal=False, q_index=None, kv_len=None, window=None):
     """Scaled dot-product attention, head by head. Q [..., n_q, d_k], K [..., n_k, d_k], V [..., n_k, d_v].
-    `kv_len` [B] (with [B, h, n, d] tensors): keys j >= kv_len[b] of batch b are padding."""
+    `kv_len` [B] (with [B, h, n, d] tensors): keys j >= kv_len[b] of batch b are padding. `window`: radius of the
+    restricted self-attention."""
     if kv_len is not None:
-        return _per_batch_head(sdpa_head, kv_len, Q, K, V, causal=causal, q_index=q_index)
-    return _per_head(sdpa_head, Q, K, V, causal=causal, q_index=q_index)
+        return _per_batch_head(sdpa_head, kv_len, Q, K, V, causal=causal, q_index=q_index, window=window)
+    return _per_head(sdpa_head, Q, K, V, causal=causal, q_index=q_index, window=window)
 
 
 def mha_ref(Xq, Xkv, Wq, Wk, Wv, Wo, h, causal=False, kv_len=None):
@@ -196,22 +214,22 @@ def sdpa_brute(q, k, v, causal=False):
     return out
 
 
-def sdpa_lse_head(q, k, causal=False, q_index=None, n_valid=None):
+def sdpa_lse_head(q, k, causal=False, q_index=None, n_valid=None, window=None):
     """Row log-sum-exp of the scaled scores of one head: lse_i = log sum_j exp(q_i . k_j / sqrt(d_k)) over the keys
     query i may see (natural log; -inf for a row with none). q [n_q, d_k], k [n_k, d_k] -> [n_q]."""
-    s = _masked_scores(q, k, causal, q_index, n_valid)
+    s = _masked_scores(q, k, causal, q_index, n_valid, window)
     empty = np.isneginf(s).all(axis=1)
     m = np.where(empty, 0.0, s.max(axis=1))              # the max shift again only avoids overflow
     with np.errstate(divide="ignore"):
         return np.where(empty, -np.inf, m + np.log(np.exp(s - m[:, None]).sum(axis=1)))
 
 
-def sdpa_lse_ref(Q, K, causal=False, q_index=None, kv_len=None):
+def sdpa_lse_ref(Q, K, causal=False, q_index=None, kv_len=None, window=None):
     """Row log-sum-exp for every leading (batch, head) index. Q [..., n_q, d_k], K [..., n_k, d_k] -> [..., n_q]."""
     fn = lambda q, k, **kw: sdpa_lse_head(q, k, **kw)[:, None]  # noqa: E731
     if kv_len is not None:
-        return _per_batch_head(fn, kv_len, Q, K, causal=causal, q_index=q_index)[..., 0]
-    return _per_head(fn, Q, K, causal=causal, q_index=q_index)[..., 0]
+        return _per_batch_head(fn, kv_len, Q, K, causal=causal, q_index=q_index, window=window)[..., 0]
+    return _per_head(fn, Q, K, causal=causal, q_index=q_index, window=window)[..., 0]
 
 
 def sdpa_backward_head(q, k, v, dout, causal=False, q_index=None, n_valid=None):
