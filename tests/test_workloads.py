@@ -36,6 +36,13 @@ def test_workloads_deterministic_and_shaped(name):
         assert a["Q"].shape == (w["B"], w["h"], w["n_q"], w["d_k"])
         assert a["K"].shape == (w["B"], w["h"], w["n_k"], w["d_k"])
         assert a["V"].shape == (w["B"], w["h"], w["n_k"], w["d_v"])
+    elif w["kind"] == "encoder":
+        assert a["X"].shape == (w["B"], w["n_q"], w["d_model"])
+        assert a["W1"].shape == (w["d_model"], w["d_ff"]) and a["W2"].shape == (w["d_ff"], w["d_model"])
+        assert a["b1"].shape == (w["d_ff"],) and a["ln2_beta"].shape == (w["d_model"],)
+        assert abs(a["W1"].f64.std() - (1 / w["d_model"]) ** 0.5) < 2e-3
+        assert abs(a["W2"].f64.std() - (1 / w["d_ff"]) ** 0.5) < 1e-3
+        assert abs(a["ln1_gamma"].f64.mean() - 1.0) < 0.02
     else:
         assert a["Xq"].shape == (w["B"], w["n_q"], w["d_model"])
         assert a["Wo"].shape == (w["h"] * w["d_v"], w["d_model"])
