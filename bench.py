@@ -12,6 +12,8 @@ output and log-sum-exp computed once before the timed region; metric: backward T
 With --workload sdpa_padded_bf16_b4_h8_n4096 a step is one sdpa_forward_padded call on the same tensors treated as a
 length bucket (real key counts per batch entry in the workload); metric: TFLOP/s over the real (query, key) pairs.
 
+With --workload sdpa_window_bf16_b4_h8_n4096_w256 a step is one sdpa_forward_window call (radius 256); metric:
+TFLOP/s over the band's (query, key) pairs.
 With --workload mha_self_bf16_b32_n128_dm512 a step is one mha_forward (B=32, n=128, d_model=512, h=8); metric:
 TFLOP/s over its products (projections, attention, W^O).
 With --workload encoder_layer_bf16_b32_n128_dm512 a step is one encoder_layer_forward (B=32, n=128, d_model=512,
@@ -32,6 +34,7 @@ ROOT = Path(__file__).resolve().parent
 sys.path.insert(0, str(ROOT))
 
 METRIC = "attention TFLOP/s (4·B·h·n_q·n_k·d_k) at h=8,d_k=64; % of bf16 MFMA peak"
+METRIC_WINDOW = "restricted self-attention TFLOP/s over the band's pairs (4·B·h·pairs·d_k) at h=8,d_k=64; % of bf16 MFMA peak"
 METRIC_PADDED = "attention TFLOP/s over real keys (4·h·n_q·Σ_b kv_len[b]·d_k) at h=8,d_k=64; % of bf16 MFMA peak"
 METRIC_ENC = "encoder layer TFLOP/s (projections, attention, W^O, FFN) at d_model=512,h=8,d_ff=2048; % of bf16 MFMA peak"
 METRIC_MHA = "multi-head attention TFLOP/s (Q/K/V projections + attention + W^O) at d_model=512,h=8; % of bf16 MFMA peak"
@@ -52,6 +55,13 @@ def _pairs(w):
 
 def flops_algorithmic(w):
     return 2.0 * w["B"] * w["h"] * _pairs(w) * (w["d_k"] + w["d_v"])
+
+
+def flops_window(w):
+    """4 * B * h * (allowed (query, key) pairs) * d_k for a band of radius w around each query."""
+    n, r = w["n_q"], w["window"]
+    pairs = sum(min(n - 1, i + r) - max(0, i - r) + 1 for i in range(n))
+    return 4.0 * w["B"] * w["h"] * pairs * w["d_k"]
 
 
 def flops_padded(w):
@@ -246,6 +256,46 @@ def bench_backward(args, w, x, m, dev):
     }
 
 
+def bench_window(args, w, x, m, dev):
+    """Time sdpa_forward_window; returns the JSON record."""
+    import numpy as np
+    import torch
+
+    from oracle import sdpa_ref
+    q, k, v = dev(x["Q"]), dev(x["K"]), dev(x["V"])
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        m.sdpa_forward_window(q, k, v, w["window"], out=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        m.sdpa_forward_window(q, k, v, w["window"], out=out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    rows = np.array([0, 1, 255, 256, 2047, w["n_q"] - 1])
+    ref = sdpa_ref(x["Q"].f64[0, 0, rows], x["K"].f64[0, 0], x["V"].f64[0, 0], q_index=rows, window=w["window"])
+    err = np.abs(out[0, 0, rows].float().cpu().numpy() - ref)
+    value = flops_window(w) / (ms * 1e-3) / 1e12
+    return {
+        "metric": METRIC_WINDOW, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w["dtype"], "data": "synthetic (seeded N(0,1) Q/K/V, no dataset)",
+        "config": {"workload": args.workload, "B": w["B"], "h": w["h"], "n_q": w["n_q"], "n_k": w["n_k"],
+                   "d_k": w["d_k"], "d_v": w["d_v"], "window": w["window"]},
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(value, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(value / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "attn_fwd_bf16_d64<4, 1, 2, 4, true>"},
+        "wall_s_timed_region": round(wall, 4),
+        "parity_last_step": {"max_abs": float(err.max()), "mean_abs": float(err.mean())},
+    }
+
+
 def bench_padded(args, w, x, m, dev):
     """Time sdpa_forward_padded on a length-bucketed batch; returns the JSON record."""
     import numpy as np
@@ -417,7 +467,7 @@ def main():
         return
     m.load_library()
     w = workloads.WORKLOADS[args.workload]
-    if w["kind"] not in ("sdpa", "sdpa_bwd", "sdpa_padded", "encoder", "mha"):
+    if w["kind"] not in ("sdpa", "sdpa_bwd", "sdpa_padded", "sdpa_window", "encoder", "mha"):
         raise SystemExit("unknown bench workload kind")
     x = workloads.make_workload(args.workload)
 
@@ -426,6 +476,9 @@ def main():
             return torch.from_numpy(q.raw.view(np.int16)).view(torch.bfloat16).cuda()
         return torch.from_numpy(q.raw).cuda()
 
+    if w["kind"] == "sdpa_window":
+        print(json.dumps(bench_window(args, w, x, m, dev)), flush=True)
+        return
     if w["kind"] == "mha":
         print(json.dumps(bench_mha(args, w, x, m, dev)), flush=True)
         return

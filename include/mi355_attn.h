@@ -91,6 +91,18 @@ int sdpa_forward_padded(const void* Q, const void* K, const void* V, const int32
                         float* lse, int dtype, int64_t B, int64_t h, int64_t n_q, int64_t n_k, int64_t d_k,
                         int64_t d_v, void* stream);
 
+/* sdpa_forward_window: restricted self-attention ("Transformer：抛弃循环与卷积的序列建模", section "Self-Attention的优势":
+ * each position attends only to a neighbourhood of size r, at cost O(r n d); section "总结": proposed for very long
+ * sequences). Query i sees keys j with |i - j| <= window (a band of 2 window + 1 keys centred on i, clipped at the
+ * ends); with ATTN_MASK_CAUSAL also j <= i, i.e. keys i - window .. i. Key tiles outside every band of a workgroup
+ * are never read.
+ *   window >= 0 (ATTN_ERR_INVALID otherwise); requires n_q == n_k (ATTN_ERR_UNSUPPORTED otherwise).
+ *   lse: optional (NULL: not written), as for sdpa_forward_lse.
+ *   Other arguments, requirements and errors as sdpa_forward. */
+int sdpa_forward_window(const void* Q, const void* K, const void* V, int64_t window, int mask_kind, void* out,
+                        float* lse, int dtype, int64_t B, int64_t h, int64_t n_q, int64_t n_k, int64_t d_k,
+                        int64_t d_v, void* stream);
+
 /* sdpa_backward: gradients of attention.
  *   Q, K, V      the forward inputs, as for sdpa_forward
  *   O   [B, h, n_q, d_v]  the forward output and lse [B, h, n_q] float32 its row log-sum-exp (sdpa_forward_lse, or

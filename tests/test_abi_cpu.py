@@ -169,6 +169,19 @@ def test_encoder_layer_workspace_size(lib):
     assert lib.encoder_layer_workspace_size(BF16, B, n, dm, h, 100) == 0
 
 
+@pytest.mark.parametrize("kw,code", [
+    (dict(window=-1), INVALID), (dict(Q=None), INVALID), (dict(n_k=17), UNSUPPORTED), (dict(dtype=4), UNSUPPORTED),
+    (dict(d_k=32), UNSUPPORTED), (dict(out=A + 8), INVALID), (dict(lse=A * 1100 + 4), INVALID),
+])
+def test_sdpa_forward_window_rejects_bad_arguments(lib, kw, code):
+    a = dict(Q=A, K=A * 2, V=A * 3, window=4, mask=0, out=A * 1000, lse=None, dtype=BF16, B=1, h=1, n_q=16, n_k=16,
+             d_k=64, d_v=64)
+    a.update(kw)
+    assert lib.sdpa_forward_window(a["Q"], a["K"], a["V"], a["window"], a["mask"], a["out"], a["lse"], a["dtype"],
+                                   a["B"], a["h"], a["n_q"], a["n_k"], a["d_k"], a["d_v"], None) == code
+    assert lib.attn_last_error().decode().startswith("sdpa_forward_window")
+
+
 def test_backward_workspace_size(lib):
     # 1 KiB per (batch, head) and 64-row query tile: lse and D of the tile's rows
     assert lib.sdpa_backward_workspace_size(BF16, 4, 8, 4096, 4096, 64, 64) == 4 * 8 * 64 * 1024

@@ -18,7 +18,7 @@ ATTN_MASK_NONE, ATTN_MASK_CAUSAL = 0, 1
 ATTN_F32, ATTN_BF16 = 0, 1
 
 # every symbol include/mi355_attn.h declares
-EXPORTED = ("sdpa_forward", "sdpa_forward_lse", "sdpa_forward_padded", "sdpa_backward", "sdpa_backward_workspace_size", "mha_forward",
+EXPORTED = ("sdpa_forward", "sdpa_forward_lse", "sdpa_forward_padded", "sdpa_forward_window", "sdpa_backward", "sdpa_backward_workspace_size", "mha_forward",
             "encoder_layer_forward", "encoder_layer_workspace_size",
             "mha_workspace_size", "attn_status_string", "attn_last_error", "probe_scratch_size", "probe_mfma_bf16", "probe_exp_f32", "probe_hbm_copy")
 
@@ -48,6 +48,8 @@ def load_library(path: Path | str | None = None) -> ctypes.CDLL:
     lib.sdpa_forward_lse.restype = ci
     lib.sdpa_forward_padded.argtypes = [vp, vp, vp, vp, ci, vp, vp, ci, i64, i64, i64, i64, i64, i64, vp]
     lib.sdpa_forward_padded.restype = ci
+    lib.sdpa_forward_window.argtypes = [vp, vp, vp, i64, ci, vp, vp, ci, i64, i64, i64, i64, i64, i64, vp]
+    lib.sdpa_forward_window.restype = ci
     lib.sdpa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, vp, vp, vp, vp, sz, ci, i64, i64, i64, i64, i64, i64,
                                   vp]
     lib.sdpa_backward.restype = ci
@@ -193,6 +195,22 @@ def sdpa_forward_padded(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_le
     if want_lse:
         lse = _out_tensor(lse, "lse", (B, h, n_q), torch.float32, q.device)
     _check(lib.sdpa_forward_padded(q.data_ptr(), k.data_ptr(), v.data_ptr(), kv_len.data_ptr(), _mask_code(mask),
+                                   out.data_ptr(), lse.data_ptr() if want_lse else None, _dtype_code(q), B, h, n_q,
+                                   n_k, d_k, d_v, _stream_handle(q.device)))
+    return (out, lse) if want_lse else out
+
+
+def sdpa_forward_window(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, window: int, mask="none",
+                        out: torch.Tensor | None = None, lse: torch.Tensor | None = None, return_lse: bool = False):
+    """Restricted self-attention: query i sees keys j with |i - j| <= window (and j <= i with mask="causal").
+    Returns out, or (out, lse) with return_lse (or when `lse` is passed)."""
+    lib = load_library()
+    q, k, v, (B, h, n_q, n_k, d_k, d_v) = _sdpa_shapes(q, k, v)
+    out = _out_tensor(out, "out", (B, h, n_q, d_v), q.dtype, q.device)
+    want_lse = return_lse or lse is not None
+    if want_lse:
+        lse = _out_tensor(lse, "lse", (B, h, n_q), torch.float32, q.device)
+    _check(lib.sdpa_forward_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), int(window), _mask_code(mask),
                                    out.data_ptr(), lse.data_ptr() if want_lse else None, _dtype_code(q), B, h, n_q,
                                    n_k, d_k, d_v, _stream_handle(q.device)))
     return (out, lse) if want_lse else out

@@ -4,6 +4,7 @@
 //                 the row log-sum-exp.
 // encoder_layer_forward -> projections, attention, W^O + residual, LayerNorm, FFN W1 + bias + ReLU, FFN W2 + bias +
 //                 residual, LayerNorm: seven launches, no host sync.
+// sdpa_forward_window -> the same launch restricted to a band of keys around each query.
 // sdpa_forward_padded -> the same launch with per-batch key counts (key padding mask).
 // sdpa_backward -> three launches: the per-row pre-pass (D = dO . O and lse into the workspace), dK/dV, dQ.
 // mha_forward  -> Q/K/V projections (one grouped GEMM launch writing per-head layout into the workspace), the fused
@@ -144,7 +145,7 @@ int check_sdpa_sizes(const char* fn, int dtype, int mask_kind, int64_t B, int64_
 
 int sdpa_forward_impl(const char* fn, const void* Q, const void* K, const void* V, const int32_t* kv_len,
                       int mask_kind, void* out, float* lse, int dtype, int64_t B, int64_t h, int64_t n_q, int64_t n_k,
-                      int64_t d_k, int64_t d_v, void* stream) {
+                      int64_t d_k, int64_t d_v, void* stream, int64_t window = -1) {
   if (int st = check_sdpa_sizes(fn, dtype, mask_kind, B, h, n_q, n_k, d_k, d_v, false)) return st;
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(out) || !aligned16(lse) || !aligned16(kv_len))
     return fail_status(ATTN_ERR_INVALID, "%s: pointers must be 16-byte aligned", fn);
@@ -175,6 +176,10 @@ int sdpa_forward_impl(const char* fn, const void* Q, const void* K, const void* 
   a.causal = mask_kind == ATTN_MASK_CAUSAL;
   a.lse = lse;
   a.kv_len = kv_len;
+  if (window >= 0) {
+    a.windowed = 1;
+    a.window = (int)(window < n_k ? window : n_k);
+  }
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = dtype == ATTN_BF16 ? mi355::launch_attn_fwd_bf16(a, s) : mi355::launch_attn_fwd_f32(a, s);
   if (e != hipSuccess) return fail_status(ATTN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
@@ -201,6 +206,18 @@ ATTN_EXPORT int sdpa_forward_padded(const void* Q, const void* K, const void* V,
     return fail_status(ATTN_ERR_INVALID, "sdpa_forward_padded: null tensor pointer");
   return sdpa_forward_impl("sdpa_forward_padded", Q, K, V, kv_len, mask_kind, out, lse, dtype, B, h, n_q, n_k, d_k, d_v,
                            stream);
+}
+
+ATTN_EXPORT int sdpa_forward_window(const void* Q, const void* K, const void* V, int64_t window, int mask_kind,
+                                    void* out, float* lse, int dtype, int64_t B, int64_t h, int64_t n_q, int64_t n_k,
+                                    int64_t d_k, int64_t d_v, void* stream) {
+  if (!Q || !K || !V || !out) return fail_status(ATTN_ERR_INVALID, "sdpa_forward_window: null tensor pointer");
+  if (window < 0) return fail_status(ATTN_ERR_INVALID, "sdpa_forward_window: window %lld < 0", (long long)window);
+  if (n_q != n_k)
+    return fail_status(ATTN_ERR_UNSUPPORTED, "sdpa_forward_window: restricted self-attention needs n_q == n_k (got "
+                       "%lld, %lld)", (long long)n_q, (long long)n_k);
+  return sdpa_forward_impl("sdpa_forward_window", Q, K, V, nullptr, mask_kind, out, lse, dtype, B, h, n_q, n_k, d_k,
+                           d_v, stream, window);
 }
 
 ATTN_EXPORT int sdpa_forward_lse(const void* Q, const void* K, const void* V, int mask_kind, void* out, float* lse,

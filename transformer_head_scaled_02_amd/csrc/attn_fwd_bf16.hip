@@ -50,7 +50,7 @@ namespace {
 template <class T>
 __device__ __forceinline__ constexpr int stage_index(T s) { return (int)s; }
 
-template <int NW, int H, int MINB, int STAGES>
+template <int NW, int H, int MINB, int STAGES, bool WIN>
 __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, int n_qblocks) {
   constexpr int kQW = 32 * H;    // queries per wave: H independent halves of 32
   constexpr int kBM = kQW * NW;  // queries per workgroup
@@ -72,7 +72,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, i
   const int b = head_of_slot(blk / n_qblocks, a.B, a.H, bh), hh = bh - b * a.H;
   if (causal) qb = n_qblocks - 1 - qb;  // heaviest query blocks first
   const int n_q = a.n_q;
-  const int n_k = real_keys(a.kv_len, b, a.n_k);  // keys from n_k on (padding) are never read
+  int n_k = real_keys(a.kv_len, b, a.n_k);  // keys from n_k on (padding) are never read
   const uint16_t* Qp = static_cast<const uint16_t*>(a.Q) + (int64_t)bh * a.q_stride_bh;
   const uint16_t* Kp = static_cast<const uint16_t*>(a.K) + (int64_t)bh * a.k_stride_bh;
   const uint16_t* Vp = static_cast<const uint16_t*>(a.V) + (int64_t)bh * a.k_stride_bh;
@@ -80,6 +80,16 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, i
 
   const int q_blk0 = qb * kBM;
   const int qw0 = q_blk0 + wave * kQW;  // first query of this wave; half h owns queries qw0 + 32h + (0..31)
+  static_assert(!WIN || H == 1, "the windowed kernel has one query half per wave");
+  // Restricted self-attention: tiles are counted from the tile of the first key any query of the workgroup may see
+  // (key kb0); from here on n_k and every key bound are relative to it.
+  int kb0 = 0;
+  if constexpr (WIN) {
+    kb0 = max(0, q_blk0 - a.window) / kBN * kBN;
+    Kp += (int64_t)kb0 * kD;
+    Vp += (int64_t)kb0 * kD;
+    n_k = max(n_k - kb0, 0);
+  }
 
   // Q as the B operand of S^T = K Q^T: lane supplies Q[q][32g + 8ks + j], ks = 0..3 (the same d order as the K
   // operand). Rows at or past n_q are zero.
@@ -97,15 +107,26 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, i
     for (int ks = 0; ks < 4; ++ks) settle(qf[h][ks]);
 
   int nt = (n_k + kBN - 1) / kBN;
-  if (causal) nt = min(nt, (q_blk0 + kBM - 1) / kBN + 1);
+  if (causal) nt = min(nt, (q_blk0 + kBM - 1 - kb0) / kBN + 1);
   // tiles before t_mask need no mask for any query of this wave; tiles from t_skip on lie entirely in its future
-  const int t_mask = min(causal ? qw0 / kBN : nt, n_k / kBN);
-  const int t_skip = causal ? min(nt, (qw0 + kQW - 1) / kBN + 1) : nt;
+  int t_mask = min(causal ? (qw0 - kb0) / kBN : nt, n_k / kBN);
+  int t_skip = causal ? min(nt, (qw0 + kQW - 1 - kb0) / kBN + 1) : nt;
   const int nt_full = n_k / kBN;  // tiles with no row past n_k
   // keys past this bound, counted from the lane's first key 4g of tile 0, are masked
   int key_lim[H];
 #pragma unroll
-  for (int h = 0; h < H; ++h) key_lim[h] = (causal ? min(qw0 + 32 * h + li, n_k - 1) : n_k - 1) - 4 * g;
+  for (int h = 0; h < H; ++h) key_lim[h] = (causal ? min(qw0 + 32 * h + li - kb0, n_k - 1) : n_k - 1) - 4 * g;
+  // window: keys before key_lo (same counting) are masked too, the workgroup's tiles end after its last query's
+  // window, and every tile takes the masked path
+  int key_lo = 0;
+  if constexpr (WIN) {
+    const int w = a.window;
+    key_lo = qw0 + li - w - kb0 - 4 * g;
+    key_lim[0] = min(key_lim[0], qw0 + li + w - kb0 - 4 * g);
+    nt = min(nt, (q_blk0 + kBM - 1 + w - kb0) / kBN + 1);
+    t_mask = 0;
+    t_skip = min(t_skip, (qw0 + kQW - 1 + w - kb0) / kBN + 1);
+  }
 
   // Tile copies: copy gi (0..15) of a tile moves rows 8*(gi%8) .. +7 of K (gi < 8) or V; lane l brings the logical
   // chunk that belongs at physical chunk l%8 of row 8*(gi%8) + l/8. The swizzle repeats every 16 rows, so two
@@ -171,7 +192,10 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, i
 #pragma unroll
   for (int h = 0; h < H; ++h) {
     o[h][0] = o[h][1] = f32x16{};
-    neg_m[h] = 0.f;
+    // (window: a finite "unset" offset far above any score, so that the first tile a row can see overflows its
+    // tile sum and takes the slow path, which sets the offset to that tile's row max; tiles the row cannot see leave
+    // it alone)
+    neg_m[h] = WIN ? 1024.f : 0.f;
     l[h] = 0.f;
   }
 
@@ -202,12 +226,13 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, i
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) s[h][kb] = mfma32x32x16(ka[ks][kb], qf[h][ks], s[h][kb]);
       if (kM) {
-        const int lim = key_lim[h] - t * kBN;
+        const int lim = key_lim[h] - t * kBN, lo = key_lo - t * kBN;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) s[h][kb][r] = -INFINITY;
+            if (32 * kb + 8 * (r >> 2) + (r & 3) > lim || (WIN && 32 * kb + 8 * (r >> 2) + (r & 3) < lo))
+              s[h][kb][r] = -INFINITY;
       }
     };
 
@@ -354,7 +379,8 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, i
     // tile 0 (every row has at least one key it may see there)
     {
       auto m0 = [&]() __attribute__((always_inline)) { mid(0, std::integral_constant<int, 1 % STAGES>{}); };
-      if (t_mask > 0) step(0, std::integral_constant<int, 0>{}, no, yes, kr, m0);
+      if constexpr (WIN) step(0, std::integral_constant<int, 0>{}, yes, no, kr, m0);
+      else if (t_mask > 0) step(0, std::integral_constant<int, 0>{}, no, yes, kr, m0);
       else step(0, std::integral_constant<int, 0>{}, yes, yes, kr, m0);
     }
     int t = 1;
@@ -403,13 +429,13 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, i
   }
 }
 
-template <int NW, int H, int MINB, int STAGES>
+template <int NW, int H, int MINB, int STAGES, bool WIN = false>
 hipError_t launch(const AttnArgs& a, hipStream_t stream) {
   constexpr int kBM = 32 * H * NW;
   const int n_qblocks = (a.n_q + kBM - 1) / kBM;
   const int64_t nblocks = (int64_t)n_qblocks * a.B * a.H;
   if (nblocks <= 0 || nblocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((attn_fwd_bf16_d64<NW, H, MINB, STAGES>), dim3((unsigned)nblocks), dim3(64 * NW), 0, stream, a,
+  hipLaunchKernelGGL((attn_fwd_bf16_d64<NW, H, MINB, STAGES, WIN>), dim3((unsigned)nblocks), dim3(64 * NW), 0, stream, a,
                      n_qblocks);
   return hipGetLastError();
 }
@@ -420,6 +446,7 @@ hipError_t launch_attn_fwd_bf16(const AttnArgs& a, hipStream_t stream) {
   // Unmasked: 4-wave workgroups of 256 queries (two halves of 32 per wave), two per CU (two waves per SIMD, 256
   // registers each), a 3-tile ring. Causal: 4-wave workgroups of 128 queries with a 4-tile ring, two per CU, which
   // balanced the triangular work best.
+  if (a.windowed) return launch<4, 1, 2, 4, true>(a, stream);
   if (!a.causal) return launch<4, 2, 2, 3>(a, stream);
   return launch<4, 1, 2, 4>(a, stream);
 }

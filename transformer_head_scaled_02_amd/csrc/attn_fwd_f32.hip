@@ -44,9 +44,13 @@ __global__ __launch_bounds__(kBQ) void attn_fwd_f32_d64(AttnArgs a, int n_qblock
   }
   float m = -INFINITY, l = 0.f;
 
-  int n_end = n_k;
+  int n_end = n_k, k_begin = 0;
   if (a.causal) n_end = min(n_k, q0 + kBQ);  // keys after the block's last query are never needed
-  for (int k0 = 0; k0 < n_end; k0 += kBK) {
+  if (a.windowed) {  // restricted self-attention: keys within a.window of some query of the block
+    n_end = min(n_end, q0 + kBQ + a.window);
+    k_begin = max(0, q0 - a.window) / kBK * kBK;
+  }
+  for (int k0 = k_begin; k0 < n_end; k0 += kBK) {
     __syncthreads();
     // 32 rows x 64 floats per tensor = 512 float4 chunks, 8 per thread; rows past n_k load as zeros
     for (int ch = tid; ch < kBK * kD / 4; ch += kBQ) {
@@ -66,7 +70,8 @@ __global__ __launch_bounds__(kBQ) void attn_fwd_f32_d64(AttnArgs a, int n_qblock
 #pragma unroll
       for (int d = 0; d < kD; ++d) acc = fmaf(q[d], Ks[j * kD + d], acc);
       const int key = k0 + j;
-      if (key >= n_k || (a.causal && key > qi)) acc = -INFINITY;
+      if (key >= n_k || (a.causal && key > qi) || (a.windowed && (key > qi + a.window || key < qi - a.window)))
+        acc = -INFINITY;
       s[j] = acc;
       mx = fmaxf(mx, acc);
     }

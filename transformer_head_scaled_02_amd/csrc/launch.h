@@ -22,6 +22,8 @@ struct AttnArgs {
   // optional (nullptr: none) key padding: batch entry b has min(max(kv_len[b], 0), n_k) real keys; later keys get
   // weight 0 and are never read; a row with no key to see gets output 0 and lse -inf
   const int* kv_len;
+  // restricted self-attention (windowed != 0, n_q == n_k): query i sees keys j with |i - j| <= window only
+  int windowed, window;
 };
 
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, hipStream_t stream);

@@ -40,6 +40,9 @@ WORKLOADS = {
     # (real key counts per entry in kv_len)
     "sdpa_padded_bf16_b4_h8_n4096": dict(kind="sdpa_padded", dtype="bf16", B=4, h=8, n_q=4096, n_k=4096, d_k=64,
                                          d_v=64, causal=False, seed=1005, kv_len=[4096, 3700, 3300, 3100]),
+    # restricted self-attention of radius 256 (a band of 513 keys per query) over the long-sequence tensors
+    "sdpa_window_bf16_b4_h8_n4096_w256": dict(kind="sdpa_window", dtype="bf16", B=4, h=8, n_q=4096, n_k=4096, d_k=64,
+                                              d_v=64, causal=False, seed=1005, window=256),
     # one encoder layer (self-attention, FFN 512 -> 2048 -> 512, two post-norm LayerNorms) at the MHA shape above
     "encoder_layer_bf16_b32_n128_dm512": dict(kind="encoder", dtype="bf16", B=32, h=8, n_q=128, n_k=128, d_model=512,
                                               d_ff=2048, d_k=64, d_v=64, causal=False, seed=1006, eps=1e-5),
@@ -149,7 +152,7 @@ def make_encoder_inputs(B, n, d_model, h, d_ff, dtype, seed):
 def make_workload(name: str):
     """Inputs of a named workload (see WORKLOADS)."""
     w = WORKLOADS[name]
-    if w["kind"] in ("sdpa", "sdpa_bwd", "sdpa_padded"):
+    if w["kind"] in ("sdpa", "sdpa_bwd", "sdpa_padded", "sdpa_window"):
         return make_sdpa_inputs(w["B"], w["h"], w["n_q"], w["n_k"], w["d_k"], w["d_v"], w["dtype"], w["seed"],
                                 dout=w["kind"] == "sdpa_bwd")
     if w["kind"] == "encoder":
