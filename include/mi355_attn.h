@@ -109,6 +109,8 @@ int sdpa_forward_window(const void* Q, const void* K, const void* V, int64_t win
  *                         sdpa_forward_padded with the same kv_len, on the same Q, K, V and mask_kind)
  *   kv_len [B] int32 or NULL: the key padding of the forward pass (NULL: none); gradients of padding keys' K and V
  *          rows are written as 0, and rows that saw no key pass no gradient
+ *   window: the radius of a restricted self-attention forward pass (sdpa_forward_window), or -1 for none; >= 0
+ *          requires n_q == n_k and kv_len == NULL (ATTN_ERR_UNSUPPORTED otherwise)
  *   dO  [B, h, n_q, d_v]  dL/dO, the upstream gradient
  *   dQ  [B, h, n_q, d_k], dK [B, h, n_k, d_k], dV [B, h, n_k, d_v]: written with dL/dQ, dL/dK, dL/dV:
  *       P = exp(Q K^T / sqrt(d_k) - lse) (0 where masked), dV = P^T dO, dP = dO V^T,
@@ -120,7 +122,7 @@ int sdpa_forward_window(const void* Q, const void* K, const void* V, int64_t win
  *   Requirements as sdpa_forward (d_k = d_v = 64, causal only with n_q == n_k). dQ, dK, dV and the workspace must not
  *   overlap each other or any input. Every element of dQ, dK and dV is written. */
 int sdpa_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse,
-                  const int32_t* kv_len, int mask_kind, void* dQ, void* dK, void* dV, void* workspace,
+                  const int32_t* kv_len, int64_t window, int mask_kind, void* dQ, void* dK, void* dV, void* workspace,
                   size_t workspace_bytes, int dtype, int64_t B, int64_t h, int64_t n_q, int64_t n_k, int64_t d_k,
                   int64_t d_v, void* stream);
 

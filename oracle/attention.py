@@ -232,7 +232,7 @@ def sdpa_lse_ref(Q, K, causal=False, q_index=None, kv_len=None, window=None):
     return _per_head(fn, Q, K, causal=causal, q_index=q_index, window=window)[..., 0]
 
 
-def sdpa_backward_head(q, k, v, dout, causal=False, q_index=None, n_valid=None):
+def sdpa_backward_head(q, k, v, dout, causal=False, q_index=None, n_valid=None, window=None):
     """Gradients (dq, dk, dv) of L = sum(dout * O) for one head, O = softmax(q k^T / sqrt(d_k)) v.
 
     The chain rule through the three steps of the forward pass, from the output back:
@@ -245,7 +245,7 @@ def sdpa_backward_head(q, k, v, dout, causal=False, q_index=None, n_valid=None):
     """
     v = _as_f64(v)
     dout = _as_f64(dout)
-    w = sdpa_weights_head(q, k, causal, q_index, n_valid)
+    w = sdpa_weights_head(q, k, causal, q_index, n_valid, window)
     if v.ndim != 2 or v.shape[0] != w.shape[1] or dout.shape != (w.shape[0], v.shape[1]):
         raise ValueError("v [n_k, d_v] and dout [n_q, d_v] expected")
     q = _as_f64(q)
@@ -259,11 +259,12 @@ def sdpa_backward_head(q, k, v, dout, causal=False, q_index=None, n_valid=None):
     return dq, dk, dv
 
 
-def sdpa_backward_ref(Q, K, V, dO, causal=False, kv_len=None):
+def sdpa_backward_ref(Q, K, V, dO, causal=False, kv_len=None, window=None):
     """(dQ, dK, dV) of attention for every leading (batch, head) index, head by head.
 
     Q [..., n_q, d_k], K [..., n_k, d_k], V [..., n_k, d_v], dO [..., n_q, d_v] -> arrays shaped like Q, K, V.
     `kv_len` [B] (with [B, h, n, d] tensors): keys j >= kv_len[b] of batch b are padding (their gradients are 0).
+    `window`: radius of the restricted self-attention.
     """
     Q, K, V, dO = (_as_f64(a) for a in (Q, K, V, dO))
     lead = Q.shape[:-2]
@@ -274,7 +275,8 @@ def sdpa_backward_ref(Q, K, V, dO, causal=False, kv_len=None):
     dQ, dK, dV = np.empty_like(Q), np.empty_like(K), np.empty_like(V)
     for idx in np.ndindex(*lead):
         n_valid = None if kv_len is None else int(kv_len[idx[0]])
-        dQ[idx], dK[idx], dV[idx] = sdpa_backward_head(Q[idx], K[idx], V[idx], dO[idx], causal, n_valid=n_valid)
+        dQ[idx], dK[idx], dV[idx] = sdpa_backward_head(Q[idx], K[idx], V[idx], dO[idx], causal, n_valid=n_valid,
+                                                       window=window)
     return dQ, dK, dV
 
 

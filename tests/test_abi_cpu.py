@@ -101,10 +101,10 @@ def test_sdpa_forward_lse_rejects_bad_arguments(lib, kw, code):
     assert lib.attn_last_error().decode().startswith("sdpa_forward_lse")
 
 
-def bwd(lib, Q=A, K=A * 2, V=A * 3, O=A * 4, dO=A * 5, lse=A * 6, kv_len=None, mask=0, dQ=A * 100, dK=A * 200,
-        dV=A * 300, ws=A * 400, ws_bytes=1 << 20, dtype=BF16, B=1, h=1, n_q=16, n_k=16, d_k=64, d_v=64):
-    return lib.sdpa_backward(Q, K, V, O, dO, lse, kv_len, mask, dQ, dK, dV, ws, ws_bytes, dtype, B, h, n_q, n_k, d_k,
-                             d_v, None)
+def bwd(lib, Q=A, K=A * 2, V=A * 3, O=A * 4, dO=A * 5, lse=A * 6, kv_len=None, window=-1, mask=0, dQ=A * 100,
+        dK=A * 200, dV=A * 300, ws=A * 400, ws_bytes=1 << 20, dtype=BF16, B=1, h=1, n_q=16, n_k=16, d_k=64, d_v=64):
+    return lib.sdpa_backward(Q, K, V, O, dO, lse, kv_len, window, mask, dQ, dK, dV, ws, ws_bytes, dtype, B, h, n_q,
+                             n_k, d_k, d_v, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -116,6 +116,7 @@ def bwd(lib, Q=A, K=A * 2, V=A * 3, O=A * 4, dO=A * 5, lse=A * 6, kv_len=None, m
     # outputs over inputs, outputs over each other, workspace over an input
     (dict(dQ=A * 4), INVALID), (dict(dV=A * 200 + 1024), INVALID), (dict(ws=A * 6), INVALID),
     (dict(dK=A * 400), INVALID), (dict(kv_len=A * 7 + 4), INVALID), (dict(kv_len=A * 100 + 64), INVALID),
+    (dict(window=3, n_k=32), UNSUPPORTED), (dict(window=3, kv_len=A * 7), UNSUPPORTED),
 ])
 def test_sdpa_backward_rejects_bad_arguments(lib, kw, code):
     assert bwd(lib, **kw) == code

@@ -76,3 +76,48 @@ def test_window_rejects_bad_arguments():
     k = torch.zeros(1, 1, 9, 64, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(m.AttnError):
         m.sdpa_forward_window(q, k, k, 2)
+
+
+def _check_grads(got, ref, dtype, what):
+    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        g = to_f64(g)
+        assert np.all(np.isfinite(g)), f"{what} {name}: non-finite"
+        if not np.any(r):
+            # radius 0: one key per row, so dS = P (dP - D) = 0 exactly and dQ = dK = 0; the kernels return the
+            # rounding residue of dP - D (terms of order 10, rounded in fp32 or fed from bf16 operands)
+            assert np.abs(g).max() <= (1e-4 if dtype == "f32" else 2e-2), f"{what} {name}: {np.abs(g).max():.3g}"
+            continue
+        d = np.abs(g - r)
+        rel = float(d.max()) / max(float(np.abs(r).max()), 0.05)
+        if dtype == "f32":
+            assert rel <= 1e-5, f"{what} {name}: max rel {rel:.3g}"
+        else:
+            nrms = float(np.sqrt(np.mean(d * d)) / max(np.sqrt(np.mean(r * r)), 0.05))
+            assert nrms <= 1e-2 and rel <= 1.5e-2, f"{what} {name}: nrms {nrms:.3g} max rel {rel:.3g}"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("n,w,causal", [(77, 0, False), (256, 31, False), (256, 64, True), (300, 65, False),
+                                        (700, 200, True), (520, 1000, False), (129, 1, False)])
+def test_window_backward_parity(dtype, n, w, causal):
+    # bars as for the unpadded backward (normalised rms <= 1e-2, max-rel <= 1.5e-2 in bf16; 1e-5 in fp32)
+    from oracle import sdpa_backward_ref
+    x = workloads.make_sdpa_inputs(2, 2, n, n, 64, 64, dtype, 9700 + n + w, dout=True)
+    q, k, v, do = (to_dev(x[nm]) for nm in ("Q", "K", "V", "dO"))
+    mask = "causal" if causal else "none"
+    out, lse = m.sdpa_forward_window(q, k, v, w, mask=mask, return_lse=True)
+    grads = m.sdpa_backward(q, k, v, out, do, lse, mask=mask, window=w)
+    torch.cuda.synchronize()
+    ref = sdpa_backward_ref(x["Q"].f64, x["K"].f64, x["V"].f64, x["dO"].f64, causal, window=w)
+    _check_grads(grads, ref, dtype, f"window backward {dtype} n={n} w={w} causal={causal}")
+
+
+def test_autograd_wrapper_with_window():
+    x = workloads.make_sdpa_inputs(2, 2, 200, 200, 64, 64, "bf16", 9800, dout=True)
+    q, k, v, do = (to_dev(x[nm]) for nm in ("Q", "K", "V", "dO"))
+    qa, ka, va = (t.clone().requires_grad_(True) for t in (q, k, v))
+    m.attention(qa, ka, va, window=40).backward(do)
+    out, lse = m.sdpa_forward_window(q, k, v, 40, return_lse=True)
+    dq, dk, dv = m.sdpa_backward(q, k, v, out, do, lse, window=40)
+    torch.cuda.synchronize()
+    assert torch.equal(qa.grad, dq) and torch.equal(ka.grad, dk) and torch.equal(va.grad, dv)

@@ -68,3 +68,28 @@ def test_window_matches_torch_banded_mask(causal):
     want = torch.nn.functional.scaled_dot_product_attention(torch.tensor(Q), torch.tensor(K), torch.tensor(V),
                                                             attn_mask=torch.tensor(mask)).numpy()
     np.testing.assert_allclose(sdpa_ref(Q, K, V, causal, window=w), want, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_window_backward_equals_central_differences(causal):
+    from oracle import sdpa_backward_ref
+    n, w = 6, 1
+    Q, K, V = _case(7, 1, 1, n, d=4, dv=3)
+    dO = np.random.Generator(np.random.PCG64(8)).standard_normal((1, 1, n, 3))
+    grads = sdpa_backward_ref(Q, K, V, dO, causal, window=w)
+
+    def loss():
+        return float(np.sum(dO * sdpa_ref(Q, K, V, causal, window=w)))
+
+    eps = 1e-5
+    for got, x in zip(grads, (Q, K, V)):
+        num = np.empty_like(x)
+        for idx in np.ndindex(*x.shape):
+            old = x[idx]
+            x[idx] = old + eps
+            fp = loss()
+            x[idx] = old - eps
+            fm = loss()
+            x[idx] = old
+            num[idx] = (fp - fm) / (2 * eps)
+        np.testing.assert_allclose(got, num, rtol=0, atol=1e-8)

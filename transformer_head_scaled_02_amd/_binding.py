@@ -50,8 +50,8 @@ def load_library(path: Path | str | None = None) -> ctypes.CDLL:
     lib.sdpa_forward_padded.restype = ci
     lib.sdpa_forward_window.argtypes = [vp, vp, vp, i64, ci, vp, vp, ci, i64, i64, i64, i64, i64, i64, vp]
     lib.sdpa_forward_window.restype = ci
-    lib.sdpa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, vp, vp, vp, vp, sz, ci, i64, i64, i64, i64, i64, i64,
-                                  vp]
+    lib.sdpa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, ci, vp, vp, vp, vp, sz, ci, i64, i64, i64, i64, i64,
+                                  i64, vp]
     lib.sdpa_backward.restype = ci
     lib.sdpa_backward_workspace_size.argtypes = [ci, i64, i64, i64, i64, i64, i64]
     lib.sdpa_backward_workspace_size.restype = sz
@@ -226,7 +226,7 @@ def sdpa_backward_workspace_size(B: int, h: int, n_q: int, n_k: int, d_k: int = 
 def sdpa_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, dout: torch.Tensor,
                   lse: torch.Tensor, mask="none", dq: torch.Tensor | None = None, dk: torch.Tensor | None = None,
                   dv: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-                  kv_len: torch.Tensor | None = None):
+                  kv_len: torch.Tensor | None = None, window: int | None = None):
     """Gradients (dq, dk, dv) of attention given the forward's output `out`, its `lse` (from sdpa_forward_lse, or
     sdpa_forward_padded with the same `kv_len`) and the upstream gradient `dout` [B,h,n_q,64]. `workspace` (uint8,
     at least sdpa_backward_workspace_size bytes) may be passed in to avoid an allocation."""
@@ -249,7 +249,8 @@ def sdpa_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.
     ws_bytes = workspace.numel() * workspace.element_size()
     kv_ptr = _kv_len_tensor(kv_len, B, q.device).data_ptr() if kv_len is not None else None
     _check(lib.sdpa_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
-                             lse.data_ptr(), kv_ptr, _mask_code(mask), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                             lse.data_ptr(), kv_ptr, -1 if window is None else int(window), _mask_code(mask),
+                             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                              workspace.data_ptr(), ws_bytes, _dtype_code(q), B, h, n_q, n_k, d_k, d_v,
                              _stream_handle(q.device)))
     return dq, dk, dv
@@ -260,27 +261,33 @@ class SDPAFunction(torch.autograd.Function):
     (all in the HIP library)."""
 
     @staticmethod
-    def forward(ctx, q, k, v, mask="none", kv_len=None):
+    def forward(ctx, q, k, v, mask="none", kv_len=None, window=None):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
-        if kv_len is None:
+        if window is not None:
+            if kv_len is not None:
+                raise ValueError("a window with key padding is not supported")
+            out, lse = sdpa_forward_window(q, k, v, window, mask, return_lse=True)
+        elif kv_len is None:
             out, lse = sdpa_forward_lse(q, k, v, mask)
         else:
             out, lse = sdpa_forward_padded(q, k, v, kv_len, mask, return_lse=True)
         ctx.save_for_backward(q, k, v, out, lse)
-        ctx.mask, ctx.kv_len = mask, kv_len
+        ctx.mask, ctx.kv_len, ctx.window = mask, kv_len, window
         return out
 
     @staticmethod
     def backward(ctx, dout):
         q, k, v, out, lse = ctx.saved_tensors
-        dq, dk, dv = sdpa_backward(q, k, v, out, dout.contiguous(), lse, ctx.mask, kv_len=ctx.kv_len)
-        return dq, dk, dv, None, None
+        dq, dk, dv = sdpa_backward(q, k, v, out, dout.contiguous(), lse, ctx.mask, kv_len=ctx.kv_len,
+                                   window=ctx.window)
+        return dq, dk, dv, None, None, None
 
 
-def attention(q, k, v, mask="none", kv_len=None):
+def attention(q, k, v, mask="none", kv_len=None, window=None):
     """Differentiable attention on the HIP library: softmax(q k^T / sqrt(d_k)) v with gradients for q, k and v;
-    `kv_len` (int32 [B] on the GPU) adds the key padding mask."""
-    return SDPAFunction.apply(q, k, v, mask, kv_len)
+    `kv_len` (int32 [B] on the GPU) adds the key padding mask, `window` restricts each query to keys within that
+    distance."""
+    return SDPAFunction.apply(q, k, v, mask, kv_len, window)
 
 
 def mha_workspace_size(B: int, n_q: int, n_k: int, h: int, d_k: int = 64, d_v: int = 64,

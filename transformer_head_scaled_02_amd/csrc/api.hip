@@ -238,14 +238,19 @@ ATTN_EXPORT size_t sdpa_backward_workspace_size(int dtype, int64_t B, int64_t h,
 }
 
 ATTN_EXPORT int sdpa_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
-                              const float* lse, const int32_t* kv_len, int mask_kind, void* dQ, void* dK, void* dV,
-                              void* workspace,
+                              const float* lse, const int32_t* kv_len, int64_t window, int mask_kind, void* dQ,
+                              void* dK, void* dV, void* workspace,
                               size_t workspace_bytes, int dtype, int64_t B, int64_t h, int64_t n_q, int64_t n_k,
                               int64_t d_k, int64_t d_v, void* stream) {
   static const char* fn = "sdpa_backward";
   if (!Q || !K || !V || !O || !dO || !lse || !dQ || !dK || !dV || !workspace)
     return fail_status(ATTN_ERR_INVALID, "%s: null pointer", fn);
   if (int st = check_sdpa_sizes(fn, dtype, mask_kind, B, h, n_q, n_k, d_k, d_v, true)) return st;
+  if (window >= 0 && n_q != n_k)
+    return fail_status(ATTN_ERR_UNSUPPORTED, "%s: a window needs n_q == n_k (got %lld, %lld)", fn, (long long)n_q,
+                       (long long)n_k);
+  if (window >= 0 && kv_len)
+    return fail_status(ATTN_ERR_UNSUPPORTED, "%s: a window with key padding has no forward entry point", fn);
   const size_t need = bwd_workspace_bytes(B, h, n_q);
   if (workspace_bytes < need)
     return fail_status(ATTN_ERR_INVALID, "%s: workspace %zu bytes, need %zu", fn, workspace_bytes, need);
@@ -275,6 +280,10 @@ ATTN_EXPORT int sdpa_backward(const void* Q, const void* K, const void* V, const
   a.B = (int)B; a.H = (int)h; a.n_q = (int)n_q; a.n_k = (int)n_k;
   a.causal = mask_kind == ATTN_MASK_CAUSAL;
   a.kv_len = kv_len;
+  if (window >= 0) {
+    a.windowed = 1;
+    a.window = (int)(window < n_k ? window : n_k);
+  }
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = dtype == ATTN_BF16 ? mi355::launch_attn_bwd_bf16(a, s) : mi355::launch_attn_bwd_f32(a, s);
   if (e != hipSuccess) return fail_status(ATTN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));

@@ -154,7 +154,7 @@ __global__ __launch_bounds__(256) void attn_bwd_pre(BwdArgs a, int n_tiles) {
 }
 
 // dK and dV: see the file comment (launch 2).
-template <int NW, int kStages>
+template <int NW, int kStages, bool WIN>
 __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16(BwdArgs a, int n_kblocks) {
   constexpr int kBK = 32 * NW;                    // keys per workgroup
   constexpr int kLPW = 16 / NW;                   // Q/dO copies per wave per tile (wave 0 also copies lse/D)
@@ -202,9 +202,22 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16(BwdArgs a, int 
 
   // Query tiles: causal work starts at the tile holding the workgroup's first key. Per wave, tiles before t_first
   // hold only rows before all its keys (all weights 0) and tiles from t_nomask on only rows at or after all of them.
-  const int t0 = causal ? k_blk0 / kBN : 0;
-  const int t_first = causal ? kw0 / kBN : 0;
+  constexpr bool win = WIN;  // restricted self-attention (a separate instantiation)
+  const int wr = a.window;
+  int t0 = causal ? k_blk0 / kBN : 0;
+  int t_first = causal ? kw0 / kBN : 0;
   const int t_nomask = causal ? (kw0 + 31) / kBN + 1 : 0;
+  int t_last = n_tiles - 1;  // this wave's last query tile
+  if (win) {  // restricted self-attention: rows key - window .. key + window (.. key when causal)
+    if (!causal) {
+      t0 = max(0, k_blk0 - wr) / kBN;
+      t_first = max(0, kw0 - wr) / kBN;
+    }
+    t_last = min(t_last, (kw0 + 31 + wr) / kBN);
+  }
+  // a query row may see this lane's key when lo_off <= key - row <= hi_off
+  const int hi_off = causal ? 0 : (win ? wr : (1 << 30));
+  const int lo_off = win ? -wr : -(1 << 30);
 
   const uint32_t smem_lds = (uint32_t)(uintptr_t)smem;
   const int lrow = lane >> 3;
@@ -234,7 +247,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16(BwdArgs a, int 
   dv[0] = dv[1] = dk[0] = dk[1] = f32x16{};
 
   // a workgroup of padding keys only writes zeros
-  const int nt = k_blk0 < n_real ? n_tiles : 0;
+  int nt = k_blk0 < n_real ? n_tiles : 0;
+  if (win) nt = min(nt, (k_blk0 + kBK - 1 + wr) / kBN + 1);
 #pragma unroll
   for (int i = 0; i < kStages - 1; ++i)
     if (t0 + i < nt) issue(t0 + i);
@@ -245,8 +259,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16(BwdArgs a, int 
     else wait_copies<kLPW, kStages>(ahead);
     lds_barrier();  // also: every wave is done with tile t-1, whose stage tile t + kStages - 1 now takes
     if (t + kStages - 1 < nt) issue(t + kStages - 1);
-    if (t < t_first || !wave_real) continue;
-    const bool masked = t < t_nomask;
+    if (t < t_first || t > t_last || !wave_real) continue;
+    const bool masked = win || t < t_nomask;
     const uint16_t* st = smem + ((t - t0) % kStages) * kStageElems;
     const float* aux = reinterpret_cast<const float*>(st + 2 * kTileElems);
 
@@ -267,11 +281,14 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16(BwdArgs a, int 
         lq[i] = *reinterpret_cast<const f32x4*>(aux + 32 * mq + 8 * i + 4 * g);
         dq[i] = *reinterpret_cast<const f32x4*>(aux + kBN + 32 * mq + 8 * i + 4 * g);
       }
+      const int base = key - t * kBN - 32 * mq - 4 * g;
+      const int ub = base - hi_off, lb = base - lo_off;
       float p[16], ds[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float sv = s[r];
-        if (masked && key > t * kBN + 32 * mq + 8 * (r >> 2) + 4 * g + (r & 3)) sv = -INFINITY;
+        // key - row = base - (8(r/4) + r%4); allowed when lo_off <= key - row <= hi_off
+        if (masked && (8 * (r >> 2) + (r & 3) < ub || (WIN && 8 * (r >> 2) + (r & 3) > lb))) sv = -INFINITY;
         p[r] = fast_exp2(__builtin_fmaf(sv, kScaleLog2, -lq[r >> 2][r & 3]));
         ds[r] = p[r] * (dp[r] - dq[r >> 2][r & 3]);
       }
@@ -321,7 +338,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16(BwdArgs a, int 
 }
 
 // dQ: see the file comment (launch 3).
-template <int NW, int kStages>
+template <int NW, int kStages, bool WIN>
 __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dq_bf16(BwdArgs a, int n_qblocks) {
   constexpr int kBM = 32 * NW;  // queries per workgroup
   static_assert(16 % NW == 0, "tile copies split evenly over the waves");
@@ -376,9 +393,22 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dq_bf16(BwdArgs a, int n_
   int nt = (n_k + kBN - 1) / kBN;
   if (causal) nt = min(nt, (q_blk0 + kBM - 1) / kBN + 1);
   // tiles before t_mask need no mask for any query of this wave; tiles from t_skip on lie entirely in its future
-  const int t_mask = min(causal ? qw0 / kBN : nt, n_k / kBN);
-  const int t_skip = causal ? min(nt, (qw0 + 31) / kBN + 1) : nt;
-  const int key_lim = (causal ? min(q, n_k - 1) : n_k - 1) - 4 * g;  // keys past it (from the lane's first) masked
+  int t_mask = min(causal ? qw0 / kBN : nt, n_k / kBN);
+  int t_skip = causal ? min(nt, (qw0 + 31) / kBN + 1) : nt;
+  int key_lim = (causal ? min(q, n_k - 1) : n_k - 1) - 4 * g;  // keys past it (from the lane's first) masked
+  // restricted self-attention: key tiles from the workgroup's first band start on; keys before key_lo also masked
+  constexpr bool win = WIN;  // restricted self-attention (a separate instantiation)
+  int t_begin = 0, t_first = 0, key_lo = -(1 << 30);
+  if (win) {
+    const int wr = a.window;
+    t_begin = max(0, q_blk0 - wr) / kBN;
+    t_first = max(0, qw0 - wr) / kBN;
+    nt = min(nt, (q_blk0 + kBM - 1 + wr) / kBN + 1);
+    t_skip = min(t_skip, (qw0 + 31 + wr) / kBN + 1);
+    t_mask = 0;
+    key_lim = min(key_lim, q + wr - 4 * g);
+    key_lo = q - wr - 4 * g;
+  }
 
   const uint32_t smem_lds = (uint32_t)(uintptr_t)smem;
   const int lrow = lane >> 3;
@@ -408,12 +438,12 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dq_bf16(BwdArgs a, int n_
   constexpr int kLPW = 16 / NW;
 #pragma unroll
   for (int i = 0; i < kStages - 1; ++i)
-    if (i < nt) issue(i);
-  for (int t = 0; t < nt; ++t) {
+    if (t_begin + i < nt) issue(t_begin + i);
+  for (int t = t_begin; t < nt; ++t) {
     wait_copies<kLPW, kStages>(min(kStages - 2, nt - 1 - t));
     lds_barrier();
     if (t + kStages - 1 < nt) issue(t + kStages - 1);
-    if (t >= t_skip) continue;
+    if (t >= t_skip || (WIN && t < t_first)) continue;
     const bool masked = t >= t_mask;
     const uint16_t* st = smem + (t % kStages) * 2 * kTileElems;
 
@@ -431,12 +461,13 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dq_bf16(BwdArgs a, int n_
                               dp[kb]);
     }
     if (masked) {
-      const int lim = key_lim - t * kBN;
+      const int lim = key_lim - t * kBN, lo = key_lo - t * kBN;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = -INFINITY;
+          if (32 * kb + 8 * (r >> 2) + (r & 3) > lim || (WIN && 32 * kb + 8 * (r >> 2) + (r & 3) < lo))
+            s[kb][r] = -INFINITY;
     }
     // dS^T in bf16, B operand of k-step ks: registers 8(ks%2) .. +7 of key block ks/2
 #pragma unroll
@@ -490,10 +521,20 @@ hipError_t launch_attn_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
   if (!grid_ok(nb_kv) || !grid_ok(nb_q)) return hipErrorInvalidValue;
   hipError_t e = launch_attn_bwd_pre(a, false, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_bwd_dkdv_bf16<NW, kStagesKV>), dim3((unsigned)nb_kv), dim3(64 * NW), 0, stream, a, n_kblocks);
+  if (a.windowed)
+    hipLaunchKernelGGL((attn_bwd_dkdv_bf16<NW, kStagesKV, true>), dim3((unsigned)nb_kv), dim3(64 * NW), 0, stream, a,
+                       n_kblocks);
+  else
+    hipLaunchKernelGGL((attn_bwd_dkdv_bf16<NW, kStagesKV, false>), dim3((unsigned)nb_kv), dim3(64 * NW), 0, stream, a,
+                       n_kblocks);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_bwd_dq_bf16<NW, kStagesQ>), dim3((unsigned)nb_q), dim3(64 * NW), 0, stream, a, n_qblocks);
+  if (a.windowed)
+    hipLaunchKernelGGL((attn_bwd_dq_bf16<NW, kStagesQ, true>), dim3((unsigned)nb_q), dim3(64 * NW), 0, stream, a,
+                       n_qblocks);
+  else
+    hipLaunchKernelGGL((attn_bwd_dq_bf16<NW, kStagesQ, false>), dim3((unsigned)nb_q), dim3(64 * NW), 0, stream, a,
+                       n_qblocks);
   return hipGetLastError();
 }
 

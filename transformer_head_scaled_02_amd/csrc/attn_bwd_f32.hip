@@ -48,7 +48,12 @@ __global__ __launch_bounds__(2 * kRows) void attn_bwd_dkdv_f32(BwdArgs a) {
     dk[d] = dv[d] = 0.f;
   }
   // causal: rows before k0 see none of these keys; a workgroup of padding keys only writes zeros
-  for (int q0 = a.causal ? k0 : 0; q0 < (k0 < n_real ? n_q : 0); q0 += kRows) {
+  int q_begin = a.causal ? k0 : 0, q_end = k0 < n_real ? n_q : 0;
+  if (a.windowed) {  // restricted self-attention: rows within a.window of some key of the block
+    if (!a.causal) q_begin = max(0, k0 - a.window) / kRows * kRows;
+    q_end = min(q_end, k0 + kRows + a.window);
+  }
+  for (int q0 = q_begin; q0 < q_end; q0 += kRows) {
     __syncthreads();
     for (int e = tid; e < kRows * kD; e += 2 * kRows) {
       const int r = e / kD, c = e % kD;
@@ -74,7 +79,8 @@ __global__ __launch_bounds__(2 * kRows) void attn_bwd_dkdv_f32(BwdArgs a) {
       dp += __shfl_xor(dp, 1);
       const int row = q0 + i;
       float p = fast_exp2(fmaf(s, kC, -Ls[i]));  // 0 for rows past n_q and rows that saw no key (lse2 = +inf)
-      if ((a.causal && key > row) || key >= n_real) p = 0.f;
+      if ((a.causal && key > row) || key >= n_real || (a.windowed && (key > row + a.window || key < row - a.window)))
+        p = 0.f;
       const float ds = p * (dp - Ds[i]);
 #pragma unroll
       for (int d = 0; d < kHalf; ++d) {
@@ -117,8 +123,13 @@ __global__ __launch_bounds__(2 * kRows) void attn_bwd_dq_f32(BwdArgs a) {
     dq[d] = 0.f;
   }
   const float2 ld = qi < n_q ? aux_row(a.aux, n_tiles, bh, qi) : float2{INFINITY, 0.f};
-  const int k_end = a.causal ? min(n_real, qb0 + kRows) : n_real;  // keys after the last query are never needed
-  for (int k0 = 0; k0 < k_end; k0 += kRows) {
+  int k_end = a.causal ? min(n_real, qb0 + kRows) : n_real;  // keys after the last query are never needed
+  int k_begin = 0;
+  if (a.windowed) {  // restricted self-attention: keys within a.window of some query of the block
+    k_end = min(k_end, qb0 + kRows + a.window);
+    k_begin = max(0, qb0 - a.window) / kRows * kRows;
+  }
+  for (int k0 = k_begin; k0 < k_end; k0 += kRows) {
     __syncthreads();
     for (int e = tid; e < kRows * kD; e += 2 * kRows) {
       const int r = e / kD, c = e % kD;
@@ -138,7 +149,8 @@ __global__ __launch_bounds__(2 * kRows) void attn_bwd_dq_f32(BwdArgs a) {
       dp += __shfl_xor(dp, 1);
       const int key = k0 + j;
       float p = fast_exp2(fmaf(s, kC, -ld.x));
-      if (key >= n_real || (a.causal && key > qi)) p = 0.f;
+      if (key >= n_real || (a.causal && key > qi) || (a.windowed && (key > qi + a.window || key < qi - a.window)))
+        p = 0.f;
       const float ds = p * (dp - ld.y);
 #pragma unroll
       for (int d = 0; d < kHalf; ++d) dq[d] = fmaf(ds, Ks[j][kHalf * h + d], dq[d]);

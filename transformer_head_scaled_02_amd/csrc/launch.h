@@ -46,6 +46,7 @@ struct BwdArgs {
   int B, H, n_q, n_k;
   int causal;
   const int* kv_len;  // optional key padding, as in AttnArgs; dK and dV rows of padding keys are written as 0
+  int windowed, window;  // optional restricted self-attention, as in AttnArgs
 };
 constexpr int kAuxFloatsPerTile = 256;
 
