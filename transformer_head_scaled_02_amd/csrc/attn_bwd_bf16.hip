@@ -170,10 +170,16 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16(BwdArgs a, int 
   const bool causal = a.causal != 0;
   const int n_tiles = (n_q + kBN - 1) / kBN;
 
-  const int blk = xcd_remap(blockIdx.x, gridDim.x);
-  const int kb = blk % n_kblocks;
+  int kb, slot;  // causal: key block 0 sees the most query tiles, so it goes first
+  if (causal) {
+    causal_order(blockIdx.x, gridDim.x, n_kblocks, slot, kb);
+  } else {
+    const int blk = xcd_remap(blockIdx.x, gridDim.x);
+    kb = blk % n_kblocks;
+    slot = blk / n_kblocks;
+  }
   int bh;
-  const int b = head_of_slot(blk / n_kblocks, a.B, a.H, bh);
+  const int b = head_of_slot(slot, a.B, a.H, bh);
   const int n_real = real_keys(a.kv_len, b, n_k);  // keys from n_real on are padding: gradient 0
   const uint16_t* Qp = static_cast<const uint16_t*>(a.Q) + (int64_t)bh * n_q * kD;
   const uint16_t* dOp = static_cast<const uint16_t*>(a.dO) + (int64_t)bh * n_q * kD;
@@ -352,11 +358,17 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dq_bf16(BwdArgs a, int n_
   const int n_q = a.n_q;
   const int n_tiles_q = (n_q + kBN - 1) / kBN;
 
-  const int blk = xcd_remap(blockIdx.x, gridDim.x);
-  int qb = blk % n_qblocks;
+  int qb, slot;
+  if (causal) {
+    causal_order(blockIdx.x, gridDim.x, n_qblocks, slot, qb);
+    qb = n_qblocks - 1 - qb;  // heaviest query blocks first
+  } else {
+    const int blk = xcd_remap(blockIdx.x, gridDim.x);
+    qb = blk % n_qblocks;
+    slot = blk / n_qblocks;
+  }
   int bh;
-  const int b = head_of_slot(blk / n_qblocks, a.B, a.H, bh);
-  if (causal) qb = n_qblocks - 1 - qb;  // heaviest query blocks first
+  const int b = head_of_slot(slot, a.B, a.H, bh);
   const int n_k = real_keys(a.kv_len, b, a.n_k);  // keys from n_k on (padding) are never read
   const uint16_t* Qp = static_cast<const uint16_t*>(a.Q) + (int64_t)bh * n_q * kD;
   const uint16_t* dOp = static_cast<const uint16_t*>(a.dO) + (int64_t)bh * n_q * kD;

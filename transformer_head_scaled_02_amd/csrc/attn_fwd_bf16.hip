@@ -66,11 +66,17 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, i
   const int g = lane >> 5, li = lane & 31;
   const bool causal = H == 1 && a.causal != 0;  // the two-half kernel serves unmasked attention only
 
-  const int blk = xcd_remap(blockIdx.x, gridDim.x);
-  int qb = blk % n_qblocks;
+  int qb, slot;
+  if (causal) {
+    causal_order(blockIdx.x, gridDim.x, n_qblocks, slot, qb);
+    qb = n_qblocks - 1 - qb;  // heaviest query blocks first
+  } else {
+    const int blk = xcd_remap(blockIdx.x, gridDim.x);
+    qb = blk % n_qblocks;
+    slot = blk / n_qblocks;
+  }
   int bh;
-  const int b = head_of_slot(blk / n_qblocks, a.B, a.H, bh), hh = bh - b * a.H;
-  if (causal) qb = n_qblocks - 1 - qb;  // heaviest query blocks first
+  const int b = head_of_slot(slot, a.B, a.H, bh), hh = bh - b * a.H;
   const int n_q = a.n_q;
   int n_k = real_keys(a.kv_len, b, a.n_k);  // keys from n_k on (padding) are never read
   const uint16_t* Qp = static_cast<const uint16_t*>(a.Q) + (int64_t)bh * a.q_stride_bh;

@@ -72,6 +72,25 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   return xcd * per + (xcd < rem ? xcd : rem) + slot;
 }
 
+// Causal workloads, whose blocks differ in cost: map the hardware block id to (head slot, block index within the head)
+// so that each XCD still owns whole heads (its blocks share K/V in its L2) but dispatches them block-index-major:
+// index 0 of all its heads first, then index 1, and so on. The caller makes index 0 the heaviest block, so the
+// longest blocks start first and the light ones fill in behind them. Falls back to xcd_remap's head-major order when
+// the heads do not divide evenly over the XCDs.
+__device__ __forceinline__ void causal_order(int bid, int nblocks, int n_per_head, int& head_slot, int& idx) {
+  constexpr int kXcds = 8;
+  const int per = nblocks / kXcds;
+  if (nblocks % kXcds == 0 && per % n_per_head == 0) {
+    const int hx = per / n_per_head, xcd = bid % kXcds, slot = bid / kXcds;
+    head_slot = xcd * hx + slot % hx;
+    idx = slot / hx;
+  } else {
+    const int l = xcd_remap(bid, nblocks);
+    head_slot = l / n_per_head;
+    idx = l % n_per_head;
+  }
+}
+
 // Head of a workgroup's slot: slots are decoded batch-minor (slot % B is the batch entry), so that the contiguous
 // slot range xcd_remap gives each XCD spans every batch entry. Heads are independent, so this costs nothing when
 // every entry does the same work, and it keeps the XCDs evenly loaded when entries differ (key padding). Returns the
