@@ -25,11 +25,11 @@ namespace mi355 {
 namespace {
 
 constexpr int kTN = 128, kTK = 64;             // workgroup tile columns and k-tile (rows: TM = 128 or 64)
-constexpr int kThreads = 256;
 constexpr int kSub = 64 * 64;                  // one 64 x 64 bf16 sub-tile, rows of 128 bytes (8 KB)
 // a stage: [A rows 0..TM-1 (TM/64 sub-tiles) | W cols 0-63 | W cols 64-127]
 constexpr int kMaxProbs = 3;
 constexpr int kGemmStages = 2;  // ring depth of the launch
+constexpr int kGemmWaves = 8;   // waves per workgroup (2 x kGemmWaves/2 over the tile)
 
 struct GemmBatch {
   GemmProblem p[kMaxProbs];
@@ -38,12 +38,15 @@ struct GemmBatch {
   int nprobs;
 };
 
-template <int kStagesG, int TM>
-__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_mfma(GemmBatch batch) {
+template <int kStagesG, int TM, int NWV>
+__global__ __launch_bounds__(64 * NWV, 1) void gemm_bf16_mfma(GemmBatch batch) {
   constexpr int kStageElemsG = (TM / 64 + 2) * kSub;
+  constexpr int WN = NWV / 2;          // waves across the 128 columns (2 down the rows)
   constexpr int MB = TM / 64;          // 32-row blocks per wave
+  constexpr int NB = 4 / WN;           // 32-column blocks per wave
   constexpr int kACopies = TM / 8;     // one-kilobyte copies of A rows per stage (W: 16)
-  constexpr int kCPW = (kACopies + 16) / 4;  // copies per wave
+  constexpr int kCPW = (kACopies + 16) / NWV;  // copies per wave
+  static_assert((kACopies + 16) % NWV == 0, "copies split evenly over the waves");
   __shared__ __attribute__((aligned(16))) uint16_t smem[kStagesG * kStageElemsG];
 
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
@@ -125,9 +128,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_mfma(GemmBatch batch) {
       }
   }
 
-  f32x16 acc[2][MB];  // [nb][mb]: register r = C[row 32mb + li][column 32nb + 8(r/4) + 4g + r%4] of this wave's part
+  f32x16 acc[NB][MB];  // [nb][mb]: register r = C[row 32mb + li][column 32nb + 8(r/4) + 4g + r%4] of this wave's part
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
+  for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = f32x16{};
 
@@ -145,28 +148,30 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_mfma(GemmBatch batch) {
     lds_barrier();
     if (t + kStagesG - 1 < nk) issue(t + kStagesG - 1);
     const uint16_t* st = smem + (t % kStagesG) * kStageElemsG;
-    const uint16_t* As = st + (wave >> 1) * (TM / 2) * kD;  // this wave's TM/2 rows of A
-    const uint16_t* Ws = st + (MB + (wave & 1)) * kSub;
+    const uint16_t* As = st + (wave / WN) * (TM / 2) * kD;  // this wave's TM/2 rows of A
+    // this wave's 32 NB columns: sub-tile (wn * NB) / 2, 32-column blocks cb0 .. cb0 + NB - 1 within it
+    const int wn = wave % WN, cb0 = (wn * NB) % 2;
+    const uint16_t* Ws = st + (MB + (wn * NB) / 2) * kSub;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      bf16x8 bo[MB], ao[2];
+      bf16x8 bo[MB], ao[NB];
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) bo[mb] = *reinterpret_cast<const bf16x8*>(As + mb * 32 * kD + aoff[ks]);
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const bf16x4 lo = lds_read_tr16x4(Ws + ks * 16 * kD + toff[nb][0]);
-        const bf16x4 hi = lds_read_tr16x4(Ws + ks * 16 * kD + toff[nb][1]);
+      for (int nb = 0; nb < NB; ++nb) {
+        const bf16x4 lo = lds_read_tr16x4(Ws + ks * 16 * kD + toff[cb0 + nb][0]);
+        const bf16x4 hi = lds_read_tr16x4(Ws + ks * 16 * kD + toff[cb0 + nb][1]);
         ao[nb] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = mfma32x32x16(ao[nb], bo[mb], acc[nb][mb]);
     }
   }
 
   // Epilogue: lane writes columns n .. n+3 of row m for each (nb, mb, r/4).
-  const int mw = m0 + (TM / 2) * (wave >> 1), nw = n0 + 64 * (wave & 1);
+  const int mw = m0 + (TM / 2) * (wave / WN), nw = n0 + (128 / WN) * (wave % WN);
   if (nw >= N) return;  // (uniform) the missing half of a 64-column-wide problem
   uint16_t* C = static_cast<uint16_t*>(P.C);
   const uint16_t* bias = static_cast<const uint16_t*>(P.bias);
@@ -177,7 +182,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_mfma(GemmBatch batch) {
     const int m = mw + 32 * mb + li;
     if (m >= M) continue;
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         const int n = nw + 32 * nb + 8 * rg + 4 * g;
@@ -307,9 +312,11 @@ hipError_t launch_gemm_bf16(const GemmProblem* probs, int nprobs, hipStream_t st
   }
   batch.tile_start[nprobs] = (int)total;
   if (tm == 128)
-    hipLaunchKernelGGL((gemm_bf16_mfma<kGemmStages, 128>), dim3((unsigned)total), dim3(kThreads), 0, stream, batch);
+    hipLaunchKernelGGL((gemm_bf16_mfma<kGemmStages, 128, kGemmWaves>), dim3((unsigned)total), dim3(64 * kGemmWaves), 0,
+                       stream, batch);
   else
-    hipLaunchKernelGGL((gemm_bf16_mfma<kGemmStages, 64>), dim3((unsigned)total), dim3(kThreads), 0, stream, batch);
+    hipLaunchKernelGGL((gemm_bf16_mfma<kGemmStages, 64, kGemmWaves>), dim3((unsigned)total), dim3(64 * kGemmWaves), 0,
+                       stream, batch);
   return hipGetLastError();
 }
 
