@@ -28,27 +28,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
-// Two non-negative finite fp32 values -> two bf16, rounded to nearest (ties away from zero) with one integer add each
-// and one byte permute: adding 0x8000 to the bit pattern carries into the kept half exactly when the dropped half is
-// at least half an ulp. (v_cvt_pk_bf16_f32 costs several times more VALU cycles on gfx950.)
-__device__ __forceinline__ uint32_t pack_bf16x2_nonneg(float lo, float hi) {
-  const uint32_t a = __float_as_uint(lo) + 0x8000u, b = __float_as_uint(hi) + 0x8000u;
-  return __builtin_amdgcn_perm(b, a, 0x07060302u);  // bytes 2,3 of a (low half) and of b (high half)
-}
-
-__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
-  return __uint_as_float(bits16 << 16);
-}
-
 // v_permlane32_swap with the same value in both operands: r[0] and r[1] together hold this lane's value and the
 // value of the lane 32 away (lanes < 32: r[0] own, r[1] partner; lanes >= 32: r[0] partner, r[1] own).
 __device__ __forceinline__ float max_with_partner32(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float sum_with_partner32(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
