@@ -33,7 +33,7 @@ from pathlib import Path
 ROOT = Path(__file__).resolve().parent
 sys.path.insert(0, str(ROOT))
 
-METRIC = "attention TFLOP/s (4·B·h·n_q·n_k·d_k) at h=8,d_k=64; % of bf16 MFMA peak"
+METRIC = "attention TFLOP/s (4·B·h·n_q·n_k·d_k) at h={h},d_k={d_k}; % of bf16 MFMA peak"
 METRIC_WINDOW = "restricted self-attention TFLOP/s over the band's pairs (4·B·h·pairs·d_k) at h=8,d_k=64; % of bf16 MFMA peak"
 METRIC_PADDED = "attention TFLOP/s over real keys (4·h·n_q·Σ_b kv_len[b]·d_k) at h=8,d_k=64; % of bf16 MFMA peak"
 METRIC_ENC = "encoder layer TFLOP/s (projections, attention, W^O, FFN) at d_model=512,h=8,d_ff=2048; % of bf16 MFMA peak"
@@ -290,7 +290,7 @@ def bench_window(args, w, x, m, dev):
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(value, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(value / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": "attn_fwd_bf16_d64<4, 1, 2, 4, true>"},
+                     "kernel": "attn_fwd_bf16<64, 4, 1, 2, 4, true>"},
         "wall_s_timed_region": round(wall, 4),
         "parity_last_step": {"max_abs": float(err.max()), "mean_abs": float(err.mean())},
     }
@@ -335,7 +335,7 @@ def bench_padded(args, w, x, m, dev):
                    "d_k": w["d_k"], "d_v": w["d_v"], "mask": "none", "kv_len": w["kv_len"]},
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(value, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(value / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": "attn_fwd_bf16_d64"},
+                     "frac": round(value / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": "attn_fwd_bf16<64, 4, 2, 2, 3, false>"},
         "wall_s_timed_region": round(wall, 4),
         "parity_last_step": {"max_abs": float(err.max()), "mean_abs": float(err.mean())},
     }
@@ -524,7 +524,8 @@ def main():
     value = flops_metric(w) / (ms * 1e-3) / 1e12
     achieved = flops_algorithmic(w) / (ms * 1e-3) / 1e12
     rec = {
-        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "metric": METRIC.format(h=w["h"], d_k=w["d_k"]), "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w["dtype"], "data": "synthetic (seeded N(0,1) Q/K/V, no dataset)",
         "config": {"workload": args.workload, "B": w["B"], "h": w["h"], "n_q": w["n_q"], "n_k": w["n_k"],
@@ -532,9 +533,9 @@ def main():
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic("attn_fwd_bf16_d64", args.workload),
+                     "traffic": measured_traffic(f"attn_fwd_bf16_d{w['d_k']}", args.workload),
                      "kernel_source_hash": kernel_source_hash(),
-                     "kernel": "attn_fwd_bf16_d64", "algorithmic_hbm_bytes": hbm_bytes(w),
+                     "kernel": f"attn_fwd_bf16<{w['d_k']}, ...>", "algorithmic_hbm_bytes": hbm_bytes(w),
                      "algorithmic_hbm_GBps": round(hbm_bytes(w) / (ms * 1e-3) / 1e9, 1)},
         "wall_s_timed_region": round(wall, 4),
         "parity_last_step": {"max_abs": float(err.max()), "mean_abs": float(err.mean())},

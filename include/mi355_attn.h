@@ -45,7 +45,8 @@ typedef enum {
   ATTN_ERR_INVALID = 1,     /* null pointer, non-positive size, misaligned pointer, output overlapping an input,
                                unknown mask kind, workspace too small */
   ATTN_ERR_UNSUPPORTED = 2, /* valid request this library does not implement: dtype other than F32/BF16, head dims
-                               other than d_k = d_v = 64, causal mask with n_q != n_k, sizes beyond the limits below */
+                               other than those an entry point lists, causal mask with n_q != n_k, sizes beyond the
+                               limits below */
   ATTN_ERR_HIP = 3          /* a HIP runtime call failed */
 } attn_status;
 
@@ -64,7 +65,9 @@ typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
  *   mask_kind: ATTN_MASK_NONE, or ATTN_MASK_CAUSAL (keys j > i excluded; requires n_q == n_k).
  *   dtype: ATTN_BF16 (bf16 in/out, float32 scores, softmax and accumulation; the softmax weights are rounded to
  *          bf16 before they multiply V) or ATTN_F32 (float32 throughout).
- *   d_k and d_v must both be 64. `out` must not overlap Q, K or V. */
+ *   Head widths: d_k = d_v, one of 32, 64, 128: d_model = 512 split over h = 16, 8 or 4 heads, the head-count
+ *   variants that keep the total work about constant ("Transformer：抛弃循环与卷积的序列建模", section
+ *   "模型变体与消融实验"); the base model uses 64. `out` must not overlap Q, K or V. */
 int sdpa_forward(const void* Q, const void* K, const void* V, int mask_kind, void* out, int dtype,
                  int64_t B, int64_t h, int64_t n_q, int64_t n_k, int64_t d_k, int64_t d_v, void* stream);
 
@@ -119,8 +122,8 @@ int sdpa_forward_window(const void* Q, const void* K, const void* V, int64_t win
  *              caller (it holds per-row lse and D between the three launches).
  *   dtype: ATTN_BF16 (bf16 tensors, float32 accumulation, P and dS rounded to bf16 where they enter the matrix core,
  *          outputs rounded to nearest even) or ATTN_F32 (float32 throughout). lse is float32 in both.
- *   Requirements as sdpa_forward (d_k = d_v = 64, causal only with n_q == n_k). dQ, dK, dV and the workspace must not
- *   overlap each other or any input. Every element of dQ, dK and dV is written. */
+ *   Requirements as sdpa_forward, but d_k = d_v = 64 only (ATTN_ERR_UNSUPPORTED otherwise). dQ, dK, dV and the
+ *   workspace must not overlap each other or any input. Every element of dQ, dK and dV is written. */
 int sdpa_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse,
                   const int32_t* kv_len, int64_t window, int mask_kind, void* dQ, void* dK, void* dV, void* workspace,
                   size_t workspace_bytes, int dtype, int64_t B, int64_t h, int64_t n_q, int64_t n_k, int64_t d_k,

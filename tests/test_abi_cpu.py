@@ -52,6 +52,9 @@ def sdpa(lib, Q=A, K=A * 2, V=A * 3, mask=0, out=A * 1000, dtype=BF16, B=1, h=1,
     (dict(out=A + 8), INVALID), (dict(n_q=1 << 25), UNSUPPORTED), (dict(B=1 << 17), UNSUPPORTED),
     # out [1,1,16,64] bf16 = 2 KiB starting inside K
     (dict(out=A * 2 + 1024), INVALID), (dict(out=A * 3 - 1024), INVALID),
+    # head widths: d_k = d_v in {32, 64, 128} only; the overlap checks use the width (out [1,1,16,128] = 4 KiB)
+    (dict(d_k=48, d_v=48), UNSUPPORTED), (dict(d_k=16, d_v=16), UNSUPPORTED), (dict(d_k=256, d_v=256), UNSUPPORTED),
+    (dict(d_k=32, d_v=64), UNSUPPORTED), (dict(d_k=128, d_v=128, out=A * 3 + 2048), INVALID),
 ])
 def test_sdpa_rejects_bad_arguments(lib, kw, code):
     assert sdpa(lib, **kw) == code
@@ -117,6 +120,8 @@ def bwd(lib, Q=A, K=A * 2, V=A * 3, O=A * 4, dO=A * 5, lse=A * 6, kv_len=None, w
     (dict(dQ=A * 4), INVALID), (dict(dV=A * 200 + 1024), INVALID), (dict(ws=A * 6), INVALID),
     (dict(dK=A * 400), INVALID), (dict(kv_len=A * 7 + 4), INVALID), (dict(kv_len=A * 100 + 64), INVALID),
     (dict(window=3, n_k=32), UNSUPPORTED), (dict(window=3, kv_len=A * 7), UNSUPPORTED),
+    # the backward kernels take d_k = d_v = 64 only
+    (dict(d_k=32, d_v=32), UNSUPPORTED), (dict(d_k=128, d_v=128), UNSUPPORTED),
 ])
 def test_sdpa_backward_rejects_bad_arguments(lib, kw, code):
     assert bwd(lib, **kw) == code

@@ -1,0 +1,130 @@
+"""Parity of the other head widths, d_k = d_v in {32, 128} (d_model = 512 over 16 or 4 heads: the head-count variants
+of "Transformer：抛弃循环与卷积的序列建模", section "模型变体与消融实验"), with the float64 oracle, through every forward
+entry point (sdpa_forward, sdpa_forward_lse, sdpa_forward_padded, sdpa_forward_window) in both dtypes.
+
+Shapes span several 64-key tiles with ragged tails, n_q != n_k both ways, a single query, and the full-size
+long-sequence workloads (checked on sampled heads and rows). Bars as for d = 64: bf16 max-abs <= 2e-2, mean-abs <=
+2e-3, normalised rms <= 1e-2; fp32 1e-5 relative; lse within 1e-2 (bf16) or 1e-5 relative (fp32).
+"""
+import numpy as np
+import pytest
+import torch
+
+import transformer_head_scaled_02_amd as m
+import workloads
+from oracle import sdpa_lse_ref, sdpa_ref
+from tests._helpers import assert_bf16_parity, assert_f32_parity, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+WIDTHS = (32, 128)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs an MI355X")
+    m.load_library()
+
+
+def _mask(causal):
+    return "causal" if causal else "none"
+
+
+def _check_out(got, ref, dtype, what):
+    if dtype == "f32":
+        assert_f32_parity(got, ref, what)
+    else:
+        assert_bf16_parity(got, ref, what)
+
+
+def _check_lse(got, ref, dtype, what):
+    finite = np.isfinite(ref)
+    assert np.array_equal(np.isfinite(got), finite), f"{what}: lse finiteness"
+    d = np.abs(got[finite] - ref[finite]) if finite.any() else np.zeros(1)
+    bar = 1e-2 if dtype == "bf16" else 1e-5 * max(1.0, float(np.abs(ref[finite]).max(initial=0.0)))
+    assert d.max() <= bar, f"{what}: lse max-abs {d.max():.3g}"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", WIDTHS)
+@pytest.mark.parametrize("n_q,n_k,causal", [
+    (1, 1, False), (64, 64, True), (200, 200, False), (200, 200, True), (100, 300, False), (300, 100, False),
+    (1, 130, False), (513, 513, True)])
+def test_headwidth_forward_and_lse(dtype, d, n_q, n_k, causal):
+    x = workloads.make_sdpa_inputs(2, 3, n_q, n_k, d, d, dtype, 9700 + n_q + n_k + d, scale_q=1.5)
+    q, k, v = (to_dev(x[nm]) for nm in "QKV")
+    out, lse = m.sdpa_forward_lse(q, k, v, mask=_mask(causal))
+    plain = m.sdpa_forward(q, k, v, mask=_mask(causal))
+    torch.cuda.synchronize()
+    what = f"d={d} {dtype} {n_q}x{n_k} causal={causal}"
+    _check_out(to_f64(out), sdpa_ref(x["Q"].f64, x["K"].f64, x["V"].f64, causal), dtype, what)
+    _check_lse(to_f64(lse), sdpa_lse_ref(x["Q"].f64, x["K"].f64, causal), dtype, what)
+    assert torch.equal(out, plain), f"{what}: sdpa_forward and sdpa_forward_lse differ"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", WIDTHS)
+@pytest.mark.parametrize("causal", [False, True])
+def test_headwidth_padded(dtype, d, causal):
+    n, lengths = 200, [0, 1, 65, 200]
+    x = workloads.make_sdpa_inputs(len(lengths), 2, n, n, d, d, dtype, 9800 + d, scale_q=1.5)
+    q, k, v = (to_dev(x[nm]) for nm in "QKV")
+    lens = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+    out, lse = m.sdpa_forward_padded(q, k, v, lens, mask=_mask(causal), return_lse=True)
+    torch.cuda.synchronize()
+    kv = np.asarray(lengths)
+    what = f"padded d={d} {dtype} causal={causal}"
+    _check_out(to_f64(out), sdpa_ref(x["Q"].f64, x["K"].f64, x["V"].f64, causal, kv_len=kv), dtype, what)
+    _check_lse(to_f64(lse), sdpa_lse_ref(x["Q"].f64, x["K"].f64, causal, kv_len=kv), dtype, what)
+    assert torch.count_nonzero(out[0]) == 0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", WIDTHS)
+@pytest.mark.parametrize("w,causal", [(0, False), (17, True), (100, False), (100, True)])
+def test_headwidth_window(dtype, d, w, causal):
+    n = 300
+    x = workloads.make_sdpa_inputs(2, 2, n, n, d, d, dtype, 9900 + d + w, scale_q=1.5)
+    q, k, v = (to_dev(x[nm]) for nm in "QKV")
+    out, lse = m.sdpa_forward_window(q, k, v, w, mask=_mask(causal), return_lse=True)
+    torch.cuda.synchronize()
+    what = f"window d={d} {dtype} w={w} causal={causal}"
+    _check_out(to_f64(out), sdpa_ref(x["Q"].f64, x["K"].f64, x["V"].f64, causal, window=w), dtype, what)
+    _check_lse(to_f64(lse), sdpa_lse_ref(x["Q"].f64, x["K"].f64, causal, window=w), dtype, what)
+
+
+@pytest.mark.parametrize("d", WIDTHS)
+def test_headwidth_writes_only_the_output(d):
+    # the output inside a guarded buffer: nothing before or after it may change
+    B, h, n = 2, 2, 150
+    x = workloads.make_sdpa_inputs(B, h, n, n, d, d, "bf16", 9950 + d)
+    q, k, v = (to_dev(x[nm]) for nm in "QKV")
+    numel = B * h * n * d
+    big = torch.full((numel + 4096,), 7.0, dtype=torch.bfloat16, device="cuda")
+    out = big[2048:2048 + numel].view(B, h, n, d)
+    for mask in ("none", "causal"):
+        m.sdpa_forward(q, k, v, mask=mask, out=out)
+        torch.cuda.synchronize()
+        assert torch.all(big[:2048] == 7.0) and torch.all(big[-2048:] == 7.0)
+        assert_bf16_parity(to_f64(out), sdpa_ref(x["Q"].f64, x["K"].f64, x["V"].f64, mask == "causal"),
+                           f"guarded d={d} {mask}")
+
+
+@pytest.mark.parametrize("name", ["sdpa_bf16_b4_h16_n4096_d32", "sdpa_causal_bf16_b4_h16_n4096_d32",
+                                  "sdpa_bf16_b4_h4_n4096_d128", "sdpa_causal_bf16_b4_h4_n4096_d128"])
+def test_headwidth_long_sequence_sampled(name):
+    # the full-size workloads in the launch configuration the bench times; the oracle checks sampled rows of the
+    # first and last head of every batch entry
+    w = workloads.WORKLOADS[name]
+    x = workloads.make_workload(name)
+    q, k, v = (to_dev(x[nm]) for nm in "QKV")
+    out = m.sdpa_forward(q, k, v, mask=_mask(w["causal"]))
+    torch.cuda.synchronize()
+    got = to_f64(out)
+    rng = np.random.Generator(np.random.PCG64(42))
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, 2047, 4095], rng.integers(0, 4096, 24)]))
+    for b in range(w["B"]):
+        for hh in (0, w["h"] - 1):
+            ref = sdpa_ref(x["Q"].f64[b, hh, rows], x["K"].f64[b, hh], x["V"].f64[b, hh], w["causal"], q_index=rows)
+            assert_bf16_parity(got[b, hh, rows], ref, f"{name} b={b} h={hh}")

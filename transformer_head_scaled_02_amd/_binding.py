@@ -119,7 +119,8 @@ def _stream_handle(device: torch.device) -> int:
 
 def sdpa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask="none",
                  out: torch.Tensor | None = None) -> torch.Tensor:
-    """softmax(q k^T / sqrt(d_k)) v per (batch, head). q [B,h,n_q,64], k/v [B,h,n_k,64] -> [B,h,n_q,64]."""
+    """softmax(q k^T / sqrt(d_k)) v per (batch, head). q [B,h,n_q,d], k/v [B,h,n_k,d] -> [B,h,n_q,d], d in
+    {32, 64, 128}."""
     lib = load_library()
     q, k, v = _dev_tensor(q, "q"), _dev_tensor(k, "k"), _dev_tensor(v, "v")
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:

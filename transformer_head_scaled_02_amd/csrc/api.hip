@@ -130,9 +130,10 @@ int check_sdpa_sizes(const char* fn, int dtype, int mask_kind, int64_t B, int64_
     return fail_status(ATTN_ERR_INVALID, "%s: sizes must be positive (B=%lld h=%lld n_q=%lld n_k=%lld d_k=%lld "
                        "d_v=%lld)", fn, (long long)B, (long long)h, (long long)n_q, (long long)n_k, (long long)d_k,
                        (long long)d_v);
-  if (d_k != 64 || d_v != 64)
-    return fail_status(ATTN_ERR_UNSUPPORTED, "%s: head dims d_k=%lld d_v=%lld (only 64 is implemented)", fn,
-                       (long long)d_k, (long long)d_v);
+  // the forward kernels take d_k = d_v in {32, 64, 128}; the backward kernels d_k = d_v = 64
+  if (d_k != d_v || (backward ? d_k != 64 : (d_k != 32 && d_k != 64 && d_k != 128)))
+    return fail_status(ATTN_ERR_UNSUPPORTED, "%s: head dims d_k=%lld d_v=%lld (implemented: %s)", fn, (long long)d_k,
+                       (long long)d_v, backward ? "64" : "d_k = d_v in {32, 64, 128}");
   if (mask_kind == ATTN_MASK_CAUSAL && n_q != n_k)
     return fail_status(ATTN_ERR_UNSUPPORTED, "%s: causal mask needs n_q == n_k (got %lld, %lld)", fn,
                        (long long)n_q, (long long)n_k);
@@ -150,7 +151,7 @@ int sdpa_forward_impl(const char* fn, const void* Q, const void* K, const void* 
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(out) || !aligned16(lse) || !aligned16(kv_len))
     return fail_status(ATTN_ERR_INVALID, "%s: pointers must be 16-byte aligned", fn);
   const size_t es = dtype == ATTN_BF16 ? 2 : 4;
-  const size_t q_bytes = (size_t)B * h * n_q * 64 * es, kv_bytes = (size_t)B * h * n_k * 64 * es;
+  const size_t q_bytes = (size_t)B * h * n_q * d_k * es, kv_bytes = (size_t)B * h * n_k * d_k * es;
   if (overlaps(out, q_bytes, Q, q_bytes) || overlaps(out, q_bytes, K, kv_bytes) || overlaps(out, q_bytes, V, kv_bytes))
     return fail_status(ATTN_ERR_INVALID, "%s: out overlaps an input", fn);
   if (lse) {
@@ -168,11 +169,11 @@ int sdpa_forward_impl(const char* fn, const void* Q, const void* K, const void* 
   mi355::AttnArgs a{};
   a.Q = Q; a.K = K; a.V = V; a.O = out;
   a.B = (int)B; a.H = (int)h; a.n_q = (int)n_q; a.n_k = (int)n_k;
-  a.q_stride_bh = n_q * 64;
-  a.k_stride_bh = n_k * 64;
-  a.o_stride_b = h * n_q * 64;
-  a.o_stride_h = n_q * 64;
-  a.o_stride_row = 64;
+  a.q_stride_bh = n_q * d_k;
+  a.k_stride_bh = n_k * d_k;
+  a.o_stride_b = h * n_q * d_k;
+  a.o_stride_h = n_q * d_k;
+  a.o_stride_row = d_k;
   a.causal = mask_kind == ATTN_MASK_CAUSAL;
   a.lse = lse;
   a.kv_len = kv_len;
@@ -181,7 +182,8 @@ int sdpa_forward_impl(const char* fn, const void* Q, const void* K, const void* 
     a.window = (int)(window < n_k ? window : n_k);
   }
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e = dtype == ATTN_BF16 ? mi355::launch_attn_fwd_bf16(a, s) : mi355::launch_attn_fwd_f32(a, s);
+  const hipError_t e =
+      dtype == ATTN_BF16 ? mi355::launch_attn_fwd_bf16(a, (int)d_k, s) : mi355::launch_attn_fwd_f32(a, (int)d_k, s);
   if (e != hipSuccess) return fail_status(ATTN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ATTN_OK;
 }
@@ -363,7 +365,7 @@ ATTN_EXPORT int mha_forward(const void* Xq, const void* Xkv, const void* Wq, con
   a.o_stride_h = 64;
   a.o_stride_row = h * 64;
   a.causal = mask_kind == ATTN_MASK_CAUSAL;
-  e = mi355::launch_attn_fwd_bf16(a, s);
+  e = mi355::launch_attn_fwd_bf16(a, 64, s);
   if (e != hipSuccess) return fail_status(ATTN_ERR_HIP, "mha_forward: attention launch failed: %s", hipGetErrorString(e));
 
   // 3. output projection: out [B*n_q, d_model] = concat [B*n_q, h*64] x Wo [h*64, d_model]
@@ -444,7 +446,7 @@ ATTN_EXPORT int encoder_layer_forward(const void* X, const int32_t* kv_len, cons
   a.o_stride_row = h * 64;
   a.causal = mask_kind == ATTN_MASK_CAUSAL;
   a.kv_len = kv_len;
-  ENC_STEP(mi355::launch_attn_fwd_bf16(a, s), "attention");
+  ENC_STEP(mi355::launch_attn_fwd_bf16(a, 64, s), "attention");
   // 3. R1 = X + Concat W^O (residual in the GEMM epilogue), H1 = LayerNorm(R1)
   mi355::GemmProblem wo = {Ch, Wo, R, M, dm, dm, 0, nullptr, X, 0};
   ENC_STEP(mi355::launch_gemm_bf16(&wo, 1, s), "W^O");

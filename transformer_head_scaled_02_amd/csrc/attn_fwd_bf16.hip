@@ -1,6 +1,6 @@
-// Fused scaled dot-product attention forward, bf16 in/out, d_k = d_v = 64, for gfx950 (MI355X).
+// Fused scaled dot-product attention forward, bf16 in/out, d_k = d_v = D in {32, 64, 128}, for gfx950 (MI355X).
 //
-// Computes, for every (batch, head) and query i:  O_i = sum_j softmax_j(Q_i . K_j / sqrt(64)) V_j, with the optional
+// Computes, for every (batch, head) and query i:  O_i = sum_j softmax_j(Q_i . K_j / sqrt(D)) V_j, with the optional
 // causal mask (keys j > i get score -inf, i.e. weight 0). Definition: "Attention Is All You Need" (lettle.cn
 // translation), section 3.2.1, equation Attention(Q,K,V); mask: "Transformer：抛弃循环与卷积的序列建模"
 // (jiashun-ye.github.io), section "Transformer 中的三种 Attention".
@@ -50,14 +50,28 @@ namespace {
 template <class T>
 __device__ __forceinline__ constexpr int stage_index(T s) { return (int)s; }
 
-template <int NW, int H, int MINB, int STAGES, bool WIN>
-__global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, int n_qblocks) {
-  constexpr int kQW = 32 * H;    // queries per wave: H independent halves of 32
-  constexpr int kBM = kQW * NW;  // queries per workgroup
-  constexpr int kLPW = 16 / NW;  // one-kilobyte tile copies per wave per tile (16 per K+V tile)
-  static_assert(16 % NW == 0 && kLPW % 2 == 0, "tile copies split evenly, in pairs, over the waves");
+template <int D, int NW, int H, int MINB, int STAGES, bool WIN>
+__global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16(AttnArgs a, int n_qblocks) {
+  static_assert(D == 32 || D == 64 || D == 128, "head width");
+  constexpr int kD = D;                   // (shadows the 64 of the shared tile header)
+  constexpr int kTileElems = kBN * D;     // one 64-key tile of K or V
+  constexpr int kKS = D / 16;             // k-steps of S^T = K Q^T
+  constexpr int kMB = D / 32;             // 32-row blocks of O^T
+  constexpr int kCPT = D / 8;             // one-kilobyte copies per K (or V) tile
+  constexpr int kRPC = 512 / D;           // tile rows per copy
+  constexpr int kNOff = D / 32;           // copies per 16 rows (one swizzle period): distinct per-lane copy offsets
+  constexpr int kQW = 32 * H;             // queries per wave: H independent halves of 32
+  constexpr int kBM = kQW * NW;           // queries per workgroup
+  constexpr int kLPW = 2 * kCPT / NW;     // one-kilobyte tile copies per wave per tile
+  // Wide heads (D = 128) read each tile's K operands at the start of its step and V's per output block, and take
+  // the ring barrier after the tile's last product: holding the next tile's K and all of V in registers as well
+  // would not fit two waves per SIMD.
+  constexpr bool kLate = D >= 128;
+  static_assert((2 * kCPT) % NW == 0 && kLPW % 2 == 0 && kLPW % kNOff == 0,
+                "tile copies split evenly, in pairs, over the waves");
   static_assert(STAGES >= 2 && STAGES <= 4, "ring depth");
   static_assert(H == 1 || H == 2, "one or two query halves per wave");
+  static_assert(!kLate || H == 1, "wide heads have one query half per wave");
   __shared__ __attribute__((aligned(16))) uint16_t smem[STAGES * 2 * kTileElems];  // [stage][K | V]
 
   const int tid = threadIdx.x;
@@ -97,20 +111,20 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, i
     n_k = max(n_k - kb0, 0);
   }
 
-  // Q as the B operand of S^T = K Q^T: lane supplies Q[q][32g + 8ks + j], ks = 0..3 (the same d order as the K
-  // operand). Rows at or past n_q are zero.
-  bf16x8 qf[H][4];
+  // Q as the B operand of S^T = K Q^T: lane supplies Q[q][(D/2)g + 8ks + j], ks = 0..D/16-1 (the same d order as
+  // the K operand). Rows at or past n_q are zero.
+  bf16x8 qf[H][kKS];
 #pragma unroll
   for (int h = 0; h < H; ++h) {
     const int q = qw0 + 32 * h + li;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      qf[h][ks] = q < n_q ? *reinterpret_cast<const bf16x8*>(Qp + (int64_t)q * kD + 32 * g + 8 * ks) : bf16x8{};
+    for (int ks = 0; ks < kKS; ++ks)
+      qf[h][ks] = q < n_q ? *reinterpret_cast<const bf16x8*>(Qp + (int64_t)q * kD + (kD / 2) * g + 8 * ks) : bf16x8{};
   }
 #pragma unroll
   for (int h = 0; h < H; ++h)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) settle(qf[h][ks]);
+    for (int ks = 0; ks < kKS; ++ks) settle(qf[h][ks]);
 
   int nt = (n_k + kBN - 1) / kBN;
   if (causal) nt = min(nt, (q_blk0 + kBM - 1 - kb0) / kBN + 1);
@@ -134,17 +148,18 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, i
     t_skip = min(t_skip, (qw0 + kQW - 1 + w - kb0) / kBN + 1);
   }
 
-  // Tile copies: copy gi (0..15) of a tile moves rows 8*(gi%8) .. +7 of K (gi < 8) or V; lane l brings the logical
-  // chunk that belongs at physical chunk l%8 of row 8*(gi%8) + l/8. The swizzle repeats every 16 rows, so two
-  // per-lane offsets (rows l/8 and 8 + l/8) serve every copy, the rest of the row offset going into the scalar base.
-  // Rows past n_k read row n_k-1 (their scores are masked and their weights are zero).
+  // Tile copies: copy gi (0 .. 2*D/8 - 1) of a tile moves rows R*c .. R*c + R-1 (R = 512/D rows of a kilobyte,
+  // c = gi mod D/8) of K (gi < D/8) or V; lane l brings the logical chunk that belongs at physical chunk l mod D/8 of
+  // row R*c + l/(D/8). The swizzle repeats every 16 rows, so D/32 per-lane offsets (rows R*i + l/(D/8)) serve every
+  // copy, the rest of the row offset going into the scalar base. Rows past n_k read row n_k-1 (their scores are
+  // masked and their weights are zero).
   const uint32_t smem_lds = (uint32_t)(uintptr_t)smem;  // LDS byte address of the ring
-  const int lrow = lane >> 3;
-  uint32_t ld_voff[2];
+  const int lrow = lane / kCPT;
+  uint32_t ld_voff[kNOff];
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const int row = 8 * c + lrow;
-    ld_voff[c] = (uint32_t)(row * kD + (((lane & 7) ^ swz(row)) << 3)) * 2u;
+  for (int c = 0; c < kNOff; ++c) {
+    const int row = kRPC * c + lrow;
+    ld_voff[c] = (uint32_t)(row * kD + (((lane % kCPT) ^ swz_d<D>(row)) << 3)) * 2u;
   }
   auto issue_tile = [&](int t) __attribute__((always_inline)) {
     const uint32_t stage = smem_lds + (uint32_t)((t % STAGES) * 2 * kTileElems * 2);
@@ -154,9 +169,9 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, i
 #pragma unroll
       for (int i = 0; i < kLPW; ++i) {
         const int gi = wave * kLPW + i;
-        const int c = gi & 7;  // this copy moves rows 8c .. 8c+7
-        lds_dma16((gi < 8 ? kt : vt) + (c >> 1) * 16 * kD, ld_voff[i & 1],
-                  stage + (gi < 8 ? 0u : kTileElems * 2u) + (uint32_t)c * 1024u);
+        const int c = gi & (kCPT - 1);  // this copy moves rows R*c .. R*c + R-1
+        lds_dma16((gi < kCPT ? kt : vt) + (c / kNOff) * 16 * kD, ld_voff[i % kNOff],
+                  stage + (gi < kCPT ? 0u : kTileElems * 2u) + (uint32_t)c * 1024u);
       }
     } else {
       // Partial tile: from the unshifted tile base, lane offset = row min(row, last_row) with the chunk swizzle of
@@ -168,36 +183,39 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, i
 #pragma unroll
       for (int i = 0; i < kLPW; ++i) {
         const int gi = wave * kLPW + i;
-        const int c = gi & 7;
-        const int row = 8 * c + lr;
-        lds_dma16(gi < 8 ? kt : vt, ld_voff[i & 1] + (uint32_t)((min(row, last_row) - (8 * (c & 1) + lr)) * kD * 2),
-                  stage + (gi < 8 ? 0u : kTileElems * 2u) + (uint32_t)c * 1024u);
+        const int c = gi & (kCPT - 1);
+        const int row = kRPC * c + lr;
+        lds_dma16(gi < kCPT ? kt : vt,
+                  ld_voff[i % kNOff] + (uint32_t)((min(row, last_row) - (kRPC * (c & (kNOff - 1)) + lr)) * kD * 2),
+                  stage + (gi < kCPT ? 0u : kTileElems * 2u) + (uint32_t)c * 1024u);
       }
     }
   };
 
-  // per-lane LDS element offsets: K operand row li, logical chunk 4g+ks; V transpose-read row 4g + (lane%16)/4 (+8
-  // for the second half), logical chunk 4mb + 2*((lane/16)%2) + (lane%4)/2, element 4*(lane%2) of the chunk
-  int koff[4];
+  // per-lane LDS element offsets: K operand row li, logical chunk (D/16)g + ks; V transpose-read row 4g +
+  // (lane%16)/4 (+8 for the second half), logical chunk 4mb + 2*((lane/16)%2) + (lane%4)/2, element 4*(lane%2) of
+  // the chunk
+  int koff[kKS];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) koff[ks] = li * kD + (((4 * g + ks) ^ swz(li)) << 3);
-  int voff[2][2];
+  for (int ks = 0; ks < kKS; ++ks) koff[ks] = li * kD + ((((kD / 16) * g + ks) ^ swz_d<D>(li)) << 3);
+  int voff[kMB][2];
   const int jj = (lane & 15) >> 2;
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
     for (int hi = 0; hi < 2; ++hi) {
       const int row = 4 * g + jj + 8 * hi;
       const int lchunk = 4 * mb + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-      voff[mb][hi] = kTileElems + row * kD + ((lchunk ^ swz(row)) << 3) + 4 * (lane & 1);
+      voff[mb][hi] = kTileElems + row * kD + ((lchunk ^ swz_d<D>(row)) << 3) + 4 * (lane & 1);
     }
   const bf16x8 lsel = lsum_selector(lane);
 
-  f32x16 o[H][2];
+  f32x16 o[H][kMB];
   float neg_m[H], l[H];  // -m (m = the row's exponent offset, log2 units, set by the first tile) and the row sum
 #pragma unroll
   for (int h = 0; h < H; ++h) {
-    o[h][0] = o[h][1] = f32x16{};
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb) o[h][mb] = f32x16{};
     // (window: a finite "unset" offset far above any score, so that the first tile a row can see overflows its
     // tile sum and takes the slow path, which sets the offset to that tile's row max; tiles the row cannot see leave
     // it alone)
@@ -209,26 +227,26 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, i
   // for each query half. The K and V operands are read from LDS once and serve every half; while one half's softmax
   // runs on the VALU, the other half's products keep the matrix core busy. Masked tiles give keys past the row's
   // bound the score -inf. The first tile sets the offset to its row max.
-  auto step = [&](int t, auto stage_c, auto masked_c, auto first_c, bf16x8(&kreg)[4][2], auto&& mid)
+  auto step = [&](int t, auto stage_c, auto masked_c, auto first_c, bf16x8(&kreg)[kKS][2], auto&& mid)
                   __attribute__((always_inline)) {
     constexpr bool kM = decltype(masked_c)::value;
     constexpr bool kFirst = decltype(first_c)::value;
     const uint16_t* stage = smem + stage_index(stage_c) * 2 * kTileElems;
 
-    auto load_k = [&](bf16x8(&ka)[4][2]) __attribute__((always_inline)) {
+    auto load_k = [&](bf16x8(&ka)[kKS][2]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
+      for (int ks = 0; ks < kKS; ++ks)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) ka[ks][kb] = *reinterpret_cast<const bf16x8*>(stage + kb * 32 * kD + koff[ks]);
     };
     f32x16 s[H][2];
     // S^T = K Q^T for half h; s[h][kb] register r holds key 32kb + 8(r/4) + 4g + r%4 of the tile
-    auto scores = [&](auto h_c, const bf16x8(&ka)[4][2]) __attribute__((always_inline)) {
+    auto scores = [&](auto h_c, const bf16x8(&ka)[kKS][2]) __attribute__((always_inline)) {
       constexpr int h = decltype(h_c)::value;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) s[h][kb] = mfma32x32x16(ka[0][kb], qf[h][0], f32x16{});
 #pragma unroll
-      for (int ks = 1; ks < 4; ++ks)
+      for (int ks = 1; ks < kKS; ++ks)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) s[h][kb] = mfma32x32x16(ka[ks][kb], qf[h][ks], s[h][kb]);
       if (kM) {
@@ -254,8 +272,8 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, i
         uint32_t w[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          w[j] = pack_bf16x2(fast_exp2(scaled_minus(sk[base + 2 * j], neg_m[h])),
-                             fast_exp2(scaled_minus(sk[base + 2 * j + 1], neg_m[h])));
+          w[j] = pack_bf16x2(fast_exp2(scaled_minus<D>(sk[base + 2 * j], neg_m[h])),
+                             fast_exp2(scaled_minus<D>(sk[base + 2 * j + 1], neg_m[h])));
         pf[h][ks] = __builtin_bit_cast(bf16x8, (uint4){w[0], w[1], w[2], w[3]});
       }
       ts[h] = mfma16x16x32(lsel, pf[h][0], f32x4{});
@@ -270,7 +288,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, i
       for (int j = 0; j < 4; ++j)
         mx[j] = fmaxf(fmaxf(fmaxf(s[h][0][4 * j], s[h][0][4 * j + 1]), fmaxf(s[h][0][4 * j + 2], s[h][0][4 * j + 3])),
                       fmaxf(fmaxf(s[h][1][4 * j], s[h][1][4 * j + 1]), fmaxf(s[h][1][4 * j + 2], s[h][1][4 * j + 3])));
-      return max_with_partner32(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]))) * kScaleLog2;
+      return max_with_partner32(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]))) * scale_log2<D>();
     };
     // the softmax of half h, ending with its row sums added to l
     auto softmax = [&](auto h_c) __attribute__((always_inline)) {
@@ -291,7 +309,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, i
           // alive across the fast path.
           asm volatile("" ::: "memory");
           {
-            bf16x8 ka[4][2];
+            bf16x8 ka[kKS][2];
             load_k(ka);
             scores(h_c, ka);
           }
@@ -304,10 +322,9 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, i
           const float alpha = fast_exp2(-d);
           l[h] *= alpha;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            o[h][0][r] *= alpha;
-            o[h][1][r] *= alpha;
-          }
+          for (int r = 0; r < 16; ++r)
+#pragma unroll
+            for (int mb = 0; mb < kMB; ++mb) o[h][mb][r] *= alpha;
           neg_m[h] -= d;
           exponentiate(h_c);
         }
@@ -318,36 +335,61 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, i
     // Masked tiles of the two-half kernel (only a ragged last tile: it serves unmasked attention) run the halves one
     // after the other, which needs fewer registers than the interleaved order.
     constexpr bool kSeq = kM && H == 2;
-    if (!kSeq) unroll<H>([&](auto h_c) __attribute__((always_inline)) { scores(h_c, kreg); });
+    if constexpr (kLate) {
+      bf16x8 ka[kKS][2];
+      load_k(ka);
+      scores(std::integral_constant<int, 0>{}, ka);
+    } else if (!kSeq) {
+      unroll<H>([&](auto h_c) __attribute__((always_inline)) { scores(h_c, kreg); });
+    }
     // V^T operands, read once for every half: k-step ks pairs P registers 8(ks%2) .. +7 of key block ks/2 with keys
     // 16ks + 4g + (0..3) and 16ks + 8 + 4g + (0..3); two transpose reads of V rows give the matching operand.
-    bf16x8 va[4][2];
-    unroll<H>([&](auto h_c) __attribute__((always_inline)) {
-      constexpr int h = decltype(h_c)::value;
-      if (kSeq) scores(h_c, kreg);
-      softmax(h_c);
-      if (h == 0) {
+    if constexpr (kLate) {
+      // one half; each 32-row block of V^T is read just before its products, and the ring barrier follows the
+      // tile's last read of V
+      softmax(std::integral_constant<int, 0>{});
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb) {
+        bf16x8 vm[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const bf16x4 lo = lds_read_tr16x4(stage + ks * 16 * kD + voff[mb][0]);
+          const bf16x4 hi = lds_read_tr16x4(stage + ks * 16 * kD + voff[mb][1]);
+          vm[ks] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) o[0][mb] = mfma32x32x16(vm[ks], pf[0][ks], o[0][mb]);
+      }
+      mid();
+    } else {
+      bf16x8 va[4][kMB];
+      unroll<H>([&](auto h_c) __attribute__((always_inline)) {
+        constexpr int h = decltype(h_c)::value;
+        if (kSeq) scores(h_c, kreg);
+        softmax(h_c);
+        if (h == 0) {
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int mb = 0; mb < kMB; ++mb) {
+              const bf16x4 lo = lds_read_tr16x4(stage + ks * 16 * kD + voff[mb][0]);
+              const bf16x4 hi = lds_read_tr16x4(stage + ks * 16 * kD + voff[mb][1]);
+              va[ks][mb] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+        }
+        if (h == H - 1) mid();
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-          for (int mb = 0; mb < 2; ++mb) {
-            const bf16x4 lo = lds_read_tr16x4(stage + ks * 16 * kD + voff[mb][0]);
-            const bf16x4 hi = lds_read_tr16x4(stage + ks * 16 * kD + voff[mb][1]);
-            va[ks][mb] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          }
-      }
-      if (h == H - 1) mid();
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) o[h][mb] = mfma32x32x16(va[ks][mb], pf[h][ks], o[h][mb]);
-    });
+          for (int mb = 0; mb < kMB; ++mb) o[h][mb] = mfma32x32x16(va[ks][mb], pf[h][ks], o[h][mb]);
+      });
+    }
   };
 
   // K operands of a tile, read from its ring stage
-  auto read_k = [&](const uint16_t* st, bf16x8(&kr)[4][2]) __attribute__((always_inline)) {
+  auto read_k = [&](const uint16_t* st, bf16x8(&kr)[kKS][2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int ks = 0; ks < kKS; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) kr[ks][kb] = *reinterpret_cast<const bf16x8*>(st + kb * 32 * kD + koff[ks]);
   };
@@ -355,7 +397,8 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, i
   // landed (later tiles may stay in flight), then for every wave's (the barrier, which also certifies that every
   // wave has read V of tile t and K of every tile up to t+1, so tile t's stage is free), read K of tile t+1 into
   // registers while the products run, and issue tile t + STAGES into the freed stage.
-  bf16x8 kr[4][2];
+  // (Wide heads: the same, after the tile's last product, and without the K read.)
+  bf16x8 kr[kKS][2];
   auto mid = [&](int t, auto next_stage_c) __attribute__((always_inline)) {
     if (t + 1 >= nt) return;
     const int ahead = min(STAGES - 2, nt - 2 - t);  // tiles issued after t+1
@@ -363,7 +406,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, i
     else if (ahead == 1) wait_vmcnt<kLPW>();
     else wait_vmcnt<0>();
     lds_barrier();
-    read_k(smem + stage_index(next_stage_c) * 2 * kTileElems, kr);
+    if constexpr (!kLate) read_k(smem + stage_index(next_stage_c) * 2 * kTileElems, kr);
     if (t + STAGES < nt) issue_tile(t + STAGES);
   };
 
@@ -380,7 +423,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, i
       else if (ahead == 1) wait_vmcnt<kLPW>();
       else wait_vmcnt<0>();
       lds_barrier();
-      read_k(smem, kr);
+      if constexpr (!kLate) read_k(smem, kr);
     }
     // tile 0 (every row has at least one key it may see there)
     {
@@ -424,7 +467,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, i
         a.lse[(int64_t)bh * n_q + q] = seen ? (__builtin_amdgcn_logf(l[h]) - neg_m[h]) * kLn2 : -INFINITY;
       uint16_t* orow = Op + (int64_t)q * a.o_stride_row;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
           const uint2 w = {pack_bf16x2(o[h][mb][4 * rg] * inv, o[h][mb][4 * rg + 1] * inv),
@@ -435,26 +478,40 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16_d64(AttnArgs a, i
   }
 }
 
-template <int NW, int H, int MINB, int STAGES, bool WIN = false>
+template <int D, int NW, int H, int MINB, int STAGES, bool WIN = false>
 hipError_t launch(const AttnArgs& a, hipStream_t stream) {
   constexpr int kBM = 32 * H * NW;
   const int n_qblocks = (a.n_q + kBM - 1) / kBM;
   const int64_t nblocks = (int64_t)n_qblocks * a.B * a.H;
   if (nblocks <= 0 || nblocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((attn_fwd_bf16_d64<NW, H, MINB, STAGES, WIN>), dim3((unsigned)nblocks), dim3(64 * NW), 0, stream, a,
-                     n_qblocks);
+  hipLaunchKernelGGL((attn_fwd_bf16<D, NW, H, MINB, STAGES, WIN>), dim3((unsigned)nblocks), dim3(64 * NW), 0, stream,
+                     a, n_qblocks);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_attn_fwd_bf16(const AttnArgs& a, hipStream_t stream) {
+hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int d, hipStream_t stream) {
   // Unmasked: 4-wave workgroups of 256 queries (two halves of 32 per wave), two per CU (two waves per SIMD, 256
   // registers each), a 3-tile ring. Causal: 4-wave workgroups of 128 queries with a 4-tile ring, two per CU, which
   // balanced the triangular work best.
-  if (a.windowed) return launch<4, 1, 2, 4, true>(a, stream);
-  if (!a.causal) return launch<4, 2, 2, 3>(a, stream);
-  return launch<4, 1, 2, 4>(a, stream);
+  // Other head widths: d = 32 as d = 64 (its tiles are half the size); d = 128 with one query half per wave and a
+  // 2-tile ring (two 64 KB rings fit the 160 KB of LDS of a CU).
+  switch (d) {
+    case 64:
+      if (a.windowed) return launch<64, 4, 1, 2, 4, true>(a, stream);
+      if (!a.causal) return launch<64, 4, 2, 2, 3>(a, stream);
+      return launch<64, 4, 1, 2, 4>(a, stream);
+    case 32:
+      if (a.windowed) return launch<32, 4, 1, 2, 4, true>(a, stream);
+      if (!a.causal) return launch<32, 4, 2, 2, 3>(a, stream);
+      return launch<32, 4, 1, 2, 4>(a, stream);
+    case 128:
+      if (a.windowed) return launch<128, 4, 1, 2, 2, true>(a, stream);
+      return launch<128, 4, 1, 2, 2>(a, stream);
+    default:
+      return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace mi355

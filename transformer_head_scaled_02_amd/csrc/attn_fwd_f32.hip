@@ -1,10 +1,11 @@
-// Scaled dot-product attention forward in fp32 throughout, d_k = d_v = 64, for gfx950.
+// Scaled dot-product attention forward in fp32 throughout, d_k = d_v = D in {32, 64, 128}, for gfx950.
 //
-// Same mathematics as the bf16 kernel (softmax(Q K^T / sqrt(64)) V per head, optional causal mask; "Attention Is All
+// Same mathematics as the bf16 kernel (softmax(Q K^T / sqrt(D)) V per head, optional causal mask; "Attention Is All
 // You Need" (lettle.cn translation), section 3.2.1), but every value stays fp32, including the softmax weights that
-// multiply V. This path serves small fp32 problems, so it is a plain VALU kernel: one thread per query row keeps q and
-// its output accumulator in registers, key/value tiles are staged in LDS and read as wave-wide broadcasts, and the
-// softmax is streamed tile by tile (running max, rescaled running sum).
+// multiply V. This path serves small fp32 problems, so it is a plain VALU kernel: one thread per query row (two for
+// D = 128, each with half of the row's dimensions, their partial dot products added across the lane pair) keeps q
+// and its output accumulator in registers, key/value tiles are staged in LDS and read as wave-wide broadcasts, and
+// the softmax is streamed tile by tile (running max, rescaled running sum).
 #include "device_common.h"
 #include "launch.h"
 
@@ -13,15 +14,23 @@
 namespace mi355 {
 namespace {
 
-constexpr int kD = 64;
-constexpr int kBQ = 64;   // queries per workgroup (one per thread)
+constexpr int kBQ = 64;   // queries per workgroup
 constexpr int kBK = 32;   // keys per tile
 
-__global__ __launch_bounds__(kBQ) void attn_fwd_f32_d64(AttnArgs a, int n_qblocks, float c) {
+template <int D>
+constexpr int threads_per_row() { return D > 64 ? 2 : 1; }
+
+template <int D>
+__global__ __launch_bounds__(kBQ * threads_per_row<D>()) void attn_fwd_f32(AttnArgs a, int n_qblocks, float c) {
+  constexpr int kD = D;
+  constexpr int kTPR = threads_per_row<D>();
+  constexpr int kDT = D / kTPR;  // dimensions per thread
+  constexpr int kThreads = kBQ * kTPR;
   __shared__ __attribute__((aligned(16))) float Ks[kBK * kD];
   __shared__ __attribute__((aligned(16))) float Vs[kBK * kD];
 
   const int tid = threadIdx.x;
+  const int part = tid % kTPR;  // this thread's dimensions: part*kDT .. part*kDT + kDT-1
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
   int qb = blk % n_qblocks;
   const int bh = blk / n_qblocks;
@@ -34,11 +43,12 @@ __global__ __launch_bounds__(kBQ) void attn_fwd_f32_d64(AttnArgs a, int n_qblock
   float* Op = static_cast<float*>(a.O) + b * a.o_stride_b + hh * a.o_stride_h;
 
   const int q0 = qb * kBQ;
-  const int qi = q0 + tid;
-  float q[kD], o[kD];
+  const int qi = q0 + tid / kTPR;
+  float q[kDT], o[kDT];
 #pragma unroll
-  for (int d = 0; d < kD; d += 4) {
-    const float4 v = qi < n_q ? *reinterpret_cast<const float4*>(Qp + (int64_t)qi * kD + d) : float4{0, 0, 0, 0};
+  for (int d = 0; d < kDT; d += 4) {
+    const float4 v =
+        qi < n_q ? *reinterpret_cast<const float4*>(Qp + (int64_t)qi * kD + part * kDT + d) : float4{0, 0, 0, 0};
     q[d] = v.x; q[d + 1] = v.y; q[d + 2] = v.z; q[d + 3] = v.w;
     o[d] = o[d + 1] = o[d + 2] = o[d + 3] = 0.f;
   }
@@ -52,8 +62,8 @@ __global__ __launch_bounds__(kBQ) void attn_fwd_f32_d64(AttnArgs a, int n_qblock
   }
   for (int k0 = k_begin; k0 < n_end; k0 += kBK) {
     __syncthreads();
-    // 32 rows x 64 floats per tensor = 512 float4 chunks, 8 per thread; rows past n_k load as zeros
-    for (int ch = tid; ch < kBK * kD / 4; ch += kBQ) {
+    // 32 rows x D floats per tensor in float4 chunks; rows past n_k load as zeros
+    for (int ch = tid; ch < kBK * kD / 4; ch += kThreads) {
       const int r = ch / (kD / 4), col = (ch % (kD / 4)) * 4;
       const bool ok = k0 + r < n_k;
       const float4 z = {0, 0, 0, 0};
@@ -68,7 +78,8 @@ __global__ __launch_bounds__(kBQ) void attn_fwd_f32_d64(AttnArgs a, int n_qblock
     for (int j = 0; j < kBK; ++j) {
       float acc = 0.f;
 #pragma unroll
-      for (int d = 0; d < kD; ++d) acc = fmaf(q[d], Ks[j * kD + d], acc);
+      for (int d = 0; d < kDT; ++d) acc = fmaf(q[d], Ks[j * kD + part * kDT + d], acc);
+      if constexpr (kTPR == 2) acc += __shfl_xor(acc, 1);  // (the same sum in both lanes of the row)
       const int key = k0 + j;
       if (key >= n_k || (a.causal && key > qi) || (a.windowed && (key > qi + a.window || key < qi - a.window)))
         acc = -INFINITY;
@@ -81,36 +92,51 @@ __global__ __launch_bounds__(kBQ) void attn_fwd_f32_d64(AttnArgs a, int n_qblock
     m = m_new;
     l *= alpha;
 #pragma unroll
-    for (int d = 0; d < kD; ++d) o[d] *= alpha;
+    for (int d = 0; d < kDT; ++d) o[d] *= alpha;
 #pragma unroll
     for (int j = 0; j < kBK; ++j) {
       const float p = fast_exp2(fmaf(s[j], c, -m_use));
       l += p;
 #pragma unroll
-      for (int d = 0; d < kD; ++d) o[d] = fmaf(p, Vs[j * kD + d], o[d]);
+      for (int d = 0; d < kDT; ++d) o[d] = fmaf(p, Vs[j * kD + part * kDT + d], o[d]);
     }
   }
   if (qi < n_q) {
     const bool seen = l > 0.f;  // false only for a row with no real key (all padding): output 0, lse -inf
     const float inv = seen ? 1.0f / l : 0.f;
     // row log-sum-exp of the scaled scores, natural log: log2(sum_j exp2(s_j c)) = m + log2(l)
-    if (a.lse != nullptr)
+    if (a.lse != nullptr && part == 0)
       a.lse[(int64_t)bh * n_q + qi] = seen ? (m + __builtin_amdgcn_logf(l)) * 0.6931471805599453f : -INFINITY;
-    float* orow = Op + (int64_t)qi * a.o_stride_row;
+    float* orow = Op + (int64_t)qi * a.o_stride_row + part * kDT;
 #pragma unroll
-    for (int d = 0; d < kD; d += 4)
+    for (int d = 0; d < kDT; d += 4)
       *reinterpret_cast<float4*>(orow + d) = float4{o[d] * inv, o[d + 1] * inv, o[d + 2] * inv, o[d + 3] * inv};
   }
 }
 
 }  // namespace
 
-hipError_t launch_attn_fwd_f32(const AttnArgs& a, hipStream_t stream) {
+hipError_t launch_attn_fwd_f32(const AttnArgs& a, int d, hipStream_t stream) {
   const int n_qblocks = (a.n_q + kBQ - 1) / kBQ;
   const int64_t nblocks = (int64_t)n_qblocks * a.B * a.H;
   if (nblocks <= 0 || nblocks > 0x7fffffff) return hipErrorInvalidValue;
-  const float c = (float)(1.4426950408889634 / 8.0);  // log2(e) / sqrt(64)
-  hipLaunchKernelGGL(attn_fwd_f32_d64, dim3((unsigned)nblocks), dim3(kBQ), 0, stream, a, n_qblocks, c);
+  const dim3 grid((unsigned)nblocks);
+  // c = log2(e) / sqrt(d)
+  switch (d) {
+    case 32:
+      hipLaunchKernelGGL(attn_fwd_f32<32>, grid, dim3(kBQ), 0, stream, a, n_qblocks,
+                         (float)(1.4426950408889634 / 5.656854249492381));
+      break;
+    case 64:
+      hipLaunchKernelGGL(attn_fwd_f32<64>, grid, dim3(kBQ), 0, stream, a, n_qblocks, (float)(1.4426950408889634 / 8.0));
+      break;
+    case 128:
+      hipLaunchKernelGGL(attn_fwd_f32<128>, grid, dim3(2 * kBQ), 0, stream, a, n_qblocks,
+                         (float)(1.4426950408889634 / 11.313708498984761));
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

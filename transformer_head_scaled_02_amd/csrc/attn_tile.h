@@ -21,6 +21,30 @@ constexpr float kTileSumLimit = 1048576.0f;  // 2^20: largest accepted per-tile 
 // 16-byte chunk swizzle of tile row r (depends on r mod 16): logical chunk c of row r is stored at chunk c ^ swz(r).
 __device__ __forceinline__ int swz(int r) { return (2 * (r & 3) + ((r >> 2) & 1)) ^ ((r >> 2) & 2); }
 
+// The same for a tile of rows of D bf16 (D / 8 chunks of 16 bytes; swz_d<64> is swz). LDS serves 16 lanes of a
+// 16-byte read (or 32 lanes of an 8-byte read) from 64 four-byte banks, i.e. sixteen 16-byte bank groups; a row of D
+// elements starts at group (r * D / 8) mod 16. The swizzle makes both read patterns of the attention kernels hit
+// sixteen different groups: the operand reads (sixteen consecutive rows, one logical chunk) and the transpose reads
+// (four consecutive rows from a multiple of 4, four consecutive chunks from a multiple of 4). D = 128 (rows of 256
+// bytes, all starting at group 0) needs a bijection of r mod 16 whose low two bits follow r mod 4 in the upper two
+// bits of the chunk; D = 32 (four rows per 256 bytes) needs only a bijection of r / 4 mod 4.
+template <int D>
+__device__ __forceinline__ int swz_d(int r) {
+  static_assert(D == 32 || D == 64 || D == 128, "head width");
+  if constexpr (D == 64) return swz(r);
+  else if constexpr (D == 128) return 4 * (r & 3) + ((r >> 2) & 3);
+  else return (r >> 2) & 3;
+}
+
+// log2(e) / sqrt(D): the exponent scale of a score of two D-wide rows (the division by sqrt(d_k) of the scaled
+// dot product, moved into the exponent of base 2)
+template <int D>
+constexpr float scale_log2() {
+  static_assert(D == 32 || D == 64 || D == 128, "head width");
+  return D == 64 ? kScaleLog2 : D == 32 ? (float)(1.4426950408889634 / 5.656854249492381)
+                                        : (float)(1.4426950408889634 / 11.313708498984761);
+}
+
 // Global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4, scalar-base form): lane l reads
 // base + voff(l) and its 16 bytes land at LDS byte address lds + 16*l. Issued as inline assembly with m0 (the LDS
 // destination) set in the same statement, so that the compiler does not treat later LDS reads as possibly reading
@@ -63,7 +87,8 @@ __device__ __forceinline__ bf16x8 lsum_selector(int lane) {
 
 // s * c - m, one fused multiply-add. Written as a builtin, not inline assembly: s comes straight from an MFMA, and
 // only instructions the compiler emits itself get the wait states a VALU read of an MFMA result needs.
-__device__ __forceinline__ float scaled_minus(float s, float neg_m) { return __builtin_fmaf(s, kScaleLog2, neg_m); }
+template <int D = 64>
+__device__ __forceinline__ float scaled_minus(float s, float neg_m) { return __builtin_fmaf(s, scale_log2<D>(), neg_m); }
 
 // The other lane of this lane's query (lane +- 32) has the flag set.
 __device__ __forceinline__ bool partner32_any(bool x) {

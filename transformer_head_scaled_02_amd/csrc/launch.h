@@ -26,8 +26,9 @@ struct AttnArgs {
   int windowed, window;
 };
 
-hipError_t launch_attn_fwd_bf16(const AttnArgs& a, hipStream_t stream);
-hipError_t launch_attn_fwd_f32(const AttnArgs& a, hipStream_t stream);
+// d: the head width d_k = d_v, 32, 64 or 128 (every other value: hipErrorInvalidValue, nothing launched)
+hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int d, hipStream_t stream);
+hipError_t launch_attn_fwd_f32(const AttnArgs& a, int d, hipStream_t stream);
 
 // Backward pass of attention over [B, H] heads of width 64, every tensor dense [B, H, n, 64] in the element type.
 // `aux` is the workspace: per head and per 64-row query tile, 256 floats = [log2(e)*lse of the 64 rows | D of the 64

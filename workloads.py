@@ -36,6 +36,16 @@ WORKLOADS = {
                                   causal=False, seed=1005),
     "sdpa_causal_bf16_b4_h8_n4096": dict(kind="sdpa", dtype="bf16", B=4, h=8, n_q=4096, n_k=4096, d_k=64, d_v=64,
                                          causal=True, seed=1005),
+    # the head-count variants at d_model = 512: 16 heads of width 32 and 4 heads of width 128 over the same sequence
+    # length (the same attention FLOPs as 8 heads of 64)
+    "sdpa_bf16_b4_h16_n4096_d32": dict(kind="sdpa", dtype="bf16", B=4, h=16, n_q=4096, n_k=4096, d_k=32, d_v=32,
+                                       causal=False, seed=1007),
+    "sdpa_causal_bf16_b4_h16_n4096_d32": dict(kind="sdpa", dtype="bf16", B=4, h=16, n_q=4096, n_k=4096, d_k=32,
+                                              d_v=32, causal=True, seed=1007),
+    "sdpa_bf16_b4_h4_n4096_d128": dict(kind="sdpa", dtype="bf16", B=4, h=4, n_q=4096, n_k=4096, d_k=128, d_v=128,
+                                       causal=False, seed=1008),
+    "sdpa_causal_bf16_b4_h4_n4096_d128": dict(kind="sdpa", dtype="bf16", B=4, h=4, n_q=4096, n_k=4096, d_k=128,
+                                              d_v=128, causal=True, seed=1008),
     # key padding: the long-sequence tensors as one length bucket of a length-grouped batch, each entry padded to 4096
     # (real key counts per entry in kv_len)
     "sdpa_padded_bf16_b4_h8_n4096": dict(kind="sdpa_padded", dtype="bf16", B=4, h=8, n_q=4096, n_k=4096, d_k=64,
