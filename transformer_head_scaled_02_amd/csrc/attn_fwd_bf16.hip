@@ -67,8 +67,8 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_bf16(AttnArgs a, int n
   // the ring barrier after the tile's last product: holding the next tile's K and all of V in registers as well
   // would not fit two waves per SIMD.
   constexpr bool kLate = D >= 128;
-  static_assert((2 * kCPT) % NW == 0 && kLPW % 2 == 0 && kLPW % kNOff == 0,
-                "tile copies split evenly, in pairs, over the waves");
+  static_assert((2 * kCPT) % NW == 0 && kLPW % kNOff == 0,
+                "tile copies split evenly over the waves, each wave's copies a whole number of swizzle periods");
   static_assert(STAGES >= 2 && STAGES <= 4, "ring depth");
   static_assert(H == 1 || H == 2, "one or two query halves per wave");
   static_assert(!kLate || H == 1, "wide heads have one query half per wave");
@@ -495,8 +495,9 @@ hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int d, hipStream_t stream) {
   // Unmasked: 4-wave workgroups of 256 queries (two halves of 32 per wave), two per CU (two waves per SIMD, 256
   // registers each), a 3-tile ring. Causal: 4-wave workgroups of 128 queries with a 4-tile ring, two per CU, which
   // balanced the triangular work best.
-  // Other head widths: d = 32 as d = 64 (its tiles are half the size); d = 128 with one query half per wave and a
-  // 2-tile ring (two 64 KB rings fit the 160 KB of LDS of a CU).
+  // Other head widths: d = 32 as d = 64 (tiles of half the size; unmasked with a 4-tile ring); d = 128 with one
+  // query half per wave and a 2-tile ring of 64 KB: unmasked in one 8-wave workgroup per CU, causal and windowed in
+  // two 4-wave workgroups per CU (the smaller blocks balance the triangular work).
   switch (d) {
     case 64:
       if (a.windowed) return launch<64, 4, 1, 2, 4, true>(a, stream);
@@ -504,10 +505,11 @@ hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int d, hipStream_t stream) {
       return launch<64, 4, 1, 2, 4>(a, stream);
     case 32:
       if (a.windowed) return launch<32, 4, 1, 2, 4, true>(a, stream);
-      if (!a.causal) return launch<32, 4, 2, 2, 3>(a, stream);
+      if (!a.causal) return launch<32, 4, 2, 2, 4>(a, stream);
       return launch<32, 4, 1, 2, 4>(a, stream);
     case 128:
       if (a.windowed) return launch<128, 4, 1, 2, 2, true>(a, stream);
+      if (!a.causal) return launch<128, 8, 1, 1, 2>(a, stream);
       return launch<128, 4, 1, 2, 2>(a, stream);
     default:
       return hipErrorInvalidValue;
