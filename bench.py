@@ -37,7 +37,8 @@ METRIC = "attention TFLOP/s (4·B·h·n_q·n_k·d_k) at h={h},d_k={d_k}; % of bf
 METRIC_WINDOW = "restricted self-attention TFLOP/s over the band's pairs (4·B·h·pairs·d_k) at h=8,d_k=64; % of bf16 MFMA peak"
 METRIC_PADDED = "attention TFLOP/s over real keys (4·h·n_q·Σ_b kv_len[b]·d_k) at h=8,d_k=64; % of bf16 MFMA peak"
 METRIC_ENC = "encoder layer TFLOP/s (projections, attention, W^O, FFN) at d_model=512,h=8,d_ff=2048; % of bf16 MFMA peak"
-METRIC_MHA = "multi-head attention TFLOP/s (Q/K/V projections + attention + W^O) at d_model=512,h=8; % of bf16 MFMA peak"
+METRIC_MHA = ("multi-head attention TFLOP/s (Q/K/V projections + attention + W^O) at d_model={d_model},h={h}; % of bf16 "
+              "MFMA peak")
 METRIC_BWD = "attention backward TFLOP/s (10·B·h·n_q·n_k·d_k) at h=8,d_k=64; % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
@@ -72,13 +73,15 @@ def flops_padded(w):
 def flops_encoder(w):
     """Products of one encoder layer: Q/K/V and W^O projections, attention (4 n^2 d per head), FFN (two GEMMs)."""
     M, d, ff = w["B"] * w["n_q"], w["d_model"], w["d_ff"]
-    return 2.0 * M * d * 3 * d + 4.0 * w["B"] * w["h"] * w["n_q"] * w["n_k"] * 64 + 2.0 * M * d * d + 4.0 * M * d * ff
+    return (2.0 * M * d * 3 * d + 4.0 * w["B"] * w["h"] * w["n_q"] * w["n_k"] * w["d_k"] + 2.0 * M * d * d
+            + 4.0 * M * d * ff)
 
 
 def flops_mha(w):
-    """Products of mha_forward: Q/K/V projections, attention (4 n_q n_k 64 per head), W^O."""
+    """Products of mha_forward: Q/K/V projections, attention (4 n_q n_k d_k per head), W^O."""
     Mq, Mk, d = w["B"] * w["n_q"], w["B"] * w["n_k"], w["d_model"]
-    return 2.0 * Mq * d * d + 4.0 * Mk * d * d + 4.0 * w["B"] * w["h"] * w["n_q"] * w["n_k"] * 64 + 2.0 * Mq * d * d
+    return (2.0 * Mq * d * d + 4.0 * Mk * d * d + 4.0 * w["B"] * w["h"] * w["n_q"] * w["n_k"] * w["d_k"]
+            + 2.0 * Mq * d * d)
 
 
 def flops_metric_bwd(w):
@@ -350,7 +353,7 @@ def bench_mha(args, w, x, m, dev):
     xq = dev(x["Xq"])
     ws_t = [dev(x[nm]) for nm in ("Wq", "Wk", "Wv", "Wo")]
     out = torch.empty_like(xq)
-    work = torch.empty(m.mha_workspace_size(w["B"], w["n_q"], w["n_k"], w["h"]), dtype=torch.uint8, device="cuda")
+    work = torch.empty(m.mha_workspace_size(w["B"], w["n_q"], w["n_k"], w["h"], w["d_k"], w["d_v"]), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
     def step():
@@ -372,11 +375,11 @@ def bench_mha(args, w, x, m, dev):
     d = np.abs(out[:2].float().cpu().numpy() - ref)
     value = flops_mha(w) / (ms * 1e-3) / 1e12
     return {
-        "metric": METRIC_MHA, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "metric": METRIC_MHA.format(d_model=w["d_model"], h=w["h"]), "value": round(value, 2), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w["dtype"], "data": "synthetic (seeded inputs and weights, no dataset)",
         "config": {"workload": args.workload, "B": w["B"], "n": w["n_q"], "d_model": w["d_model"], "h": w["h"],
-                   "mask": "none"},
+                   "d_k": w["d_k"], "mask": "none"},
         "tokens_per_s": round(w["B"] * w["n_q"] / (ms * 1e-3), 1),
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(value, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

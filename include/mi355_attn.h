@@ -143,8 +143,10 @@ size_t sdpa_backward_workspace_size(int dtype, int64_t B, int64_t h, int64_t n_q
  *   workspace: device scratch of at least mha_workspace_size(...) bytes, 16-byte aligned, owned by the caller; it
  *              holds the projected Q/K/V (head-major) and the concatenated heads, in `dtype`.
  *   dtype: ATTN_BF16 only (the projections accumulate in float32 and round to bf16).
- *   Requirements: d_k = d_v = 64, d_model a positive multiple of 64, causal only with n_q == n_k. `out` must not
- *   overlap any input or the workspace, and the workspace must not overlap any input. */
+ *   Requirements: d_k = d_v in {32, 64, 128} with h * d_k a multiple of 64 (the head-count variants of
+ *   "Transformer：抛弃循环与卷积的序列建模", section "模型变体与消融实验"), d_model a positive multiple of 64, causal
+ *   only with n_q == n_k. `out` must not overlap any input or the workspace, and the workspace must not overlap any
+ *   input. */
 int mha_forward(const void* Xq, const void* Xkv, const void* Wq, const void* Wk, const void* Wv, const void* Wo,
                 int mask_kind, void* out, void* workspace, size_t workspace_bytes, int dtype,
                 int64_t B, int64_t n_q, int64_t n_k, int64_t d_model, int64_t h, int64_t d_k, int64_t d_v,
@@ -169,8 +171,9 @@ size_t mha_workspace_size(int dtype, int64_t B, int64_t n_q, int64_t n_k, int64_
  *              heads, the residual sums, H1 and the FFN hidden activations, all bf16).
  *   dtype: ATTN_BF16 only: every tensor above is bf16; products accumulate in float32, the LayerNorm statistics are
  *          float32, and every intermediate listed for the workspace is rounded to bf16.
- *   Requirements: d_model = 64 h <= 1024, d_ff a positive multiple of 64. `out` must not overlap any input or the
- *   workspace; the workspace must not overlap any input. */
+ *   Requirements: d_model = d h <= 1024 with head width d in {32, 64, 128} and d_model a multiple of 64, d_ff a
+ *   positive multiple of 64. `out` must not overlap any input or the workspace; the workspace must not overlap any
+ *   input. */
 int encoder_layer_forward(const void* X, const int32_t* kv_len, const void* Wq, const void* Wk, const void* Wv,
                           const void* Wo, const void* ln1_gamma, const void* ln1_beta, const void* W1, const void* b1,
                           const void* W2, const void* b2, const void* ln2_gamma, const void* ln2_beta, float eps,

@@ -70,6 +70,7 @@ def mha(lib, Xq=A, Xkv=A, Wq=A * 100, Wk=A * 200, Wv=A * 300, Wo=A * 400, mask=0
 @pytest.mark.parametrize("kw,code", [
     (dict(Wo=None), INVALID), (dict(ws=None), INVALID), (dict(dtype=F32), UNSUPPORTED), (dict(h=0), INVALID),
     (dict(d_model=96), UNSUPPORTED), (dict(d_k=32), UNSUPPORTED), (dict(mask=1, n_k=9), UNSUPPORTED),
+    (dict(d_k=32, d_v=32), UNSUPPORTED), (dict(d_k=48, d_v=48, h=4), UNSUPPORTED), (dict(d_k=256, d_v=256), UNSUPPORTED),
     (dict(mask=3), INVALID), (dict(ws_bytes=100), INVALID), (dict(Wq=A * 100 + 4), INVALID),
     (dict(out=A * 100), INVALID), (dict(ws=A * 300), INVALID), (dict(out=A * 2000 + 4096), INVALID),
 ])
@@ -86,6 +87,11 @@ def test_workspace_size(lib):
     assert got >= (3 + 5 + 5 + 3) * 64 * 2 and got % 256 == 0
     assert lib.mha_workspace_size(F32, 1, 3, 5, 1, 64, 64) == 0
     assert lib.mha_workspace_size(BF16, 1, 3, 5, 1, 32, 64) == 0
+    # other head widths: [B, h, n, d] regions for d in {32, 128}; h * d must be a multiple of 64
+    assert lib.mha_workspace_size(BF16, 2, 10, 12, 16, 32, 32) == 90112  # 20480 + 24576 + 24576 + 20480
+    assert lib.mha_workspace_size(BF16, 2, 10, 12, 4, 128, 128) == 90112
+    assert lib.mha_workspace_size(BF16, 1, 3, 5, 1, 32, 32) == 0
+    assert lib.mha_workspace_size(BF16, 1, 3, 5, 2, 48, 48) == 0
 
 
 def sdpa_lse(lib, Q=A, K=A * 2, V=A * 3, mask=0, out=A * 1000, lse=A * 1100, dtype=BF16, B=1, h=1, n_q=16, n_k=16,
@@ -154,7 +160,9 @@ def enc(lib, X=A, kv_len=None, W=A * 10, ln=A * 20, W1=A * 30, b1=A * 40, W2=A *
 @pytest.mark.parametrize("kw,code", [
     (dict(X=None), INVALID), (dict(W1=None), INVALID), (dict(out=None), INVALID), (dict(ws=None), INVALID),
     (dict(dtype=F32), UNSUPPORTED), (dict(mask=4), INVALID), (dict(eps=-1.0), INVALID),
-    (dict(eps=float("nan")), INVALID), (dict(d_model=512, h=4), UNSUPPORTED), (dict(d_ff=100), UNSUPPORTED),
+    (dict(eps=float("nan")), INVALID), (dict(d_model=512, h=32), UNSUPPORTED), (dict(d_ff=100), UNSUPPORTED),
+    # head width d_model / h in {32, 64, 128} with d_model a multiple of 64
+    (dict(d_model=512, h=3), UNSUPPORTED), (dict(d_model=96, h=3), UNSUPPORTED), (dict(d_model=1024, h=4), UNSUPPORTED),
     (dict(d_model=2048, h=32), UNSUPPORTED), (dict(n=0), INVALID), (dict(ws_bytes=1000), INVALID),
     (dict(b1=A * 40 + 2), INVALID), (dict(kv_len=A * 70 + 4), INVALID),
     # out [1,16,512] bf16 = 16 KiB over X; the workspace over W1
@@ -171,7 +179,10 @@ def test_encoder_layer_workspace_size(lib):
     # Q, K, V, the concat, the residual sums and H1 (six [B, n, d_model] regions) plus the FFN hidden [B, n, d_ff]
     assert lib.encoder_layer_workspace_size(BF16, B, n, dm, h, ff) == 6 * act + B * n * ff * 2
     assert lib.encoder_layer_workspace_size(F32, B, n, dm, h, ff) == 0
-    assert lib.encoder_layer_workspace_size(BF16, B, n, dm, 4, ff) == 0
+    # 4 heads of 128 and 16 of 32 need the same regions; 32 heads of 16 are not implemented
+    assert lib.encoder_layer_workspace_size(BF16, B, n, dm, 4, ff) == 6 * act + B * n * ff * 2
+    assert lib.encoder_layer_workspace_size(BF16, B, n, dm, 16, ff) == 6 * act + B * n * ff * 2
+    assert lib.encoder_layer_workspace_size(BF16, B, n, dm, 32, ff) == 0
     assert lib.encoder_layer_workspace_size(BF16, B, n, dm, h, 100) == 0
 
 

@@ -1,6 +1,7 @@
 """Parity of the other head widths, d_k = d_v in {32, 128} (d_model = 512 over 16 or 4 heads: the head-count variants
 of "Transformer：抛弃循环与卷积的序列建模", section "模型变体与消融实验"), with the float64 oracle, through every forward
-entry point (sdpa_forward, sdpa_forward_lse, sdpa_forward_padded, sdpa_forward_window) in both dtypes.
+entry point (sdpa_forward, sdpa_forward_lse, sdpa_forward_padded, sdpa_forward_window) in both dtypes, and through
+mha_forward and encoder_layer_forward at 16 and 4 heads.
 
 Shapes span several 64-key tiles with ragged tails, n_q != n_k both ways, a single query, and the full-size
 long-sequence workloads (checked on sampled heads and rows). Bars as for d = 64: bf16 max-abs <= 2e-2, mean-abs <=
@@ -12,7 +13,7 @@ import torch
 
 import transformer_head_scaled_02_amd as m
 import workloads
-from oracle import sdpa_lse_ref, sdpa_ref
+from oracle import encoder_layer_ref, mha_ref, sdpa_lse_ref, sdpa_ref
 from tests._helpers import assert_bf16_parity, assert_f32_parity, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
@@ -128,3 +129,41 @@ def test_headwidth_long_sequence_sampled(name):
         for hh in (0, w["h"] - 1):
             ref = sdpa_ref(x["Q"].f64[b, hh, rows], x["K"].f64[b, hh], x["V"].f64[b, hh], w["causal"], q_index=rows)
             assert_bf16_parity(got[b, hh, rows], ref, f"{name} b={b} h={hh}")
+
+
+# --- multi-head attention and the encoder layer at other head counts ---------------------------------------------
+
+@pytest.mark.parametrize("B,n_q,n_k,d_model,h,causal,cross", [
+    (2, 100, 100, 512, 16, False, False), (2, 100, 100, 512, 4, True, False), (2, 50, 77, 512, 16, False, True),
+    (3, 129, 260, 512, 4, False, True), (2, 65, 65, 128, 4, True, False), (2, 70, 70, 256, 2, False, False)])
+def test_headwidth_mha(B, n_q, n_k, d_model, h, causal, cross):
+    d = d_model // h
+    x = workloads.make_mha_inputs(B, n_q, n_k, d_model, h, d, d, "bf16", 9960 + n_q + h, cross=cross)
+    xq, xkv = to_dev(x["Xq"]), to_dev(x["Xkv"])
+    ws = [to_dev(x[nm]) for nm in ("Wq", "Wk", "Wv", "Wo")]
+    got = to_f64(m.mha_forward(xq, xkv, *ws, h=h, mask=_mask(causal)))
+    ref = mha_ref(x["Xq"].f64, x["Xkv"].f64, x["Wq"].f64, x["Wk"].f64, x["Wv"].f64, x["Wo"].f64, h=h, causal=causal)
+    assert_bf16_parity(got, ref, f"mha d={d} {(B, n_q, n_k, d_model, h, causal, cross)}")
+
+
+ENC_NAMES = ("Wq", "Wk", "Wv", "Wo", "ln1_gamma", "ln1_beta", "W1", "b1", "W2", "b2", "ln2_gamma", "ln2_beta")
+
+
+@pytest.mark.parametrize("B,n,h,causal,kv_len", [
+    (4, 128, 16, False, None), (4, 128, 4, False, None), (3, 77, 4, True, None), (4, 65, 16, False, [65, 30, 1, 0])])
+def test_headwidth_encoder_layer(B, n, h, causal, kv_len):
+    # bars as for the 8-head layer: normalised rms <= 1e-2, mean-abs <= 6e-3, max-abs <= 0.1 (every intermediate is
+    # stored in bf16; the output is LayerNorm-scaled)
+    x = workloads.make_encoder_inputs(B, n, 512, h, 2048, "bf16", 9980 + n + h)
+    lens = None if kv_len is None else torch.tensor(kv_len, dtype=torch.int32, device="cuda")
+    out = m.encoder_layer_forward(to_dev(x["X"]), *(to_dev(x[nm]) for nm in ENC_NAMES), h=h, eps=1e-5,
+                                  mask=_mask(causal), kv_len=lens)
+    torch.cuda.synchronize()
+    got = to_f64(out)
+    ref = encoder_layer_ref(x["X"].f64, *(x[nm].f64 for nm in ENC_NAMES), h, 1e-5, causal,
+                            None if kv_len is None else np.asarray(kv_len))
+    assert np.all(np.isfinite(got))
+    dd = np.abs(got - ref)
+    nrms = float(np.sqrt(np.mean(dd * dd)) / np.sqrt(np.mean(ref * ref)))
+    assert nrms <= 1e-2 and dd.mean() <= 6e-3 and dd.max() <= 0.1, \
+        f"encoder h={h}: max_abs {dd.max():.3g} mean_abs {dd.mean():.3g} nrms {nrms:.3g}"

@@ -59,8 +59,8 @@ struct MhaLayout {
   size_t q_off, k_off, v_off, c_off, total;
 };
 
-MhaLayout mha_layout(int64_t B, int64_t n_q, int64_t n_k, int64_t h) {
-  const size_t q = (size_t)B * h * n_q * 64 * 2, kv = (size_t)B * h * n_k * 64 * 2;
+MhaLayout mha_layout(int64_t B, int64_t n_q, int64_t n_k, int64_t h, int64_t d) {
+  const size_t q = (size_t)B * h * n_q * d * 2, kv = (size_t)B * h * n_k * d * 2;
   MhaLayout L;
   L.q_off = 0;
   L.k_off = round_up(L.q_off + q, 256);
@@ -99,8 +99,16 @@ EncLayout enc_layout(int64_t B, int64_t n, int64_t d_model, int64_t d_ff) {
   return L;
 }
 
+// Head widths of the multi-head paths: 32, 64 or 128 (the attention kernels' widths), with h * d a multiple of 64
+// (the GEMM's column granule); log2 of the width, or -1.
+int head_shift(int64_t h, int64_t d) {
+  if (h <= 0 || (h * d) % 64) return -1;
+  return d == 32 ? 5 : d == 64 ? 6 : d == 128 ? 7 : -1;
+}
+
 bool enc_sizes_ok(int64_t B, int64_t n, int64_t d_model, int64_t h, int64_t d_ff) {
-  return B > 0 && n > 0 && h > 0 && d_model == h * 64 && d_model <= 1024 && d_ff > 0 && d_ff % 64 == 0 &&
+  return B > 0 && n > 0 && h > 0 && d_model % h == 0 && head_shift(h, d_model / h) >= 0 && d_model <= 1024 &&
+         d_ff > 0 && d_ff % 64 == 0 &&
          d_ff <= 65536 && n <= ATTN_MAX_SEQ && B * h <= ATTN_MAX_HEADS && B * n <= 0x7fffffffLL && grid_fits(B, h, n);
 }
 
@@ -294,9 +302,9 @@ ATTN_EXPORT int sdpa_backward(const void* Q, const void* K, const void* V, const
 
 ATTN_EXPORT size_t mha_workspace_size(int dtype, int64_t B, int64_t n_q, int64_t n_k, int64_t h, int64_t d_k,
                                       int64_t d_v) {
-  if (dtype != ATTN_BF16 || B <= 0 || n_q <= 0 || n_k <= 0 || h <= 0 || d_k != 64 || d_v != 64) return 0;
+  if (dtype != ATTN_BF16 || B <= 0 || n_q <= 0 || n_k <= 0 || h <= 0 || d_k != d_v || head_shift(h, d_k) < 0) return 0;
   if (n_q > ATTN_MAX_SEQ || n_k > ATTN_MAX_SEQ || B > ATTN_MAX_HEADS || h > ATTN_MAX_HEADS) return 0;
-  return mha_layout(B, n_q, n_k, h).total;
+  return mha_layout(B, n_q, n_k, h, d_k).total;
 }
 
 ATTN_EXPORT int mha_forward(const void* Xq, const void* Xkv, const void* Wq, const void* Wk, const void* Wv,
@@ -310,9 +318,10 @@ ATTN_EXPORT int mha_forward(const void* Xq, const void* Xkv, const void* Wq, con
     return fail_status(ATTN_ERR_INVALID, "mha_forward: mask_kind %d", mask_kind);
   if (B <= 0 || n_q <= 0 || n_k <= 0 || d_model <= 0 || h <= 0 || d_k <= 0 || d_v <= 0)
     return fail_status(ATTN_ERR_INVALID, "mha_forward: sizes must be positive");
-  if (d_k != 64 || d_v != 64)
-    return fail_status(ATTN_ERR_UNSUPPORTED, "mha_forward: head dims d_k=%lld d_v=%lld (only 64 is implemented)",
-                (long long)d_k, (long long)d_v);
+  const int hsh = d_k == d_v ? head_shift(h, d_k) : -1;
+  if (hsh < 0)
+    return fail_status(ATTN_ERR_UNSUPPORTED, "mha_forward: head dims d_k=%lld d_v=%lld with h=%lld (implemented: d_k = "
+                       "d_v in {32, 64, 128}, h*d_k a multiple of 64)", (long long)d_k, (long long)d_v, (long long)h);
   if (d_model % 64) return fail_status(ATTN_ERR_UNSUPPORTED, "mha_forward: d_model=%lld is not a multiple of 64",
                                 (long long)d_model);
   if (mask_kind == ATTN_MASK_CAUSAL && n_q != n_k)
@@ -321,14 +330,14 @@ ATTN_EXPORT int mha_forward(const void* Xq, const void* Xkv, const void* Wq, con
       B * h > ATTN_MAX_HEADS || d_model > 65536 || B * n_q > 0x7fffffffLL || B * n_k > 0x7fffffffLL ||
       !grid_fits(B, h, n_q))
     return fail_status(ATTN_ERR_UNSUPPORTED, "mha_forward: sizes beyond the library limits");
-  const MhaLayout L = mha_layout(B, n_q, n_k, h);
+  const MhaLayout L = mha_layout(B, n_q, n_k, h, d_k);
   if (workspace_bytes < L.total)
     return fail_status(ATTN_ERR_INVALID, "mha_forward: workspace %zu bytes, need %zu", workspace_bytes, L.total);
   const void* ptrs[] = {Xq, Xkv, Wq, Wk, Wv, Wo, out, workspace};
   for (const void* p : ptrs)
     if (!aligned16(p)) return fail_status(ATTN_ERR_INVALID, "mha_forward: pointers must be 16-byte aligned");
   const size_t xq_b = (size_t)B * n_q * d_model * 2, xkv_b = (size_t)B * n_k * d_model * 2;
-  const size_t w_b = (size_t)d_model * h * 64 * 2;
+  const size_t w_b = (size_t)d_model * h * d_k * 2;
   const void* ins[] = {Xq, Xkv, Wq, Wk, Wv, Wo};
   const size_t in_b[] = {xq_b, xkv_b, w_b, w_b, w_b, w_b};
   for (int i = 0; i < 6; ++i) {
@@ -343,32 +352,32 @@ ATTN_EXPORT int mha_forward(const void* Xq, const void* Xkv, const void* Wq, con
   void* Kh = ws + L.k_off;
   void* Vh = ws + L.v_off;
   void* Ch = ws + L.c_off;
-  const int hd = (int)(h * 64);
+  const int hd = (int)(h * d_k);
   const hipStream_t s = static_cast<hipStream_t>(stream);
 
-  // 1. projections, written per head: Qh [B,h,n_q,64], Kh/Vh [B,h,n_k,64]
+  // 1. projections, written per head: Qh [B,h,n_q,d], Kh/Vh [B,h,n_k,d]
   mi355::GemmProblem proj[3] = {
-      {Xq, Wq, Qh, (int)(B * n_q), hd, (int)d_model, (int)n_q},
-      {Xkv, Wk, Kh, (int)(B * n_k), hd, (int)d_model, (int)n_k},
-      {Xkv, Wv, Vh, (int)(B * n_k), hd, (int)d_model, (int)n_k},
+      {Xq, Wq, Qh, (int)(B * n_q), hd, (int)d_model, (int)n_q, nullptr, nullptr, 0, hsh},
+      {Xkv, Wk, Kh, (int)(B * n_k), hd, (int)d_model, (int)n_k, nullptr, nullptr, 0, hsh},
+      {Xkv, Wv, Vh, (int)(B * n_k), hd, (int)d_model, (int)n_k, nullptr, nullptr, 0, hsh},
   };
   hipError_t e = mi355::launch_gemm_bf16(proj, 3, s);
   if (e != hipSuccess) return fail_status(ATTN_ERR_HIP, "mha_forward: projection launch failed: %s", hipGetErrorString(e));
 
-  // 2. attention per head, output written into the concatenated layout [B, n_q, h*64]
+  // 2. attention per head, output written into the concatenated layout [B, n_q, h*d]
   mi355::AttnArgs a{};
   a.Q = Qh; a.K = Kh; a.V = Vh; a.O = Ch;
   a.B = (int)B; a.H = (int)h; a.n_q = (int)n_q; a.n_k = (int)n_k;
-  a.q_stride_bh = n_q * 64;
-  a.k_stride_bh = n_k * 64;
-  a.o_stride_b = n_q * h * 64;
-  a.o_stride_h = 64;
-  a.o_stride_row = h * 64;
+  a.q_stride_bh = n_q * d_k;
+  a.k_stride_bh = n_k * d_k;
+  a.o_stride_b = n_q * hd;
+  a.o_stride_h = d_k;
+  a.o_stride_row = hd;
   a.causal = mask_kind == ATTN_MASK_CAUSAL;
-  e = mi355::launch_attn_fwd_bf16(a, 64, s);
+  e = mi355::launch_attn_fwd_bf16(a, (int)d_k, s);
   if (e != hipSuccess) return fail_status(ATTN_ERR_HIP, "mha_forward: attention launch failed: %s", hipGetErrorString(e));
 
-  // 3. output projection: out [B*n_q, d_model] = concat [B*n_q, h*64] x Wo [h*64, d_model]
+  // 3. output projection: out [B*n_q, d_model] = concat [B*n_q, h*d] x Wo [h*d, d_model]
   mi355::GemmProblem outp = {Ch, Wo, out, (int)(B * n_q), (int)d_model, hd, 0};
   e = mi355::launch_gemm_bf16(&outp, 1, s);
   if (e != hipSuccess) return fail_status(ATTN_ERR_HIP, "mha_forward: W^O launch failed: %s", hipGetErrorString(e));
@@ -399,7 +408,8 @@ ATTN_EXPORT int encoder_layer_forward(const void* X, const int32_t* kv_len, cons
     return fail_status(ATTN_ERR_INVALID, "%s: sizes must be positive", fn);
   if (!finite_nonneg(eps)) return fail_status(ATTN_ERR_INVALID, "%s: eps must be finite and >= 0", fn);
   if (!enc_sizes_ok(B, n, d_model, h, d_ff))
-    return fail_status(ATTN_ERR_UNSUPPORTED, "%s: needs d_model = 64 h <= 1024 and d_ff a multiple of 64 (got "
+    return fail_status(ATTN_ERR_UNSUPPORTED, "%s: needs d_model = d h <= 1024 with d in {32, 64, 128}, d_model a "
+                       "multiple of 64 and d_ff a multiple of 64 (got "
                        "d_model=%lld h=%lld d_ff=%lld), sizes within the library limits", fn, (long long)d_model,
                        (long long)h, (long long)d_ff);
   const EncLayout L = enc_layout(B, n, d_model, d_ff);
@@ -433,20 +443,22 @@ ATTN_EXPORT int encoder_layer_forward(const void* X, const int32_t* kv_len, cons
   if (e != hipSuccess) return fail_status(ATTN_ERR_HIP, "%s: %s launch failed: %s", fn, what, hipGetErrorString(e));
 
   // 1. Q/K/V projections into the per-head layout, 2. attention into the concatenated heads
-  mi355::GemmProblem proj[3] = {{X, Wq, Qh, M, dm, dm, (int)n}, {X, Wk, Kh, M, dm, dm, (int)n},
-                                {X, Wv, Vh, M, dm, dm, (int)n}};
+  const int dh = (int)(d_model / h), hsh = head_shift(h, dh);
+  mi355::GemmProblem proj[3] = {{X, Wq, Qh, M, dm, dm, (int)n, nullptr, nullptr, 0, hsh},
+                                {X, Wk, Kh, M, dm, dm, (int)n, nullptr, nullptr, 0, hsh},
+                                {X, Wv, Vh, M, dm, dm, (int)n, nullptr, nullptr, 0, hsh}};
   ENC_STEP(mi355::launch_gemm_bf16(proj, 3, s), "projection");
   mi355::AttnArgs a{};
   a.Q = Qh; a.K = Kh; a.V = Vh; a.O = Ch;
   a.B = (int)B; a.H = (int)h; a.n_q = (int)n; a.n_k = (int)n;
-  a.q_stride_bh = n * 64;
-  a.k_stride_bh = n * 64;
-  a.o_stride_b = n * h * 64;
-  a.o_stride_h = 64;
-  a.o_stride_row = h * 64;
+  a.q_stride_bh = n * dh;
+  a.k_stride_bh = n * dh;
+  a.o_stride_b = n * d_model;
+  a.o_stride_h = dh;
+  a.o_stride_row = d_model;
   a.causal = mask_kind == ATTN_MASK_CAUSAL;
   a.kv_len = kv_len;
-  ENC_STEP(mi355::launch_attn_fwd_bf16(a, 64, s), "attention");
+  ENC_STEP(mi355::launch_attn_fwd_bf16(a, dh, s), "attention");
   // 3. R1 = X + Concat W^O (residual in the GEMM epilogue), H1 = LayerNorm(R1)
   mi355::GemmProblem wo = {Ch, Wo, R, M, dm, dm, 0, nullptr, X, 0};
   ENC_STEP(mi355::launch_gemm_bf16(&wo, 1, s), "W^O");

@@ -13,11 +13,12 @@
 // sub-tiles with 128-byte rows and the XOR chunk swizzle of attn_tile.h, which keeps both the row reads and the
 // transposed reads free of bank conflicts. Up to three independent problems share one launch (the Q, K and V
 // projections).
-// The "head-major" epilogue writes column block n/64 of row (b, i) straight to [b][n/64][i][n%64], which is the
-// per-head layout the attention kernel reads, so no separate reshape pass exists. The row-major epilogue can add a
-// bias, apply ReLU and add a residual before the rounding to bf16: the position-wise FFN max(0, x W1 + b1) W2 + b2 and
-// the residual connection x + Sublayer(x) of the encoder layer ("Transformer：抛弃循环与卷积的序列建模", sections
-// "FFN" and "Residual Connection 与 LayerNorm") then cost no extra pass over memory.
+// The "head-major" epilogue writes column block n/w of row (b, i) straight to [b][n/w][i][n%w] (w the head width),
+// which is the per-head layout the attention kernel reads, so no separate reshape pass exists. The row-major epilogue
+// can add a bias, apply ReLU and add a residual before the rounding to bf16: the position-wise FFN
+// max(0, x W1 + b1) W2 + b2 and the residual connection x + Sublayer(x) of the encoder layer
+// ("Transformer：抛弃循环与卷积的序列建模", sections "FFN" and "Residual Connection 与 LayerNorm") then cost no extra
+// pass over memory.
 #include "attn_tile.h"
 #include "launch.h"
 
@@ -211,8 +212,9 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_bf16_mfma(GemmBatch batch) {
             v[3] += __uint_as_float(rw.y & 0xffff0000u);
           }
         } else {
-          const int bb = m / hs, i = m % hs;
-          off = (((int64_t)bb * (N / 64) + n / 64) * hs + i) * 64 + (n & 63);
+          // (a lane's four columns n .. n+3 lie in one head: n is a multiple of 4 and the width of 32 or more)
+          const int bb = m / hs, i = m % hs, hsh = P.head_shift;
+          off = ((((int64_t)bb * (N >> hsh) + (n >> hsh)) * hs + i) << hsh) + (n & ((1 << hsh) - 1));
         }
         *reinterpret_cast<uint2*>(C + off) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
       }

@@ -60,8 +60,9 @@ hipError_t launch_attn_bwd_bf16(const BwdArgs& a, hipStream_t stream);  // pre-p
 hipError_t launch_attn_bwd_f32(const BwdArgs& a, hipStream_t stream);
 
 // C = A[M,K] * W[K,N] in bf16 with fp32 accumulation, up to three independent problems in one launch.
-// Row-major C (ldc = N) when head_seq == 0; otherwise "head-major": column n of row m goes to
-// C[((m / head_seq) * (N / 64) + n / 64) * head_seq + m % head_seq][n % 64], i.e. [B, N/64, head_seq, 64].
+// Row-major C (ldc = N) when head_seq == 0; otherwise "head-major" with heads of w = 2^head_shift columns (w in
+// {32, 64, 128}): column n of row m goes to C[((m / head_seq) * (N / w) + n / w) * head_seq + m % head_seq][n % w],
+// i.e. [B, N/w, head_seq, w].
 // Optional row-major epilogue (head_seq == 0 only): v = acc + bias[n]; if relu: v = max(v, 0); v += residual[m][n];
 // then rounded to bf16. bias [N] and residual [M, N] are bf16; nullptr skips the step.
 struct GemmProblem {
@@ -73,6 +74,7 @@ struct GemmProblem {
   const void* bias;
   const void* residual;
   int relu;
+  int head_shift;  // head-major only: log2 of the head width
 };
 hipError_t launch_gemm_bf16(const GemmProblem* probs, int nprobs, hipStream_t stream);
 
