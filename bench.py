@@ -39,7 +39,7 @@ METRIC_PADDED = "attention TFLOP/s over real keys (4·h·n_q·Σ_b kv_len[b]·d_
 METRIC_ENC = "encoder layer TFLOP/s (projections, attention, W^O, FFN) at d_model=512,h=8,d_ff=2048; % of bf16 MFMA peak"
 METRIC_MHA = ("multi-head attention TFLOP/s (Q/K/V projections + attention + W^O) at d_model={d_model},h={h}; % of bf16 "
               "MFMA peak")
-METRIC_BWD = "attention backward TFLOP/s (10·B·h·n_q·n_k·d_k) at h=8,d_k=64; % of bf16 MFMA peak"
+METRIC_BWD = "attention backward TFLOP/s (10·B·h·n_q·n_k·d_k) at h={h},d_k={d_k}; % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
 PROFILES = ROOT / "profiles"
@@ -212,8 +212,8 @@ def bench_backward(args, w, x, m, dev):
     mask = "causal" if w["causal"] else "none"
     out, lse = m.sdpa_forward_lse(q, k, v, mask=mask)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(m.sdpa_backward_workspace_size(w["B"], w["h"], w["n_q"], w["n_k"]), dtype=torch.uint8,
-                     device="cuda")
+    ws = torch.empty(m.sdpa_backward_workspace_size(w["B"], w["h"], w["n_q"], w["n_k"], w["d_k"], w["d_v"]),
+                     dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
     def step():
@@ -243,7 +243,7 @@ def bench_backward(args, w, x, m, dev):
     value = flops_metric_bwd(w) / (ms * 1e-3) / 1e12
     achieved = flops_algorithmic_bwd(w) / (ms * 1e-3) / 1e12
     return {
-        "metric": METRIC_BWD, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "metric": METRIC_BWD.format(h=w["h"], d_k=w["d_k"]), "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w["dtype"], "data": "synthetic (seeded N(0,1) Q/K/V/dO, no dataset)",
         "config": {"workload": args.workload, "B": w["B"], "h": w["h"], "n_q": w["n_q"], "n_k": w["n_k"],

@@ -122,7 +122,7 @@ int sdpa_forward_window(const void* Q, const void* K, const void* V, int64_t win
  *              caller (it holds per-row lse and D between the three launches).
  *   dtype: ATTN_BF16 (bf16 tensors, float32 accumulation, P and dS rounded to bf16 where they enter the matrix core,
  *          outputs rounded to nearest even) or ATTN_F32 (float32 throughout). lse is float32 in both.
- *   Requirements as sdpa_forward, but d_k = d_v = 64 only (ATTN_ERR_UNSUPPORTED otherwise). dQ, dK, dV and the
+ *   Requirements as sdpa_forward, but d_k = d_v in {32, 64} (ATTN_ERR_UNSUPPORTED otherwise). dQ, dK, dV and the
  *   workspace must not overlap each other or any input. Every element of dQ, dK and dV is written. */
 int sdpa_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse,
                   const int32_t* kv_len, int64_t window, int mask_kind, void* dQ, void* dK, void* dV, void* workspace,

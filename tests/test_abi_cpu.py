@@ -126,8 +126,8 @@ def bwd(lib, Q=A, K=A * 2, V=A * 3, O=A * 4, dO=A * 5, lse=A * 6, kv_len=None, w
     (dict(dQ=A * 4), INVALID), (dict(dV=A * 200 + 1024), INVALID), (dict(ws=A * 6), INVALID),
     (dict(dK=A * 400), INVALID), (dict(kv_len=A * 7 + 4), INVALID), (dict(kv_len=A * 100 + 64), INVALID),
     (dict(window=3, n_k=32), UNSUPPORTED), (dict(window=3, kv_len=A * 7), UNSUPPORTED),
-    # the backward kernels take d_k = d_v = 64 only
-    (dict(d_k=32, d_v=32), UNSUPPORTED), (dict(d_k=128, d_v=128), UNSUPPORTED),
+    # the backward kernels take d_k = d_v in {32, 64}
+    (dict(d_k=128, d_v=128), UNSUPPORTED), (dict(d_k=48, d_v=48), UNSUPPORTED), (dict(d_k=32, d_v=64), UNSUPPORTED),
 ])
 def test_sdpa_backward_rejects_bad_arguments(lib, kw, code):
     assert bwd(lib, **kw) == code

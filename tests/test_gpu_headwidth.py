@@ -13,7 +13,7 @@ import torch
 
 import transformer_head_scaled_02_amd as m
 import workloads
-from oracle import encoder_layer_ref, mha_ref, sdpa_lse_ref, sdpa_ref
+from oracle import encoder_layer_ref, mha_ref, sdpa_backward_ref, sdpa_lse_ref, sdpa_ref
 from tests._helpers import assert_bf16_parity, assert_f32_parity, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
@@ -167,3 +167,58 @@ def test_headwidth_encoder_layer(B, n, h, causal, kv_len):
     nrms = float(np.sqrt(np.mean(dd * dd)) / np.sqrt(np.mean(ref * ref)))
     assert nrms <= 1e-2 and dd.mean() <= 6e-3 and dd.max() <= 0.1, \
         f"encoder h={h}: max_abs {dd.max():.3g} mean_abs {dd.mean():.3g} nrms {nrms:.3g}"
+
+
+# --- backward at head width 32 (the backward kernels take 32 and 64) ---------------------------------------------
+
+SCALE_FLOOR = 0.05  # as in the d = 64 backward tests: the scale of a gradient that vanishes identically
+
+
+def _check_grads(got, ref, dtype, what):
+    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        g = to_f64(g)
+        assert np.all(np.isfinite(g)), f"{what} {name}: non-finite"
+        dd = np.abs(g - r)
+        rel = float(dd.max()) / max(float(np.abs(r).max()), SCALE_FLOOR)
+        if dtype == "f32":
+            assert rel <= 1e-5, f"{what} {name}: max rel {rel:.3g}"
+        else:
+            nrms = float(np.sqrt(np.mean(dd * dd)) / max(np.sqrt(np.mean(r * r)), SCALE_FLOOR))
+            assert nrms <= 1e-2 and rel <= 1.5e-2, f"{what} {name}: nrms {nrms:.3g} max rel {rel:.3g}"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("n_q,n_k,causal,kv_len,w", [
+    (200, 200, False, None, None), (200, 200, True, None, None), (100, 300, False, None, None),
+    (300, 100, False, None, None), (1, 130, False, None, None), (200, 200, False, [0, 1, 65, 200], None),
+    (200, 200, True, [200, 64, 63, 7], None), (300, 300, False, None, 17), (300, 300, True, None, 100)])
+def test_headwidth32_backward(dtype, n_q, n_k, causal, kv_len, w):
+    B = 4 if kv_len else 2
+    x = workloads.make_sdpa_inputs(B, 2, n_q, n_k, 32, 32, dtype, 9990 + n_q + n_k, dout=True)
+    q, k, v, do = (to_dev(x[nm]) for nm in ("Q", "K", "V", "dO"))
+    lens = None if kv_len is None else torch.tensor(kv_len, dtype=torch.int32, device="cuda")
+    if w is not None:
+        out, lse = m.sdpa_forward_window(q, k, v, w, mask=_mask(causal), return_lse=True)
+    elif lens is not None:
+        out, lse = m.sdpa_forward_padded(q, k, v, lens, mask=_mask(causal), return_lse=True)
+    else:
+        out, lse = m.sdpa_forward_lse(q, k, v, mask=_mask(causal))
+    grads = m.sdpa_backward(q, k, v, out, do, lse, mask=_mask(causal), kv_len=lens, window=w)
+    torch.cuda.synchronize()
+    ref = sdpa_backward_ref(x["Q"].f64, x["K"].f64, x["V"].f64, x["dO"].f64, causal,
+                            kv_len=None if kv_len is None else np.asarray(kv_len), window=w)
+    _check_grads(grads, ref, dtype, f"d=32 backward {dtype} {n_q}x{n_k} causal={causal} kv={kv_len} w={w}")
+
+
+def test_headwidth32_backward_long_sampled():
+    # n = 4096 with 16 heads of 32 (the bench tensors plus an upstream gradient); the oracle checks two heads
+    w = workloads.WORKLOADS["sdpa_bf16_b4_h16_n4096_d32"]
+    x = workloads.make_sdpa_inputs(w["B"], w["h"], w["n_q"], w["n_k"], 32, 32, "bf16", w["seed"], dout=True)
+    q, k, v, do = (to_dev(x[nm]) for nm in ("Q", "K", "V", "dO"))
+    out, lse = m.sdpa_forward_lse(q, k, v)
+    grads = m.sdpa_backward(q, k, v, out, do, lse)
+    torch.cuda.synchronize()
+    for b, hh in ((0, 0), (w["B"] - 1, w["h"] - 1)):
+        ins = [x[nm].f64[b:b + 1, hh:hh + 1] for nm in ("Q", "K", "V", "dO")]
+        ref = [r[0, 0] for r in sdpa_backward_ref(*ins)]
+        _check_grads([g[b, hh] for g in grads], ref, "bf16", f"d=32 n=4096 backward b={b} h={hh}")

@@ -229,8 +229,8 @@ def sdpa_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.
                   dv: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
                   kv_len: torch.Tensor | None = None, window: int | None = None):
     """Gradients (dq, dk, dv) of attention given the forward's output `out`, its `lse` (from sdpa_forward_lse, or
-    sdpa_forward_padded with the same `kv_len`) and the upstream gradient `dout` [B,h,n_q,64]. `workspace` (uint8,
-    at least sdpa_backward_workspace_size bytes) may be passed in to avoid an allocation."""
+    sdpa_forward_padded with the same `kv_len`) and the upstream gradient `dout` [B,h,n_q,d], d in {32, 64}.
+    `workspace` (uint8, at least sdpa_backward_workspace_size bytes) may be passed in to avoid an allocation."""
     lib = load_library()
     q, k, v, (B, h, n_q, n_k, d_k, d_v) = _sdpa_shapes(q, k, v)
     out, dout, lse = _dev_tensor(out, "out"), _dev_tensor(dout, "dout"), _dev_tensor(lse, "lse")

@@ -138,10 +138,10 @@ int check_sdpa_sizes(const char* fn, int dtype, int mask_kind, int64_t B, int64_
     return fail_status(ATTN_ERR_INVALID, "%s: sizes must be positive (B=%lld h=%lld n_q=%lld n_k=%lld d_k=%lld "
                        "d_v=%lld)", fn, (long long)B, (long long)h, (long long)n_q, (long long)n_k, (long long)d_k,
                        (long long)d_v);
-  // the forward kernels take d_k = d_v in {32, 64, 128}; the backward kernels d_k = d_v = 64
-  if (d_k != d_v || (backward ? d_k != 64 : (d_k != 32 && d_k != 64 && d_k != 128)))
+  // the forward kernels take d_k = d_v in {32, 64, 128}; the backward kernels d_k = d_v in {32, 64}
+  if (d_k != d_v || (d_k != 32 && d_k != 64 && (backward || d_k != 128)))
     return fail_status(ATTN_ERR_UNSUPPORTED, "%s: head dims d_k=%lld d_v=%lld (implemented: %s)", fn, (long long)d_k,
-                       (long long)d_v, backward ? "64" : "d_k = d_v in {32, 64, 128}");
+                       (long long)d_v, backward ? "d_k = d_v in {32, 64}" : "d_k = d_v in {32, 64, 128}");
   if (mask_kind == ATTN_MASK_CAUSAL && n_q != n_k)
     return fail_status(ATTN_ERR_UNSUPPORTED, "%s: causal mask needs n_q == n_k (got %lld, %lld)", fn,
                        (long long)n_q, (long long)n_k);
@@ -241,7 +241,7 @@ ATTN_EXPORT int sdpa_forward_lse(const void* Q, const void* K, const void* V, in
 ATTN_EXPORT size_t sdpa_backward_workspace_size(int dtype, int64_t B, int64_t h, int64_t n_q, int64_t n_k,
                                                 int64_t d_k, int64_t d_v) {
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return 0;
-  if (B <= 0 || h <= 0 || n_q <= 0 || n_k <= 0 || d_k != 64 || d_v != 64) return 0;
+  if (B <= 0 || h <= 0 || n_q <= 0 || n_k <= 0 || d_k != d_v || (d_k != 32 && d_k != 64)) return 0;
   if (n_q > ATTN_MAX_SEQ || n_k > ATTN_MAX_SEQ || B > ATTN_MAX_HEADS || h > ATTN_MAX_HEADS || B * h > ATTN_MAX_HEADS)
     return 0;
   return bwd_workspace_bytes(B, h, n_q);
@@ -268,7 +268,7 @@ ATTN_EXPORT int sdpa_backward(const void* Q, const void* K, const void* V, const
   for (const void* p : ptrs)
     if (!aligned16(p)) return fail_status(ATTN_ERR_INVALID, "%s: pointers must be 16-byte aligned", fn);
   const size_t es = dtype == ATTN_BF16 ? 2 : 4;
-  const size_t q_b = (size_t)B * h * n_q * 64 * es, kv_b = (size_t)B * h * n_k * 64 * es;
+  const size_t q_b = (size_t)B * h * n_q * d_k * es, kv_b = (size_t)B * h * n_k * d_k * es;
   const size_t lse_b = (size_t)B * h * n_q * 4;
   const void* ins[] = {Q, K, V, O, dO, lse, kv_len};
   const size_t in_b[] = {q_b, kv_b, kv_b, q_b, q_b, lse_b, kv_len ? (size_t)B * 4 : 0};
@@ -295,7 +295,8 @@ ATTN_EXPORT int sdpa_backward(const void* Q, const void* K, const void* V, const
     a.window = (int)(window < n_k ? window : n_k);
   }
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e = dtype == ATTN_BF16 ? mi355::launch_attn_bwd_bf16(a, s) : mi355::launch_attn_bwd_f32(a, s);
+  const hipError_t e = dtype == ATTN_BF16 ? mi355::launch_attn_bwd_bf16(a, (int)d_k, s)
+                                          : mi355::launch_attn_bwd_f32(a, (int)d_k, s);
   if (e != hipSuccess) return fail_status(ATTN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ATTN_OK;
 }

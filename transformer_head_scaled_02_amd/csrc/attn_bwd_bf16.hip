@@ -1,12 +1,12 @@
-// Backward pass of scaled dot-product attention, bf16 in/out, d_k = d_v = 64, for gfx950 (MI355X).
+// Backward pass of scaled dot-product attention, bf16 in/out, d_k = d_v = D in {32, 64}, for gfx950 (MI355X).
 //
 // The forward pass is O = P V with P = softmax(Q K^T / sqrt(64)) row by row ("Attention Is All You Need", lettle.cn
 // translation, section 3.2.1, equation Attention(Q,K,V)); training carries the loss back through it by the chain
 // rule ("Transformer：抛弃循环与卷积的序列建模", jiashun-ye.github.io, section "训练样本", subsection "反向传播").
 // Given Q, K, V, the forward output O, the forward's row log-sum-exp lse and the upstream gradient dO:
-//   P  = exp(Q K^T / 8 - lse)            (recomputed tile by tile from the saved lse, never stored)
-//   dV = P^T dO,   dP = dO V^T,   dS = P o (dP - D) with D_i = dO_i . O_i = sum_j P_ij dP_ij,
-//   dQ = dS K / 8,   dK = dS^T Q / 8.
+//   P  = exp(Q K^T / sqrt(D) - lse)      (recomputed tile by tile from the saved lse, never stored)
+//   dV = P^T dO,   dP = dO V^T,   dS = P o (dP - Dg) with Dg_i = dO_i . O_i = sum_j P_ij dP_ij,
+//   dQ = dS K / sqrt(D),   dK = dS^T Q / sqrt(D).
 // Masked weights (causal: key after query) are exactly 0 and pass no gradient. fp32 accumulation throughout; P and
 // dS are rounded to bf16 where they enter the matrix core; outputs are rounded to bf16 (nearest even).
 //
@@ -38,46 +38,59 @@ namespace {
 
 constexpr int kAuxElems = kAuxFloatsPerTile * 2;            // one tile's lse/D block in 16-bit LDS elements (1 KB)
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kInvSqrtD = 0.125f;                         // 1 / sqrt(64), exact
+
+// 1 / sqrt(D), the scale of dQ and dK (exact for D = 64)
+template <int D>
+constexpr float inv_sqrt_d() {
+  static_assert(D == 32 || D == 64, "head width of the backward kernels");
+  return D == 64 ? 0.125f : (float)(1.0 / 5.656854249492381);
+}
 
 // LDS element offset of lane (li, g)'s operand row read in k-step ks: row li of a 32-row block, logical 16-byte
-// chunk 4g + ks (the d order every product here uses: k-step ks holds d = 8(4g + ks) .. +7 of lane group g).
-__device__ __forceinline__ int row_off(int li, int g, int ks) { return li * kD + (((4 * g + ks) ^ swz(li)) << 3); }
+// chunk (D/16)g + ks (the d order every product here uses: k-step ks holds d = 8((D/16)g + ks) .. +7 of lane group g).
+template <int D>
+__device__ __forceinline__ int row_off(int li, int g, int ks) {
+  return li * D + ((((D / 16) * g + ks) ^ swz_d<D>(li)) << 3);
+}
 
 // Offsets of the two transposed reads that give the A operand of a product contracting over the 64 rows of an LDS
 // tile: for output rows 32mb + (0..31) (tile columns) and k-step ks, lane l needs tile rows 16ks + 4g + (0..3) and
 // 16ks + 8 + 4g + (0..3) of column 32mb + l%32, which is the k order of a 32x32 accumulator's registers 8(ks%2) ..
 // +7 read as a B operand.
+template <int D>
 __device__ __forceinline__ int tr_off(int lane, int mb, int hi) {
   const int g = lane >> 5, jj = (lane & 15) >> 2;
   const int row = 4 * g + jj + 8 * hi;
   const int lchunk = 4 * mb + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-  return row * kD + ((lchunk ^ swz(row)) << 3) + 4 * (lane & 1);
+  return row * D + ((lchunk ^ swz_d<D>(row)) << 3) + 4 * (lane & 1);
 }
-__device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, int ks, const int (&off)[2][2], int mb) {
-  const bf16x4 lo = lds_read_tr16x4(tile + ks * 16 * kD + off[mb][0]);
-  const bf16x4 hi = lds_read_tr16x4(tile + ks * 16 * kD + off[mb][1]);
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, int ks, const int (&off)[D / 32][2], int mb) {
+  const bf16x4 lo = lds_read_tr16x4(tile + ks * 16 * D + off[mb][0]);
+  const bf16x4 hi = lds_read_tr16x4(tile + ks * 16 * D + off[mb][1]);
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 __device__ __forceinline__ void settle_f(float& v) { asm volatile("" : "+v"(v)); }
 
-// Copies of one ring stage: 64 rows of tensor `ta` (first 8 KB of the stage) and of `tb` (next 8 KB), each wave
-// moving 16/NW of the 16 one-kilobyte pieces; rows at or past `rows_left` read row rows_left-1 instead. Copy gi
-// moves rows 8(gi%8) .. +7; lane l brings the logical chunk that belongs at physical chunk l%8 of row 8(gi%8) + l/8
-// (the XOR swizzle of swz()). Two per-lane offsets (rows l/8 and 8 + l/8, which carry the swizzle of every row
-// congruent to them mod 16) serve every copy; the rest of the row offset goes into the scalar base.
-template <int NW>
+// Copies of one ring stage: 64 rows of D elements of tensor `ta` (the first 128 D bytes of the stage) and of `tb`
+// (the next), each wave moving its share of the 2 D/8 one-kilobyte pieces; rows at or past `rows_left` read row
+// rows_left-1 instead. Copy gi moves R = 512/D rows from row R (gi mod D/8); lane l brings the logical chunk that
+// belongs at physical chunk l mod D/8 of its row (the XOR swizzle of swz_d). D/32 per-lane offsets (one per copy of
+// a 16-row swizzle period) serve every copy; the rest of the row offset goes into the scalar base.
+template <int NW, int D>
 __device__ __forceinline__ void issue_rows(const uint16_t* ta, const uint16_t* tb, int rows_left, uint32_t stage,
-                                           int wave, int lrow, const uint32_t (&ld_voff)[2]) {
-  constexpr int kLPW = 16 / NW;
+                                           int wave, int lrow, const uint32_t (&ld_voff)[D / 32]) {
+  constexpr int kCPT = D / 8, kRPC = 512 / D, kNOff = D / 32, kTileElemsD = kBN * D;
+  constexpr int kLPW = 2 * kCPT / NW;
+  static_assert((2 * kCPT) % NW == 0 && kLPW % kNOff == 0, "copies split evenly over the waves");
   if (rows_left >= kBN) {
 #pragma unroll
     for (int i = 0; i < kLPW; ++i) {
       const int gi = wave * kLPW + i;
-      const int c = gi & 7;
-      lds_dma16((gi < 8 ? ta : tb) + (c >> 1) * 16 * kD, ld_voff[c & 1],
-                stage + (gi < 8 ? 0u : kTileElems * 2u) + (uint32_t)c * 1024u);
+      const int c = gi & (kCPT - 1);
+      lds_dma16((gi < kCPT ? ta : tb) + (c / kNOff) * 16 * D, ld_voff[c & (kNOff - 1)],
+                stage + (gi < kCPT ? 0u : kTileElemsD * 2u) + (uint32_t)c * 1024u);
     }
   } else {
     // from the unshifted tile base: lane offset = row min(row, last) with the swizzle of destination row `row` (the
@@ -88,10 +101,11 @@ __device__ __forceinline__ void issue_rows(const uint16_t* ta, const uint16_t* t
 #pragma unroll
     for (int i = 0; i < kLPW; ++i) {
       const int gi = wave * kLPW + i;
-      const int c = gi & 7;
-      const int row = 8 * c + lr;
-      lds_dma16(gi < 8 ? ta : tb, ld_voff[c & 1] + (uint32_t)((min(row, last) - (8 * (c & 1) + lr)) * kD * 2),
-                stage + (gi < 8 ? 0u : kTileElems * 2u) + (uint32_t)c * 1024u);
+      const int c = gi & (kCPT - 1);
+      const int row = kRPC * c + lr;
+      lds_dma16(gi < kCPT ? ta : tb,
+                ld_voff[c & (kNOff - 1)] + (uint32_t)((min(row, last) - (kRPC * (c & (kNOff - 1)) + lr)) * D * 2),
+                stage + (gi < kCPT ? 0u : kTileElemsD * 2u) + (uint32_t)c * 1024u);
     }
   }
 }
@@ -105,8 +119,8 @@ __device__ __forceinline__ void wait_copies(int ahead) {
   else wait_vmcnt<0>();
 }
 
-// D_i = dO_i . O_i and log2(e) * lse_i for one 64-row query tile of one head; 4 threads per row.
-template <class T>
+// D_i = dO_i . O_i and log2(e) * lse_i for one 64-row query tile of one head (rows of D elements); 4 threads per row.
+template <class T, int D>
 __global__ __launch_bounds__(256) void attn_bwd_pre(BwdArgs a, int n_tiles) {
   const int bh = blockIdx.x / n_tiles, t = blockIdx.x % n_tiles;
   const int r = threadIdx.x >> 2, part = threadIdx.x & 3;
@@ -114,12 +128,12 @@ __global__ __launch_bounds__(256) void attn_bwd_pre(BwdArgs a, int n_tiles) {
   const int row = t * kBN + r;
   float dot = 0.f;
   if (row < n_q) {
-    const int64_t base = ((int64_t)bh * n_q + row) * kD + 16 * part;
+    const int64_t base = ((int64_t)bh * n_q + row) * D + (D / 4) * part;
     if constexpr (sizeof(T) == 2) {
       const uint4* o = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.O) + base);
       const uint4* d = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.dO) + base);
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
+      for (int c = 0; c < D / 32; ++c) {
         const uint4 ov = o[c], dv = d[c];
         const uint32_t ow[4] = {ov.x, ov.y, ov.z, ov.w}, dw[4] = {dv.x, dv.y, dv.z, dv.w};
 #pragma unroll
@@ -132,7 +146,7 @@ __global__ __launch_bounds__(256) void attn_bwd_pre(BwdArgs a, int n_tiles) {
       const float4* o = reinterpret_cast<const float4*>(static_cast<const float*>(a.O) + base);
       const float4* d = reinterpret_cast<const float4*>(static_cast<const float*>(a.dO) + base);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      for (int c = 0; c < D / 16; ++c) {
         const float4 ov = o[c], dv = d[c];
         dot = fmaf(ov.x, dv.x, dot);
         dot = fmaf(ov.y, dv.y, dot);
@@ -154,12 +168,16 @@ __global__ __launch_bounds__(256) void attn_bwd_pre(BwdArgs a, int n_tiles) {
 }
 
 // dK and dV: see the file comment (launch 2).
-template <int NW, int kStages, bool WIN>
+template <int D, int NW, int kStages, bool WIN>
 __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16(BwdArgs a, int n_kblocks) {
+  constexpr int kD = D;                           // (shadows the 64 of the shared tile header)
+  constexpr int kTileElems = kBN * D;             // one 64-row tile of D elements
+  constexpr int kKS = D / 16, kMB = D / 32;       // k-steps over d; 32-wide blocks of d
+  constexpr int kCPT = D / 8, kRPC = 512 / D, kNOff = D / 32;  // tile copies: per tensor, rows each, offsets
   constexpr int kBK = 32 * NW;                    // keys per workgroup
-  constexpr int kLPW = 16 / NW;                   // Q/dO copies per wave per tile (wave 0 also copies lse/D)
+  constexpr int kLPW = 2 * kCPT / NW;             // Q/dO copies per wave per tile (wave 0 also copies lse/D)
   constexpr int kStageElems = 2 * kTileElems + kAuxElems;
-  static_assert(16 % NW == 0, "tile copies split evenly over the waves");
+  static_assert((2 * kCPT) % NW == 0, "tile copies split evenly over the waves");
   __shared__ __attribute__((aligned(16))) uint16_t smem[kStages * kStageElems];  // [stage][Q | dO | lse, D]
 
   const int tid = threadIdx.x;
@@ -193,15 +211,15 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16(BwdArgs a, int 
   const bool wave_real = kw0 < n_real;  // (uniform) the wave has at least one real key
 
   // K and V rows as B operands of S = Q K^T and dP = dO V^T: lane supplies row `key`, d = 8(4g + ks) .. +7.
-  bf16x8 kf[4], vf[4];
+  bf16x8 kf[kKS], vf[kKS];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    const int64_t off = (int64_t)key * kD + 8 * (4 * g + ks);
+  for (int ks = 0; ks < kKS; ++ks) {
+    const int64_t off = (int64_t)key * kD + 8 * ((kD / 16) * g + ks);
     kf[ks] = key < n_real ? *reinterpret_cast<const bf16x8*>(Kp + off) : bf16x8{};
     vf[ks] = key < n_real ? *reinterpret_cast<const bf16x8*>(Vp + off) : bf16x8{};
   }
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
+  for (int ks = 0; ks < kKS; ++ks) {
     settle(kf[ks]);
     settle(vf[ks]);
   }
@@ -226,31 +244,32 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16(BwdArgs a, int 
   const int lo_off = win ? -wr : -(1 << 30);
 
   const uint32_t smem_lds = (uint32_t)(uintptr_t)smem;
-  const int lrow = lane >> 3;
-  uint32_t ld_voff[2];
+  const int lrow = lane / kCPT;
+  uint32_t ld_voff[kNOff];
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const int row = 8 * c + lrow;
-    ld_voff[c] = (uint32_t)(row * kD + (((lane & 7) ^ swz(row)) << 3)) * 2u;
+  for (int c = 0; c < kNOff; ++c) {
+    const int row = kRPC * c + lrow;
+    ld_voff[c] = (uint32_t)(row * kD + (((lane % kCPT) ^ swz_d<D>(row)) << 3)) * 2u;
   }
   auto issue = [&](int t) __attribute__((always_inline)) {
     const uint32_t stage = smem_lds + (uint32_t)(((t - t0) % kStages) * kStageElems * 2);
-    issue_rows<NW>(Qp + (int64_t)t * kBN * kD, dOp + (int64_t)t * kBN * kD, n_q - t * kBN, stage, wave, lrow,
+    issue_rows<NW, D>(Qp + (int64_t)t * kBN * kD, dOp + (int64_t)t * kBN * kD, n_q - t * kBN, stage, wave, lrow,
                    ld_voff);
     if (wave == 0) lds_dma16(auxp + (int64_t)t * kAuxFloatsPerTile, (uint32_t)lane * 16u, stage + kTileElems * 4u);
   };
 
-  int roff[4];
+  int roff[kKS];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) roff[ks] = row_off(li, g, ks);
-  int toff[2][2];
+  for (int ks = 0; ks < kKS; ++ks) roff[ks] = row_off<D>(li, g, ks);
+  int toff[kMB][2];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
-    for (int hi = 0; hi < 2; ++hi) toff[mb][hi] = tr_off(lane, mb, hi);
+    for (int hi = 0; hi < 2; ++hi) toff[mb][hi] = tr_off<D>(lane, mb, hi);
 
-  f32x16 dv[2], dk[2];
-  dv[0] = dv[1] = dk[0] = dk[1] = f32x16{};
+  f32x16 dv[kMB], dk[kMB];
+#pragma unroll
+  for (int mb = 0; mb < kMB; ++mb) dv[mb] = dk[mb] = f32x16{};
 
   // a workgroup of padding keys only writes zeros
   int nt = k_blk0 < n_real ? n_tiles : 0;
@@ -275,10 +294,10 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16(BwdArgs a, int 
     for (int mq = 0; mq < 2; ++mq) {
       f32x16 s = {}, dp = {};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
+      for (int ks = 0; ks < kKS; ++ks)
         s = mfma32x32x16(*reinterpret_cast<const bf16x8*>(st + mq * 32 * kD + roff[ks]), kf[ks], s);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
+      for (int ks = 0; ks < kKS; ++ks)
         dp = mfma32x32x16(*reinterpret_cast<const bf16x8*>(st + kTileElems + mq * 32 * kD + roff[ks]), vf[ks], dp);
       // register r holds query row 32mq + 8(r/4) + 4g + r%4 of the tile: its lse and D come in fours
       f32x4 lq[4], dq[4];
@@ -295,7 +314,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16(BwdArgs a, int 
         float sv = s[r];
         // key - row = base - (8(r/4) + r%4); allowed when lo_off <= key - row <= hi_off
         if (masked && (8 * (r >> 2) + (r & 3) < ub || (WIN && 8 * (r >> 2) + (r & 3) > lb))) sv = -INFINITY;
-        p[r] = fast_exp2(__builtin_fmaf(sv, kScaleLog2, -lq[r >> 2][r & 3]));
+        p[r] = fast_exp2(__builtin_fmaf(sv, scale_log2<D>(), -lq[r >> 2][r & 3]));
         ds[r] = p[r] * (dp[r] - dq[r >> 2][r & 3]);
       }
 #pragma unroll
@@ -314,29 +333,29 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16(BwdArgs a, int 
 #pragma unroll
     for (int kq = 0; kq < 4; ++kq)
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        dv[mb] = mfma32x32x16(tr_operand(st + kTileElems, kq, toff, mb), pp[kq], dv[mb]);
-        dk[mb] = mfma32x32x16(tr_operand(st, kq, toff, mb), ps[kq], dk[mb]);
+      for (int mb = 0; mb < kMB; ++mb) {
+        dv[mb] = mfma32x32x16(tr_operand<D>(st + kTileElems, kq, toff, mb), pp[kq], dv[mb]);
+        dk[mb] = mfma32x32x16(tr_operand<D>(st, kq, toff, mb), ps[kq], dk[mb]);
       }
   }
 
   // lane holds d = 32mb + 8(r/4) + 4g + r%4 of its key's dV and dK rows; padding keys get 0
   if (key >= n_real) {
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) dv[mb] = dk[mb] = f32x16{};
+    for (int mb = 0; mb < kMB; ++mb) dv[mb] = dk[mb] = f32x16{};
   }
   if (key < n_k) {
     uint16_t* dvrow = static_cast<uint16_t*>(a.dV) + ((int64_t)bh * n_k + key) * kD;
     uint16_t* dkrow = static_cast<uint16_t*>(a.dK) + ((int64_t)bh * n_k + key) * kD;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         const int d = 32 * mb + 8 * rg + 4 * g;
         const uint2 wv = {pack_bf16x2(dv[mb][4 * rg], dv[mb][4 * rg + 1]),
                           pack_bf16x2(dv[mb][4 * rg + 2], dv[mb][4 * rg + 3])};
-        const uint2 wk = {pack_bf16x2(dk[mb][4 * rg] * kInvSqrtD, dk[mb][4 * rg + 1] * kInvSqrtD),
-                          pack_bf16x2(dk[mb][4 * rg + 2] * kInvSqrtD, dk[mb][4 * rg + 3] * kInvSqrtD)};
+        const uint2 wk = {pack_bf16x2(dk[mb][4 * rg] * inv_sqrt_d<D>(), dk[mb][4 * rg + 1] * inv_sqrt_d<D>()),
+                          pack_bf16x2(dk[mb][4 * rg + 2] * inv_sqrt_d<D>(), dk[mb][4 * rg + 3] * inv_sqrt_d<D>())};
         *reinterpret_cast<uint2*>(dvrow + d) = wv;
         *reinterpret_cast<uint2*>(dkrow + d) = wk;
       }
@@ -344,10 +363,14 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16(BwdArgs a, int 
 }
 
 // dQ: see the file comment (launch 3).
-template <int NW, int kStages, bool WIN>
+template <int D, int NW, int kStages, bool WIN>
 __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dq_bf16(BwdArgs a, int n_qblocks) {
+  constexpr int kD = D;                           // (shadows the 64 of the shared tile header)
+  constexpr int kTileElems = kBN * D;             // one 64-row tile of D elements
+  constexpr int kKS = D / 16, kMB = D / 32;       // k-steps over d; 32-wide blocks of d
+  constexpr int kCPT = D / 8, kRPC = 512 / D, kNOff = D / 32;  // tile copies: per tensor, rows each, offsets
   constexpr int kBM = 32 * NW;  // queries per workgroup
-  static_assert(16 % NW == 0, "tile copies split evenly over the waves");
+  static_assert((2 * kCPT) % NW == 0, "tile copies split evenly over the waves");
   __shared__ __attribute__((aligned(16))) uint16_t smem[kStages * 2 * kTileElems];  // [stage][K | V]
 
   const int tid = threadIdx.x;
@@ -381,10 +404,10 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dq_bf16(BwdArgs a, int n_
   const int q = qw0 + li;
 
   // Q and dO rows as B operands of S^T = K Q^T and dP^T = V dO^T (d = 8(4g + ks) .. +7); zero past n_q
-  bf16x8 qf[4], df[4];
+  bf16x8 qf[kKS], df[kKS];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    const int64_t off = (int64_t)q * kD + 8 * (4 * g + ks);
+  for (int ks = 0; ks < kKS; ++ks) {
+    const int64_t off = (int64_t)q * kD + 8 * ((kD / 16) * g + ks);
     qf[ks] = q < n_q ? *reinterpret_cast<const bf16x8*>(Qp + off) : bf16x8{};
     df[ks] = q < n_q ? *reinterpret_cast<const bf16x8*>(dOp + off) : bf16x8{};
   }
@@ -395,7 +418,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dq_bf16(BwdArgs a, int n_
     dq_d = at[kBN + q % kBN];
   }
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
+  for (int ks = 0; ks < kKS; ++ks) {
     settle(qf[ks]);
     settle(df[ks]);
   }
@@ -423,31 +446,32 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dq_bf16(BwdArgs a, int n_
   }
 
   const uint32_t smem_lds = (uint32_t)(uintptr_t)smem;
-  const int lrow = lane >> 3;
-  uint32_t ld_voff[2];
+  const int lrow = lane / kCPT;
+  uint32_t ld_voff[kNOff];
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const int row = 8 * c + lrow;
-    ld_voff[c] = (uint32_t)(row * kD + (((lane & 7) ^ swz(row)) << 3)) * 2u;
+  for (int c = 0; c < kNOff; ++c) {
+    const int row = kRPC * c + lrow;
+    ld_voff[c] = (uint32_t)(row * kD + (((lane % kCPT) ^ swz_d<D>(row)) << 3)) * 2u;
   }
   auto issue = [&](int t) __attribute__((always_inline)) {
     const uint32_t stage = smem_lds + (uint32_t)((t % kStages) * 2 * kTileElems * 2);
-    issue_rows<NW>(Kp + (int64_t)t * kBN * kD, Vp + (int64_t)t * kBN * kD, n_k - t * kBN, stage, wave, lrow, ld_voff);
+    issue_rows<NW, D>(Kp + (int64_t)t * kBN * kD, Vp + (int64_t)t * kBN * kD, n_k - t * kBN, stage, wave, lrow, ld_voff);
   };
 
-  int roff[4];
+  int roff[kKS];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) roff[ks] = row_off(li, g, ks);
-  int toff[2][2];
+  for (int ks = 0; ks < kKS; ++ks) roff[ks] = row_off<D>(li, g, ks);
+  int toff[kMB][2];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
-    for (int hi = 0; hi < 2; ++hi) toff[mb][hi] = tr_off(lane, mb, hi);
+    for (int hi = 0; hi < 2; ++hi) toff[mb][hi] = tr_off<D>(lane, mb, hi);
 
-  f32x16 dq[2];
-  dq[0] = dq[1] = f32x16{};
+  f32x16 dq[kMB];
+#pragma unroll
+  for (int mb = 0; mb < kMB; ++mb) dq[mb] = f32x16{};
 
-  constexpr int kLPW = 16 / NW;
+  constexpr int kLPW = 2 * kCPT / NW;
 #pragma unroll
   for (int i = 0; i < kStages - 1; ++i)
     if (t_begin + i < nt) issue(t_begin + i);
@@ -465,10 +489,10 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dq_bf16(BwdArgs a, int n_
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = dp[kb] = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
+      for (int ks = 0; ks < kKS; ++ks)
         s[kb] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(st + kb * 32 * kD + roff[ks]), qf[ks], s[kb]);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
+      for (int ks = 0; ks < kKS; ++ks)
         dp[kb] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(st + kTileElems + kb * 32 * kD + roff[ks]), df[ks],
                               dp[kb]);
     }
@@ -488,25 +512,25 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dq_bf16(BwdArgs a, int n_
       uint32_t w[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float p0 = fast_exp2(__builtin_fmaf(s[kb][base + 2 * j], kScaleLog2, -lse2));
-        const float p1 = fast_exp2(__builtin_fmaf(s[kb][base + 2 * j + 1], kScaleLog2, -lse2));
+        const float p0 = fast_exp2(__builtin_fmaf(s[kb][base + 2 * j], scale_log2<D>(), -lse2));
+        const float p1 = fast_exp2(__builtin_fmaf(s[kb][base + 2 * j + 1], scale_log2<D>(), -lse2));
         w[j] = pack_bf16x2(p0 * (dp[kb][base + 2 * j] - dq_d), p1 * (dp[kb][base + 2 * j + 1] - dq_d));
       }
       const bf16x8 pds = __builtin_bit_cast(bf16x8, (uint4){w[0], w[1], w[2], w[3]});
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) dq[mb] = mfma32x32x16(tr_operand(st, ks, toff, mb), pds, dq[mb]);
+      for (int mb = 0; mb < kMB; ++mb) dq[mb] = mfma32x32x16(tr_operand<D>(st, ks, toff, mb), pds, dq[mb]);
     }
   }
 
-  // dQ = dQ^T / 8; lane holds d = 32mb + 8(r/4) + 4g + r%4 of its query
+  // dQ = dQ^T / sqrt(D); lane holds d = 32mb + 8(r/4) + 4g + r%4 of its query
   if (q < n_q) {
     uint16_t* row = static_cast<uint16_t*>(a.dQ) + ((int64_t)bh * n_q + q) * kD;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
-        const uint2 w = {pack_bf16x2(dq[mb][4 * rg] * kInvSqrtD, dq[mb][4 * rg + 1] * kInvSqrtD),
-                         pack_bf16x2(dq[mb][4 * rg + 2] * kInvSqrtD, dq[mb][4 * rg + 3] * kInvSqrtD)};
+        const uint2 w = {pack_bf16x2(dq[mb][4 * rg] * inv_sqrt_d<D>(), dq[mb][4 * rg + 1] * inv_sqrt_d<D>()),
+                         pack_bf16x2(dq[mb][4 * rg + 2] * inv_sqrt_d<D>(), dq[mb][4 * rg + 3] * inv_sqrt_d<D>())};
         *reinterpret_cast<uint2*>(row + 32 * mb + 8 * rg + 4 * g) = w;
       }
   }
@@ -516,38 +540,52 @@ bool grid_ok(int64_t n) { return n > 0 && n <= 0x7fffffff; }
 
 }  // namespace
 
-hipError_t launch_attn_bwd_pre(const BwdArgs& a, bool f32, hipStream_t stream) {
+hipError_t launch_attn_bwd_pre(const BwdArgs& a, bool f32, int d, hipStream_t stream) {
   const int n_tiles = (a.n_q + kBN - 1) / kBN;
   const int64_t nb = (int64_t)n_tiles * a.B * a.H;
-  if (!grid_ok(nb)) return hipErrorInvalidValue;
-  if (f32) hipLaunchKernelGGL(attn_bwd_pre<float>, dim3((unsigned)nb), dim3(256), 0, stream, a, n_tiles);
-  else hipLaunchKernelGGL(attn_bwd_pre<uint16_t>, dim3((unsigned)nb), dim3(256), 0, stream, a, n_tiles);
+  if (!grid_ok(nb) || (d != 32 && d != 64)) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)nb);
+  if (f32 && d == 64) hipLaunchKernelGGL((attn_bwd_pre<float, 64>), grid, dim3(256), 0, stream, a, n_tiles);
+  else if (f32) hipLaunchKernelGGL((attn_bwd_pre<float, 32>), grid, dim3(256), 0, stream, a, n_tiles);
+  else if (d == 64) hipLaunchKernelGGL((attn_bwd_pre<uint16_t, 64>), grid, dim3(256), 0, stream, a, n_tiles);
+  else hipLaunchKernelGGL((attn_bwd_pre<uint16_t, 32>), grid, dim3(256), 0, stream, a, n_tiles);
   return hipGetLastError();
 }
 
-hipError_t launch_attn_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
+namespace {
+
+template <int D>
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
   constexpr int NW = 4, kStagesKV = 3, kStagesQ = 3;
   const int n_kblocks = (a.n_k + 32 * NW - 1) / (32 * NW);
   const int n_qblocks = (a.n_q + 32 * NW - 1) / (32 * NW);
   const int64_t nb_kv = (int64_t)n_kblocks * a.B * a.H, nb_q = (int64_t)n_qblocks * a.B * a.H;
   if (!grid_ok(nb_kv) || !grid_ok(nb_q)) return hipErrorInvalidValue;
-  hipError_t e = launch_attn_bwd_pre(a, false, stream);
+  hipError_t e = launch_attn_bwd_pre(a, false, D, stream);
   if (e != hipSuccess) return e;
   if (a.windowed)
-    hipLaunchKernelGGL((attn_bwd_dkdv_bf16<NW, kStagesKV, true>), dim3((unsigned)nb_kv), dim3(64 * NW), 0, stream, a,
-                       n_kblocks);
+    hipLaunchKernelGGL((attn_bwd_dkdv_bf16<D, NW, kStagesKV, true>), dim3((unsigned)nb_kv), dim3(64 * NW), 0, stream,
+                       a, n_kblocks);
   else
-    hipLaunchKernelGGL((attn_bwd_dkdv_bf16<NW, kStagesKV, false>), dim3((unsigned)nb_kv), dim3(64 * NW), 0, stream, a,
-                       n_kblocks);
+    hipLaunchKernelGGL((attn_bwd_dkdv_bf16<D, NW, kStagesKV, false>), dim3((unsigned)nb_kv), dim3(64 * NW), 0, stream,
+                       a, n_kblocks);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.windowed)
-    hipLaunchKernelGGL((attn_bwd_dq_bf16<NW, kStagesQ, true>), dim3((unsigned)nb_q), dim3(64 * NW), 0, stream, a,
+    hipLaunchKernelGGL((attn_bwd_dq_bf16<D, NW, kStagesQ, true>), dim3((unsigned)nb_q), dim3(64 * NW), 0, stream, a,
                        n_qblocks);
   else
-    hipLaunchKernelGGL((attn_bwd_dq_bf16<NW, kStagesQ, false>), dim3((unsigned)nb_q), dim3(64 * NW), 0, stream, a,
+    hipLaunchKernelGGL((attn_bwd_dq_bf16<D, NW, kStagesQ, false>), dim3((unsigned)nb_q), dim3(64 * NW), 0, stream, a,
                        n_qblocks);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd_bf16(const BwdArgs& a, int d, hipStream_t stream) {
+  if (d == 64) return launch_bwd_bf16<64>(a, stream);
+  if (d == 32) return launch_bwd_bf16<32>(a, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace mi355

@@ -1,9 +1,9 @@
-// Backward pass of scaled dot-product attention in fp32 throughout, d_k = d_v = 64, for gfx950.
+// Backward pass of scaled dot-product attention in fp32 throughout, d_k = d_v = D in {32, 64}, for gfx950.
 //
-// Same mathematics as the bf16 backward (the chain rule through O = P V, the row softmax and S = Q K^T / sqrt(64):
+// Same mathematics as the bf16 backward (the chain rule through O = P V, the row softmax and S = Q K^T / sqrt(D):
 // "Transformer：抛弃循环与卷积的序列建模", section "训练样本", subsection "反向传播"; forward definition "Attention Is
 // All You Need", lettle.cn translation, section 3.2.1), with every value in fp32, P and dS included. This path serves
-// small fp32 problems, so it is plain VALU code: two threads per row, each holding one 32-wide half of the row's
+// small fp32 problems, so it is plain VALU code: two threads per row, each holding one D/2-wide half of the row's
 // vectors, partial dot products combined with one lane exchange; the other side's rows are staged in LDS in tiles of
 // 32 and read as broadcasts. The per-row lse and D come from the shared pre-pass (workspace tiles of 64 rows).
 #include <math.h>
@@ -14,11 +14,16 @@
 namespace mi355 {
 namespace {
 
-constexpr int kD = 64;
-constexpr int kHalf = 32;
 constexpr int kRows = 32;  // rows per workgroup (two threads each) and per staged tile
-constexpr float kC = (float)(1.4426950408889634 / 8.0);  // log2(e) / sqrt(64)
-constexpr float kInvSqrtD = 0.125f;
+
+// the width-dependent constants: row width, half row, log2(e) / sqrt(D) and 1 / sqrt(D)
+template <int D>
+struct Width {
+  static_assert(D == 32 || D == 64, "head width of the backward kernels");
+  static constexpr int kD = D, kHalf = D / 2;
+  static constexpr float kC = D == 64 ? (float)(1.4426950408889634 / 8.0) : (float)(1.4426950408889634 / 5.656854249492381);
+  static constexpr float kInvSqrtD = D == 64 ? 0.125f : (float)(1.0 / 5.656854249492381);
+};
 
 // lse2 (= log2(e) * lse) and D of query row i of head bh, from the workspace tiles
 __device__ __forceinline__ float2 aux_row(const float* aux, int n_tiles, int bh, int i) {
@@ -27,7 +32,10 @@ __device__ __forceinline__ float2 aux_row(const float* aux, int n_tiles, int bh,
 }
 
 // dK and dV: a workgroup owns 32 keys; query rows stream through LDS.
+template <int D>
 __global__ __launch_bounds__(2 * kRows) void attn_bwd_dkdv_f32(BwdArgs a) {
+  constexpr int kD = Width<D>::kD, kHalf = Width<D>::kHalf;
+  constexpr float kC = Width<D>::kC, kInvSqrtD = Width<D>::kInvSqrtD;
   __shared__ float Qs[kRows][kD], dOs[kRows][kD], Ls[kRows], Ds[kRows];
   const int tid = threadIdx.x, h = tid & 1;
   const int n_q = a.n_q, n_k = a.n_k, n_tiles = (n_q + 63) / 64;
@@ -102,7 +110,10 @@ __global__ __launch_bounds__(2 * kRows) void attn_bwd_dkdv_f32(BwdArgs a) {
 }
 
 // dQ: a workgroup owns 32 queries; key/value rows stream through LDS.
+template <int D>
 __global__ __launch_bounds__(2 * kRows) void attn_bwd_dq_f32(BwdArgs a) {
+  constexpr int kD = Width<D>::kD, kHalf = Width<D>::kHalf;
+  constexpr float kC = Width<D>::kC, kInvSqrtD = Width<D>::kInvSqrtD;
   __shared__ float Ks[kRows][kD], Vs[kRows][kD];
   const int tid = threadIdx.x, h = tid & 1;
   const int n_q = a.n_q, n_k = a.n_k, n_tiles = (n_q + 63) / 64;
@@ -167,16 +178,19 @@ __global__ __launch_bounds__(2 * kRows) void attn_bwd_dq_f32(BwdArgs a) {
 
 }  // namespace
 
-hipError_t launch_attn_bwd_f32(const BwdArgs& a, hipStream_t stream) {
+hipError_t launch_attn_bwd_f32(const BwdArgs& a, int d, hipStream_t stream) {
   const int64_t nb_kv = (int64_t)((a.n_k + kRows - 1) / kRows) * a.B * a.H;
   const int64_t nb_q = (int64_t)((a.n_q + kRows - 1) / kRows) * a.B * a.H;
-  if (nb_kv <= 0 || nb_kv > 0x7fffffff || nb_q <= 0 || nb_q > 0x7fffffff) return hipErrorInvalidValue;
-  hipError_t e = launch_attn_bwd_pre(a, true, stream);
+  if (nb_kv <= 0 || nb_kv > 0x7fffffff || nb_q <= 0 || nb_q > 0x7fffffff || (d != 32 && d != 64))
+    return hipErrorInvalidValue;
+  hipError_t e = launch_attn_bwd_pre(a, true, d, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_bwd_dkdv_f32, dim3((unsigned)nb_kv), dim3(2 * kRows), 0, stream, a);
+  if (d == 64) hipLaunchKernelGGL(attn_bwd_dkdv_f32<64>, dim3((unsigned)nb_kv), dim3(2 * kRows), 0, stream, a);
+  else hipLaunchKernelGGL(attn_bwd_dkdv_f32<32>, dim3((unsigned)nb_kv), dim3(2 * kRows), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_bwd_dq_f32, dim3((unsigned)nb_q), dim3(2 * kRows), 0, stream, a);
+  if (d == 64) hipLaunchKernelGGL(attn_bwd_dq_f32<64>, dim3((unsigned)nb_q), dim3(2 * kRows), 0, stream, a);
+  else hipLaunchKernelGGL(attn_bwd_dq_f32<32>, dim3((unsigned)nb_q), dim3(2 * kRows), 0, stream, a);
   return hipGetLastError();
 }
 

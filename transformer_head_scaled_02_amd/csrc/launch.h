@@ -30,7 +30,8 @@ struct AttnArgs {
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int d, hipStream_t stream);
 hipError_t launch_attn_fwd_f32(const AttnArgs& a, int d, hipStream_t stream);
 
-// Backward pass of attention over [B, H] heads of width 64, every tensor dense [B, H, n, 64] in the element type.
+// Backward pass of attention over [B, H] heads of width d (32 or 64), every tensor dense [B, H, n, d] in the element
+// type.
 // `aux` is the workspace: per head and per 64-row query tile, 256 floats = [log2(e)*lse of the 64 rows | D of the 64
 // rows | 128 zeros], where D_i = dO_i . O_i; rows past n_q hold lse = +inf and D = 0 (their weights come out 0).
 struct BwdArgs {
@@ -55,9 +56,10 @@ constexpr int kAuxFloatsPerTile = 256;
 __device__ __forceinline__ int real_keys(const int* kv_len, int b, int n_k) {
   return kv_len == nullptr ? n_k : min(max(kv_len[b], 0), n_k);
 }
-hipError_t launch_attn_bwd_pre(const BwdArgs& a, bool f32, hipStream_t stream);  // fills `aux`
-hipError_t launch_attn_bwd_bf16(const BwdArgs& a, hipStream_t stream);  // pre-pass, dK/dV, dQ
-hipError_t launch_attn_bwd_f32(const BwdArgs& a, hipStream_t stream);
+// d: the head width, 32 or 64 (every other value: hipErrorInvalidValue, nothing launched)
+hipError_t launch_attn_bwd_pre(const BwdArgs& a, bool f32, int d, hipStream_t stream);  // fills `aux`
+hipError_t launch_attn_bwd_bf16(const BwdArgs& a, int d, hipStream_t stream);  // pre-pass, dK/dV, dQ
+hipError_t launch_attn_bwd_f32(const BwdArgs& a, int d, hipStream_t stream);
 
 // C = A[M,K] * W[K,N] in bf16 with fp32 accumulation, up to three independent problems in one launch.
 // Row-major C (ldc = N) when head_seq == 0; otherwise "head-major" with heads of w = 2^head_shift columns (w in

@@ -66,6 +66,9 @@ WORKLOADS = {
                                       causal=False, seed=1005),
     "sdpa_bwd_causal_bf16_b4_h8_n4096": dict(kind="sdpa_bwd", dtype="bf16", B=4, h=8, n_q=4096, n_k=4096, d_k=64,
                                              d_v=64, causal=True, seed=1005),
+    # the backward at 16 heads of 32 (the d = 32 forward workload's tensors and an upstream gradient)
+    "sdpa_bwd_bf16_b4_h16_n4096_d32": dict(kind="sdpa_bwd", dtype="bf16", B=4, h=16, n_q=4096, n_k=4096, d_k=32,
+                                           d_v=32, causal=False, seed=1007),
 }
 
 
