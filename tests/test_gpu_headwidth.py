@@ -222,3 +222,25 @@ def test_headwidth32_backward_long_sampled():
         ins = [x[nm].f64[b:b + 1, hh:hh + 1] for nm in ("Q", "K", "V", "dO")]
         ref = [r[0, 0] for r in sdpa_backward_ref(*ins)]
         _check_grads([g[b, hh] for g in grads], ref, "bf16", f"d=32 n=4096 backward b={b} h={hh}")
+
+
+def test_headwidth_autograd_wrapper():
+    # width 32: the autograd function's gradients are exactly sdpa_backward's; width 128: the forward runs and the
+    # backward is refused with ATTN_ERR_UNSUPPORTED before anything is launched
+    x = workloads.make_sdpa_inputs(2, 3, 96, 96, 32, 32, "bf16", 9995, dout=True)
+    q, k, v, do = (to_dev(x[nm]) for nm in ("Q", "K", "V", "dO"))
+    qa, ka, va = (t.clone().requires_grad_(True) for t in (q, k, v))
+    m.attention(qa, ka, va, mask="causal").backward(do)
+    out, lse = m.sdpa_forward_lse(q, k, v, mask="causal")
+    dq, dk, dv = m.sdpa_backward(q, k, v, out, do, lse, mask="causal")
+    torch.cuda.synchronize()
+    assert torch.equal(qa.grad, dq) and torch.equal(ka.grad, dk) and torch.equal(va.grad, dv)
+
+    x = workloads.make_sdpa_inputs(1, 2, 64, 64, 128, 128, "bf16", 9996, dout=True)
+    q, k, v, do = (to_dev(x[nm]) for nm in ("Q", "K", "V", "dO"))
+    qa = q.clone().requires_grad_(True)
+    y = m.attention(qa, k, v)
+    assert_bf16_parity(to_f64(y), sdpa_ref(x["Q"].f64, x["K"].f64, x["V"].f64), "autograd forward d=128")
+    with pytest.raises(m.AttnError) as e:
+        y.backward(do)
+    assert e.value.status == m.ATTN_ERR_UNSUPPORTED
