@@ -33,6 +33,12 @@ from pathlib import Path
 ROOT = Path(__file__).resolve().parent
 sys.path.insert(0, str(ROOT))
 
+# The CPU baseline's BLAS thread count: the cores this process may run on, unless the environment already fixes it.
+# Set before numpy (and its BLAS) is first imported.
+_AFFINITY = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+for _var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+    os.environ.setdefault(_var, str(_AFFINITY))
+
 METRIC = "attention TFLOP/s (4·B·h·n_q·n_k·d_k) at h={h},d_k={d_k}; % of bf16 MFMA peak"
 METRIC_WINDOW = "restricted self-attention TFLOP/s over the band's pairs (4·B·h·pairs·d_k) at h=8,d_k=64; % of bf16 MFMA peak"
 METRIC_PADDED = "attention TFLOP/s over real keys (4·h·n_q·Σ_b kv_len[b]·d_k) at h=8,d_k=64; % of bf16 MFMA peak"
@@ -42,6 +48,7 @@ METRIC_MHA = ("multi-head attention TFLOP/s (Q/K/V projections + attention + W^O
 METRIC_BWD = "attention backward TFLOP/s (10·B·h·n_q·n_k·d_k) at h={h},d_k={d_k}; % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector (the fp32 path runs on the VALU)
 PROFILES = ROOT / "profiles"
 
 
@@ -136,6 +143,112 @@ def measured_traffic(kernel: str, workload: str):
     return d.get("bytes_per_launch")
 
 
+def time_steps(step, steps: int, warmup: int, stream):
+    """W untimed warm-up calls, then exactly K calls timed with HIP events recorded on `stream` (the stream the
+    library launches on), bracketed by device synchronisation. Returns (ms per call, wall seconds of the region)."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps, time.perf_counter() - t0
+
+
+def repeat_median(step, stream, ms_hint: float, loops: int, min_ms: float = 5.0):
+    """`loops` more timed loops after the main region, each of N back-to-back calls lasting at least `min_ms`; the
+    median over loops of the per-call time is the steady-state figure (the main region's K calls can be too short to
+    average out the clock ramp)."""
+    import statistics
+
+    import torch
+    if loops <= 0:
+        return None
+    n = max(1, int(-(-min_ms // max(ms_hint, 1e-4))))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    per_call = []
+    for _ in range(loops):
+        e0.record(stream)
+        for _ in range(n):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per_call.append(e0.elapsed_time(e1) / n)
+    return {"loops": loops, "calls_per_loop": n, "median_ms": round(statistics.median(per_call), 5),
+            "min_ms": round(min(per_call), 5), "max_ms": round(max(per_call), 5)}
+
+
+def smi_snapshot():
+    """Clock, power and temperature readings of the GPU as amd-smi (else rocm-smi) reports them, flattened to a few
+    key/value pairs; None when neither tool answers. Best effort: the measurement does not depend on it."""
+    import re
+    import subprocess
+    want = re.compile(r"(gfx|sclk|clk|clock|power|temp|hotspot|edge)", re.I)
+    for cmd in (["amd-smi", "metric", "--clock", "--power", "--temperature", "--json"],
+                ["rocm-smi", "--showclocks", "--showpower", "--showtemp", "--json"]):
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=30)
+            data = json.loads(r.stdout)
+        except Exception:
+            continue
+        flat = {}
+
+        def walk(x, path):
+            if len(flat) >= 24:
+                return
+            if isinstance(x, dict):
+                for k, v in x.items():
+                    walk(v, f"{path}.{k}" if path else str(k))
+            elif isinstance(x, list):
+                for i, v in enumerate(x[:2]):
+                    walk(v, f"{path}[{i}]")
+            elif want.search(path) and x not in (None, "", "N/A"):
+                flat[path] = x
+        walk(data, "")
+        if flat:
+            return {"tool": cmd[0], "readings": flat}
+    return None
+
+
+def smi_under_load(step, seconds: float = 2.0):
+    """An smi snapshot taken while `step` runs back to back (at least `seconds`, at most 30 s, until the snapshot is
+    in): the clock the chip holds under this load, not at idle. Best effort, like smi_snapshot."""
+    import threading
+
+    import torch
+    res = {}
+
+    def sample():
+        time.sleep(0.5)  # let the load settle first
+        res["snap"] = smi_snapshot()
+
+    th = threading.Thread(target=sample, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0 < seconds or th.is_alive()) and time.perf_counter() - t0 < 30.0:
+        for _ in range(64):
+            step()
+        torch.cuda.synchronize()
+    th.join(timeout=30)
+    return res.get("snap")
+
+
+def host_cores():
+    """What the CPU baseline could use: logical CPUs, the ones this process may run on, and the BLAS threads."""
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:
+        blas = None
+    return {"os_cpu_count": os.cpu_count(), "affinity": _AFFINITY, "blas_threads": blas,
+            "env": {v: os.environ.get(v) for v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}}
+
+
 def copy_calibration(nbytes: int = 512 << 20, reps: int = 3):
     """A plain device-to-device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
     import torch
@@ -153,11 +266,8 @@ def cpu_baseline(w, x, budget_s: float):
     import numpy as np
 
     from oracle import sdpa_head
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
+    host = host_cores()
+    threads = host["blas_threads"] or int(os.environ.get("OMP_NUM_THREADS", _AFFINITY))
     Q, K, V = x["Q"].f64, x["K"].f64, x["V"].f64
     heads = [(b, hh) for b in range(w["B"]) for hh in range(w["h"])]
     done, t_total = 0, 0.0
@@ -171,7 +281,7 @@ def cpu_baseline(w, x, budget_s: float):
         done += 1
         assert np.isfinite(o).all()
     per_head = flops_metric(w) / (w["B"] * w["h"])
-    return {"value": per_head * done / t_total / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    return {"value": per_head * done / t_total / 1e12, "unit": "TFLOP/s", "cores": threads, "host": host, "kind": "oracle",
             "sample": f"{done} head evaluations over the workload's {len(heads)} heads ({w['n_q']}x{w['n_k']} "
                       f"scores each, float64 NumPy), {t_total:.1f} s"}
 
@@ -181,11 +291,8 @@ def cpu_baseline_bwd(w, x, budget_s: float):
     import numpy as np
 
     from oracle import sdpa_backward_head
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
+    host = host_cores()
+    threads = host["blas_threads"] or int(os.environ.get("OMP_NUM_THREADS", _AFFINITY))
     heads = [(b, hh) for b in range(w["B"]) for hh in range(w["h"])]
     done, t_total = 0, 0.0
     sdpa_backward_head(x["Q"].f64[0, 0, :64], x["K"].f64[0, 0, :64], x["V"].f64[0, 0, :64], x["dO"].f64[0, 0, :64])
@@ -197,7 +304,7 @@ def cpu_baseline_bwd(w, x, budget_s: float):
         done += 1
         assert all(np.isfinite(a).all() for a in g)
     per_head = flops_metric_bwd(w) / (w["B"] * w["h"])
-    return {"value": per_head * done / t_total / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    return {"value": per_head * done / t_total / 1e12, "unit": "TFLOP/s", "cores": threads, "host": host, "kind": "oracle",
             "sample": f"{done} head backward evaluations over the workload's {len(heads)} heads ({w['n_q']}x{w['n_k']}"
                       f" scores each, float64 NumPy), {t_total:.1f} s"}
 
@@ -219,18 +326,8 @@ def bench_backward(args, w, x, m, dev):
     def step():
         m.sdpa_backward(q, k, v, out, do, lse, mask=mask, dq=dq, dk=dk, dv=dv, workspace=ws)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = e0.elapsed_time(e1) / args.steps
+    ms, wall = time_steps(step, args.steps, args.warmup, stream)
+    reps = repeat_median(step, stream, ms, args.repeats)
 
     # parity of the last timed step on one whole head (float64 oracle, same inputs)
     ref = sdpa_backward_head(*(x[n].f64[0, 0] for n in ("Q", "K", "V", "dO")), w["causal"])
@@ -255,6 +352,7 @@ def bench_backward(args, w, x, m, dev):
                      "algorithmic_hbm_bytes": hbm_bytes_bwd(w),
                      "algorithmic_hbm_GBps": round(hbm_bytes_bwd(w) / (ms * 1e-3) / 1e9, 1)},
         "wall_s_timed_region": round(wall, 4),
+        "timing_repeats": reps,
         "parity_last_step_head0": errs,
     }
 
@@ -268,18 +366,11 @@ def bench_window(args, w, x, m, dev):
     q, k, v = dev(x["Q"]), dev(x["K"]), dev(x["V"])
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream()
-    for _ in range(args.warmup):
+    def step():
         m.sdpa_forward_window(q, k, v, w["window"], out=out)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        m.sdpa_forward_window(q, k, v, w["window"], out=out)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = e0.elapsed_time(e1) / args.steps
+
+    ms, wall = time_steps(step, args.steps, args.warmup, stream)
+    reps = repeat_median(step, stream, ms, args.repeats)
     rows = np.array([0, 1, 255, 256, 2047, w["n_q"] - 1])
     ref = sdpa_ref(x["Q"].f64[0, 0, rows], x["K"].f64[0, 0], x["V"].f64[0, 0], q_index=rows, window=w["window"])
     err = np.abs(out[0, 0, rows].float().cpu().numpy() - ref)
@@ -295,6 +386,7 @@ def bench_window(args, w, x, m, dev):
                      "frac": round(value / PEAK_BF16_TFLOPS, 4), "traffic": None,
                      "kernel": "attn_fwd_bf16<64, 4, 1, 2, 4, true>"},
         "wall_s_timed_region": round(wall, 4),
+        "timing_repeats": reps,
         "parity_last_step": {"max_abs": float(err.max()), "mean_abs": float(err.mean())},
     }
 
@@ -309,18 +401,11 @@ def bench_padded(args, w, x, m, dev):
     lens = torch.tensor(w["kv_len"], dtype=torch.int32, device="cuda")
     out = torch.empty(w["B"], w["h"], w["n_q"], w["d_v"], dtype=q.dtype, device="cuda")
     stream = torch.cuda.current_stream()
-    for _ in range(args.warmup):
+    def step():
         m.sdpa_forward_padded(q, k, v, lens, out=out)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        m.sdpa_forward_padded(q, k, v, lens, out=out)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = e0.elapsed_time(e1) / args.steps
+
+    ms, wall = time_steps(step, args.steps, args.warmup, stream)
+    reps = repeat_median(step, stream, ms, args.repeats)
     got = out.float().cpu().numpy()
     rows = np.array([0, 1, 127, 128, 2047, w["n_q"] - 1])
     errs = []
@@ -340,6 +425,7 @@ def bench_padded(args, w, x, m, dev):
         "roofline": {"bound": "mfma", "achieved": round(value, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(value / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": "attn_fwd_bf16<64, 4, 2, 2, 3, false>"},
         "wall_s_timed_region": round(wall, 4),
+        "timing_repeats": reps,
         "parity_last_step": {"max_abs": float(err.max()), "mean_abs": float(err.mean())},
     }
 
@@ -359,18 +445,8 @@ def bench_mha(args, w, x, m, dev):
     def step():
         m.mha_forward(xq, xq, *ws_t, h=w["h"], out=out, workspace=work)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = e0.elapsed_time(e1) / args.steps
+    ms, wall = time_steps(step, args.steps, args.warmup, stream)
+    reps = repeat_median(step, stream, ms, args.repeats)
     ref = mha_ref(x["Xq"].f64[:2], x["Xq"].f64[:2], *(x[nm].f64 for nm in ("Wq", "Wk", "Wv", "Wo")), h=w["h"])
     d = np.abs(out[:2].float().cpu().numpy() - ref)
     value = flops_mha(w) / (ms * 1e-3) / 1e12
@@ -386,6 +462,7 @@ def bench_mha(args, w, x, m, dev):
                      "frac": round(value / PEAK_BF16_TFLOPS, 4), "traffic": None,
                      "kernel": "mha_forward step (3 launches)"},
         "wall_s_timed_region": round(wall, 4),
+        "timing_repeats": reps,
         "parity_last_step_first2": {"max_abs": float(d.max()), "mean_abs": float(d.mean())},
     }
 
@@ -407,18 +484,8 @@ def bench_encoder(args, w, x, m, dev):
     def step():
         m.encoder_layer_forward(X, *ts, h=w["h"], eps=w["eps"], out=out, workspace=ws)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = e0.elapsed_time(e1) / args.steps
+    ms, wall = time_steps(step, args.steps, args.warmup, stream)
+    reps = repeat_median(step, stream, ms, args.repeats)
     ref = encoder_layer_ref(x["X"].f64[:2], *(x[nm].f64 for nm in names), w["h"], w["eps"])
     d = np.abs(out[:2].float().cpu().numpy() - ref)
     value = flops_encoder(w) / (ms * 1e-3) / 1e12
@@ -435,6 +502,7 @@ def bench_encoder(args, w, x, m, dev):
                      "frac": round(value / PEAK_BF16_TFLOPS, 4), "traffic": None,
                      "kernel": "encoder_layer_forward step (7 launches)"},
         "wall_s_timed_region": round(wall, 4),
+        "timing_repeats": reps,
         "parity_last_step_first2": {"max_abs": float(d.max()), "mean_abs": float(d.mean())},
     }
 
@@ -448,6 +516,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probes", action="store_true", help="skip the measured-ceiling microbenchmarks")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--repeats", type=int, default=7,
+                    help="timed loops of >= 5 ms each after the main region (their median is reported too)")
+    ap.add_argument("--rotate-mb", type=float, default=0.0,
+                    help="also time the call cycling over input/output copies totalling more than this many MiB")
+    ap.add_argument("--no-smi", action="store_true", help="skip the amd-smi clock/power snapshots")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain copy of known size (for scaling HBM byte counters)")
     args = ap.parse_args()
@@ -503,29 +576,64 @@ def main():
     mask = "causal" if w["causal"] else "none"
     stream = torch.cuda.current_stream()
 
-    for _ in range(args.warmup):
+    def step():
         m.sdpa_forward(q, k, v, mask=mask, out=out)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        m.sdpa_forward(q, k, v, mask=mask, out=out)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = e0.elapsed_time(e1) / args.steps
+
+    smi_before = None if args.no_smi else smi_snapshot()
+    ms, wall = time_steps(step, args.steps, args.warmup, stream)
+    reps = repeat_median(step, stream, ms, args.repeats)
+    smi_load = None if args.no_smi else smi_under_load(step)
 
     # parity of the last timed output on sampled rows (float64 oracle, same inputs)
     from oracle import sdpa_ref
     got = out.float().cpu().numpy()
-    rows = np.array([0, 1, 127, 128, 2047, w["n_q"] - 1])
+    rows = np.unique(np.array([0, 1, 127, 128, 2047, w["n_q"] - 1]).clip(0, w["n_q"] - 1))
     ref = np.stack([sdpa_ref(x["Q"].f64[b, hh, rows], x["K"].f64[b, hh], x["V"].f64[b, hh], w["causal"], q_index=rows)
                     for b, hh in ((0, 0), (w["B"] - 1, w["h"] - 1))])
     err = np.abs(np.stack([got[0, 0, rows], got[-1, -1, rows]]) - ref)
 
+    # Cold-ish: the same calls cycling over copies of the inputs and outputs whose total exceeds --rotate-mb, so
+    # that a call's operands have left the 256 MB last-level cache by the time they come round again.
+    cold = None
+    if args.rotate_mb > 0:
+        per_set = hbm_bytes(w)
+        nsets = min(1024, max(2, -(-int(args.rotate_mb * 2**20) // per_set)))
+        sets = [(q.clone(), k.clone(), v.clone(), torch.empty_like(out)) for _ in range(nsets)]
+        it = [0]
+
+        def step_cold():
+            qq, kk, vv, oo = sets[it[0] % nsets]
+            it[0] += 1
+            m.sdpa_forward(qq, kk, vv, mask=mask, out=oo)
+
+        for _ in range(nsets):
+            step_cold()
+        torch.cuda.synchronize()
+        rc = repeat_median(step_cold, stream, ms, max(args.repeats, 3), min_ms=max(5.0, 2.0 * nsets * ms))
+        cold = {"buffer_sets": nsets, "bytes_cycled": nsets * per_set, **rc,
+                "algorithmic_hbm_GBps": round(per_set / (rc["median_ms"] * 1e-3) / 1e9, 1)}
+        del sets
+
     value = flops_metric(w) / (ms * 1e-3) / 1e12
     achieved = flops_algorithmic(w) / (ms * 1e-3) / 1e12
+    # the roofline that bounds this shape: the matrix core when its arithmetic intensity (algorithmic FLOPs per
+    # algorithmic byte) is above the ridge of the bf16 peak over the HBM peak, HBM otherwise
+    intensity = flops_algorithmic(w) / hbm_bytes(w)
+    dtype_peak = PEAK_BF16_TFLOPS if w["dtype"] == "bf16" else PEAK_F32_TFLOPS
+    kernel = (f"attn_fwd_bf16<{w['d_k']}, ...>" if w["dtype"] == "bf16" else f"attn_fwd_f32<{w['d_k']}>")
+    traffic = measured_traffic(f"attn_fwd_bf16_d{w['d_k']}", args.workload) if w["dtype"] == "bf16" else None
+    if intensity * PEAK_HBM_GBS * 1e9 / 1e12 >= dtype_peak:
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": dtype_peak, "unit": "TFLOP/s",
+                "frac": round(achieved / dtype_peak, 4)}
+    else:
+        gbps = hbm_bytes(w) / (ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbps / PEAK_HBM_GBS, 4)}
+    roof.update({"traffic": traffic, "kernel_source_hash": kernel_source_hash(), "kernel": kernel,
+                 "algorithmic_flops": flops_algorithmic(w), "algorithmic_hbm_bytes": hbm_bytes(w),
+                 "arithmetic_intensity": round(intensity, 1),
+                 "algorithmic_TFLOPs": round(achieved, 2),
+                 "algorithmic_hbm_GBps": round(hbm_bytes(w) / (ms * 1e-3) / 1e9, 1)})
     rec = {
         "metric": METRIC.format(h=w["h"], d_k=w["d_k"]), "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps,
@@ -534,15 +642,16 @@ def main():
         "config": {"workload": args.workload, "B": w["B"], "h": w["h"], "n_q": w["n_q"], "n_k": w["n_k"],
                    "d_k": w["d_k"], "d_v": w["d_v"], "mask": mask},
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic(f"attn_fwd_bf16_d{w['d_k']}", args.workload),
-                     "kernel_source_hash": kernel_source_hash(),
-                     "kernel": f"attn_fwd_bf16<{w['d_k']}, ...>", "algorithmic_hbm_bytes": hbm_bytes(w),
-                     "algorithmic_hbm_GBps": round(hbm_bytes(w) / (ms * 1e-3) / 1e9, 1)},
+        "roofline": roof,
         "wall_s_timed_region": round(wall, 4),
+        "timing_repeats": reps,
         "parity_last_step": {"max_abs": float(err.max()), "mean_abs": float(err.mean())},
+        "gpu_state": {"before": smi_before, "under_load": smi_load},
     }
+    if reps is not None:
+        rec["value_at_repeat_median"] = round(flops_metric(w) / (reps["median_ms"] * 1e-3) / 1e12, 2)
+    if cold is not None:
+        rec["cold"] = cold
     if not args.no_probes:
         # measured ceilings on this chip, taken after the timed region: dense bf16 MFMA throughput with every CU busy
         # (and the clock it holds under that load), the v_exp_f32 rate and device-to-device copy bandwidth

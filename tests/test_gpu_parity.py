@@ -58,18 +58,15 @@ def test_workload_sdpa_full(name):
 
 
 @pytest.mark.parametrize("name", ["sdpa_bf16_b4_h8_n4096", "sdpa_causal_bf16_b4_h8_n4096"])
-def test_workload_sdpa_n4096_sampled(name):
+def test_workload_sdpa_n4096_full(name):
+    # every element of every head at full size (the oracle takes about 0.1 s per 4096 x 4096 head)
     w = workloads.WORKLOADS[name]
     x, got = _sdpa_case(w["B"], w["h"], w["n_q"], w["n_k"], "bf16", w["causal"], w["seed"])
-    Q, K, V = x["Q"].f64, x["K"].f64, x["V"].f64
-    rng = np.random.Generator(np.random.PCG64(7))
-    rows = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, 4095], rng.choice(4096, 57, replace=False)]))
-    ref_rows = np.stack([sdpa_ref(Q[b, hh, rows], K[b, hh], V[b, hh], w["causal"], q_index=rows)
-                         for b in range(w["B"]) for hh in range(w["h"])])
-    got_rows = got[:, :, rows].reshape(ref_rows.shape)
-    assert_bf16_parity(got_rows, ref_rows, name + " sampled rows")
-    for b, hh in ((0, 0), (w["B"] - 1, w["h"] - 1)):
-        assert_bf16_parity(got[b, hh], sdpa_ref(Q[b, hh], K[b, hh], V[b, hh], w["causal"]), f"{name} head {b},{hh}")
+    ref = sdpa_ref(x["Q"].f64, x["K"].f64, x["V"].f64, w["causal"])
+    assert_bf16_parity(got, ref, name + " all heads")
+    for b in range(w["B"]):
+        for hh in range(w["h"]):
+            assert_bf16_parity(got[b, hh], ref[b, hh], f"{name} head {b},{hh}")
 
 
 # --- ragged shapes and tile tails --------------------------------------------------------------------------------

@@ -58,15 +58,22 @@ def test_radius_zero_returns_values(dtype):
             torch.testing.assert_close(out, v, rtol=1e-6, atol=1e-7)
 
 
-def test_window_n4096_sampled_rows():
-    # the long-sequence tensors with a band of radius 256 (513 keys per row)
+def test_window_n4096_every_head():
+    # the long-sequence tensors with a band of radius 256 (513 keys per row): sampled rows of every head, and two
+    # heads in full
     x = workloads.make_workload("sdpa_bf16_b4_h8_n4096")
     q, k, v = (to_dev(x[nm]) for nm in "QKV")
     got = to_f64(m.sdpa_forward_window(q, k, v, 256))
-    rows = np.array([0, 1, 255, 256, 257, 1000, 2047, 3839, 3840, 4095])
+    rng = np.random.Generator(np.random.PCG64(11))
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, 257, 1000, 2047, 3839, 3840, 4095],
+                                     rng.choice(4096, 54, replace=False)]))
+    for b in range(4):
+        for hh in range(8):
+            ref = sdpa_ref(x["Q"].f64[b, hh, rows], x["K"].f64[b, hh], x["V"].f64[b, hh], q_index=rows, window=256)
+            assert_bf16_parity(got[b, hh, rows], ref, f"window n4096 head {b},{hh} sampled rows")
     for b, hh in ((0, 0), (3, 7)):
-        ref = sdpa_ref(x["Q"].f64[b, hh, rows], x["K"].f64[b, hh], x["V"].f64[b, hh], q_index=rows, window=256)
-        assert_bf16_parity(got[b, hh, rows], ref, f"window n4096 head {b},{hh}")
+        ref = sdpa_ref(x["Q"].f64[b, hh], x["K"].f64[b, hh], x["V"].f64[b, hh], window=256)
+        assert_bf16_parity(got[b, hh], ref, f"window n4096 head {b},{hh} in full")
 
 
 def test_window_rejects_bad_arguments():

@@ -501,6 +501,7 @@ hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int d, hipStream_t stream) {
   switch (d) {
     case 64:
       if (a.windowed) return launch<64, 4, 1, 2, 4, true>(a, stream);
+      if (!a.causal && a.n_q >= 512) return launch_attn_fwd_pp_bf16(a, stream);
       if (!a.causal) return launch<64, 4, 2, 2, 3>(a, stream);
       return launch<64, 4, 1, 2, 4>(a, stream);
     case 32:

@@ -29,6 +29,9 @@ struct AttnArgs {
 // d: the head width d_k = d_v, 32, 64 or 128 (every other value: hipErrorInvalidValue, nothing launched)
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int d, hipStream_t stream);
 hipError_t launch_attn_fwd_f32(const AttnArgs& a, int d, hipStream_t stream);
+// Unmasked (optionally key-padded) attention at width 64 with eight-wave ping-pong workgroups of 512 queries
+// (causal or windowed arguments: hipErrorInvalidValue, nothing launched)
+hipError_t launch_attn_fwd_pp_bf16(const AttnArgs& a, hipStream_t stream);
 
 // Backward pass of attention over [B, H] heads of width d (32 or 64), every tensor dense [B, H, n, d] in the element
 // type.

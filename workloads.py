@@ -30,6 +30,10 @@ WORKLOADS = {
                                              d_k=32, d_v=32, causal=False, seed=1002),
     "mha_self_bf16_b32_n128_dm512_h4": dict(kind="mha", dtype="bf16", B=32, h=4, n_q=128, n_k=128, d_model=512,
                                             d_k=128, d_v=128, causal=False, seed=1002),
+    # the attention step of the MHA workload above on its own: per-head Q/K/V [32, 8, 128, 64] ~ N(0,1) (the
+    # projections of X ~ N(0,1) by W ~ N(0, 1/512) have unit variance)
+    "sdpa_bf16_b32_h8_n128": dict(kind="sdpa", dtype="bf16", B=32, h=8, n_q=128, n_k=128, d_k=64, d_v=64,
+                                  causal=False, seed=1002),
     # decoder masked self-attention
     "sdpa_causal_bf16_b32_h8_n256": dict(kind="sdpa", dtype="bf16", B=32, h=8, n_q=256, n_k=256, d_k=64, d_v=64,
                                          causal=True, seed=1003),
