@@ -155,6 +155,24 @@ int mha_forward(const void* Xq, const void* Xkv, const void* Wq, const void* Wk,
 /* Bytes of workspace mha_forward needs for these sizes (0 if the sizes are invalid). */
 size_t mha_workspace_size(int dtype, int64_t B, int64_t n_q, int64_t n_k, int64_t h, int64_t d_k, int64_t d_v);
 
+/* mha_forward_noalloc: mha_forward without a caller workspace, for callers that cannot allocate device memory
+ * (code being captured into a HIP graph, tight serving loops, harnesses that forbid allocation). The projected
+ * Q/K/V and the concatenated heads go to a scratch array the library holds in device memory: one array of
+ * ATTN_NOALLOC_SCRATCH_BYTES per GPU it runs on, kept until the process ends. The call allocates nothing and
+ * frees nothing.
+ *   Arguments, layouts and requirements as mha_forward, without workspace and workspace_bytes. The sizes must need
+ *   at most ATTN_NOALLOC_SCRATCH_BYTES of workspace (mha_workspace_size(...) <= ATTN_NOALLOC_SCRATCH_BYTES; the
+ *   base model's B = 32, n = 128, d_model = 512 needs 16 MiB); larger sizes return ATTN_ERR_INVALID before any HIP
+ *   call. The scratch of the current device is used, so `stream` must belong to the current device.
+ *   Calls on one GPU share its scratch: calls that overlap in time on one GPU (on different streams, or from
+ *   different threads) race and must be ordered by the caller. Every byte of scratch a call reads is written earlier
+ *   in the same call, so nothing needs clearing between calls.
+ *   Errors: as mha_forward; ATTN_ERR_HIP also when the scratch's device address cannot be obtained. */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20) /* 32 MiB */
+int mha_forward_noalloc(const void* Xq, const void* Xkv, const void* Wq, const void* Wk, const void* Wv,
+                        const void* Wo, int mask_kind, void* out, int dtype, int64_t B, int64_t n_q, int64_t n_k,
+                        int64_t d_model, int64_t h, int64_t d_k, int64_t d_v, void* stream);
+
 /* encoder_layer_forward: one Transformer encoder layer in the pages' post-norm form (each sub-layer's output is
  * LayerNorm(x + Sublayer(x)): "Attention Is All You Need", lettle.cn translation, section 3.1; "Transformer：抛弃循环与
  * 卷积的序列建模", sections "FFN" and "Residual Connection 与 LayerNorm"):

@@ -253,3 +253,21 @@ def test_probe_copy_rejects_bad_arguments(lib, kw):
     args.update(kw)
     g = ctypes.c_double()
     assert lib.probe_hbm_copy(args["src"], args["dst"], args["nbytes"], args["reps"], None, ctypes.byref(g)) == INVALID
+
+
+def mha_noalloc(lib, Xq=A, Xkv=A, W=A * 2, out=A * 1000, mask=0, dtype=BF16, B=2, n_q=16, n_k=16, d_model=512, h=8,
+                d_k=64, d_v=64):
+    return lib.mha_forward_noalloc(Xq, Xkv, W, W + 0x100000, W + 0x200000, W + 0x300000, mask, out, dtype, B, n_q, n_k,
+                                   d_model, h, d_k, d_v, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Xq=None), INVALID), (dict(out=None), INVALID), (dict(B=0), INVALID), (dict(dtype=F32), UNSUPPORTED),
+    (dict(mask=1, n_k=17), UNSUPPORTED), (dict(d_k=48, d_v=48), UNSUPPORTED),
+    # sizes whose intermediates need more than the library's 32 MiB scratch: rejected before any HIP call
+    (dict(B=64, n_q=512, n_k=512), INVALID), (dict(B=1, n_q=1 << 16, n_k=1 << 16), INVALID),
+])
+def test_mha_noalloc_rejects_bad_arguments(lib, kw, code):
+    assert mha_noalloc(lib, **kw) == code
+    if kw.get("B") == 64:
+        assert b"scratch" in lib.attn_last_error()

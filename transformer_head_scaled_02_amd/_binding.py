@@ -18,7 +18,7 @@ ATTN_MASK_NONE, ATTN_MASK_CAUSAL = 0, 1
 ATTN_F32, ATTN_BF16 = 0, 1
 
 # every symbol include/mi355_attn.h declares
-EXPORTED = ("sdpa_forward", "sdpa_forward_lse", "sdpa_forward_padded", "sdpa_forward_window", "sdpa_backward", "sdpa_backward_workspace_size", "mha_forward",
+EXPORTED = ("sdpa_forward", "sdpa_forward_lse", "sdpa_forward_padded", "sdpa_forward_window", "sdpa_backward", "sdpa_backward_workspace_size", "mha_forward", "mha_forward_noalloc",
             "encoder_layer_forward", "encoder_layer_workspace_size",
             "mha_workspace_size", "attn_status_string", "attn_last_error", "probe_scratch_size", "probe_mfma_bf16", "probe_exp_f32", "probe_hbm_copy")
 
@@ -57,6 +57,8 @@ def load_library(path: Path | str | None = None) -> ctypes.CDLL:
     lib.sdpa_backward_workspace_size.restype = sz
     lib.mha_forward.argtypes = [vp, vp, vp, vp, vp, vp, ci, vp, vp, sz, ci, i64, i64, i64, i64, i64, i64, i64, vp]
     lib.mha_forward.restype = ci
+    lib.mha_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, ci, vp, ci, i64, i64, i64, i64, i64, i64, i64, vp]
+    lib.mha_forward_noalloc.restype = ci
     lib.mha_workspace_size.argtypes = [ci, i64, i64, i64, i64, i64, i64]
     lib.mha_workspace_size.restype = sz
     lib.encoder_layer_forward.argtypes = [vp] * 14 + [ctypes.c_float, ci, vp, vp, sz, ci, i64, i64, i64, i64, i64, vp]
@@ -336,6 +338,36 @@ def mha_forward(xq: torch.Tensor, xkv: torch.Tensor, wq: torch.Tensor, wk: torch
     _check(lib.mha_forward(xq.data_ptr(), xkv.data_ptr(), wq.data_ptr(), wk.data_ptr(), wv.data_ptr(), wo.data_ptr(),
                            _mask_code(mask), out.data_ptr(), workspace.data_ptr(), ws_bytes, _dtype_code(xq),
                            B, n_q, n_k, d_model, h, d_k, d_v, _stream_handle(xq.device)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # ATTN_NOALLOC_SCRATCH_BYTES of the header
+
+
+def mha_forward_noalloc(xq: torch.Tensor, xkv: torch.Tensor, wq: torch.Tensor, wk: torch.Tensor, wv: torch.Tensor,
+                        wo: torch.Tensor, h: int, *, out: torch.Tensor, mask="none") -> torch.Tensor:
+    """mha_forward with its intermediates in the library's own device scratch (no workspace argument, no allocation
+    by the library; `out` must be passed in). Calls that overlap in time on one GPU race on that scratch."""
+    lib = load_library()
+    ts = [_dev_tensor(t, n) for t, n in ((xq, "xq"), (xkv, "xkv"), (wq, "wq"), (wk, "wk"), (wv, "wv"), (wo, "wo"))]
+    xq, xkv, wq, wk, wv, wo = ts
+    if len({t.dtype for t in ts}) != 1 or len({t.device for t in ts}) != 1:
+        raise ValueError("all inputs must share dtype and device")
+    if xq.dim() != 3 or xkv.dim() != 3:
+        raise ValueError("xq and xkv must be [B, n, d_model]")
+    B, n_q, d_model = xq.shape
+    n_k = xkv.shape[1]
+    if xkv.shape != (B, n_k, d_model) or wq.shape[0] != d_model or wq.shape[1] % h or wv.shape[1] % h:
+        raise ValueError("shape mismatch")
+    d_k, d_v = wq.shape[1] // h, wv.shape[1] // h
+    if wk.shape != wq.shape or wv.shape[0] != d_model or wo.shape != (h * d_v, d_model):
+        raise ValueError("weight shape mismatch")
+    out = _dev_tensor(out, "out")
+    if out.shape != (B, n_q, d_model) or out.dtype != xq.dtype:
+        raise ValueError("out has the wrong shape or dtype")
+    _check(lib.mha_forward_noalloc(xq.data_ptr(), xkv.data_ptr(), wq.data_ptr(), wk.data_ptr(), wv.data_ptr(),
+                                   wo.data_ptr(), _mask_code(mask), out.data_ptr(), _dtype_code(xq),
+                                   B, n_q, n_k, d_model, h, d_k, d_v, _stream_handle(xq.device)))
     return out
 
 

@@ -18,6 +18,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/mi355_attn.h"
 #include "launch.h"
 
@@ -308,53 +310,70 @@ ATTN_EXPORT size_t mha_workspace_size(int dtype, int64_t B, int64_t n_q, int64_t
   return mha_layout(B, n_q, n_k, h, d_k).total;
 }
 
-ATTN_EXPORT int mha_forward(const void* Xq, const void* Xkv, const void* Wq, const void* Wk, const void* Wv,
-                            const void* Wo, int mask_kind, void* out, void* workspace, size_t workspace_bytes,
-                            int dtype, int64_t B, int64_t n_q, int64_t n_k, int64_t d_model, int64_t h, int64_t d_k,
-                            int64_t d_v, void* stream) {
-  if (!Xq || !Xkv || !Wq || !Wk || !Wv || !Wo || !out || !workspace)
-    return fail_status(ATTN_ERR_INVALID, "mha_forward: null pointer");
-  if (dtype != ATTN_BF16) return fail_status(ATTN_ERR_UNSUPPORTED, "mha_forward: dtype %d (only ATTN_BF16)", dtype);
+namespace {
+
+// Argument checks of mha_forward and its allocation-free variant (no HIP call). `name` prefixes the error detail.
+// `workspace` may be null when `check_ws` is false (the variant's scratch is the library's own).
+int mha_check(const char* name, const void* Xq, const void* Xkv, const void* Wq, const void* Wk, const void* Wv,
+              const void* Wo, int mask_kind, const void* out, const void* workspace, size_t workspace_bytes,
+              bool check_ws, int dtype, int64_t B, int64_t n_q, int64_t n_k, int64_t d_model, int64_t h,
+              int64_t d_k, int64_t d_v, MhaLayout* layout, int* hshift) {
+  if (!Xq || !Xkv || !Wq || !Wk || !Wv || !Wo || !out || (check_ws && !workspace))
+    return fail_status(ATTN_ERR_INVALID, "%s: null pointer", name);
+  if (dtype != ATTN_BF16) return fail_status(ATTN_ERR_UNSUPPORTED, "%s: dtype %d (only ATTN_BF16)", name, dtype);
   if (mask_kind != ATTN_MASK_NONE && mask_kind != ATTN_MASK_CAUSAL)
-    return fail_status(ATTN_ERR_INVALID, "mha_forward: mask_kind %d", mask_kind);
+    return fail_status(ATTN_ERR_INVALID, "%s: mask_kind %d", name, mask_kind);
   if (B <= 0 || n_q <= 0 || n_k <= 0 || d_model <= 0 || h <= 0 || d_k <= 0 || d_v <= 0)
-    return fail_status(ATTN_ERR_INVALID, "mha_forward: sizes must be positive");
+    return fail_status(ATTN_ERR_INVALID, "%s: sizes must be positive", name);
   const int hsh = d_k == d_v ? head_shift(h, d_k) : -1;
   if (hsh < 0)
-    return fail_status(ATTN_ERR_UNSUPPORTED, "mha_forward: head dims d_k=%lld d_v=%lld with h=%lld (implemented: d_k = "
-                       "d_v in {32, 64, 128}, h*d_k a multiple of 64)", (long long)d_k, (long long)d_v, (long long)h);
-  if (d_model % 64) return fail_status(ATTN_ERR_UNSUPPORTED, "mha_forward: d_model=%lld is not a multiple of 64",
-                                (long long)d_model);
+    return fail_status(ATTN_ERR_UNSUPPORTED, "%s: head dims d_k=%lld d_v=%lld with h=%lld (implemented: d_k = "
+                       "d_v in {32, 64, 128}, h*d_k a multiple of 64)", name, (long long)d_k, (long long)d_v,
+                       (long long)h);
+  if (d_model % 64)
+    return fail_status(ATTN_ERR_UNSUPPORTED, "%s: d_model=%lld is not a multiple of 64", name, (long long)d_model);
   if (mask_kind == ATTN_MASK_CAUSAL && n_q != n_k)
-    return fail_status(ATTN_ERR_UNSUPPORTED, "mha_forward: causal mask needs n_q == n_k");
+    return fail_status(ATTN_ERR_UNSUPPORTED, "%s: causal mask needs n_q == n_k", name);
   if (n_q > ATTN_MAX_SEQ || n_k > ATTN_MAX_SEQ || B > ATTN_MAX_HEADS || h > ATTN_MAX_HEADS ||
       B * h > ATTN_MAX_HEADS || d_model > 65536 || B * n_q > 0x7fffffffLL || B * n_k > 0x7fffffffLL ||
       !grid_fits(B, h, n_q))
-    return fail_status(ATTN_ERR_UNSUPPORTED, "mha_forward: sizes beyond the library limits");
+    return fail_status(ATTN_ERR_UNSUPPORTED, "%s: sizes beyond the library limits", name);
   const MhaLayout L = mha_layout(B, n_q, n_k, h, d_k);
+  if (!check_ws && workspace_bytes < L.total)
+    return fail_status(ATTN_ERR_INVALID, "%s: these sizes need %zu bytes of scratch; the library's scratch holds %zu "
+                       "(mha_forward takes a caller workspace of any size)", name, L.total, workspace_bytes);
   if (workspace_bytes < L.total)
-    return fail_status(ATTN_ERR_INVALID, "mha_forward: workspace %zu bytes, need %zu", workspace_bytes, L.total);
-  const void* ptrs[] = {Xq, Xkv, Wq, Wk, Wv, Wo, out, workspace};
+    return fail_status(ATTN_ERR_INVALID, "%s: workspace %zu bytes, need %zu", name, workspace_bytes, L.total);
+  const void* ptrs[] = {Xq, Xkv, Wq, Wk, Wv, Wo, out, check_ws ? workspace : out};
   for (const void* p : ptrs)
-    if (!aligned16(p)) return fail_status(ATTN_ERR_INVALID, "mha_forward: pointers must be 16-byte aligned");
+    if (!aligned16(p)) return fail_status(ATTN_ERR_INVALID, "%s: pointers must be 16-byte aligned", name);
   const size_t xq_b = (size_t)B * n_q * d_model * 2, xkv_b = (size_t)B * n_k * d_model * 2;
   const size_t w_b = (size_t)d_model * h * d_k * 2;
   const void* ins[] = {Xq, Xkv, Wq, Wk, Wv, Wo};
   const size_t in_b[] = {xq_b, xkv_b, w_b, w_b, w_b, w_b};
   for (int i = 0; i < 6; ++i) {
-    if (overlaps(out, xq_b, ins[i], in_b[i])) return fail_status(ATTN_ERR_INVALID, "mha_forward: out overlaps an input");
-    if (overlaps(workspace, L.total, ins[i], in_b[i]))
-      return fail_status(ATTN_ERR_INVALID, "mha_forward: workspace overlaps an input");
+    if (overlaps(out, xq_b, ins[i], in_b[i])) return fail_status(ATTN_ERR_INVALID, "%s: out overlaps an input", name);
+    if (check_ws && overlaps(workspace, L.total, ins[i], in_b[i]))
+      return fail_status(ATTN_ERR_INVALID, "%s: workspace overlaps an input", name);
   }
-  if (overlaps(out, xq_b, workspace, L.total)) return fail_status(ATTN_ERR_INVALID, "mha_forward: out overlaps workspace");
+  if (check_ws && overlaps(out, xq_b, workspace, L.total))
+    return fail_status(ATTN_ERR_INVALID, "%s: out overlaps workspace", name);
+  *layout = L;
+  *hshift = hsh;
+  return ATTN_OK;
+}
 
+// The three launches of mha_forward (arguments already checked): projections into the workspace, attention into the
+// concatenated heads, W^O into `out`.
+int mha_run(const char* name, const void* Xq, const void* Xkv, const void* Wq, const void* Wk, const void* Wv,
+            const void* Wo, int mask_kind, void* out, void* workspace, const MhaLayout& L, int hsh, int64_t B,
+            int64_t n_q, int64_t n_k, int64_t d_model, int64_t h, int64_t d_k, hipStream_t s) {
   char* ws = static_cast<char*>(workspace);
   void* Qh = ws + L.q_off;
   void* Kh = ws + L.k_off;
   void* Vh = ws + L.v_off;
   void* Ch = ws + L.c_off;
   const int hd = (int)(h * d_k);
-  const hipStream_t s = static_cast<hipStream_t>(stream);
 
   // 1. projections, written per head: Qh [B,h,n_q,d], Kh/Vh [B,h,n_k,d]
   mi355::GemmProblem proj[3] = {
@@ -363,7 +382,7 @@ ATTN_EXPORT int mha_forward(const void* Xq, const void* Xkv, const void* Wq, con
       {Xkv, Wv, Vh, (int)(B * n_k), hd, (int)d_model, (int)n_k, nullptr, nullptr, 0, hsh},
   };
   hipError_t e = mi355::launch_gemm_bf16(proj, 3, s);
-  if (e != hipSuccess) return fail_status(ATTN_ERR_HIP, "mha_forward: projection launch failed: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail_status(ATTN_ERR_HIP, "%s: projection launch failed: %s", name, hipGetErrorString(e));
 
   // 2. attention per head, output written into the concatenated layout [B, n_q, h*d]
   mi355::AttnArgs a{};
@@ -376,13 +395,70 @@ ATTN_EXPORT int mha_forward(const void* Xq, const void* Xkv, const void* Wq, con
   a.o_stride_row = hd;
   a.causal = mask_kind == ATTN_MASK_CAUSAL;
   e = mi355::launch_attn_fwd_bf16(a, (int)d_k, s);
-  if (e != hipSuccess) return fail_status(ATTN_ERR_HIP, "mha_forward: attention launch failed: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail_status(ATTN_ERR_HIP, "%s: attention launch failed: %s", name, hipGetErrorString(e));
 
   // 3. output projection: out [B*n_q, d_model] = concat [B*n_q, h*d] x Wo [h*d, d_model]
   mi355::GemmProblem outp = {Ch, Wo, out, (int)(B * n_q), (int)d_model, hd, 0};
   e = mi355::launch_gemm_bf16(&outp, 1, s);
-  if (e != hipSuccess) return fail_status(ATTN_ERR_HIP, "mha_forward: W^O launch failed: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail_status(ATTN_ERR_HIP, "%s: W^O launch failed: %s", name, hipGetErrorString(e));
   return ATTN_OK;
+}
+
+// The allocation-free variant's scratch: one array per GPU the library runs on, held until the process ends. In
+// host code `scratch` names a host-side stand-in, not device memory: its device address is taken once per device
+// with hipGetSymbolAddress (with that device current) and only that address is used.
+constexpr size_t kNoAllocScratchBytes = ATTN_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// This device's scratch address (the current device's), looked up on its first use.
+int scratch_address(const char* name, void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_status(ATTN_ERR_HIP, "%s: hipGetDevice failed: %s", name, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail_status(ATTN_ERR_UNSUPPORTED, "%s: device index %d", name, dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail_status(ATTN_ERR_HIP, "%s: hipGetSymbolAddress(scratch) failed: %s", name, hipGetErrorString(e));
+    g_scratch_dev[dev] = p;
+  }
+  *ptr = g_scratch_dev[dev];
+  return ATTN_OK;
+}
+
+}  // namespace
+
+ATTN_EXPORT int mha_forward(const void* Xq, const void* Xkv, const void* Wq, const void* Wk, const void* Wv,
+                            const void* Wo, int mask_kind, void* out, void* workspace, size_t workspace_bytes,
+                            int dtype, int64_t B, int64_t n_q, int64_t n_k, int64_t d_model, int64_t h, int64_t d_k,
+                            int64_t d_v, void* stream) {
+  MhaLayout L;
+  int hsh = 0;
+  const int st = mha_check("mha_forward", Xq, Xkv, Wq, Wk, Wv, Wo, mask_kind, out, workspace, workspace_bytes, true,
+                           dtype, B, n_q, n_k, d_model, h, d_k, d_v, &L, &hsh);
+  if (st != ATTN_OK) return st;
+  return mha_run("mha_forward", Xq, Xkv, Wq, Wk, Wv, Wo, mask_kind, out, workspace, L, hsh, B, n_q, n_k, d_model, h,
+                 d_k, static_cast<hipStream_t>(stream));
+}
+
+ATTN_EXPORT int mha_forward_noalloc(const void* Xq, const void* Xkv, const void* Wq, const void* Wk, const void* Wv,
+                                    const void* Wo, int mask_kind, void* out, int dtype, int64_t B, int64_t n_q,
+                                    int64_t n_k, int64_t d_model, int64_t h, int64_t d_k, int64_t d_v, void* stream) {
+  MhaLayout L;
+  int hsh = 0;
+  const int st = mha_check("mha_forward_noalloc", Xq, Xkv, Wq, Wk, Wv, Wo, mask_kind, out, nullptr,
+                           kNoAllocScratchBytes, false, dtype, B, n_q, n_k, d_model, h, d_k, d_v, &L, &hsh);
+  if (st != ATTN_OK) return st;
+  void* ws = nullptr;
+  const int sa = scratch_address("mha_forward_noalloc", &ws);
+  if (sa != ATTN_OK) return sa;
+  return mha_run("mha_forward_noalloc", Xq, Xkv, Wq, Wk, Wv, Wo, mask_kind, out, ws, L, hsh, B, n_q, n_k, d_model,
+                 h, d_k, static_cast<hipStream_t>(stream));
 }
 
 ATTN_EXPORT size_t encoder_layer_workspace_size(int dtype, int64_t B, int64_t n, int64_t d_model, int64_t h,
