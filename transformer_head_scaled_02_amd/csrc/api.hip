@@ -52,8 +52,9 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 constexpr size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Largest grid any attention launch would use for these sizes (64 queries per workgroup is the smallest block).
-bool grid_fits(int64_t B, int64_t h, int64_t n_q) { return ((n_q + 63) / 64) * B * h <= 0x7fffffffLL; }
+// Largest grid any attention launch would use for these sizes (8 queries per workgroup, the fp32 kernel at width 128,
+// is the smallest block).
+bool grid_fits(int64_t B, int64_t h, int64_t n_q) { return ((n_q + 7) / 8) * B * h <= 0x7fffffffLL; }
 // The backward launches use blocks of as few as 32 rows of either side.
 bool grid_fits32(int64_t B, int64_t h, int64_t n) { return ((n + 31) / 32) * B * h <= 0x7fffffffLL; }
 

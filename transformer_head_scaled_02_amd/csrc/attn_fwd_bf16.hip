@@ -492,9 +492,14 @@ hipError_t launch(const AttnArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int d, hipStream_t stream) {
-  // Unmasked: 4-wave workgroups of 256 queries (two halves of 32 per wave), two per CU (two waves per SIMD, 256
-  // registers each), a 3-tile ring. Causal: 4-wave workgroups of 128 queries with a 4-tile ring, two per CU, which
-  // balanced the triangular work best.
+  // Unmasked: from 512 queries on, the eight-wave ping-pong kernel; below, 4-wave workgroups of 256 queries (two
+  // halves of 32 per wave), two per CU (two waves per SIMD, 256 registers each), a 3-tile ring; up to 256 queries
+  // (short sequences, where a call is bound by latency), 128-query workgroups with one half per wave and a 2-tile
+  // ring, so that no wave runs with queries all past n_q at 128 queries and more workgroups share the work.
+  // Causal: 4-wave workgroups of 128 queries with a 4-tile ring, two per CU, which balanced the triangular work best;
+  // up to 512 queries, 2-wave workgroups of 64 queries (four per CU, 2-tile ring), for shorter chains per workgroup.
+  // (Measured with the calls replayed from a HIP graph: B=32 h=8 n=128 6.8 -> 5.8 us, B=16 h=8 n_q=200 n_k=256
+  // 9.0 -> 6.8 us, causal B=32 h=8 n=256 9.5 -> 9.1 us.)
   // Other head widths: d = 32 as d = 64 (tiles of half the size; unmasked with a 4-tile ring); d = 128 with one
   // query half per wave and a 2-tile ring of 64 KB: unmasked in one 8-wave workgroup per CU, causal and windowed in
   // two 4-wave workgroups per CU (the smaller blocks balance the triangular work).
@@ -502,7 +507,9 @@ hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int d, hipStream_t stream) {
     case 64:
       if (a.windowed) return launch<64, 4, 1, 2, 4, true>(a, stream);
       if (!a.causal && a.n_q >= 512) return launch_attn_fwd_pp_bf16(a, stream);
+      if (!a.causal && a.n_q <= 256) return launch<64, 4, 1, 2, 2>(a, stream);
       if (!a.causal) return launch<64, 4, 2, 2, 3>(a, stream);
+      if (a.n_q <= 512) return launch<64, 2, 1, 4, 2>(a, stream);
       return launch<64, 4, 1, 2, 4>(a, stream);
     case 32:
       if (a.windowed) return launch<32, 4, 1, 2, 4, true>(a, stream);

@@ -2,10 +2,10 @@
 //
 // Same mathematics as the bf16 kernel (softmax(Q K^T / sqrt(D)) V per head, optional causal mask; "Attention Is All
 // You Need" (lettle.cn translation), section 3.2.1), but every value stays fp32, including the softmax weights that
-// multiply V. This path serves small fp32 problems, so it is a plain VALU kernel: one thread per query row (two for
-// D = 128, each with half of the row's dimensions, their partial dot products added across the lane pair) keeps q
-// and its output accumulator in registers, key/value tiles are staged in LDS and read as wave-wide broadcasts, and
-// the softmax is streamed tile by tile (running max, rescaled running sum).
+// multiply V. This path serves small fp32 problems, so it is a plain VALU kernel: D/16 threads per query row, each
+// with sixteen of the row's dimensions in registers (q and its share of the output accumulator; the partial dot
+// products are added across the row's lanes), key/value tiles staged in LDS and read as broadcasts, and the softmax
+// streamed tile by tile (running max, rescaled running sum). A workgroup is one wave of 64 / (D/16) query rows.
 #include "device_common.h"
 #include "launch.h"
 
@@ -14,18 +14,23 @@
 namespace mi355 {
 namespace {
 
-constexpr int kBQ = 64;   // queries per workgroup
-constexpr int kBK = 32;   // keys per tile
+constexpr int kThreads = 64;  // one wave per workgroup
+constexpr int kBK = 32;       // keys per tile
+constexpr int kDT = 16;       // dimensions of a row per thread
+
+// threads per query row (D / 16): a thread's share of every K and V row is four 16-byte LDS reads, so one wave issues
+// a quarter of the LDS reads that one thread per row would (those reads, not the arithmetic, set this kernel's time)
+template <int D>
+constexpr int threads_per_row() { return D / kDT; }
+// queries per workgroup
+template <int D>
+constexpr int rows_per_block() { return kThreads / threads_per_row<D>(); }
 
 template <int D>
-constexpr int threads_per_row() { return D > 64 ? 2 : 1; }
-
-template <int D>
-__global__ __launch_bounds__(kBQ * threads_per_row<D>()) void attn_fwd_f32(AttnArgs a, int n_qblocks, float c) {
+__global__ __launch_bounds__(kThreads) void attn_fwd_f32(AttnArgs a, int n_qblocks, float c) {
   constexpr int kD = D;
   constexpr int kTPR = threads_per_row<D>();
-  constexpr int kDT = D / kTPR;  // dimensions per thread
-  constexpr int kThreads = kBQ * kTPR;
+  constexpr int kBQ = rows_per_block<D>();
   __shared__ __attribute__((aligned(16))) float Ks[kBK * kD];
   __shared__ __attribute__((aligned(16))) float Vs[kBK * kD];
 
@@ -76,10 +81,14 @@ __global__ __launch_bounds__(kBQ * threads_per_row<D>()) void attn_fwd_f32(AttnA
     float mx = -INFINITY;
 #pragma unroll
     for (int j = 0; j < kBK; ++j) {
-      float acc = 0.f;
+      // four partial sums over d mod 4: four independent fma chains of D/4 (one chain of D would serialise on the
+      // fma latency)
+      float acc4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int d = 0; d < kDT; ++d) acc = fmaf(q[d], Ks[j * kD + part * kDT + d], acc);
-      if constexpr (kTPR == 2) acc += __shfl_xor(acc, 1);  // (the same sum in both lanes of the row)
+      for (int d = 0; d < kDT; ++d) acc4[d & 3] = fmaf(q[d], Ks[j * kD + part * kDT + d], acc4[d & 3]);
+      float acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+#pragma unroll
+      for (int off = 1; off < kTPR; off <<= 1) acc += __shfl_xor(acc, off);  // (the same sum in every lane of the row)
       const int key = k0 + j;
       if (key >= n_k || (a.causal && key > qi) || (a.windowed && (key > qi + a.window || key < qi - a.window)))
         acc = -INFINITY;
@@ -117,25 +126,26 @@ __global__ __launch_bounds__(kBQ * threads_per_row<D>()) void attn_fwd_f32(AttnA
 }  // namespace
 
 hipError_t launch_attn_fwd_f32(const AttnArgs& a, int d, hipStream_t stream) {
-  const int n_qblocks = (a.n_q + kBQ - 1) / kBQ;
+  if (d != 32 && d != 64 && d != 128) return hipErrorInvalidValue;
+  const int rows = kThreads / (d / kDT);
+  const int n_qblocks = (a.n_q + rows - 1) / rows;
   const int64_t nblocks = (int64_t)n_qblocks * a.B * a.H;
   if (nblocks <= 0 || nblocks > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid((unsigned)nblocks);
   // c = log2(e) / sqrt(d)
   switch (d) {
     case 32:
-      hipLaunchKernelGGL(attn_fwd_f32<32>, grid, dim3(kBQ), 0, stream, a, n_qblocks,
+      hipLaunchKernelGGL(attn_fwd_f32<32>, grid, dim3(kThreads), 0, stream, a, n_qblocks,
                          (float)(1.4426950408889634 / 5.656854249492381));
       break;
     case 64:
-      hipLaunchKernelGGL(attn_fwd_f32<64>, grid, dim3(kBQ), 0, stream, a, n_qblocks, (float)(1.4426950408889634 / 8.0));
-      break;
-    case 128:
-      hipLaunchKernelGGL(attn_fwd_f32<128>, grid, dim3(2 * kBQ), 0, stream, a, n_qblocks,
-                         (float)(1.4426950408889634 / 11.313708498984761));
+      hipLaunchKernelGGL(attn_fwd_f32<64>, grid, dim3(kThreads), 0, stream, a, n_qblocks,
+                         (float)(1.4426950408889634 / 8.0));
       break;
     default:
-      return hipErrorInvalidValue;
+      hipLaunchKernelGGL(attn_fwd_f32<128>, grid, dim3(kThreads), 0, stream, a, n_qblocks,
+                         (float)(1.4426950408889634 / 11.313708498984761));
+      break;
   }
   return hipGetLastError();
 }
