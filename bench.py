@@ -113,6 +113,7 @@ def hbm_bytes(w):
 
 
 KERNEL_SOURCES = ("transformer_head_scaled_02_amd/csrc/attn_fwd_bf16.hip",
+                  "transformer_head_scaled_02_amd/csrc/attn_fwd_pp_bf16.hip",
                   "transformer_head_scaled_02_amd/csrc/attn_tile.h",
                   "transformer_head_scaled_02_amd/csrc/device_common.h")
 
@@ -128,10 +129,10 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from the committed rocprofv3 --pmc summary for this kernel and workload, or None when
-    there is none or the kernel source has changed since the counters were taken."""
-    f = PROFILES / f"{kernel}_{workload}_hbm_traffic.json"
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary for this workload's attention kernel, or None
+    when there is none or the kernel source has changed since the counters were taken."""
+    f = PROFILES / f"{workload}_hbm_traffic.json"
     if not f.exists():
         return None
     try:
@@ -143,10 +144,34 @@ def measured_traffic(kernel: str, workload: str):
     return d.get("bytes_per_launch")
 
 
-def time_steps(step, steps: int, warmup: int, stream):
-    """W untimed warm-up calls, then exactly K calls timed with HIP events recorded on `stream` (the stream the
-    library launches on), bracketed by device synchronisation. Returns (ms per call, wall seconds of the region)."""
+PREWARM = {"ms": 0.0, "calls": 0}
+
+
+def prewarm(step, ms: float):
+    """Untimed calls for about `ms` milliseconds before the warm-up steps. Coming out of idle, the GPU raises its
+    clock over the first few milliseconds of load (measured: the first 50 back-to-back long-sequence calls averaged
+    161 us per call, the same calls a few milliseconds later 135 us), so a handful of warm-up calls still falls in
+    that ramp; this brings the chip to the state a sustained workload runs in. Recorded in the output line."""
     import torch
+    if ms <= 0:
+        return
+    t0 = time.perf_counter()
+    calls = 0
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(8):
+            step()
+        calls += 8
+        torch.cuda.synchronize()
+    PREWARM["ms"] = round((time.perf_counter() - t0) * 1e3, 1)
+    PREWARM["calls"] += calls
+
+
+def time_steps(step, steps: int, warmup: int, stream, prewarm_ms: float = 0.0):
+    """Untimed pre-warm (about `prewarm_ms` milliseconds of calls), W untimed warm-up calls, then exactly K calls
+    timed with HIP events recorded on `stream` (the stream the library launches on), bracketed by device
+    synchronisation. Returns (ms per call, wall seconds of the region)."""
+    import torch
+    prewarm(step, prewarm_ms)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -326,7 +351,7 @@ def bench_backward(args, w, x, m, dev):
     def step():
         m.sdpa_backward(q, k, v, out, do, lse, mask=mask, dq=dq, dk=dk, dv=dv, workspace=ws)
 
-    ms, wall = time_steps(step, args.steps, args.warmup, stream)
+    ms, wall = time_steps(step, args.steps, args.warmup, stream, args.prewarm_ms)
     reps = repeat_median(step, stream, ms, args.repeats)
 
     # parity of the last timed step on one whole head (float64 oracle, same inputs)
@@ -353,6 +378,7 @@ def bench_backward(args, w, x, m, dev):
                      "algorithmic_hbm_GBps": round(hbm_bytes_bwd(w) / (ms * 1e-3) / 1e9, 1)},
         "wall_s_timed_region": round(wall, 4),
         "timing_repeats": reps,
+        "prewarm": dict(PREWARM),
         "parity_last_step_head0": errs,
     }
 
@@ -369,7 +395,7 @@ def bench_window(args, w, x, m, dev):
     def step():
         m.sdpa_forward_window(q, k, v, w["window"], out=out)
 
-    ms, wall = time_steps(step, args.steps, args.warmup, stream)
+    ms, wall = time_steps(step, args.steps, args.warmup, stream, args.prewarm_ms)
     reps = repeat_median(step, stream, ms, args.repeats)
     rows = np.array([0, 1, 255, 256, 2047, w["n_q"] - 1])
     ref = sdpa_ref(x["Q"].f64[0, 0, rows], x["K"].f64[0, 0], x["V"].f64[0, 0], q_index=rows, window=w["window"])
@@ -387,6 +413,7 @@ def bench_window(args, w, x, m, dev):
                      "kernel": "attn_fwd_bf16<64, 4, 1, 2, 4, true>"},
         "wall_s_timed_region": round(wall, 4),
         "timing_repeats": reps,
+        "prewarm": dict(PREWARM),
         "parity_last_step": {"max_abs": float(err.max()), "mean_abs": float(err.mean())},
     }
 
@@ -404,7 +431,7 @@ def bench_padded(args, w, x, m, dev):
     def step():
         m.sdpa_forward_padded(q, k, v, lens, out=out)
 
-    ms, wall = time_steps(step, args.steps, args.warmup, stream)
+    ms, wall = time_steps(step, args.steps, args.warmup, stream, args.prewarm_ms)
     reps = repeat_median(step, stream, ms, args.repeats)
     got = out.float().cpu().numpy()
     rows = np.array([0, 1, 127, 128, 2047, w["n_q"] - 1])
@@ -426,6 +453,7 @@ def bench_padded(args, w, x, m, dev):
                      "frac": round(value / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": "attn_fwd_bf16<64, 4, 2, 2, 3, false>"},
         "wall_s_timed_region": round(wall, 4),
         "timing_repeats": reps,
+        "prewarm": dict(PREWARM),
         "parity_last_step": {"max_abs": float(err.max()), "mean_abs": float(err.mean())},
     }
 
@@ -445,7 +473,7 @@ def bench_mha(args, w, x, m, dev):
     def step():
         m.mha_forward(xq, xq, *ws_t, h=w["h"], out=out, workspace=work)
 
-    ms, wall = time_steps(step, args.steps, args.warmup, stream)
+    ms, wall = time_steps(step, args.steps, args.warmup, stream, args.prewarm_ms)
     reps = repeat_median(step, stream, ms, args.repeats)
     ref = mha_ref(x["Xq"].f64[:2], x["Xq"].f64[:2], *(x[nm].f64 for nm in ("Wq", "Wk", "Wv", "Wo")), h=w["h"])
     d = np.abs(out[:2].float().cpu().numpy() - ref)
@@ -463,6 +491,7 @@ def bench_mha(args, w, x, m, dev):
                      "kernel": "mha_forward step (3 launches)"},
         "wall_s_timed_region": round(wall, 4),
         "timing_repeats": reps,
+        "prewarm": dict(PREWARM),
         "parity_last_step_first2": {"max_abs": float(d.max()), "mean_abs": float(d.mean())},
     }
 
@@ -484,7 +513,7 @@ def bench_encoder(args, w, x, m, dev):
     def step():
         m.encoder_layer_forward(X, *ts, h=w["h"], eps=w["eps"], out=out, workspace=ws)
 
-    ms, wall = time_steps(step, args.steps, args.warmup, stream)
+    ms, wall = time_steps(step, args.steps, args.warmup, stream, args.prewarm_ms)
     reps = repeat_median(step, stream, ms, args.repeats)
     ref = encoder_layer_ref(x["X"].f64[:2], *(x[nm].f64 for nm in names), w["h"], w["eps"])
     d = np.abs(out[:2].float().cpu().numpy() - ref)
@@ -503,6 +532,7 @@ def bench_encoder(args, w, x, m, dev):
                      "kernel": "encoder_layer_forward step (7 launches)"},
         "wall_s_timed_region": round(wall, 4),
         "timing_repeats": reps,
+        "prewarm": dict(PREWARM),
         "parity_last_step_first2": {"max_abs": float(d.max()), "mean_abs": float(d.mean())},
     }
 
@@ -521,6 +551,12 @@ def main():
     ap.add_argument("--rotate-mb", type=float, default=0.0,
                     help="also time the call cycling over input/output copies totalling more than this many MiB")
     ap.add_argument("--no-smi", action="store_true", help="skip the amd-smi clock/power snapshots")
+    ap.add_argument("--sustain-s", type=float, default=2.0,
+                    help="after the timed region, seconds of held load whose last calls are timed again (reported "
+                         "beside the value)")
+    ap.add_argument("--prewarm-ms", type=float, default=200.0,
+                    help="untimed calls for about this many milliseconds before the warm-up steps (the GPU's clock "
+                         "ramps up over the first milliseconds of load)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain copy of known size (for scaling HBM byte counters)")
     args = ap.parse_args()
@@ -580,7 +616,7 @@ def main():
         m.sdpa_forward(q, k, v, mask=mask, out=out)
 
     smi_before = None if args.no_smi else smi_snapshot()
-    ms, wall = time_steps(step, args.steps, args.warmup, stream)
+    ms, wall = time_steps(step, args.steps, args.warmup, stream, args.prewarm_ms)
     reps = repeat_median(step, stream, ms, args.repeats)
     smi_load = None if args.no_smi else smi_under_load(step)
 
@@ -620,8 +656,13 @@ def main():
     # algorithmic byte) is above the ridge of the bf16 peak over the HBM peak, HBM otherwise
     intensity = flops_algorithmic(w) / hbm_bytes(w)
     dtype_peak = PEAK_BF16_TFLOPS if w["dtype"] == "bf16" else PEAK_F32_TFLOPS
-    kernel = (f"attn_fwd_bf16<{w['d_k']}, ...>" if w["dtype"] == "bf16" else f"attn_fwd_f32<{w['d_k']}>")
-    traffic = measured_traffic(f"attn_fwd_bf16_d{w['d_k']}", args.workload) if w["dtype"] == "bf16" else None
+    if w["dtype"] != "bf16":
+        kernel = f"attn_fwd_f32<{w['d_k']}>"
+    elif w["d_k"] == 64 and not w["causal"] and w["n_q"] >= 512:
+        kernel = "attn_fwd_pp_bf16 (eight-wave ping-pong)"
+    else:
+        kernel = f"attn_fwd_bf16<{w['d_k']}, ...>"
+    traffic = measured_traffic(args.workload) if w["dtype"] == "bf16" else None
     if intensity * PEAK_HBM_GBS * 1e9 / 1e12 >= dtype_peak:
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": dtype_peak, "unit": "TFLOP/s",
                 "frac": round(achieved / dtype_peak, 4)}
@@ -645,11 +686,24 @@ def main():
         "roofline": roof,
         "wall_s_timed_region": round(wall, 4),
         "timing_repeats": reps,
+        "prewarm": dict(PREWARM),
         "parity_last_step": {"max_abs": float(err.max()), "mean_abs": float(err.mean())},
         "gpu_state": {"before": smi_before, "under_load": smi_load},
     }
     if reps is not None:
         rec["value_at_repeat_median"] = round(flops_metric(w) / (reps["median_ms"] * 1e-3) / 1e12, 2)
+    if args.sustain_s > 0:
+        # held load: calls back to back for sustain_s seconds, the last >= 5 ms of them timed (the clock a long run
+        # settles at, warmth included)
+        import torch
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < args.sustain_s:
+            for _ in range(16):
+                step()
+            torch.cuda.synchronize()
+        last = repeat_median(step, stream, ms, 1)
+        rec["sustained"] = {"seconds": args.sustain_s, "ms_per_call_at_end": last["median_ms"],
+                            "value_at_end": round(flops_metric(w) / (last["median_ms"] * 1e-3) / 1e12, 2)}
     if cold is not None:
         rec["cold"] = cold
     if not args.no_probes:
