@@ -7,11 +7,14 @@ library has not been built, loading fails loudly: there is no fallback.
 from __future__ import annotations
 
 import ctypes
+import os
 from pathlib import Path
 
 import torch
 
-LIB_PATH = Path(__file__).resolve().parent / "libmi355_attn.so"
+# The library this package loads: the in-tree build, or another build of the same sources named by MI355_ATTN_LIB
+# (the host-sanitized copy the CPU argument-checking tests run against).
+LIB_PATH = Path(os.environ.get("MI355_ATTN_LIB") or Path(__file__).resolve().parent / "libmi355_attn.so")
 
 ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
 ATTN_MASK_NONE, ATTN_MASK_CAUSAL = 0, 1
