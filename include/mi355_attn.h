@@ -51,7 +51,12 @@ typedef enum {
 } attn_status;
 
 typedef enum { ATTN_MASK_NONE = 0, ATTN_MASK_CAUSAL = 1 } attn_mask_kind;
-typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
+typedef enum {
+  ATTN_F32 = 0,
+  ATTN_BF16 = 1,
+  ATTN_BF16_F32O = 2 /* sdpa_backward only: bf16 tensors except O, which is the float32 forward output (out_f32 of
+                        sdpa_forward_train) */
+} attn_dtype;
 
 /* Size limits (ATTN_ERR_UNSUPPORTED beyond them). */
 #define ATTN_MAX_SEQ   (1 << 24) /* n_q, n_k */
@@ -106,6 +111,24 @@ int sdpa_forward_window(const void* Q, const void* K, const void* V, int64_t win
                         float* lse, int dtype, int64_t B, int64_t h, int64_t n_q, int64_t n_k, int64_t d_k,
                         int64_t d_v, void* stream);
 
+/* sdpa_forward_train: the forward pass of training, in one entry point for every mask: sdpa_forward_lse,
+ * sdpa_forward_padded (kv_len != NULL) or sdpa_forward_window (window >= 0), which can also keep the output before
+ * its rounding to bf16 for the backward pass ("Transformer：抛弃循环与卷积的序列建模", section "训练样本", subsection
+ * "反向传播": the loss is carried back through the forward computation, which needs what the forward pass produced).
+ *   kv_len: NULL or the key padding, as for sdpa_forward_padded.
+ *   window: -1 for none, or the radius of restricted self-attention as for sdpa_forward_window (requires n_q == n_k
+ *           and kv_len == NULL: ATTN_ERR_UNSUPPORTED otherwise).
+ *   out [B, h, n_q, d_v] in dtype, and lse [B, h, n_q] float32 (required), as for sdpa_forward_lse.
+ *   out_f32: NULL, or for ATTN_BF16 a float32 [B, h, n_q, d_v] tensor that receives the output before it is rounded
+ *            to bf16 (out is exactly its round-to-nearest-even). Passing it to sdpa_backward with dtype
+ *            ATTN_BF16_F32O lets the backward pass form D_i = dO_i . O_i from the unrounded output: where the weights
+ *            are nearly one-hot, dP - D is a small difference of two nearly equal numbers and the bf16 rounding of
+ *            O would dominate it. ATTN_F32 with out_f32 != NULL: ATTN_ERR_INVALID.
+ *   Other arguments, requirements and errors as sdpa_forward_lse; out_f32 must not overlap any other tensor. */
+int sdpa_forward_train(const void* Q, const void* K, const void* V, const int32_t* kv_len, int64_t window,
+                       int mask_kind, void* out, float* out_f32, float* lse, int dtype, int64_t B, int64_t h,
+                       int64_t n_q, int64_t n_k, int64_t d_k, int64_t d_v, void* stream);
+
 /* sdpa_backward: gradients of attention.
  *   Q, K, V      the forward inputs, as for sdpa_forward
  *   O   [B, h, n_q, d_v]  the forward output and lse [B, h, n_q] float32 its row log-sum-exp (sdpa_forward_lse, or
@@ -121,7 +144,9 @@ int sdpa_forward_window(const void* Q, const void* K, const void* V, int64_t win
  *   workspace: device scratch of at least sdpa_backward_workspace_size(...) bytes, 16-byte aligned, owned by the
  *              caller (it holds per-row lse and D between the three launches).
  *   dtype: ATTN_BF16 (bf16 tensors, float32 accumulation, P and dS rounded to bf16 where they enter the matrix core,
- *          outputs rounded to nearest even) or ATTN_F32 (float32 throughout). lse is float32 in both.
+ *          outputs rounded to nearest even), ATTN_BF16_F32O (the same, but O is the float32 out_f32 of
+ *          sdpa_forward_train, so D is formed from the unrounded output) or ATTN_F32 (float32 throughout). lse is
+ *          float32 in all three.
  *   Requirements as sdpa_forward, but d_k = d_v in {32, 64} (ATTN_ERR_UNSUPPORTED otherwise). dQ, dK, dV and the
  *   workspace must not overlap each other or any input. Every element of dQ, dK and dV is written. */
 int sdpa_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse,

@@ -271,3 +271,32 @@ def test_mha_noalloc_rejects_bad_arguments(lib, kw, code):
     assert mha_noalloc(lib, **kw) == code
     if kw.get("B") == 64:
         assert b"scratch" in lib.attn_last_error()
+
+
+def train(lib, Q=A, K=A * 2, V=A * 3, kv_len=None, window=-1, mask=0, out=A * 1000, out32=None, lse=A * 1100,
+          dtype=BF16, B=1, h=1, n_q=16, n_k=16, d_k=64, d_v=64):
+    return lib.sdpa_forward_train(Q, K, V, kv_len, window, mask, out, out32, lse, dtype, B, h, n_q, n_k, d_k, d_v,
+                                  None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(lse=None), INVALID), (dict(Q=None), INVALID), (dict(out=None), INVALID),
+    # out_f32 is for bf16 only; aligned; [1,1,16,64] float32 = 4 KiB must not overlap out, Q or lse
+    (dict(out32=A * 1200, dtype=F32), INVALID), (dict(out32=A * 1200 + 4), INVALID),
+    (dict(out32=A * 1000 + 512), INVALID), (dict(out32=A + 64), INVALID), (dict(out32=A * 1100 - 2048), INVALID),
+    (dict(window=3, n_k=32), UNSUPPORTED), (dict(window=3, kv_len=A * 7), UNSUPPORTED),
+    (dict(dtype=m.ATTN_BF16_F32O), UNSUPPORTED), (dict(d_k=48, d_v=48), UNSUPPORTED),
+    (dict(mask=1, n_k=17), UNSUPPORTED), (dict(kv_len=A * 7 + 4), INVALID), (dict(mask=2), INVALID),
+])
+def test_sdpa_forward_train_rejects_bad_arguments(lib, kw, code):
+    assert train(lib, **kw) == code
+    assert lib.attn_last_error().decode().startswith("sdpa_forward_train")
+
+
+def test_backward_with_f32_output_checks_its_size(lib):
+    # O float32 [1,1,16,64] = 4 KiB at A*4: dQ 2 KiB + 16 bytes in overlaps it only when O is counted as float32
+    assert bwd(lib, dtype=m.ATTN_BF16_F32O, dQ=A * 4 + 2048 + 16) == INVALID
+    assert "overlaps" in lib.attn_last_error().decode()
+    assert bwd(lib, dtype=m.ATTN_BF16_F32O, O=None) == INVALID
+    assert bwd(lib, dtype=m.ATTN_BF16_F32O, d_k=128, d_v=128) == UNSUPPORTED
+    assert lib.sdpa_backward_workspace_size(m.ATTN_BF16_F32O, 4, 8, 4096, 4096, 64, 64) == 4 * 8 * 64 * 1024

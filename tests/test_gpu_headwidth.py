@@ -231,8 +231,8 @@ def test_headwidth_autograd_wrapper():
     q, k, v, do = (to_dev(x[nm]) for nm in ("Q", "K", "V", "dO"))
     qa, ka, va = (t.clone().requires_grad_(True) for t in (q, k, v))
     m.attention(qa, ka, va, mask="causal").backward(do)
-    out, lse = m.sdpa_forward_lse(q, k, v, mask="causal")
-    dq, dk, dv = m.sdpa_backward(q, k, v, out, do, lse, mask="causal")
+    out, out32, lse = m.sdpa_forward_train(q, k, v, "causal")  # the wrapper keeps the float32 output for D
+    dq, dk, dv = m.sdpa_backward(q, k, v, out32, do, lse, mask="causal")
     torch.cuda.synchronize()
     assert torch.equal(qa.grad, dq) and torch.equal(ka.grad, dk) and torch.equal(va.grad, dv)
 

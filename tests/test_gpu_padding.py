@@ -175,7 +175,8 @@ def test_autograd_wrapper_with_padding():
     lens = _lens([96, 40, 0])
     qa, ka, va = (t.clone().requires_grad_(True) for t in (q, k, v))
     m.attention(qa, ka, va, mask="causal", kv_len=lens).backward(do)
-    out, lse = m.sdpa_forward_padded(q, k, v, lens, mask="causal", return_lse=True)
-    dq, dk, dv = m.sdpa_backward(q, k, v, out, do, lse, mask="causal", kv_len=lens)
+    # the wrapper keeps the float32 output for D (sdpa_forward_train's out_f32)
+    out, out32, lse = m.sdpa_forward_train(q, k, v, "causal", kv_len=lens)
+    dq, dk, dv = m.sdpa_backward(q, k, v, out32, do, lse, mask="causal", kv_len=lens)
     torch.cuda.synchronize()
     assert torch.equal(qa.grad, dq) and torch.equal(ka.grad, dk) and torch.equal(va.grad, dv)

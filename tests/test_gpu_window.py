@@ -124,7 +124,7 @@ def test_autograd_wrapper_with_window():
     q, k, v, do = (to_dev(x[nm]) for nm in ("Q", "K", "V", "dO"))
     qa, ka, va = (t.clone().requires_grad_(True) for t in (q, k, v))
     m.attention(qa, ka, va, window=40).backward(do)
-    out, lse = m.sdpa_forward_window(q, k, v, 40, return_lse=True)
-    dq, dk, dv = m.sdpa_backward(q, k, v, out, do, lse, window=40)
+    out, out32, lse = m.sdpa_forward_train(q, k, v, window=40)  # the wrapper keeps the float32 output for D
+    dq, dk, dv = m.sdpa_backward(q, k, v, out32, do, lse, window=40)
     torch.cuda.synchronize()
     assert torch.equal(qa.grad, dq) and torch.equal(ka.grad, dk) and torch.equal(va.grad, dv)

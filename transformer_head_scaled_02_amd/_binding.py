@@ -18,10 +18,11 @@ LIB_PATH = Path(os.environ.get("MI355_ATTN_LIB") or Path(__file__).resolve().par
 
 ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
 ATTN_MASK_NONE, ATTN_MASK_CAUSAL = 0, 1
-ATTN_F32, ATTN_BF16 = 0, 1
+ATTN_F32, ATTN_BF16, ATTN_BF16_F32O = 0, 1, 2
 
 # every symbol include/mi355_attn.h declares
-EXPORTED = ("sdpa_forward", "sdpa_forward_lse", "sdpa_forward_padded", "sdpa_forward_window", "sdpa_backward", "sdpa_backward_workspace_size", "mha_forward", "mha_forward_noalloc",
+EXPORTED = ("sdpa_forward", "sdpa_forward_lse", "sdpa_forward_padded", "sdpa_forward_window", "sdpa_forward_train",
+            "sdpa_backward", "sdpa_backward_workspace_size", "mha_forward", "mha_forward_noalloc",
             "encoder_layer_forward", "encoder_layer_workspace_size",
             "mha_workspace_size", "attn_status_string", "attn_last_error", "probe_scratch_size", "probe_mfma_bf16", "probe_exp_f32", "probe_hbm_copy")
 
@@ -53,6 +54,8 @@ def load_library(path: Path | str | None = None) -> ctypes.CDLL:
     lib.sdpa_forward_padded.restype = ci
     lib.sdpa_forward_window.argtypes = [vp, vp, vp, i64, ci, vp, vp, ci, i64, i64, i64, i64, i64, i64, vp]
     lib.sdpa_forward_window.restype = ci
+    lib.sdpa_forward_train.argtypes = [vp, vp, vp, vp, i64, ci, vp, vp, vp, ci, i64, i64, i64, i64, i64, i64, vp]
+    lib.sdpa_forward_train.restype = ci
     lib.sdpa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, ci, vp, vp, vp, vp, sz, ci, i64, i64, i64, i64, i64,
                                   i64, vp]
     lib.sdpa_backward.restype = ci
@@ -222,6 +225,26 @@ def sdpa_forward_window(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, windo
     return (out, lse) if want_lse else out
 
 
+def sdpa_forward_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask="none", kv_len=None, window=None,
+                       keep_f32: bool = True, out: torch.Tensor | None = None, out_f32: torch.Tensor | None = None,
+                       lse: torch.Tensor | None = None):
+    """The training forward pass for every mask (key padding with `kv_len`, restricted attention with `window`):
+    returns (out, out_f32, lse). For bf16 inputs with keep_f32 (or when `out_f32` is passed), out_f32 [B,h,n_q,d]
+    float32 is the output before its rounding to bf16, from which sdpa_backward forms D = dO . O; otherwise None."""
+    lib = load_library()
+    q, k, v, (B, h, n_q, n_k, d_k, d_v) = _sdpa_shapes(q, k, v)
+    out = _out_tensor(out, "out", (B, h, n_q, d_v), q.dtype, q.device)
+    lse = _out_tensor(lse, "lse", (B, h, n_q), torch.float32, q.device)
+    want32 = q.dtype == torch.bfloat16 and (keep_f32 or out_f32 is not None)
+    if want32:
+        out_f32 = _out_tensor(out_f32, "out_f32", (B, h, n_q, d_v), torch.float32, q.device)
+    kv_ptr = _kv_len_tensor(kv_len, B, q.device).data_ptr() if kv_len is not None else None
+    _check(lib.sdpa_forward_train(q.data_ptr(), k.data_ptr(), v.data_ptr(), kv_ptr, -1 if window is None else int(window),
+                                  _mask_code(mask), out.data_ptr(), out_f32.data_ptr() if want32 else None,
+                                  lse.data_ptr(), _dtype_code(q), B, h, n_q, n_k, d_k, d_v, _stream_handle(q.device)))
+    return out, (out_f32 if want32 else None), lse
+
+
 def sdpa_backward_workspace_size(B: int, h: int, n_q: int, n_k: int, d_k: int = 64, d_v: int = 64,
                                  dtype: torch.dtype = torch.bfloat16) -> int:
     lib = load_library()
@@ -235,12 +258,15 @@ def sdpa_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.
                   kv_len: torch.Tensor | None = None, window: int | None = None):
     """Gradients (dq, dk, dv) of attention given the forward's output `out`, its `lse` (from sdpa_forward_lse, or
     sdpa_forward_padded with the same `kv_len`) and the upstream gradient `dout` [B,h,n_q,d], d in {32, 64}.
-    `workspace` (uint8, at least sdpa_backward_workspace_size bytes) may be passed in to avoid an allocation."""
+    For bf16 inputs `out` may be the float32 out_f32 of sdpa_forward_train (D = dO . O is then formed from the
+    unrounded output). `workspace` (uint8, at least sdpa_backward_workspace_size bytes) may be passed in to avoid an
+    allocation."""
     lib = load_library()
     q, k, v, (B, h, n_q, n_k, d_k, d_v) = _sdpa_shapes(q, k, v)
     out, dout, lse = _dev_tensor(out, "out"), _dev_tensor(dout, "dout"), _dev_tensor(lse, "lse")
-    for t, name in ((out, "out"), (dout, "dout")):
-        if tuple(t.shape) != (B, h, n_q, d_v) or t.dtype != q.dtype or t.device != q.device:
+    o32 = q.dtype == torch.bfloat16 and out.dtype == torch.float32
+    for t, name, dt in ((out, "out", torch.float32 if o32 else q.dtype), (dout, "dout", q.dtype)):
+        if tuple(t.shape) != (B, h, n_q, d_v) or t.dtype != dt or t.device != q.device:
             raise ValueError(f"{name} must be [B, h, n_q, d_v] like the forward output")
     if tuple(lse.shape) != (B, h, n_q) or lse.dtype != torch.float32 or lse.device != q.device:
         raise ValueError("lse must be float32 [B, h, n_q]")
@@ -257,27 +283,22 @@ def sdpa_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.
     _check(lib.sdpa_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
                              lse.data_ptr(), kv_ptr, -1 if window is None else int(window), _mask_code(mask),
                              dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                             workspace.data_ptr(), ws_bytes, _dtype_code(q), B, h, n_q, n_k, d_k, d_v,
-                             _stream_handle(q.device)))
+                             workspace.data_ptr(), ws_bytes, ATTN_BF16_F32O if o32 else _dtype_code(q), B, h, n_q,
+                             n_k, d_k, d_v, _stream_handle(q.device)))
     return dq, dk, dv
 
 
 class SDPAFunction(torch.autograd.Function):
-    """torch.autograd wrapper: forward = sdpa_forward_lse (sdpa_forward_padded with kv_len), backward = sdpa_backward
-    (all in the HIP library)."""
+    """torch.autograd wrapper: forward = sdpa_forward_train, backward = sdpa_backward (all in the HIP library). For
+    bf16 the float32 output before rounding is kept for the backward pass (D = dO . O from the unrounded output)."""
 
     @staticmethod
     def forward(ctx, q, k, v, mask="none", kv_len=None, window=None):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
-        if window is not None:
-            if kv_len is not None:
-                raise ValueError("a window with key padding is not supported")
-            out, lse = sdpa_forward_window(q, k, v, window, mask, return_lse=True)
-        elif kv_len is None:
-            out, lse = sdpa_forward_lse(q, k, v, mask)
-        else:
-            out, lse = sdpa_forward_padded(q, k, v, kv_len, mask, return_lse=True)
-        ctx.save_for_backward(q, k, v, out, lse)
+        if window is not None and kv_len is not None:
+            raise ValueError("a window with key padding is not supported")
+        out, out32, lse = sdpa_forward_train(q, k, v, mask, kv_len=kv_len, window=window)
+        ctx.save_for_backward(q, k, v, out if out32 is None else out32, lse)
         ctx.mask, ctx.kv_len, ctx.window = mask, kv_len, window
         return out
 

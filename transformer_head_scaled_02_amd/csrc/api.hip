@@ -157,10 +157,13 @@ int check_sdpa_sizes(const char* fn, int dtype, int mask_kind, int64_t B, int64_
 
 int sdpa_forward_impl(const char* fn, const void* Q, const void* K, const void* V, const int32_t* kv_len,
                       int mask_kind, void* out, float* lse, int dtype, int64_t B, int64_t h, int64_t n_q, int64_t n_k,
-                      int64_t d_k, int64_t d_v, void* stream, int64_t window = -1) {
+                      int64_t d_k, int64_t d_v, void* stream, int64_t window = -1, float* out32 = nullptr) {
   if (int st = check_sdpa_sizes(fn, dtype, mask_kind, B, h, n_q, n_k, d_k, d_v, false)) return st;
-  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(out) || !aligned16(lse) || !aligned16(kv_len))
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(out) || !aligned16(lse) || !aligned16(kv_len) ||
+      !aligned16(out32))
     return fail_status(ATTN_ERR_INVALID, "%s: pointers must be 16-byte aligned", fn);
+  if (out32 && dtype != ATTN_BF16)
+    return fail_status(ATTN_ERR_INVALID, "%s: out_f32 is for ATTN_BF16 (the ATTN_F32 output is already float32)", fn);
   const size_t es = dtype == ATTN_BF16 ? 2 : 4;
   const size_t q_bytes = (size_t)B * h * n_q * d_k * es, kv_bytes = (size_t)B * h * n_k * d_k * es;
   if (overlaps(out, q_bytes, Q, q_bytes) || overlaps(out, q_bytes, K, kv_bytes) || overlaps(out, q_bytes, V, kv_bytes))
@@ -176,6 +179,14 @@ int sdpa_forward_impl(const char* fn, const void* Q, const void* K, const void* 
     if (overlaps(kv_len, len_bytes, out, q_bytes) || (lse && overlaps(kv_len, len_bytes, lse, (size_t)B * h * n_q * 4)))
       return fail_status(ATTN_ERR_INVALID, "%s: kv_len overlaps an output", fn);
   }
+  if (out32) {
+    const size_t o32_bytes = (size_t)B * h * n_q * d_v * 4;
+    if (overlaps(out32, o32_bytes, Q, q_bytes) || overlaps(out32, o32_bytes, K, kv_bytes) ||
+        overlaps(out32, o32_bytes, V, kv_bytes) || overlaps(out32, o32_bytes, out, q_bytes) ||
+        (lse && overlaps(out32, o32_bytes, lse, (size_t)B * h * n_q * 4)) ||
+        (kv_len && overlaps(out32, o32_bytes, kv_len, (size_t)B * 4)))
+      return fail_status(ATTN_ERR_INVALID, "%s: out_f32 overlaps another tensor", fn);
+  }
 
   mi355::AttnArgs a{};
   a.Q = Q; a.K = K; a.V = V; a.O = out;
@@ -188,6 +199,7 @@ int sdpa_forward_impl(const char* fn, const void* Q, const void* K, const void* 
   a.causal = mask_kind == ATTN_MASK_CAUSAL;
   a.lse = lse;
   a.kv_len = kv_len;
+  a.o32 = out32;
   if (window >= 0) {
     a.windowed = 1;
     a.window = (int)(window < n_k ? window : n_k);
@@ -241,9 +253,23 @@ ATTN_EXPORT int sdpa_forward_lse(const void* Q, const void* K, const void* V, in
                            stream);
 }
 
+ATTN_EXPORT int sdpa_forward_train(const void* Q, const void* K, const void* V, const int32_t* kv_len, int64_t window,
+                                   int mask_kind, void* out, float* out_f32, float* lse, int dtype, int64_t B,
+                                   int64_t h, int64_t n_q, int64_t n_k, int64_t d_k, int64_t d_v, void* stream) {
+  static const char* fn = "sdpa_forward_train";
+  if (!Q || !K || !V || !out || !lse) return fail_status(ATTN_ERR_INVALID, "%s: null tensor pointer", fn);
+  if (window >= 0 && n_q != n_k)
+    return fail_status(ATTN_ERR_UNSUPPORTED, "%s: restricted self-attention needs n_q == n_k (got %lld, %lld)", fn,
+                       (long long)n_q, (long long)n_k);
+  if (window >= 0 && kv_len)
+    return fail_status(ATTN_ERR_UNSUPPORTED, "%s: a window together with key padding is not implemented", fn);
+  return sdpa_forward_impl(fn, Q, K, V, kv_len, mask_kind, out, lse, dtype, B, h, n_q, n_k, d_k, d_v, stream,
+                           window < 0 ? -1 : window, out_f32);
+}
+
 ATTN_EXPORT size_t sdpa_backward_workspace_size(int dtype, int64_t B, int64_t h, int64_t n_q, int64_t n_k,
                                                 int64_t d_k, int64_t d_v) {
-  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return 0;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16 && dtype != ATTN_BF16_F32O) return 0;
   if (B <= 0 || h <= 0 || n_q <= 0 || n_k <= 0 || d_k != d_v || (d_k != 32 && d_k != 64)) return 0;
   if (n_q > ATTN_MAX_SEQ || n_k > ATTN_MAX_SEQ || B > ATTN_MAX_HEADS || h > ATTN_MAX_HEADS || B * h > ATTN_MAX_HEADS)
     return 0;
@@ -258,6 +284,8 @@ ATTN_EXPORT int sdpa_backward(const void* Q, const void* K, const void* V, const
   static const char* fn = "sdpa_backward";
   if (!Q || !K || !V || !O || !dO || !lse || !dQ || !dK || !dV || !workspace)
     return fail_status(ATTN_ERR_INVALID, "%s: null pointer", fn);
+  const bool o32 = dtype == ATTN_BF16_F32O;  // bf16 tensors, O float32
+  if (o32) dtype = ATTN_BF16;
   if (int st = check_sdpa_sizes(fn, dtype, mask_kind, B, h, n_q, n_k, d_k, d_v, true)) return st;
   if (window >= 0 && n_q != n_k)
     return fail_status(ATTN_ERR_UNSUPPORTED, "%s: a window needs n_q == n_k (got %lld, %lld)", fn, (long long)n_q,
@@ -274,7 +302,7 @@ ATTN_EXPORT int sdpa_backward(const void* Q, const void* K, const void* V, const
   const size_t q_b = (size_t)B * h * n_q * d_k * es, kv_b = (size_t)B * h * n_k * d_k * es;
   const size_t lse_b = (size_t)B * h * n_q * 4;
   const void* ins[] = {Q, K, V, O, dO, lse, kv_len};
-  const size_t in_b[] = {q_b, kv_b, kv_b, q_b, q_b, lse_b, kv_len ? (size_t)B * 4 : 0};
+  const size_t in_b[] = {q_b, kv_b, kv_b, o32 ? 2 * q_b : q_b, q_b, lse_b, kv_len ? (size_t)B * 4 : 0};
   void* outs[] = {dQ, dK, dV, workspace};
   const size_t out_b[] = {q_b, kv_b, kv_b, need};
   for (int i = 0; i < 4; ++i) {
@@ -293,6 +321,7 @@ ATTN_EXPORT int sdpa_backward(const void* Q, const void* K, const void* V, const
   a.B = (int)B; a.H = (int)h; a.n_q = (int)n_q; a.n_k = (int)n_k;
   a.causal = mask_kind == ATTN_MASK_CAUSAL;
   a.kv_len = kv_len;
+  a.o_f32 = o32;
   if (window >= 0) {
     a.windowed = 1;
     a.window = (int)(window < n_k ? window : n_k);

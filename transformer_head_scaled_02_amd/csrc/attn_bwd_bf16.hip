@@ -120,7 +120,8 @@ __device__ __forceinline__ void wait_copies(int ahead) {
 }
 
 // D_i = dO_i . O_i and log2(e) * lse_i for one 64-row query tile of one head (rows of D elements); 4 threads per row.
-template <class T, int D>
+// kO32: bf16 dO with the float32 (unrounded) forward output O.
+template <class T, int D, bool kO32 = false>
 __global__ __launch_bounds__(256) void attn_bwd_pre(BwdArgs a, int n_tiles) {
   const int bh = blockIdx.x / n_tiles, t = blockIdx.x % n_tiles;
   const int r = threadIdx.x >> 2, part = threadIdx.x & 3;
@@ -129,7 +130,22 @@ __global__ __launch_bounds__(256) void attn_bwd_pre(BwdArgs a, int n_tiles) {
   float dot = 0.f;
   if (row < n_q) {
     const int64_t base = ((int64_t)bh * n_q + row) * D + (D / 4) * part;
-    if constexpr (sizeof(T) == 2) {
+    if constexpr (sizeof(T) == 2 && kO32) {
+      const float4* o = reinterpret_cast<const float4*>(static_cast<const float*>(a.O) + base);
+      const uint4* d = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.dO) + base);
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) {
+        const uint4 dv = d[c];
+        const float4 o0 = o[2 * c], o1 = o[2 * c + 1];
+        const float of[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+        const uint32_t dw[4] = {dv.x, dv.y, dv.z, dv.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          dot = fmaf(of[2 * j], __uint_as_float(dw[j] << 16), dot);
+          dot = fmaf(of[2 * j + 1], __uint_as_float(dw[j] & 0xffff0000u), dot);
+        }
+      }
+    } else if constexpr (sizeof(T) == 2) {
       const uint4* o = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.O) + base);
       const uint4* d = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.dO) + base);
 #pragma unroll
@@ -547,6 +563,9 @@ hipError_t launch_attn_bwd_pre(const BwdArgs& a, bool f32, int d, hipStream_t st
   const dim3 grid((unsigned)nb);
   if (f32 && d == 64) hipLaunchKernelGGL((attn_bwd_pre<float, 64>), grid, dim3(256), 0, stream, a, n_tiles);
   else if (f32) hipLaunchKernelGGL((attn_bwd_pre<float, 32>), grid, dim3(256), 0, stream, a, n_tiles);
+  else if (a.o_f32 && d == 64)
+    hipLaunchKernelGGL((attn_bwd_pre<uint16_t, 64, true>), grid, dim3(256), 0, stream, a, n_tiles);
+  else if (a.o_f32) hipLaunchKernelGGL((attn_bwd_pre<uint16_t, 32, true>), grid, dim3(256), 0, stream, a, n_tiles);
   else if (d == 64) hipLaunchKernelGGL((attn_bwd_pre<uint16_t, 64>), grid, dim3(256), 0, stream, a, n_tiles);
   else hipLaunchKernelGGL((attn_bwd_pre<uint16_t, 32>), grid, dim3(256), 0, stream, a, n_tiles);
   return hipGetLastError();

@@ -344,6 +344,16 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_fwd_pp_bf16(AttnArgs a,
                            pack_bf16x2(o[h][mb][4 * rg + 2] * inv, o[h][mb][4 * rg + 3] * inv)};
           *reinterpret_cast<uint2*>(orow + 32 * mb + 8 * rg + 4 * g) = w;
         }
+      if (a.o32 != nullptr) {
+        float* frow = a.o32 + ((int64_t)bh * n_q + q) * 64;
+#pragma unroll
+        for (int mb = 0; mb < 64 / 32; ++mb)
+#pragma unroll
+          for (int rg = 0; rg < 4; ++rg)
+            *reinterpret_cast<float4*>(frow + 32 * mb + 8 * rg + 4 * g) =
+                float4{o[h][mb][4 * rg] * inv, o[h][mb][4 * rg + 1] * inv, o[h][mb][4 * rg + 2] * inv,
+                       o[h][mb][4 * rg + 3] * inv};
+      }
     }
   }
 }

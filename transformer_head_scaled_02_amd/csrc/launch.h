@@ -24,6 +24,9 @@ struct AttnArgs {
   const int* kv_len;
   // restricted self-attention (windowed != 0, n_q == n_k): query i sees keys j with |i - j| <= window only
   int windowed, window;
+  // optional (nullptr: not written), bf16 kernels only: the output before its rounding to bf16, float32, dense
+  // [B, H, n_q, D] whatever the strides of O (the operand from which the backward pass forms D = dO . O)
+  float* o32;
 };
 
 // d: the head width d_k = d_v, 32, 64 or 128 (every other value: hipErrorInvalidValue, nothing launched)
@@ -52,6 +55,7 @@ struct BwdArgs {
   int causal;
   const int* kv_len;  // optional key padding, as in AttnArgs; dK and dV rows of padding keys are written as 0
   int windowed, window;  // optional restricted self-attention, as in AttnArgs
+  int o_f32;             // bf16 tensors with O in float32 (AttnArgs::o32 of the forward pass)
 };
 constexpr int kAuxFloatsPerTile = 256;
 
