@@ -4,10 +4,11 @@ A step is one sdpa_forward call (scores, scale, mask, online softmax, weighted s
 over the long-sequence workload B=4, h=8, n_q=n_k=4096, d_k=d_v=64, bf16, unmasked, with Q/K/V ~ N(0,1) seeded and
 already resident in HBM. Metric: attention TFLOP/s = 4*B*h*n_q*n_k*d_k / time, against the bf16 dense MFMA peak.
 
-With a backward workload (--workload sdpa_bwd_bf16_b4_h8_n4096 or sdpa_bwd_causal_bf16_b4_h8_n4096) a step is one
-sdpa_backward call (pre-pass, dK/dV, dQ) on the same tensors plus a seeded upstream gradient, with the forward's
+With a backward workload (--workload sdpa_bwd_bf16_b4_h8_n4096, sdpa_bwd_causal_bf16_b4_h8_n4096, or the head widths
+32 and 128: sdpa_bwd_bf16_b4_h16_n4096_d32, sdpa_bwd_bf16_b4_h4_n4096_d128) a step is one sdpa_backward call
+(pre-pass, dK/dV, dQ) on the same tensors plus a seeded upstream gradient, with the training forward's float32
 output and log-sum-exp computed once before the timed region; metric: backward TFLOP/s = 10*B*h*n_q*n_k*d_k / time
-(the five n_q x n_k x 64 products the gradient needs).
+(the five n_q x n_k x d_k products the gradient needs).
 
 With --workload sdpa_padded_bf16_b4_h8_n4096 a step is one sdpa_forward_padded call on the same tensors treated as a
 length bucket (real key counts per batch entry in the workload); metric: TFLOP/s over the real (query, key) pairs.
@@ -101,10 +102,11 @@ def flops_algorithmic_bwd(w):
 
 
 def hbm_bytes_bwd(w):
-    # read Q, K, V, O, dO (and lse); write dQ, dK, dV
+    # read Q, K, V, O, dO (and lse); write dQ, dK, dV. O is the float32 output of the training forward pass (the
+    # operand D = dO . O is formed from), 4 bytes an element in both dtypes.
     es = 2 if w["dtype"] == "bf16" else 4
     nq, nk = w["n_q"], w["n_k"]
-    return w["B"] * w["h"] * (es * (3 * nq * w["d_k"] + 4 * nk * w["d_k"]) + es * nq * w["d_v"] + 4 * nq)
+    return w["B"] * w["h"] * (es * (3 * nq * w["d_k"] + 4 * nk * w["d_k"]) + 4 * nq * w["d_v"] + 4 * nq)
 
 
 def hbm_bytes(w):
@@ -342,14 +344,16 @@ def bench_backward(args, w, x, m, dev):
     from oracle import sdpa_backward_head
     q, k, v, do = (dev(x[n]) for n in ("Q", "K", "V", "dO"))
     mask = "causal" if w["causal"] else "none"
-    out, lse = m.sdpa_forward_lse(q, k, v, mask=mask)
+    # the training path: the forward keeps its float32 output, from which the backward forms D = dO . O
+    out, out32, lse = m.sdpa_forward_train(q, k, v, mask)
+    o_for_d = out32 if out32 is not None else out
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = torch.empty(m.sdpa_backward_workspace_size(w["B"], w["h"], w["n_q"], w["n_k"], w["d_k"], w["d_v"]),
                      dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
     def step():
-        m.sdpa_backward(q, k, v, out, do, lse, mask=mask, dq=dq, dk=dk, dv=dv, workspace=ws)
+        m.sdpa_backward(q, k, v, o_for_d, do, lse, mask=mask, dq=dq, dk=dk, dv=dv, workspace=ws)
 
     ms, wall = time_steps(step, args.steps, args.warmup, stream, args.prewarm_ms)
     reps = repeat_median(step, stream, ms, args.repeats)

@@ -147,7 +147,7 @@ int sdpa_forward_train(const void* Q, const void* K, const void* V, const int32_
  *          outputs rounded to nearest even), ATTN_BF16_F32O (the same, but O is the float32 out_f32 of
  *          sdpa_forward_train, so D is formed from the unrounded output) or ATTN_F32 (float32 throughout). lse is
  *          float32 in all three.
- *   Requirements as sdpa_forward, but d_k = d_v in {32, 64} (ATTN_ERR_UNSUPPORTED otherwise). dQ, dK, dV and the
+ *   Requirements as sdpa_forward (d_k = d_v in {32, 64, 128}). dQ, dK, dV and the
  *   workspace must not overlap each other or any input. Every element of dQ, dK and dV is written. */
 int sdpa_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse,
                   const int32_t* kv_len, int64_t window, int mask_kind, void* dQ, void* dK, void* dV, void* workspace,

@@ -126,8 +126,9 @@ def bwd(lib, Q=A, K=A * 2, V=A * 3, O=A * 4, dO=A * 5, lse=A * 6, kv_len=None, w
     (dict(dQ=A * 4), INVALID), (dict(dV=A * 200 + 1024), INVALID), (dict(ws=A * 6), INVALID),
     (dict(dK=A * 400), INVALID), (dict(kv_len=A * 7 + 4), INVALID), (dict(kv_len=A * 100 + 64), INVALID),
     (dict(window=3, n_k=32), UNSUPPORTED), (dict(window=3, kv_len=A * 7), UNSUPPORTED),
-    # the backward kernels take d_k = d_v in {32, 64}
-    (dict(d_k=128, d_v=128), UNSUPPORTED), (dict(d_k=48, d_v=48), UNSUPPORTED), (dict(d_k=32, d_v=64), UNSUPPORTED),
+    # the backward kernels take d_k = d_v in {32, 64, 128}
+    (dict(d_k=256, d_v=256), UNSUPPORTED), (dict(d_k=48, d_v=48), UNSUPPORTED), (dict(d_k=32, d_v=64), UNSUPPORTED),
+    (dict(d_k=128, d_v=128, dQ=A * 4 + 2048 + 16), INVALID),
 ])
 def test_sdpa_backward_rejects_bad_arguments(lib, kw, code):
     assert bwd(lib, **kw) == code
@@ -298,5 +299,5 @@ def test_backward_with_f32_output_checks_its_size(lib):
     assert bwd(lib, dtype=m.ATTN_BF16_F32O, dQ=A * 4 + 2048 + 16) == INVALID
     assert "overlaps" in lib.attn_last_error().decode()
     assert bwd(lib, dtype=m.ATTN_BF16_F32O, O=None) == INVALID
-    assert bwd(lib, dtype=m.ATTN_BF16_F32O, d_k=128, d_v=128) == UNSUPPORTED
+    assert bwd(lib, dtype=m.ATTN_BF16_F32O, d_k=256, d_v=256) == UNSUPPORTED
     assert lib.sdpa_backward_workspace_size(m.ATTN_BF16_F32O, 4, 8, 4096, 4096, 64, 64) == 4 * 8 * 64 * 1024

@@ -187,14 +187,15 @@ def _check_grads(got, ref, dtype, what):
             assert nrms <= 1e-2 and rel <= 1.5e-2, f"{what} {name}: nrms {nrms:.3g} max rel {rel:.3g}"
 
 
+@pytest.mark.parametrize("d", WIDTHS)
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("n_q,n_k,causal,kv_len,w", [
     (200, 200, False, None, None), (200, 200, True, None, None), (100, 300, False, None, None),
     (300, 100, False, None, None), (1, 130, False, None, None), (200, 200, False, [0, 1, 65, 200], None),
     (200, 200, True, [200, 64, 63, 7], None), (300, 300, False, None, 17), (300, 300, True, None, 100)])
-def test_headwidth32_backward(dtype, n_q, n_k, causal, kv_len, w):
+def test_headwidth_backward(d, dtype, n_q, n_k, causal, kv_len, w):
     B = 4 if kv_len else 2
-    x = workloads.make_sdpa_inputs(B, 2, n_q, n_k, 32, 32, dtype, 9990 + n_q + n_k, dout=True)
+    x = workloads.make_sdpa_inputs(B, 2, n_q, n_k, d, d, dtype, 9990 + n_q + n_k + d, dout=True)
     q, k, v, do = (to_dev(x[nm]) for nm in ("Q", "K", "V", "dO"))
     lens = None if kv_len is None else torch.tensor(kv_len, dtype=torch.int32, device="cuda")
     if w is not None:
@@ -207,13 +208,16 @@ def test_headwidth32_backward(dtype, n_q, n_k, causal, kv_len, w):
     torch.cuda.synchronize()
     ref = sdpa_backward_ref(x["Q"].f64, x["K"].f64, x["V"].f64, x["dO"].f64, causal,
                             kv_len=None if kv_len is None else np.asarray(kv_len), window=w)
-    _check_grads(grads, ref, dtype, f"d=32 backward {dtype} {n_q}x{n_k} causal={causal} kv={kv_len} w={w}")
+    _check_grads(grads, ref, dtype, f"d={d} backward {dtype} {n_q}x{n_k} causal={causal} kv={kv_len} w={w}")
 
 
-def test_headwidth32_backward_long_sampled():
-    # n = 4096 with 16 heads of 32 (the bench tensors plus an upstream gradient); the oracle checks two heads
-    w = workloads.WORKLOADS["sdpa_bf16_b4_h16_n4096_d32"]
-    x = workloads.make_sdpa_inputs(w["B"], w["h"], w["n_q"], w["n_k"], 32, 32, "bf16", w["seed"], dout=True)
+@pytest.mark.parametrize("name", ["sdpa_bf16_b4_h16_n4096_d32", "sdpa_bf16_b4_h4_n4096_d128"])
+def test_headwidth_backward_long_sampled(name):
+    # n = 4096 with 16 heads of 32 or 4 of 128 (the bench tensors plus an upstream gradient); the oracle checks two
+    # heads
+    w = workloads.WORKLOADS[name]
+    d = w["d_k"]
+    x = workloads.make_sdpa_inputs(w["B"], w["h"], w["n_q"], w["n_k"], d, d, "bf16", w["seed"], dout=True)
     q, k, v, do = (to_dev(x[nm]) for nm in ("Q", "K", "V", "dO"))
     out, lse = m.sdpa_forward_lse(q, k, v)
     grads = m.sdpa_backward(q, k, v, out, do, lse)
@@ -221,13 +225,13 @@ def test_headwidth32_backward_long_sampled():
     for b, hh in ((0, 0), (w["B"] - 1, w["h"] - 1)):
         ins = [x[nm].f64[b:b + 1, hh:hh + 1] for nm in ("Q", "K", "V", "dO")]
         ref = [r[0, 0] for r in sdpa_backward_ref(*ins)]
-        _check_grads([g[b, hh] for g in grads], ref, "bf16", f"d=32 n=4096 backward b={b} h={hh}")
+        _check_grads([g[b, hh] for g in grads], ref, "bf16", f"d={d} n=4096 backward b={b} h={hh}")
 
 
-def test_headwidth_autograd_wrapper():
-    # width 32: the autograd function's gradients are exactly sdpa_backward's; width 128: the forward runs and the
-    # backward is refused with ATTN_ERR_UNSUPPORTED before anything is launched
-    x = workloads.make_sdpa_inputs(2, 3, 96, 96, 32, 32, "bf16", 9995, dout=True)
+@pytest.mark.parametrize("d", WIDTHS)
+def test_headwidth_autograd_wrapper(d):
+    # the autograd function's gradients are exactly those of sdpa_forward_train + sdpa_backward, and match the oracle
+    x = workloads.make_sdpa_inputs(2, 3, 96, 96, d, d, "bf16", 9995 + d, dout=True)
     q, k, v, do = (to_dev(x[nm]) for nm in ("Q", "K", "V", "dO"))
     qa, ka, va = (t.clone().requires_grad_(True) for t in (q, k, v))
     m.attention(qa, ka, va, mask="causal").backward(do)
@@ -235,12 +239,5 @@ def test_headwidth_autograd_wrapper():
     dq, dk, dv = m.sdpa_backward(q, k, v, out32, do, lse, mask="causal")
     torch.cuda.synchronize()
     assert torch.equal(qa.grad, dq) and torch.equal(ka.grad, dk) and torch.equal(va.grad, dv)
-
-    x = workloads.make_sdpa_inputs(1, 2, 64, 64, 128, 128, "bf16", 9996, dout=True)
-    q, k, v, do = (to_dev(x[nm]) for nm in ("Q", "K", "V", "dO"))
-    qa = q.clone().requires_grad_(True)
-    y = m.attention(qa, k, v)
-    assert_bf16_parity(to_f64(y), sdpa_ref(x["Q"].f64, x["K"].f64, x["V"].f64), "autograd forward d=128")
-    with pytest.raises(m.AttnError) as e:
-        y.backward(do)
-    assert e.value.status == m.ATTN_ERR_UNSUPPORTED
+    ref = sdpa_backward_ref(x["Q"].f64, x["K"].f64, x["V"].f64, x["dO"].f64, True)
+    _check_grads((dq, dk, dv), ref, "bf16", f"autograd d={d}")

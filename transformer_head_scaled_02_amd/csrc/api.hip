@@ -141,10 +141,10 @@ int check_sdpa_sizes(const char* fn, int dtype, int mask_kind, int64_t B, int64_
     return fail_status(ATTN_ERR_INVALID, "%s: sizes must be positive (B=%lld h=%lld n_q=%lld n_k=%lld d_k=%lld "
                        "d_v=%lld)", fn, (long long)B, (long long)h, (long long)n_q, (long long)n_k, (long long)d_k,
                        (long long)d_v);
-  // the forward kernels take d_k = d_v in {32, 64, 128}; the backward kernels d_k = d_v in {32, 64}
-  if (d_k != d_v || (d_k != 32 && d_k != 64 && (backward || d_k != 128)))
-    return fail_status(ATTN_ERR_UNSUPPORTED, "%s: head dims d_k=%lld d_v=%lld (implemented: %s)", fn, (long long)d_k,
-                       (long long)d_v, backward ? "d_k = d_v in {32, 64}" : "d_k = d_v in {32, 64, 128}");
+  // the forward and backward kernels take d_k = d_v in {32, 64, 128}
+  if (d_k != d_v || (d_k != 32 && d_k != 64 && d_k != 128))
+    return fail_status(ATTN_ERR_UNSUPPORTED, "%s: head dims d_k=%lld d_v=%lld (implemented: d_k = d_v in {32, 64, "
+                       "128})", fn, (long long)d_k, (long long)d_v);
   if (mask_kind == ATTN_MASK_CAUSAL && n_q != n_k)
     return fail_status(ATTN_ERR_UNSUPPORTED, "%s: causal mask needs n_q == n_k (got %lld, %lld)", fn,
                        (long long)n_q, (long long)n_k);
@@ -270,7 +270,7 @@ ATTN_EXPORT int sdpa_forward_train(const void* Q, const void* K, const void* V, 
 ATTN_EXPORT size_t sdpa_backward_workspace_size(int dtype, int64_t B, int64_t h, int64_t n_q, int64_t n_k,
                                                 int64_t d_k, int64_t d_v) {
   if (dtype != ATTN_F32 && dtype != ATTN_BF16 && dtype != ATTN_BF16_F32O) return 0;
-  if (B <= 0 || h <= 0 || n_q <= 0 || n_k <= 0 || d_k != d_v || (d_k != 32 && d_k != 64)) return 0;
+  if (B <= 0 || h <= 0 || n_q <= 0 || n_k <= 0 || d_k != d_v || (d_k != 32 && d_k != 64 && d_k != 128)) return 0;
   if (n_q > ATTN_MAX_SEQ || n_k > ATTN_MAX_SEQ || B > ATTN_MAX_HEADS || h > ATTN_MAX_HEADS || B * h > ATTN_MAX_HEADS)
     return 0;
   return bwd_workspace_bytes(B, h, n_q);

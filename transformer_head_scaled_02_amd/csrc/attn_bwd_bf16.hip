@@ -42,8 +42,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 // 1 / sqrt(D), the scale of dQ and dK (exact for D = 64)
 template <int D>
 constexpr float inv_sqrt_d() {
-  static_assert(D == 32 || D == 64, "head width of the backward kernels");
-  return D == 64 ? 0.125f : (float)(1.0 / 5.656854249492381);
+  static_assert(D == 32 || D == 64 || D == 128, "head width of the backward kernels");
+  return D == 64 ? 0.125f : D == 32 ? (float)(1.0 / 5.656854249492381) : (float)(1.0 / 11.313708498984761);
 }
 
 // LDS element offset of lane (li, g)'s operand row read in k-step ks: row li of a 32-row block, logical 16-byte
@@ -185,7 +185,7 @@ __global__ __launch_bounds__(256) void attn_bwd_pre(BwdArgs a, int n_tiles) {
 
 // dK and dV: see the file comment (launch 2).
 template <int D, int NW, int kStages, bool WIN>
-__global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16(BwdArgs a, int n_kblocks) {
+__global__ __launch_bounds__(64 * NW, D == 128 ? 1 : 2) void attn_bwd_dkdv_bf16(BwdArgs a, int n_kblocks) {
   constexpr int kD = D;                           // (shadows the 64 of the shared tile header)
   constexpr int kTileElems = kBN * D;             // one 64-row tile of D elements
   constexpr int kKS = D / 16, kMB = D / 32;       // k-steps over d; 32-wide blocks of d
@@ -380,7 +380,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv_bf16(BwdArgs a, int 
 
 // dQ: see the file comment (launch 3).
 template <int D, int NW, int kStages, bool WIN>
-__global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dq_bf16(BwdArgs a, int n_qblocks) {
+__global__ __launch_bounds__(64 * NW, D == 128 ? 1 : 2) void attn_bwd_dq_bf16(BwdArgs a, int n_qblocks) {
   constexpr int kD = D;                           // (shadows the 64 of the shared tile header)
   constexpr int kTileElems = kBN * D;             // one 64-row tile of D elements
   constexpr int kKS = D / 16, kMB = D / 32;       // k-steps over d; 32-wide blocks of d
@@ -556,18 +556,25 @@ bool grid_ok(int64_t n) { return n > 0 && n <= 0x7fffffff; }
 
 }  // namespace
 
+namespace {
+
+template <int D>
+void launch_pre_d(const BwdArgs& a, bool f32, dim3 grid, int n_tiles, hipStream_t stream) {
+  if (f32) hipLaunchKernelGGL((attn_bwd_pre<float, D>), grid, dim3(256), 0, stream, a, n_tiles);
+  else if (a.o_f32) hipLaunchKernelGGL((attn_bwd_pre<uint16_t, D, true>), grid, dim3(256), 0, stream, a, n_tiles);
+  else hipLaunchKernelGGL((attn_bwd_pre<uint16_t, D>), grid, dim3(256), 0, stream, a, n_tiles);
+}
+
+}  // namespace
+
 hipError_t launch_attn_bwd_pre(const BwdArgs& a, bool f32, int d, hipStream_t stream) {
   const int n_tiles = (a.n_q + kBN - 1) / kBN;
   const int64_t nb = (int64_t)n_tiles * a.B * a.H;
-  if (!grid_ok(nb) || (d != 32 && d != 64)) return hipErrorInvalidValue;
+  if (!grid_ok(nb) || (d != 32 && d != 64 && d != 128)) return hipErrorInvalidValue;
   const dim3 grid((unsigned)nb);
-  if (f32 && d == 64) hipLaunchKernelGGL((attn_bwd_pre<float, 64>), grid, dim3(256), 0, stream, a, n_tiles);
-  else if (f32) hipLaunchKernelGGL((attn_bwd_pre<float, 32>), grid, dim3(256), 0, stream, a, n_tiles);
-  else if (a.o_f32 && d == 64)
-    hipLaunchKernelGGL((attn_bwd_pre<uint16_t, 64, true>), grid, dim3(256), 0, stream, a, n_tiles);
-  else if (a.o_f32) hipLaunchKernelGGL((attn_bwd_pre<uint16_t, 32, true>), grid, dim3(256), 0, stream, a, n_tiles);
-  else if (d == 64) hipLaunchKernelGGL((attn_bwd_pre<uint16_t, 64>), grid, dim3(256), 0, stream, a, n_tiles);
-  else hipLaunchKernelGGL((attn_bwd_pre<uint16_t, 32>), grid, dim3(256), 0, stream, a, n_tiles);
+  if (d == 64) launch_pre_d<64>(a, f32, grid, n_tiles, stream);
+  else if (d == 32) launch_pre_d<32>(a, f32, grid, n_tiles, stream);
+  else launch_pre_d<128>(a, f32, grid, n_tiles, stream);
   return hipGetLastError();
 }
 
@@ -604,6 +611,7 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
 hipError_t launch_attn_bwd_bf16(const BwdArgs& a, int d, hipStream_t stream) {
   if (d == 64) return launch_bwd_bf16<64>(a, stream);
   if (d == 32) return launch_bwd_bf16<32>(a, stream);
+  if (d == 128) return launch_bwd_bf16<128>(a, stream);
   return hipErrorInvalidValue;
 }
 

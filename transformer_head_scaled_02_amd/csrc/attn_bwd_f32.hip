@@ -1,11 +1,11 @@
-// Backward pass of scaled dot-product attention in fp32 throughout, d_k = d_v = D in {32, 64}, for gfx950.
+// Backward pass of scaled dot-product attention in fp32 throughout, d_k = d_v = D in {32, 64, 128}, for gfx950.
 //
 // Same mathematics as the bf16 backward (the chain rule through O = P V, the row softmax and S = Q K^T / sqrt(D):
 // "Transformer：抛弃循环与卷积的序列建模", section "训练样本", subsection "反向传播"; forward definition "Attention Is
 // All You Need", lettle.cn translation, section 3.2.1), with every value in fp32, P and dS included. This path serves
-// small fp32 problems, so it is plain VALU code: two threads per row, each holding one D/2-wide half of the row's
-// vectors, partial dot products combined with one lane exchange; the other side's rows are staged in LDS in tiles of
-// 32 and read as broadcasts. The per-row lse and D come from the shared pre-pass (workspace tiles of 64 rows).
+// small fp32 problems, so it is plain VALU code: two threads per row (four at D = 128), each holding one part of the
+// row's vectors, partial dot products combined by lane exchanges; the other side's rows are staged in LDS in tiles
+// of 32 and read as broadcasts. The per-row lse and D come from the shared pre-pass (workspace tiles of 64 rows).
 #include <math.h>
 
 #include "device_common.h"
@@ -16,14 +16,24 @@ namespace {
 
 constexpr int kRows = 32;  // rows per workgroup (two threads each) and per staged tile
 
-// the width-dependent constants: row width, half row, log2(e) / sqrt(D) and 1 / sqrt(D)
+// the width-dependent constants: row width, threads per row, the part of a row one thread holds, log2(e) / sqrt(D)
+// and 1 / sqrt(D)
 template <int D>
 struct Width {
-  static_assert(D == 32 || D == 64, "head width of the backward kernels");
-  static constexpr int kD = D, kHalf = D / 2;
-  static constexpr float kC = D == 64 ? (float)(1.4426950408889634 / 8.0) : (float)(1.4426950408889634 / 5.656854249492381);
-  static constexpr float kInvSqrtD = D == 64 ? 0.125f : (float)(1.0 / 5.656854249492381);
+  static_assert(D == 32 || D == 64 || D == 128, "head width of the backward kernels");
+  static constexpr int kD = D, kParts = D == 128 ? 4 : 2, kHalf = D / kParts;
+  static constexpr double kSqrtD = D == 64 ? 8.0 : D == 32 ? 5.656854249492381 : 11.313708498984761;
+  static constexpr float kC = (float)(1.4426950408889634 / kSqrtD);
+  static constexpr float kInvSqrtD = (float)(1.0 / kSqrtD);
 };
+
+// sum of a partial dot product over the kParts threads of a row
+template <int kParts>
+__device__ __forceinline__ float row_sum(float x) {
+#pragma unroll
+  for (int off = 1; off < kParts; off <<= 1) x += __shfl_xor(x, off);
+  return x;
+}
 
 // lse2 (= log2(e) * lse) and D of query row i of head bh, from the workspace tiles
 __device__ __forceinline__ float2 aux_row(const float* aux, int n_tiles, int bh, int i) {
@@ -33,15 +43,15 @@ __device__ __forceinline__ float2 aux_row(const float* aux, int n_tiles, int bh,
 
 // dK and dV: a workgroup owns 32 keys; query rows stream through LDS.
 template <int D>
-__global__ __launch_bounds__(2 * kRows) void attn_bwd_dkdv_f32(BwdArgs a) {
-  constexpr int kD = Width<D>::kD, kHalf = Width<D>::kHalf;
+__global__ __launch_bounds__(Width<D>::kParts * kRows) void attn_bwd_dkdv_f32(BwdArgs a) {
+  constexpr int kD = Width<D>::kD, kHalf = Width<D>::kHalf, kParts = Width<D>::kParts;
   constexpr float kC = Width<D>::kC, kInvSqrtD = Width<D>::kInvSqrtD;
   __shared__ float Qs[kRows][kD], dOs[kRows][kD], Ls[kRows], Ds[kRows];
-  const int tid = threadIdx.x, h = tid & 1;
+  const int tid = threadIdx.x, h = tid % kParts;
   const int n_q = a.n_q, n_k = a.n_k, n_tiles = (n_q + 63) / 64;
   const int nkb = (n_k + kRows - 1) / kRows;
   const int bh = blockIdx.x / nkb, k0 = (blockIdx.x % nkb) * kRows;
-  const int key = k0 + (tid >> 1);
+  const int key = k0 + tid / kParts;
   const int n_real = real_keys(a.kv_len, bh / a.H, n_k);  // keys from n_real on are padding: gradient 0
   const float* Qp = static_cast<const float*>(a.Q) + (int64_t)bh * n_q * kD;
   const float* dOp = static_cast<const float*>(a.dO) + (int64_t)bh * n_q * kD;
@@ -63,7 +73,7 @@ __global__ __launch_bounds__(2 * kRows) void attn_bwd_dkdv_f32(BwdArgs a) {
   }
   for (int q0 = q_begin; q0 < q_end; q0 += kRows) {
     __syncthreads();
-    for (int e = tid; e < kRows * kD; e += 2 * kRows) {
+    for (int e = tid; e < kRows * kD; e += kParts * kRows) {
       const int r = e / kD, c = e % kD;
       const bool ok = q0 + r < n_q;
       Qs[r][c] = ok ? Qp[(int64_t)(q0 + r) * kD + c] : 0.f;
@@ -83,8 +93,8 @@ __global__ __launch_bounds__(2 * kRows) void attn_bwd_dkdv_f32(BwdArgs a) {
         s = fmaf(k[d], Qs[i][kHalf * h + d], s);
         dp = fmaf(v[d], dOs[i][kHalf * h + d], dp);
       }
-      s += __shfl_xor(s, 1);
-      dp += __shfl_xor(dp, 1);
+      s = row_sum<kParts>(s);
+      dp = row_sum<kParts>(dp);
       const int row = q0 + i;
       float p = fast_exp2(fmaf(s, kC, -Ls[i]));  // 0 for rows past n_q and rows that saw no key (lse2 = +inf)
       if ((a.causal && key > row) || key >= n_real || (a.windowed && (key > row + a.window || key < row - a.window)))
@@ -111,15 +121,15 @@ __global__ __launch_bounds__(2 * kRows) void attn_bwd_dkdv_f32(BwdArgs a) {
 
 // dQ: a workgroup owns 32 queries; key/value rows stream through LDS.
 template <int D>
-__global__ __launch_bounds__(2 * kRows) void attn_bwd_dq_f32(BwdArgs a) {
-  constexpr int kD = Width<D>::kD, kHalf = Width<D>::kHalf;
+__global__ __launch_bounds__(Width<D>::kParts * kRows) void attn_bwd_dq_f32(BwdArgs a) {
+  constexpr int kD = Width<D>::kD, kHalf = Width<D>::kHalf, kParts = Width<D>::kParts;
   constexpr float kC = Width<D>::kC, kInvSqrtD = Width<D>::kInvSqrtD;
   __shared__ float Ks[kRows][kD], Vs[kRows][kD];
-  const int tid = threadIdx.x, h = tid & 1;
+  const int tid = threadIdx.x, h = tid % kParts;
   const int n_q = a.n_q, n_k = a.n_k, n_tiles = (n_q + 63) / 64;
   const int nqb = (n_q + kRows - 1) / kRows;
   const int bh = blockIdx.x / nqb, qb0 = (blockIdx.x % nqb) * kRows;
-  const int qi = qb0 + (tid >> 1);
+  const int qi = qb0 + tid / kParts;
   const int n_real = real_keys(a.kv_len, bh / a.H, n_k);  // keys from n_real on (padding) are never read
   const float* Qp = static_cast<const float*>(a.Q) + (int64_t)bh * n_q * kD;
   const float* dOp = static_cast<const float*>(a.dO) + (int64_t)bh * n_q * kD;
@@ -142,7 +152,7 @@ __global__ __launch_bounds__(2 * kRows) void attn_bwd_dq_f32(BwdArgs a) {
   }
   for (int k0 = k_begin; k0 < k_end; k0 += kRows) {
     __syncthreads();
-    for (int e = tid; e < kRows * kD; e += 2 * kRows) {
+    for (int e = tid; e < kRows * kD; e += kParts * kRows) {
       const int r = e / kD, c = e % kD;
       const bool ok = k0 + r < n_real;
       Ks[r][c] = ok ? Kp[(int64_t)(k0 + r) * kD + c] : 0.f;
@@ -156,8 +166,8 @@ __global__ __launch_bounds__(2 * kRows) void attn_bwd_dq_f32(BwdArgs a) {
         s = fmaf(q[d], Ks[j][kHalf * h + d], s);
         dp = fmaf(o[d], Vs[j][kHalf * h + d], dp);
       }
-      s += __shfl_xor(s, 1);
-      dp += __shfl_xor(dp, 1);
+      s = row_sum<kParts>(s);
+      dp = row_sum<kParts>(dp);
       const int key = k0 + j;
       float p = fast_exp2(fmaf(s, kC, -ld.x));
       if (key >= n_real || (a.causal && key > qi) || (a.windowed && (key > qi + a.window || key < qi - a.window)))
@@ -178,20 +188,30 @@ __global__ __launch_bounds__(2 * kRows) void attn_bwd_dq_f32(BwdArgs a) {
 
 }  // namespace
 
+namespace {
+
+template <int D>
+hipError_t launch_bwd_f32_d(const BwdArgs& a, int64_t nb_kv, int64_t nb_q, hipStream_t stream) {
+  constexpr int kThreads = Width<D>::kParts * kRows;
+  hipLaunchKernelGGL(attn_bwd_dkdv_f32<D>, dim3((unsigned)nb_kv), dim3(kThreads), 0, stream, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_bwd_dq_f32<D>, dim3((unsigned)nb_q), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_attn_bwd_f32(const BwdArgs& a, int d, hipStream_t stream) {
   const int64_t nb_kv = (int64_t)((a.n_k + kRows - 1) / kRows) * a.B * a.H;
   const int64_t nb_q = (int64_t)((a.n_q + kRows - 1) / kRows) * a.B * a.H;
-  if (nb_kv <= 0 || nb_kv > 0x7fffffff || nb_q <= 0 || nb_q > 0x7fffffff || (d != 32 && d != 64))
+  if (nb_kv <= 0 || nb_kv > 0x7fffffff || nb_q <= 0 || nb_q > 0x7fffffff || (d != 32 && d != 64 && d != 128))
     return hipErrorInvalidValue;
-  hipError_t e = launch_attn_bwd_pre(a, true, d, stream);
+  const hipError_t e = launch_attn_bwd_pre(a, true, d, stream);
   if (e != hipSuccess) return e;
-  if (d == 64) hipLaunchKernelGGL(attn_bwd_dkdv_f32<64>, dim3((unsigned)nb_kv), dim3(2 * kRows), 0, stream, a);
-  else hipLaunchKernelGGL(attn_bwd_dkdv_f32<32>, dim3((unsigned)nb_kv), dim3(2 * kRows), 0, stream, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (d == 64) hipLaunchKernelGGL(attn_bwd_dq_f32<64>, dim3((unsigned)nb_q), dim3(2 * kRows), 0, stream, a);
-  else hipLaunchKernelGGL(attn_bwd_dq_f32<32>, dim3((unsigned)nb_q), dim3(2 * kRows), 0, stream, a);
-  return hipGetLastError();
+  if (d == 64) return launch_bwd_f32_d<64>(a, nb_kv, nb_q, stream);
+  if (d == 32) return launch_bwd_f32_d<32>(a, nb_kv, nb_q, stream);
+  return launch_bwd_f32_d<128>(a, nb_kv, nb_q, stream);
 }
 
 }  // namespace mi355

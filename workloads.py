@@ -73,6 +73,9 @@ WORKLOADS = {
     # the backward at 16 heads of 32 (the d = 32 forward workload's tensors and an upstream gradient)
     "sdpa_bwd_bf16_b4_h16_n4096_d32": dict(kind="sdpa_bwd", dtype="bf16", B=4, h=16, n_q=4096, n_k=4096, d_k=32,
                                            d_v=32, causal=False, seed=1007),
+    # and at 4 heads of 128
+    "sdpa_bwd_bf16_b4_h4_n4096_d128": dict(kind="sdpa_bwd", dtype="bf16", B=4, h=4, n_q=4096, n_k=4096, d_k=128,
+                                           d_v=128, causal=False, seed=1008),
 }
 
 
