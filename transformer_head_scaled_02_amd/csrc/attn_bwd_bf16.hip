@@ -1,4 +1,4 @@
-// Backward pass of scaled dot-product attention, bf16 in/out, d_k = d_v = D in {32, 64}, for gfx950 (MI355X).
+// Backward pass of scaled dot-product attention, bf16 in/out, d_k = d_v = D in {32, 64, 128}, for gfx950 (MI355X).
 //
 // The forward pass is O = P V with P = softmax(Q K^T / sqrt(64)) row by row ("Attention Is All You Need", lettle.cn
 // translation, section 3.2.1, equation Attention(Q,K,V)); training carries the loss back through it by the chain
@@ -13,6 +13,10 @@
 // Three launches:
 //  1. attn_bwd_pre: D = dO . O per query row (fp32) and log2(e) * lse, written to the workspace in 64-row tiles;
 //     rows past n_q get lse = +inf and D = 0, so their recomputed weights are exactly 0 wherever they are read.
+//     Each row's -D is also stored as three bf16 parts whose sum is -D to float32 precision: one extra k-step of the
+//     dP product (those parts against a column of ones) then yields dP - D straight from the matrix core, which
+//     saves a VALU subtraction per score in both gradient kernels (widths 32 and 64; at 128, where a wave's
+//     registers are already full, the subtraction measured faster and stays on the VALU).
 //  2. attn_bwd_dkdv: a workgroup of NW waves owns NW*32 keys of one head; each wave keeps the K and V rows of its 32
 //     keys in registers as MFMA B operands. 64-row query tiles (Q rows, dO rows and the tile's lse/D, 17 KB) stream
 //     through a 3-stage LDS ring by global_load_lds_dwordx4. Per tile and 32-row half, S = Q K^T and dP = dO V^T
@@ -73,6 +77,25 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, int ks, const
 
 __device__ __forceinline__ void settle_f(float& v) { asm volatile("" : "+v"(v)); }
 
+// -x as three bf16 parts, packed {hi | mid << 16, lo}: hi = bf16(-x), mid = bf16(-x - hi), lo = bf16(-x - hi - mid)
+// (each remainder exact in float32), so hi + mid + lo equals -x to about 2^-24 relative. As an extra k-step of an
+// MFMA against a column of ones, they subtract x from every accumulator of the row in float32.
+__device__ __forceinline__ uint2 neg_bf16_split3(float x) {
+  const float nx = -x;
+  const uint32_t h = pack_bf16x2(nx, 0.f) & 0xffffu;
+  const float r1 = nx - __uint_as_float(h << 16);
+  const uint32_t m = pack_bf16x2(r1, 0.f) & 0xffffu;
+  const float r2 = r1 - __uint_as_float(m << 16);
+  const uint32_t l = pack_bf16x2(r2, 0.f) & 0xffffu;
+  return uint2{h | (m << 16), l};
+}
+
+// The matching column of ones: k = 0, 1, 2 of a k-step are 1 in the lanes that supply k = 0..7 (g = 0), all else 0.
+__device__ __forceinline__ bf16x8 ones3_operand(int g) {
+  const uint32_t one2 = 0x3f803f80u, one1 = 0x00003f80u;  // bf16 1.0 = 0x3f80
+  return __builtin_bit_cast(bf16x8, g == 0 ? uint4{one2, one1, 0u, 0u} : uint4{0u, 0u, 0u, 0u});
+}
+
 // Copies of one ring stage: 64 rows of D elements of tensor `ta` (the first 128 D bytes of the stage) and of `tb`
 // (the next), each wave moving its share of the 2 D/8 one-kilobyte pieces; rows at or past `rows_left` read row
 // rows_left-1 instead. Copy gi moves R = 512/D rows from row R (gi mod D/8); lane l brings the logical chunk that
@@ -120,7 +143,8 @@ __device__ __forceinline__ void wait_copies(int ahead) {
 }
 
 // D_i = dO_i . O_i and log2(e) * lse_i for one 64-row query tile of one head (rows of D elements); 4 threads per row.
-// kO32: bf16 dO with the float32 (unrounded) forward output O.
+// kO32: bf16 dO with the float32 (unrounded) forward output O. The tile's block of 256 floats holds [log2(e) lse of
+// the 64 rows | D of the 64 rows | per row 8 bytes: bf16 {-D_hi, -D_mid, -D_lo, 0}] (neg_bf16_split3).
 template <class T, int D, bool kO32 = false>
 __global__ __launch_bounds__(256) void attn_bwd_pre(BwdArgs a, int n_tiles) {
   const int bh = blockIdx.x / n_tiles, t = blockIdx.x % n_tiles;
@@ -178,9 +202,15 @@ __global__ __launch_bounds__(256) void attn_bwd_pre(BwdArgs a, int n_tiles) {
     // +inf for padding rows and for rows that saw no key (lse = -inf): their weights come out exactly 0
     const float lse = row < n_q ? a.lse[(int64_t)bh * n_q + row] : -INFINITY;
     at[r] = lse == -INFINITY ? INFINITY : lse * kLog2e;
+  } else {
+    const float dv = row < n_q ? dot : 0.f;
+    if (part == 1) {
+      at[kBN + r] = dv;
+    } else {
+      const uint2 w = neg_bf16_split3(dv);
+      at[2 * kBN + 2 * r + (part - 2)] = __uint_as_float(part == 2 ? w.x : w.y);
+    }
   }
-  else if (part == 1) at[kBN + r] = row < n_q ? dot : 0.f;
-  else at[2 * kBN + (part - 2) * kBN + r] = 0.f;
 }
 
 // dK and dV: see the file comment (launch 2).
@@ -286,6 +316,8 @@ __global__ __launch_bounds__(64 * NW, D == 128 ? 1 : 2) void attn_bwd_dkdv_bf16(
   f32x16 dv[kMB], dk[kMB];
 #pragma unroll
   for (int mb = 0; mb < kMB; ++mb) dv[mb] = dk[mb] = f32x16{};
+  constexpr bool kFoldD = D != 128;  // D subtracted by an extra k-step of dP (see the file comment)
+  const bf16x8 ones3 = ones3_operand(g);  // B operand of the k-step that subtracts each query row's D from dP
 
   // a workgroup of padding keys only writes zeros
   int nt = k_blk0 < n_real ? n_tiles : 0;
@@ -315,23 +347,32 @@ __global__ __launch_bounds__(64 * NW, D == 128 ? 1 : 2) void attn_bwd_dkdv_bf16(
 #pragma unroll
       for (int ks = 0; ks < kKS; ++ks)
         dp = mfma32x32x16(*reinterpret_cast<const bf16x8*>(st + kTileElems + mq * 32 * kD + roff[ks]), vf[ks], dp);
-      // register r holds query row 32mq + 8(r/4) + 4g + r%4 of the tile: its lse and D come in fours
+      if constexpr (kFoldD) {
+        // dP - D: A operand row li = query 32mq + li with k = 0..2 the parts of its -D (the lanes of g = 1 supply
+        // k = 8..15, which meet zeros in ones3)
+        const uint2 nd = *reinterpret_cast<const uint2*>(aux + 2 * kBN + 2 * (32 * mq + li));
+        dp = mfma32x32x16(__builtin_bit_cast(bf16x8, uint4{nd.x, nd.y, 0u, 0u}), ones3, dp);
+      }
+      // register r holds query row 32mq + 8(r/4) + 4g + r%4 of the tile: its lse (and D) come in fours
       f32x4 lq[4], dq[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         lq[i] = *reinterpret_cast<const f32x4*>(aux + 32 * mq + 8 * i + 4 * g);
-        dq[i] = *reinterpret_cast<const f32x4*>(aux + kBN + 32 * mq + 8 * i + 4 * g);
+        if constexpr (!kFoldD) dq[i] = *reinterpret_cast<const f32x4*>(aux + kBN + 32 * mq + 8 * i + 4 * g);
       }
-      const int base = key - t * kBN - 32 * mq - 4 * g;
-      const int ub = base - hi_off, lb = base - lo_off;
+      if (masked) {  // uniform: tiles that straddle the wave's keys, and every tile of the window
+        const int base = key - t * kBN - 32 * mq - 4 * g;
+        const int ub = base - hi_off, lb = base - lo_off;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          // key - row = base - (8(r/4) + r%4); allowed when lo_off <= key - row <= hi_off
+          if (8 * (r >> 2) + (r & 3) < ub || (WIN && 8 * (r >> 2) + (r & 3) > lb)) s[r] = -INFINITY;
+      }
       float p[16], ds[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float sv = s[r];
-        // key - row = base - (8(r/4) + r%4); allowed when lo_off <= key - row <= hi_off
-        if (masked && (8 * (r >> 2) + (r & 3) < ub || (WIN && 8 * (r >> 2) + (r & 3) > lb))) sv = -INFINITY;
-        p[r] = fast_exp2(__builtin_fmaf(sv, scale_log2<D>(), -lq[r >> 2][r & 3]));
-        ds[r] = p[r] * (dp[r] - dq[r >> 2][r & 3]);
+        p[r] = fast_exp2(__builtin_fmaf(s[r], scale_log2<D>(), -lq[r >> 2][r & 3]));
+        ds[r] = kFoldD ? p[r] * dp[r] : p[r] * (dp[r] - dq[r >> 2][r & 3]);  // folded: dp holds dP - D
       }
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
@@ -427,19 +468,25 @@ __global__ __launch_bounds__(64 * NW, D == 128 ? 1 : 2) void attn_bwd_dq_bf16(Bw
     qf[ks] = q < n_q ? *reinterpret_cast<const bf16x8*>(Qp + off) : bf16x8{};
     df[ks] = q < n_q ? *reinterpret_cast<const bf16x8*>(dOp + off) : bf16x8{};
   }
+  constexpr bool kFoldD = D != 128;  // D subtracted by an extra k-step of dP^T (see the file comment)
   float lse2 = INFINITY, dq_d = 0.f;  // rows past n_q: weights 0
+  uint2 nd = {0u, 0u};                 // the query's -D as three bf16 parts (0 past n_q)
   if (q < n_q) {
     const float* at = auxp + (int64_t)(q / kBN) * kAuxFloatsPerTile;
     lse2 = at[q % kBN];
-    dq_d = at[kBN + q % kBN];
+    if constexpr (kFoldD) nd = *reinterpret_cast<const uint2*>(at + 2 * kBN + 2 * (q % kBN));
+    else dq_d = at[kBN + q % kBN];
   }
+  // the extra k-step of dP^T = V dO^T that subtracts D: A = a column of ones (keys x k), B = the query's -D parts
+  const bf16x8 ones3 = ones3_operand(g);
+  const bf16x8 ndop = __builtin_bit_cast(bf16x8, uint4{nd.x, nd.y, 0u, 0u});
 #pragma unroll
   for (int ks = 0; ks < kKS; ++ks) {
     settle(qf[ks]);
     settle(df[ks]);
   }
   settle_f(lse2);
-  settle_f(dq_d);
+  if constexpr (!kFoldD) settle_f(dq_d);
 
   int nt = (n_k + kBN - 1) / kBN;
   if (causal) nt = min(nt, (q_blk0 + kBM - 1) / kBN + 1);
@@ -511,6 +558,7 @@ __global__ __launch_bounds__(64 * NW, D == 128 ? 1 : 2) void attn_bwd_dq_bf16(Bw
       for (int ks = 0; ks < kKS; ++ks)
         dp[kb] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(st + kTileElems + kb * 32 * kD + roff[ks]), df[ks],
                               dp[kb]);
+      if constexpr (kFoldD) dp[kb] = mfma32x32x16(ones3, ndop, dp[kb]);  // dP^T - D
     }
     if (masked) {
       const int lim = key_lim - t * kBN, lo = key_lo - t * kBN;
@@ -530,7 +578,8 @@ __global__ __launch_bounds__(64 * NW, D == 128 ? 1 : 2) void attn_bwd_dq_bf16(Bw
       for (int j = 0; j < 4; ++j) {
         const float p0 = fast_exp2(__builtin_fmaf(s[kb][base + 2 * j], scale_log2<D>(), -lse2));
         const float p1 = fast_exp2(__builtin_fmaf(s[kb][base + 2 * j + 1], scale_log2<D>(), -lse2));
-        w[j] = pack_bf16x2(p0 * (dp[kb][base + 2 * j] - dq_d), p1 * (dp[kb][base + 2 * j + 1] - dq_d));
+        w[j] = kFoldD ? pack_bf16x2(p0 * dp[kb][base + 2 * j], p1 * dp[kb][base + 2 * j + 1])
+                      : pack_bf16x2(p0 * (dp[kb][base + 2 * j] - dq_d), p1 * (dp[kb][base + 2 * j + 1] - dq_d));
       }
       const bf16x8 pds = __builtin_bit_cast(bf16x8, (uint4){w[0], w[1], w[2], w[3]});
 #pragma unroll

@@ -39,7 +39,8 @@ hipError_t launch_attn_fwd_pp_bf16(const AttnArgs& a, hipStream_t stream);
 // Backward pass of attention over [B, H] heads of width d (32 or 64), every tensor dense [B, H, n, d] in the element
 // type.
 // `aux` is the workspace: per head and per 64-row query tile, 256 floats = [log2(e)*lse of the 64 rows | D of the 64
-// rows | 128 zeros], where D_i = dO_i . O_i; rows past n_q hold lse = +inf and D = 0 (their weights come out 0).
+// rows | per row 8 bytes: -D as three bf16 parts and a zero], where D_i = dO_i . O_i; rows past n_q hold lse = +inf
+// and D = 0 (their weights come out 0).
 struct BwdArgs {
   const void* Q;
   const void* K;
