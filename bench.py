@@ -187,6 +187,46 @@ def time_steps(step, steps: int, warmup: int, stream, prewarm_ms: float = 0.0):
     return e0.elapsed_time(e1) / steps, time.perf_counter() - t0
 
 
+def graph_replay(step, out, calls: int, loops: int = 7):
+    """Short calls replayed from a HIP graph: `calls` back-to-back calls of `step` captured once (on a side stream,
+    after eager warm-up calls there), the graph replayed `loops` times with HIP events around each replay, the output
+    compared bitwise with the eager result after every replay. Host launch cost then no longer sits between the
+    kernels, so the per-call time is the device-side figure. The entry points make no allocation, memset or
+    synchronisation, which is what capture needs. Returns a dict, or None when calls <= 0."""
+    import statistics
+
+    import torch
+    if calls <= 0:
+        return None
+    torch.cuda.synchronize()
+    want = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    per_call, same = [], True
+    for _ in range(loops + 1):
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        per_call.append(e0.elapsed_time(e1) / calls)
+        same = same and torch.equal(out, want)
+    del g
+    per_call = per_call[1:]  # the first replay also uploads the graph
+    return {"calls_per_graph": calls, "loops": loops, "median_ms": round(statistics.median(per_call), 6),
+            "min_ms": round(min(per_call), 6), "bitwise_equal_to_eager": bool(same)}
+
+
 def repeat_median(step, stream, ms_hint: float, loops: int, min_ms: float = 5.0):
     """`loops` more timed loops after the main region, each of N back-to-back calls lasting at least `min_ms`; the
     median over loops of the per-call time is the steady-state figure (the main region's K calls can be too short to
@@ -555,6 +595,8 @@ def main():
     ap.add_argument("--rotate-mb", type=float, default=0.0,
                     help="also time the call cycling over input/output copies totalling more than this many MiB")
     ap.add_argument("--no-smi", action="store_true", help="skip the amd-smi clock/power snapshots")
+    ap.add_argument("--graph-below-ms", type=float, default=0.05,
+                    help="calls shorter than this are also timed replayed from a HIP graph (graph_replay)")
     ap.add_argument("--sustain-s", type=float, default=2.0,
                     help="after the timed region, seconds of held load whose last calls are timed again (reported "
                          "beside the value)")
@@ -710,6 +752,11 @@ def main():
                             "value_at_end": round(flops_metric(w) / (last["median_ms"] * 1e-3) / 1e12, 2)}
     if cold is not None:
         rec["cold"] = cold
+    if ms < args.graph_below_ms:
+        # launch-bound sizes: the same calls replayed from a HIP graph, the device-side per-call time
+        gr = graph_replay(step, out, max(1, int(2.0 / max(ms, 1e-3))))
+        gr["algorithmic_hbm_GBps"] = round(hbm_bytes(w) / (gr["median_ms"] * 1e-3) / 1e9, 1)
+        rec["graph_replay"] = gr
     if not args.no_probes:
         # measured ceilings on this chip, taken after the timed region: dense bf16 MFMA throughput with every CU busy
         # (and the clock it holds under that load), the v_exp_f32 rate and device-to-device copy bandwidth

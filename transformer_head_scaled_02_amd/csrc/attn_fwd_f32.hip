@@ -2,10 +2,11 @@
 //
 // Same mathematics as the bf16 kernel (softmax(Q K^T / sqrt(D)) V per head, optional causal mask; "Attention Is All
 // You Need" (lettle.cn translation), section 3.2.1), but every value stays fp32, including the softmax weights that
-// multiply V. This path serves small fp32 problems, so it is a plain VALU kernel: D/16 threads per query row, each
-// with sixteen of the row's dimensions in registers (q and its share of the output accumulator; the partial dot
+// multiply V. This path serves small fp32 problems, so it is a plain VALU kernel: D/8 threads per query row, each
+// with eight of the row's dimensions in registers (q and its share of the output accumulator; the partial dot
 // products are added across the row's lanes), key/value tiles staged in LDS and read as broadcasts, and the softmax
-// streamed tile by tile (running max, rescaled running sum). A workgroup is one wave of 64 / (D/16) query rows.
+// streamed tile by tile (running max, rescaled running sum). A workgroup is one wave of 64 / (D/8) query rows; a tile's
+// key loop stops at the last key any row of the workgroup may see.
 #include "device_common.h"
 #include "launch.h"
 
@@ -16,10 +17,10 @@ namespace {
 
 constexpr int kThreads = 64;  // one wave per workgroup
 constexpr int kBK = 32;       // keys per tile
-constexpr int kDT = 16;       // dimensions of a row per thread
+constexpr int kDT = 8;        // dimensions of a row per thread
 
-// threads per query row (D / 16): a thread's share of every K and V row is four 16-byte LDS reads, so one wave issues
-// a quarter of the LDS reads that one thread per row would (those reads, not the arithmetic, set this kernel's time)
+// threads per query row (D / 8): a thread's share of every K and V row is two 16-byte LDS reads, and the short
+// problems this kernel serves (a handful of query rows) spread over more waves
 template <int D>
 constexpr int threads_per_row() { return D / kDT; }
 // queries per workgroup
@@ -70,19 +71,27 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32(AttnArgs a, int n_qbloc
     // 32 rows x D floats per tensor in float4 chunks; rows past n_k load as zeros
     for (int ch = tid; ch < kBK * kD / 4; ch += kThreads) {
       const int r = ch / (kD / 4), col = (ch % (kD / 4)) * 4;
-      const bool ok = k0 + r < n_k;
-      const float4 z = {0, 0, 0, 0};
-      *reinterpret_cast<float4*>(&Ks[r * kD + col]) = ok ? *reinterpret_cast<const float4*>(Kp + (int64_t)(k0 + r) * kD + col) : z;
-      *reinterpret_cast<float4*>(&Vs[r * kD + col]) = ok ? *reinterpret_cast<const float4*>(Vp + (int64_t)(k0 + r) * kD + col) : z;
+      // (a branch, not a select between a global row and a zero constant: the select became a flat load from a
+      // private copy of the constant)
+      float4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
+      if (k0 + r < n_k) {
+        kv = *reinterpret_cast<const float4*>(Kp + (int64_t)(k0 + r) * kD + col);
+        vv = *reinterpret_cast<const float4*>(Vp + (int64_t)(k0 + r) * kD + col);
+      }
+      *reinterpret_cast<float4*>(&Ks[r * kD + col]) = kv;
+      *reinterpret_cast<float4*>(&Vs[r * kD + col]) = vv;
     }
     __syncthreads();
 
     float s[kBK];
+#pragma unroll
+    for (int j = 0; j < kBK; ++j) s[j] = -INFINITY;
     float mx = -INFINITY;
 #pragma unroll
     for (int j = 0; j < kBK; ++j) {
       // four partial sums over d mod 4: four independent fma chains of D/4 (one chain of D would serialise on the
       // fma latency)
+      if (k0 + j >= n_end) continue;  // (uniform) no row of the workgroup sees a later key of this tile
       float acc4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int d = 0; d < kDT; ++d) acc4[d & 3] = fmaf(q[d], Ks[j * kD + part * kDT + d], acc4[d & 3]);
@@ -104,6 +113,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32(AttnArgs a, int n_qbloc
     for (int d = 0; d < kDT; ++d) o[d] *= alpha;
 #pragma unroll
     for (int j = 0; j < kBK; ++j) {
+      if (k0 + j >= n_end) continue;
       const float p = fast_exp2(fmaf(s[j], c, -m_use));
       l += p;
 #pragma unroll
