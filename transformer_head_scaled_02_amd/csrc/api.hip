@@ -405,6 +405,22 @@ int mha_run(const char* name, const void* Xq, const void* Xkv, const void* Wq, c
   void* Ch = ws + L.c_off;
   const int hd = (int)(h * d_k);
 
+  // Short self-attention at head width 64: projections and attention in one launch per (batch entry, head), the
+  // heads written straight into the concatenated layout; then the output projection.
+  if (Xq == Xkv && n_q == n_k && n_q <= mi355::kFusedMhaMaxSeq && d_k == 64 && d_model % 64 == 0) {
+    mi355::FusedMhaArgs f{};
+    f.X = Xq; f.Wq = Wq; f.Wk = Wk; f.Wv = Wv; f.C = Ch;
+    f.B = (int)B; f.H = (int)h; f.n = (int)n_q; f.dm = (int)d_model;
+    f.causal = mask_kind == ATTN_MASK_CAUSAL;
+    hipError_t e = mi355::launch_mha_self_fused_bf16(f, s);
+    if (e != hipSuccess)
+      return fail_status(ATTN_ERR_HIP, "%s: projection/attention launch failed: %s", name, hipGetErrorString(e));
+    mi355::GemmProblem outp = {Ch, Wo, out, (int)(B * n_q), (int)d_model, hd, 0};
+    e = mi355::launch_gemm_bf16(&outp, 1, s);
+    if (e != hipSuccess) return fail_status(ATTN_ERR_HIP, "%s: W^O launch failed: %s", name, hipGetErrorString(e));
+    return ATTN_OK;
+  }
+
   // 1. projections, written per head: Qh [B,h,n_q,d], Kh/Vh [B,h,n_k,d]
   mi355::GemmProblem proj[3] = {
       {Xq, Wq, Qh, (int)(B * n_q), hd, (int)d_model, (int)n_q, nullptr, nullptr, 0, hsh},
@@ -549,23 +565,32 @@ ATTN_EXPORT int encoder_layer_forward(const void* X, const int32_t* kv_len, cons
   e = (call);                                                                                        \
   if (e != hipSuccess) return fail_status(ATTN_ERR_HIP, "%s: %s launch failed: %s", fn, what, hipGetErrorString(e));
 
-  // 1. Q/K/V projections into the per-head layout, 2. attention into the concatenated heads
+  // 1. Q/K/V projections into the per-head layout, 2. attention into the concatenated heads (short sequences at head
+  // width 64: both in one launch per (batch entry, head))
   const int dh = (int)(d_model / h), hsh = head_shift(h, dh);
-  mi355::GemmProblem proj[3] = {{X, Wq, Qh, M, dm, dm, (int)n, nullptr, nullptr, 0, hsh},
-                                {X, Wk, Kh, M, dm, dm, (int)n, nullptr, nullptr, 0, hsh},
-                                {X, Wv, Vh, M, dm, dm, (int)n, nullptr, nullptr, 0, hsh}};
-  ENC_STEP(mi355::launch_gemm_bf16(proj, 3, s), "projection");
-  mi355::AttnArgs a{};
-  a.Q = Qh; a.K = Kh; a.V = Vh; a.O = Ch;
-  a.B = (int)B; a.H = (int)h; a.n_q = (int)n; a.n_k = (int)n;
-  a.q_stride_bh = n * dh;
-  a.k_stride_bh = n * dh;
-  a.o_stride_b = n * d_model;
-  a.o_stride_h = dh;
-  a.o_stride_row = d_model;
-  a.causal = mask_kind == ATTN_MASK_CAUSAL;
-  a.kv_len = kv_len;
-  ENC_STEP(mi355::launch_attn_fwd_bf16(a, dh, s), "attention");
+  if (n <= mi355::kFusedMhaMaxSeq && dh == 64) {
+    mi355::FusedMhaArgs f{};
+    f.X = X; f.Wq = Wq; f.Wk = Wk; f.Wv = Wv; f.C = Ch; f.kv_len = kv_len;
+    f.B = (int)B; f.H = (int)h; f.n = (int)n; f.dm = dm;
+    f.causal = mask_kind == ATTN_MASK_CAUSAL;
+    ENC_STEP(mi355::launch_mha_self_fused_bf16(f, s), "projection/attention");
+  } else {
+    mi355::GemmProblem proj[3] = {{X, Wq, Qh, M, dm, dm, (int)n, nullptr, nullptr, 0, hsh},
+                                  {X, Wk, Kh, M, dm, dm, (int)n, nullptr, nullptr, 0, hsh},
+                                  {X, Wv, Vh, M, dm, dm, (int)n, nullptr, nullptr, 0, hsh}};
+    ENC_STEP(mi355::launch_gemm_bf16(proj, 3, s), "projection");
+    mi355::AttnArgs a{};
+    a.Q = Qh; a.K = Kh; a.V = Vh; a.O = Ch;
+    a.B = (int)B; a.H = (int)h; a.n_q = (int)n; a.n_k = (int)n;
+    a.q_stride_bh = n * dh;
+    a.k_stride_bh = n * dh;
+    a.o_stride_b = n * d_model;
+    a.o_stride_h = dh;
+    a.o_stride_row = d_model;
+    a.causal = mask_kind == ATTN_MASK_CAUSAL;
+    a.kv_len = kv_len;
+    ENC_STEP(mi355::launch_attn_fwd_bf16(a, dh, s), "attention");
+  }
   // 3. R1 = X + Concat W^O (residual in the GEMM epilogue), H1 = LayerNorm(R1)
   mi355::GemmProblem wo = {Ch, Wo, R, M, dm, dm, 0, nullptr, X, 0};
   ENC_STEP(mi355::launch_gemm_bf16(&wo, 1, s), "W^O");

@@ -69,6 +69,24 @@ hipError_t launch_attn_bwd_pre(const BwdArgs& a, bool f32, int d, hipStream_t st
 hipError_t launch_attn_bwd_bf16(const BwdArgs& a, int d, hipStream_t stream);  // pre-pass, dK/dV, dQ
 hipError_t launch_attn_bwd_f32(const BwdArgs& a, int d, hipStream_t stream);
 
+// Multi-head self-attention of short sequences in one launch (bf16, head width 64): for every (batch entry b, head i)
+// the projections Q_i = X_b W_i^Q, K_i = X_b W_i^K, V_i = X_b W_i^V and head_i = softmax(Q_i K_i^T / 8) V_i (causal
+// and key padding as in AttnArgs), written to columns 64i .. 64i+63 of C [B, n, H*64]. X [B, n, dm], Wq/Wk/Wv
+// [dm, H*64] row-major bf16. Requires 1 <= n <= 128 and dm a positive multiple of 64 (hipErrorInvalidValue
+// otherwise, nothing launched).
+struct FusedMhaArgs {
+  const void* X;
+  const void* Wq;
+  const void* Wk;
+  const void* Wv;
+  void* C;
+  const int* kv_len;  // optional key padding (nullptr: none), as in AttnArgs
+  int B, H, n, dm;
+  int causal;
+};
+constexpr int kFusedMhaMaxSeq = 128;
+hipError_t launch_mha_self_fused_bf16(const FusedMhaArgs& a, hipStream_t stream);
+
 // C = A[M,K] * W[K,N] in bf16 with fp32 accumulation, up to three independent problems in one launch.
 // Row-major C (ldc = N) when head_seq == 0; otherwise "head-major" with heads of w = 2^head_shift columns (w in
 // {32, 64, 128}): column n of row m goes to C[((m / head_seq) * (N / w) + n / w) * head_seq + m % head_seq][n % w],

@@ -1,0 +1,264 @@
+// Multi-head self-attention for short sequences, bf16, head width 64, for gfx950 (MI355X): one workgroup per
+// (batch entry, head) computes the head's projections and its attention without leaving the CU.
+//
+// For batch entry b and head i (no biases, row-vector convention X W):
+//   Q_i = X_b W_i^Q,  K_i = X_b W_i^K,  V_i = X_b W_i^V      (W_i = column block i of the packed [d_model, h*64])
+//   head_i = softmax(Q_i K_i^T / sqrt(64)) V_i                (optional causal mask, optional key padding)
+// and head_i is written to columns 64i .. 64i+63 of Concat(head_1..head_h) [B, n, h*64], which the W^O product then
+// reads. Definitions: "Transformer：抛弃循环与卷积的序列建模" (jiashun-ye.github.io), section "Multi-Head Attention";
+// "Attention Is All You Need" (lettle.cn translation), sections 3.2.1 (equation Attention(Q,K,V)) and 3.2.2.
+//
+// Why: at n <= 128 the projection GEMM and the attention kernel are each a few microseconds of fixed cost (launch,
+// pipeline fill, one HBM round trip of Q/K/V written and read back). Here the 128 x 192 block [Q_i | K_i | V_i] is
+// formed in the workgroup (X rows and the three 64-column weight blocks stream through a two-stage LDS ring by
+// global_load_lds_dwordx4; the product is formed transposed, C^T = W^T X^T, exactly as in the projection GEMM, so the
+// bf16 Q_i, K_i, V_i are the same numbers), rounded to bf16 into LDS, and the attention runs on them from there: with
+// every key in LDS the softmax is the plain one (row max over all keys, exp2, row sums on the matrix core from the
+// same bf16 weights that multiply V), no online rescaling. Eight waves share the projection (each a 32-row block of
+// X against three 32-column blocks of the weights); four of them then each take 32 queries.
+#include "attn_tile.h"
+#include "launch.h"
+
+namespace mi355 {
+namespace {
+
+constexpr int kFWaves = 8;
+constexpr int kFMaxN = 128;                   // sequence length limit (rows of X, queries and keys)
+constexpr int kFTK = 64;                      // k-tile of the projections
+constexpr int kFSub = 64 * 64;                // one 64 x 64 bf16 sub-tile, rows of 128 bytes (8 KB)
+constexpr int kFStageElems = 5 * kFSub;       // a stage: [X rows 0-63 | X rows 64-127 | W^Q_i | W^K_i | W^V_i]
+constexpr int kFStages = 2;
+constexpr int kFCPW = (16 + 24) / kFWaves;    // one-kilobyte copies per wave per stage (16 of X, 8 per weight)
+
+__global__ __launch_bounds__(64 * kFWaves, 1) void mha_self_fused_bf16(FusedMhaArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[kFStages * kFStageElems + 3 * kFMaxN * kD];
+  uint16_t* const qkv = smem + kFStages * kFStageElems;  // [Q_i | K_i | V_i], rows of 64, swizzled as a tile
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, g = lane >> 5, li = lane & 31;
+  // consecutive logical blocks are the heads of one batch entry, so an XCD's heads share X_b in its L2
+  const int blk = xcd_remap(blockIdx.x, gridDim.x);
+  const int b = blk / a.H, hh = blk % a.H;
+  const int n = a.n, dm = a.dm, N = a.H * kD;
+  const uint16_t* X = static_cast<const uint16_t*>(a.X) + (int64_t)b * n * dm;
+  const uint16_t* Wm[3] = {static_cast<const uint16_t*>(a.Wq) + kD * hh, static_cast<const uint16_t*>(a.Wk) + kD * hh,
+                           static_cast<const uint16_t*>(a.Wv) + kD * hh};
+
+  // Copies of one stage (k-tile t): copy gi = kFCPW*wave + i; gi < 16 brings X rows 8gi .. 8gi+7 (rows past n read
+  // row n-1: their results are never used), gi >= 16 brings k-rows 8c .. 8c+7 of weight block (gi-16)/8. Lane l
+  // brings the logical 16-byte chunk that belongs at physical chunk l%8 of row l/8 of its eight rows (the XOR swizzle
+  // of attn_tile.h, which repeats every 16 rows: two per-lane offsets serve every full copy).
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)smem;
+  const int lr = lane >> 3;
+  uint32_t x_voff[2], w_voff[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const uint32_t chunk = (uint32_t)(((lane & 7) ^ swz(8 * c + lr)) << 4);
+    x_voff[c] = (uint32_t)(lr * dm * 2) + chunk;
+    w_voff[c] = (uint32_t)(lr * N * 2) + chunk;
+  }
+  auto issue = [&](int t) __attribute__((always_inline)) {
+    const int k0 = t * kFTK;
+    const uint32_t stage = smem_lds + (uint32_t)((t % kFStages) * kFStageElems * 2);
+#pragma unroll
+    for (int i = 0; i < kFCPW; ++i) {
+      const int gi = kFCPW * wave + i;  // (uniform)
+      if (gi < 16) {
+        const uint32_t dst = stage + (uint32_t)(gi >> 3) * kFSub * 2u + (uint32_t)(gi & 7) * 1024u;
+        if (8 * gi + 8 <= n) {
+          lds_dma16(X + (int64_t)(8 * gi) * dm + k0, x_voff[gi & 1], dst);
+        } else {
+          int l8 = lr;
+          asm volatile("" : "+v"(l8));
+          const int row = 8 * gi + l8;
+          const uint32_t chunk = (uint32_t)(((lane & 7) ^ swz(row)) << 4);
+          lds_dma16(X + k0, (uint32_t)(min(row, n - 1) * dm * 2) + chunk, dst);
+        }
+      } else {
+        const int gw = gi - 16, m = gw >> 3, c = gw & 7;
+        const uint32_t dst = stage + (uint32_t)(2 + m) * kFSub * 2u + (uint32_t)c * 1024u;
+        lds_dma16(Wm[m] + (int64_t)(k0 + 8 * c) * N, w_voff[c & 1], dst);
+      }
+    }
+  };
+
+  // Projection operands, as in the projection GEMM. Second operand (X^T): row 32mb + li of X, k = 16ks + 8g .. +7
+  // (logical chunk 2ks + g). First operand (W^T): two transposed reads give column 32nb + l%32 of a weight block at
+  // k-rows 16ks + 8g + (0..3) and 16ks + 8g + 4 + (0..3).
+  const int mb = wave >> 1;               // this wave's 32 rows of X
+  const int cb0 = 3 * (wave & 1);         // and its three 32-column blocks of [W^Q_i | W^K_i | W^V_i]
+  int aoff[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) aoff[ks] = li * kD + (((2 * ks + g) ^ swz(li)) << 3);
+  int toff[2][2];
+  {
+    const int jj = (lane & 15) >> 2;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi) {
+        const int row = 8 * g + jj + 4 * hi;
+        const int lchunk = 4 * nb + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+        toff[nb][hi] = row * kD + ((lchunk ^ swz(row)) << 3) + 4 * (lane & 1);
+      }
+  }
+  f32x16 acc[3];  // register r = C[row 32mb + li][column 32(cb % 2) + 8(r/4) + 4g + r%4] of block cb = cb0 + c
+#pragma unroll
+  for (int c = 0; c < 3; ++c) acc[c] = f32x16{};
+
+  const int nk = dm / kFTK;
+  issue(0);
+  for (int t = 0; t < nk; ++t) {
+    // this wave's copies of k-tile t (those of t + 1 may stay in flight), then everyone's
+    if (t + 1 < nk) {
+      issue(t + 1);
+      wait_vmcnt<kFCPW>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    lds_barrier();
+    const uint16_t* st = smem + (t % kFStages) * kFStageElems;
+    const uint16_t* Xs = st + (mb >> 1) * kFSub + (mb & 1) * 32 * kD;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 bo = *reinterpret_cast<const bf16x8*>(Xs + aoff[ks]);
+      bf16x8 ao[3];
+#pragma unroll
+      for (int c = 0; c < 3; ++c) {
+        const int cb = cb0 + c;
+        const uint16_t* Ws = st + (2 + (cb >> 1)) * kFSub + ks * 16 * kD;
+        const bf16x4 lo = lds_read_tr16x4(Ws + toff[cb & 1][0]);
+        const bf16x4 hi = lds_read_tr16x4(Ws + toff[cb & 1][1]);
+        ao[c] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+#pragma unroll
+      for (int c = 0; c < 3; ++c) acc[c] = mfma32x32x16(ao[c], bo, acc[c]);
+    }
+    lds_barrier();  // every wave is done with stage t % 2 before the copies of t + 2 refill it
+  }
+
+  // [Q_i | K_i | V_i] rounded to bf16 into LDS: row r of matrix m at qkv + m*128*64 + r*64, logical chunk c of the
+  // row at physical chunk c ^ swz(r); a lane's four columns are half a chunk.
+  {
+    const int row = 32 * mb + li;
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+      const int cb = cb0 + c, m = cb >> 1;
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int chunk = 4 * (cb & 1) + rg;
+        uint16_t* dst = qkv + m * kFMaxN * kD + row * kD + ((chunk ^ swz(row)) << 3) + 4 * g;
+        *reinterpret_cast<uint2*>(dst) = uint2{pack_bf16x2(acc[c][4 * rg], acc[c][4 * rg + 1]),
+                                               pack_bf16x2(acc[c][4 * rg + 2], acc[c][4 * rg + 3])};
+      }
+    }
+  }
+  lds_barrier();
+  if (wave >= 4) return;  // (uniform) the attention needs four waves of 32 queries
+
+  // Attention of queries 32w .. 32w+31 over every key, transposed as in the attention kernels: S^T = K Q^T with the
+  // wave's queries in the lane index (B operand: lane supplies Q[q][32g + 8ks + j]) and keys in the registers.
+  const uint16_t* Qs = qkv;
+  const uint16_t* Ks = qkv + kFMaxN * kD;
+  const uint16_t* Vs = qkv + 2 * kFMaxN * kD;
+  const int q = 32 * wave + li;
+  const int n_real = real_keys(a.kv_len, b, n);  // keys from n_real on are padding: weight 0
+  const int nkb = (n_real + 31) / 32;             // 32-key blocks holding a real key (uniform)
+  bf16x8 qf[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(Qs + q * kD + (((4 * g + ks) ^ swz(q)) << 3));
+  f32x16 s[4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    s[kb] = f32x16{};
+    if (kb >= nkb) continue;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 kr = *reinterpret_cast<const bf16x8*>(Ks + (32 * kb + li) * kD + (((4 * g + ks) ^ swz(li)) << 3));
+      s[kb] = mfma32x32x16(kr, qf[ks], s[kb]);
+    }
+    // register r holds key 32kb + 8(r/4) + 4g + r%4: padding keys and (causal) keys after the query get -inf
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
+      if (key >= n_real || (a.causal && key > q)) s[kb][r] = -INFINITY;
+      mx = fmaxf(mx, s[kb][r]);
+    }
+  }
+  mx = max_with_partner32(mx);  // the other half of this query's keys sits in lane li +- 32
+  // exp2(s c - max c); a row with no key to see (all -inf) keeps offset 0, so its weights are exactly 0
+  const float neg_m = mx == -INFINITY ? 0.f : -mx * kScaleLog2;
+
+  // P in bf16 as the B operands of O^T = V^T P^T: k-step ks holds registers 8(ks%2) .. +7 of key block ks/2
+  bf16x8 pf[8];
+  f32x4 ts = {};
+  const bf16x8 lsel = lsum_selector(lane);
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    if (ks >= 2 * nkb) continue;
+    const f32x16& sk = s[ks >> 1];
+    const int base = 8 * (ks & 1);
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = pack_bf16x2(fast_exp2(scaled_minus(sk[base + 2 * j], neg_m)),
+                         fast_exp2(scaled_minus(sk[base + 2 * j + 1], neg_m)));
+    pf[ks] = __builtin_bit_cast(bf16x8, (uint4){w[0], w[1], w[2], w[3]});
+    ts = mfma16x16x32(lsel, pf[ks], ts);  // row sums of the same bf16 weights
+  }
+  // V^T operands: transposed reads of V rows 16ks + 4g + (lane%16)/4 (+8), logical chunk 4mb2 + 2((lane/16)%2) +
+  // (lane%4)/2, element 4(lane%2)
+  int voff[2][2];
+  {
+    const int jj = (lane & 15) >> 2;
+#pragma unroll
+    for (int mb2 = 0; mb2 < 2; ++mb2)
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi) {
+        const int row = 4 * g + jj + 8 * hi;
+        const int lchunk = 4 * mb2 + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+        voff[mb2][hi] = row * kD + ((lchunk ^ swz(row)) << 3) + 4 * (lane & 1);
+      }
+  }
+  f32x16 o[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    if (ks >= 2 * nkb) continue;
+#pragma unroll
+    for (int mb2 = 0; mb2 < 2; ++mb2) {
+      const bf16x4 lo = lds_read_tr16x4(Vs + ks * 16 * kD + voff[mb2][0]);
+      const bf16x4 hi = lds_read_tr16x4(Vs + ks * 16 * kD + voff[mb2][1]);
+      o[mb2] = mfma32x32x16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pf[ks], o[mb2]);
+    }
+  }
+
+  // O = O^T / l; lane holds d = 32mb2 + 8(r/4) + 4g + r%4 of query q
+  if (q < n) {
+    const float l = ts[0];
+    const float inv = l > 0.f ? 1.0f / l : 0.f;  // a row with no real key: output 0
+    uint16_t* orow = static_cast<uint16_t*>(a.C) + ((int64_t)b * n + q) * N + kD * hh;
+#pragma unroll
+    for (int mb2 = 0; mb2 < 2; ++mb2)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg)
+        *reinterpret_cast<uint2*>(orow + 32 * mb2 + 8 * rg + 4 * g) =
+            uint2{pack_bf16x2(o[mb2][4 * rg] * inv, o[mb2][4 * rg + 1] * inv),
+                  pack_bf16x2(o[mb2][4 * rg + 2] * inv, o[mb2][4 * rg + 3] * inv)};
+  }
+}
+
+}  // namespace
+
+hipError_t launch_mha_self_fused_bf16(const FusedMhaArgs& a, hipStream_t stream) {
+  if (a.n < 1 || a.n > kFMaxN || a.dm < kFTK || a.dm % kFTK || a.H < 1) return hipErrorInvalidValue;
+  // the copies' per-lane offsets are 32-bit: eight rows of X or of the weights must stay below 4 GiB
+  if ((int64_t)8 * a.dm * 2 > 0xffffffffLL || (int64_t)8 * a.H * kD * 2 > 0xffffffffLL) return hipErrorInvalidValue;
+  const int64_t nblocks = (int64_t)a.B * a.H;
+  if (nblocks <= 0 || nblocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(mha_self_fused_bf16, dim3((unsigned)nblocks), dim3(64 * kFWaves), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace mi355
