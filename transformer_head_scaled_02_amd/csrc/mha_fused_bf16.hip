@@ -10,12 +10,14 @@
 //
 // Why: at n <= 128 the projection GEMM and the attention kernel are each a few microseconds of fixed cost (launch,
 // pipeline fill, one HBM round trip of Q/K/V written and read back). Here the 128 x 192 block [Q_i | K_i | V_i] is
-// formed in the workgroup (X rows and the three 64-column weight blocks stream through a two-stage LDS ring by
-// global_load_lds_dwordx4; the product is formed transposed, C^T = W^T X^T, exactly as in the projection GEMM, so the
-// bf16 Q_i, K_i, V_i are the same numbers), rounded to bf16 into LDS, and the attention runs on them from there: with
+// formed in the workgroup (X rows and the three 64-column weight blocks stream through a four-stage LDS ring by
+// global_load_lds_dwordx4, up to three k-tiles in flight behind the one in use; the product is formed transposed,
+// C^T = W^T X^T, exactly as in the projection GEMM, so the bf16 Q_i, K_i, V_i are the same numbers), rounded to bf16
+// into LDS over the ring's space, and the attention runs on them from there: with
 // every key in LDS the softmax is the plain one (row max over all keys, exp2, row sums on the matrix core from the
-// same bf16 weights that multiply V), no online rescaling. Eight waves share the projection (each a 32-row block of
-// X against three 32-column blocks of the weights); four of them then each take 32 queries.
+// same bf16 weights that multiply V), no online rescaling. Eight waves share the projection (waves w and w + 4 split
+// each k-tile; each covers 64 rows of X against three 32-column blocks of the weights) and the attention (waves w
+// and w + 4 take the same 32 queries against the first and the second 64 keys, merged through LDS).
 #include "attn_tile.h"
 #include "launch.h"
 
@@ -27,12 +29,11 @@ constexpr int kFMaxN = 128;                   // sequence length limit (rows of 
 constexpr int kFTK = 64;                      // k-tile of the projections
 constexpr int kFSub = 64 * 64;                // one 64 x 64 bf16 sub-tile, rows of 128 bytes (8 KB)
 constexpr int kFStageElems = 5 * kFSub;       // a stage: [X rows 0-63 | X rows 64-127 | W^Q_i | W^K_i | W^V_i]
-constexpr int kFStages = 2;
+constexpr int kFStages = 4;                  // the whole 160 KB of LDS; Q/K/V reuse it after the last k-tile
 constexpr int kFCPW = (16 + 24) / kFWaves;    // one-kilobyte copies per wave per stage (16 of X, 8 per weight)
 
 __global__ __launch_bounds__(64 * kFWaves, 1) void mha_self_fused_bf16(FusedMhaArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[kFStages * kFStageElems + 3 * kFMaxN * kD];
-  uint16_t* const qkv = smem + kFStages * kFStageElems;  // [Q_i | K_i | V_i], rows of 64, swizzled as a tile
+  __shared__ __attribute__((aligned(16))) uint16_t smem[kFStages * kFStageElems];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -86,11 +87,14 @@ __global__ __launch_bounds__(64 * kFWaves, 1) void mha_self_fused_bf16(FusedMhaA
   // Projection operands, as in the projection GEMM. Second operand (X^T): row 32mb + li of X, k = 16ks + 8g .. +7
   // (logical chunk 2ks + g). First operand (W^T): two transposed reads give column 32nb + l%32 of a weight block at
   // k-rows 16ks + 8g + (0..3) and 16ks + 8g + 4 + (0..3).
-  const int mb = wave >> 1;               // this wave's 32 rows of X
-  const int cb0 = 3 * (wave & 1);         // and its three 32-column blocks of [W^Q_i | W^K_i | W^V_i]
-  int aoff[4];
+  // Waves w and w + 4 split each k-tile (k-steps 0-1 and 2-3: half the LDS operand reads per product of one wave
+  // per block) and each covers 64 rows of X against three 32-column blocks; their partial sums are added at the end.
+  const int kh = wave >> 2, r4 = wave & 3;
+  const int mbp = r4 >> 1;          // this wave's 64 rows of X: sub-tile mbp of a stage
+  const int cb0 = 3 * (r4 & 1);     // and its three 32-column blocks of [W^Q_i | W^K_i | W^V_i]
+  int aoff[2];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) aoff[ks] = li * kD + (((2 * ks + g) ^ swz(li)) << 3);
+  for (int kk = 0; kk < 2; ++kk) aoff[kk] = li * kD + (((2 * (2 * kh + kk) + g) ^ swz(li)) << 3);
   int toff[2][2];
   {
     const int jj = (lane & 15) >> 2;
@@ -103,27 +107,34 @@ __global__ __launch_bounds__(64 * kFWaves, 1) void mha_self_fused_bf16(FusedMhaA
         toff[nb][hi] = row * kD + ((lchunk ^ swz(row)) << 3) + 4 * (lane & 1);
       }
   }
-  f32x16 acc[3];  // register r = C[row 32mb + li][column 32(cb % 2) + 8(r/4) + 4g + r%4] of block cb = cb0 + c
+  // acc[mi][c]: register r = C[row 64mbp + 32mi + li][column 32(cb % 2) + 8(r/4) + 4g + r%4] of block cb = cb0 + c
+  f32x16 acc[2][3];
 #pragma unroll
-  for (int c = 0; c < 3; ++c) acc[c] = f32x16{};
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int c = 0; c < 3; ++c) acc[mi][c] = f32x16{};
 
   const int nk = dm / kFTK;
-  issue(0);
-  for (int t = 0; t < nk; ++t) {
-    // this wave's copies of k-tile t (those of t + 1 may stay in flight), then everyone's
-    if (t + 1 < nk) {
-      issue(t + 1);
-      wait_vmcnt<kFCPW>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    lds_barrier();
-    const uint16_t* st = smem + (t % kFStages) * kFStageElems;
-    const uint16_t* Xs = st + (mb >> 1) * kFSub + (mb & 1) * 32 * kD;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 bo = *reinterpret_cast<const bf16x8*>(Xs + aoff[ks]);
-      bf16x8 ao[3];
+  for (int i = 0; i < kFStages - 1; ++i)
+    if (i < nk) issue(i);
+  for (int t = 0; t < nk; ++t) {
+    // this wave's copies of k-tile t (those of up to two later tiles may stay in flight), then everyone's; everyone
+    // is also done with k-tile t - 1, whose stage the copies of t + 3 now refill
+    const int ahead = min(kFStages - 2, nk - 1 - t);
+    if (ahead >= 2) wait_vmcnt<2 * kFCPW>();
+    else if (ahead == 1) wait_vmcnt<kFCPW>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    if (t + kFStages - 1 < nk) issue(t + kFStages - 1);
+    const uint16_t* st = smem + (t % kFStages) * kFStageElems;
+    const uint16_t* Xs = st + mbp * kFSub;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int ks = 2 * kh + kk;
+      bf16x8 bo[2], ao[3];
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) bo[mi] = *reinterpret_cast<const bf16x8*>(Xs + mi * 32 * kD + aoff[kk]);
 #pragma unroll
       for (int c = 0; c < 3; ++c) {
         const int cb = cb0 + c;
@@ -133,80 +144,108 @@ __global__ __launch_bounds__(64 * kFWaves, 1) void mha_self_fused_bf16(FusedMhaA
         ao[c] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
 #pragma unroll
-      for (int c = 0; c < 3; ++c) acc[c] = mfma32x32x16(ao[c], bo, acc[c]);
+      for (int c = 0; c < 3; ++c)
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi) acc[mi][c] = mfma32x32x16(ao[c], bo[mi], acc[mi][c]);
     }
-    lds_barrier();  // every wave is done with stage t % 2 before the copies of t + 2 refill it
   }
+  lds_barrier();  // every wave is done with the ring before its space is reused
 
-  // [Q_i | K_i | V_i] rounded to bf16 into LDS: row r of matrix m at qkv + m*128*64 + r*64, logical chunk c of the
-  // row at physical chunk c ^ swz(r); a lane's four columns are half a chunk.
-  {
-    const int row = 32 * mb + li;
+  // The two k-halves meet in LDS: waves 4-7 store their partial sums (f32x4 pieces, lane-contiguous), waves 0-3 add
+  // them, round [Q_i | K_i | V_i] to bf16 and store it at qkv: row r of matrix m at qkv + m*128*64 + r*64, logical
+  // chunk c of the row at physical chunk c ^ swz(r) (a lane's four columns are half a chunk).
+  float* const red = reinterpret_cast<float*>(smem);           // 4 waves x 6 blocks x 16 registers x 64 lanes
+  uint16_t* const qkv = smem + 4 * 6 * 16 * 64 * 2;            // after the partial sums (96 KB)
+  static_assert(4 * 6 * 16 * 64 * 2 + 3 * kFMaxN * kD <= kFStages * kFStageElems, "partial sums and Q/K/V fit");
+  if (kh == 1) {
 #pragma unroll
-    for (int c = 0; c < 3; ++c) {
-      const int cb = cb0 + c, m = cb >> 1;
+    for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int chunk = 4 * (cb & 1) + rg;
-        uint16_t* dst = qkv + m * kFMaxN * kD + row * kD + ((chunk ^ swz(row)) << 3) + 4 * g;
-        *reinterpret_cast<uint2*>(dst) = uint2{pack_bf16x2(acc[c][4 * rg], acc[c][4 * rg + 1]),
-                                               pack_bf16x2(acc[c][4 * rg + 2], acc[c][4 * rg + 3])};
+      for (int c = 0; c < 3; ++c)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<f32x4*>(red + (((r4 * 6 + 3 * mi + c) * 4 + q4) * 64 + lane) * 4) =
+              f32x4{acc[mi][c][4 * q4], acc[mi][c][4 * q4 + 1], acc[mi][c][4 * q4 + 2], acc[mi][c][4 * q4 + 3]};
+  }
+  lds_barrier();
+  if (kh == 0) {
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+      const int row = 64 * mbp + 32 * mi + li;
+#pragma unroll
+      for (int c = 0; c < 3; ++c) {
+        const int cb = cb0 + c, m = cb >> 1;
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const f32x4 o = *reinterpret_cast<const f32x4*>(red + (((r4 * 6 + 3 * mi + c) * 4 + rg) * 64 + lane) * 4);
+          const int chunk = 4 * (cb & 1) + rg;
+          uint16_t* dst = qkv + m * kFMaxN * kD + row * kD + ((chunk ^ swz(row)) << 3) + 4 * g;
+          *reinterpret_cast<uint2*>(dst) = uint2{pack_bf16x2(acc[mi][c][4 * rg] + o[0], acc[mi][c][4 * rg + 1] + o[1]),
+                                                 pack_bf16x2(acc[mi][c][4 * rg + 2] + o[2], acc[mi][c][4 * rg + 3] + o[3])};
+        }
       }
     }
   }
   lds_barrier();
-  if (wave >= 4) return;  // (uniform) the attention needs four waves of 32 queries
 
-  // Attention of queries 32w .. 32w+31 over every key, transposed as in the attention kernels: S^T = K Q^T with the
-  // wave's queries in the lane index (B operand: lane supplies Q[q][32g + 8ks + j]) and keys in the registers.
+  // Attention, transposed as in the attention kernels: S^T = K Q^T with a wave's 32 queries in the lane index (B
+  // operand: lane supplies Q[q][32g + 8ks + j]) and keys in the registers. Waves w and w + 4 take queries
+  // 32(w%4) .. +31 against keys 0-63 and 64-127 respectively; each forms its part with its own row max, and wave w
+  // merges the two parts through LDS.
   const uint16_t* Qs = qkv;
   const uint16_t* Ks = qkv + kFMaxN * kD;
   const uint16_t* Vs = qkv + 2 * kFMaxN * kD;
-  const int q = 32 * wave + li;
+  const int q = 32 * r4 + li;
   const int n_real = real_keys(a.kv_len, b, n);  // keys from n_real on are padding: weight 0
   const int nkb = (n_real + 31) / 32;             // 32-key blocks holding a real key (uniform)
+  const int kb0 = 2 * kh;                         // this wave's key blocks kb0, kb0 + 1
   bf16x8 qf[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(Qs + q * kD + (((4 * g + ks) ^ swz(q)) << 3));
-  f32x16 s[4];
+  f32x16 s[2];
   float mx = -INFINITY;
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    s[kb] = f32x16{};
+  for (int j = 0; j < 2; ++j) {
+    const int kb = kb0 + j;
+    s[j] = f32x16{};
     if (kb >= nkb) continue;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const bf16x8 kr = *reinterpret_cast<const bf16x8*>(Ks + (32 * kb + li) * kD + (((4 * g + ks) ^ swz(li)) << 3));
-      s[kb] = mfma32x32x16(kr, qf[ks], s[kb]);
+      s[j] = mfma32x32x16(kr, qf[ks], s[j]);
     }
     // register r holds key 32kb + 8(r/4) + 4g + r%4: padding keys and (causal) keys after the query get -inf
+    if (a.causal || 32 * kb + 32 > n_real) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-      if (key >= n_real || (a.causal && key > q)) s[kb][r] = -INFINITY;
-      mx = fmaxf(mx, s[kb][r]);
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (key >= n_real || (a.causal && key > q)) s[j][r] = -INFINITY;
+      }
     }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[j][r]);
   }
-  mx = max_with_partner32(mx);  // the other half of this query's keys sits in lane li +- 32
-  // exp2(s c - max c); a row with no key to see (all -inf) keeps offset 0, so its weights are exactly 0
+  mx = max_with_partner32(mx);  // the other half of this query's keys of the block sits in lane li +- 32
+  // exp2(s c - max c); a part with no key to see (all -inf) keeps offset 0, so its weights are exactly 0
   const float neg_m = mx == -INFINITY ? 0.f : -mx * kScaleLog2;
 
-  // P in bf16 as the B operands of O^T = V^T P^T: k-step ks holds registers 8(ks%2) .. +7 of key block ks/2
-  bf16x8 pf[8];
+  // P in bf16 as the B operands of O^T = V^T P^T: k-step kk holds registers 8(kk%2) .. +7 of key block kb0 + kk/2
+  bf16x8 pf[4];
   f32x4 ts = {};
   const bf16x8 lsel = lsum_selector(lane);
+  const int nks = 2 * min(max(nkb - kb0, 0), 2);  // this wave's 16-key steps holding a real key
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    if (ks >= 2 * nkb) continue;
-    const f32x16& sk = s[ks >> 1];
-    const int base = 8 * (ks & 1);
+  for (int kk = 0; kk < 4; ++kk) {
+    if (kk >= nks) continue;
+    const f32x16& sk = s[kk >> 1];
+    const int base = 8 * (kk & 1);
     uint32_t w[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       w[j] = pack_bf16x2(fast_exp2(scaled_minus(sk[base + 2 * j], neg_m)),
                          fast_exp2(scaled_minus(sk[base + 2 * j + 1], neg_m)));
-    pf[ks] = __builtin_bit_cast(bf16x8, (uint4){w[0], w[1], w[2], w[3]});
-    ts = mfma16x16x32(lsel, pf[ks], ts);  // row sums of the same bf16 weights
+    pf[kk] = __builtin_bit_cast(bf16x8, (uint4){w[0], w[1], w[2], w[3]});
+    ts = mfma16x16x32(lsel, pf[kk], ts);  // row sums of the same bf16 weights
   }
   // V^T operands: transposed reads of V rows 16ks + 4g + (lane%16)/4 (+8), logical chunk 4mb2 + 2((lane/16)%2) +
   // (lane%4)/2, element 4(lane%2)
@@ -224,28 +263,51 @@ __global__ __launch_bounds__(64 * kFWaves, 1) void mha_self_fused_bf16(FusedMhaA
   }
   f32x16 o[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    if (ks >= 2 * nkb) continue;
+  for (int kk = 0; kk < 4; ++kk) {
+    if (kk >= nks) continue;
+    const uint16_t* vt = Vs + (2 * kb0 + kk) * 16 * kD;  // keys 32kb0 + 16kk .. +15
 #pragma unroll
     for (int mb2 = 0; mb2 < 2; ++mb2) {
-      const bf16x4 lo = lds_read_tr16x4(Vs + ks * 16 * kD + voff[mb2][0]);
-      const bf16x4 hi = lds_read_tr16x4(Vs + ks * 16 * kD + voff[mb2][1]);
-      o[mb2] = mfma32x32x16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pf[ks], o[mb2]);
+      const bf16x4 lo = lds_read_tr16x4(vt + voff[mb2][0]);
+      const bf16x4 hi = lds_read_tr16x4(vt + voff[mb2][1]);
+      o[mb2] = mfma32x32x16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pf[kk], o[mb2]);
     }
   }
 
+  // merge: wave w + 4 hands over its part (offset, row sum, O) through LDS (the partial-sum space, free again)
+  float* const part = red + r4 * 34 * 64;  // per wave pair: [O^T registers 0..31 | -offset | row sum] x 64 lanes
+  if (kh == 1) {
+#pragma unroll
+    for (int mb2 = 0; mb2 < 2; ++mb2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) part[(16 * mb2 + r) * 64 + lane] = o[mb2][r];
+    part[32 * 64 + lane] = neg_m;
+    part[33 * 64 + lane] = ts[0];
+  }
+  lds_barrier();
+  if (kh == 1) return;
+  const float neg_m2 = part[32 * 64 + lane], l2 = part[33 * 64 + lane];
+  const float l1 = ts[0];
+  // scale each part to the larger of the two offsets; a part without keys (row sum 0) contributes nothing
+  const float neg_mm = l1 > 0.f ? (l2 > 0.f ? fminf(neg_m, neg_m2) : neg_m) : neg_m2;
+  const float a1 = l1 > 0.f ? fast_exp2(neg_mm - neg_m) : 0.f;
+  const float a2 = l2 > 0.f ? fast_exp2(neg_mm - neg_m2) : 0.f;
+  const float l = a1 * l1 + a2 * l2;
+
   // O = O^T / l; lane holds d = 32mb2 + 8(r/4) + 4g + r%4 of query q
   if (q < n) {
-    const float l = ts[0];
     const float inv = l > 0.f ? 1.0f / l : 0.f;  // a row with no real key: output 0
     uint16_t* orow = static_cast<uint16_t*>(a.C) + ((int64_t)b * n + q) * N + kD * hh;
 #pragma unroll
     for (int mb2 = 0; mb2 < 2; ++mb2)
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg)
+      for (int rg = 0; rg < 4; ++rg) {
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = (a1 * o[mb2][4 * rg + i] + a2 * part[(16 * mb2 + 4 * rg + i) * 64 + lane]) * inv;
         *reinterpret_cast<uint2*>(orow + 32 * mb2 + 8 * rg + 4 * g) =
-            uint2{pack_bf16x2(o[mb2][4 * rg] * inv, o[mb2][4 * rg + 1] * inv),
-                  pack_bf16x2(o[mb2][4 * rg + 2] * inv, o[mb2][4 * rg + 3] * inv)};
+            uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      }
   }
 }
 
