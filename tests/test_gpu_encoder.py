@@ -59,7 +59,11 @@ def test_encoder_layer_workload():
 @pytest.mark.parametrize("B,n,d_model,h,d_ff,causal,kv_len", [
     (2, 1, 512, 8, 2048, False, None), (3, 77, 512, 8, 2048, True, None), (2, 130, 256, 4, 1024, False, None),
     (4, 65, 512, 8, 2048, False, [65, 30, 1, 0]), (2, 200, 1024, 16, 4096, True, [200, 100]),
-    (1, 64, 64, 1, 64, False, None)])
+    (1, 64, 64, 1, 64, False, None),
+    # d_model = 320: three column tiles per row, the last one half wide, and 150 rows (a ragged last row tile)
+    (3, 50, 320, 5, 640, False, None),
+    # 8192 rows x 1024 columns: the W^O and W2 products take 128-row tiles (the LayerNorm covers 128 rows per tile)
+    (64, 128, 1024, 16, 1024, False, None)])
 def test_encoder_layer_shapes(B, n, d_model, h, d_ff, causal, kv_len):
     x = workloads.make_encoder_inputs(B, n, d_model, h, d_ff, "bf16", 1100 + n + d_model)
     got = to_f64(_run(x, h, 1e-5, causal, kv_len))
@@ -87,3 +91,21 @@ def test_encoder_layer_workspace_reuse_and_no_writes_outside():
         _run(x, h, 1e-5, out=out, workspace=ws)
         assert torch.all(big[:1024] == 5.0) and torch.all(big[-1024:] == 5.0)
         _check(to_f64(out), _ref(x, h, 1e-5), f"reuse n={n_i}")
+
+
+@pytest.mark.parametrize("n", [128, 200])
+def test_encoder_layer_workspace_contents_do_not_matter(n):
+    # Every workspace region is written before it is read within a call: the result must not depend on what the
+    # workspace held before (here: all bits set, random bytes, the previous call's intermediates).
+    B, d_model, h, d_ff = 8, 512, 8, 2048
+    x = workloads.make_encoder_inputs(B, n, d_model, h, d_ff, "bf16", 1400 + n)
+    ws = torch.empty(m.encoder_layer_workspace_size(B, n, d_model, h, d_ff), dtype=torch.uint8, device="cuda")
+    outs = []
+    for fill in ("ones", "random", "previous"):
+        if fill == "ones":
+            ws.fill_(255)
+        elif fill == "random":
+            ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, device="cuda"))
+        outs.append(_run(x, h, 1e-5, workspace=ws).clone())
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+    _check(to_f64(outs[0]), _ref(x, h, 1e-5), f"workspace contents n={n}")
