@@ -3,6 +3,8 @@
 A step is one sdpa_forward call (scores, scale, mask, online softmax, weighted sum of V: the whole fused attention)
 over the long-sequence workload B=4, h=8, n_q=n_k=4096, d_k=d_v=64, bf16, unmasked, with Q/K/V ~ N(0,1) seeded and
 already resident in HBM. Metric: attention TFLOP/s = 4*B*h*n_q*n_k*d_k / time, against the bf16 dense MFMA peak.
+The line also carries the ceilings measured on the chip after the timed region (dense MFMA, v_exp_f32, copy
+bandwidth) and the softmax's exp2 throughput (one per visible score) against the measured exp ceiling.
 
 With a backward workload (--workload sdpa_bwd_bf16_b4_h8_n4096, sdpa_bwd_causal_bf16_b4_h8_n4096, or the head widths
 32 and 128: sdpa_bwd_bf16_b4_h16_n4096_d32, sdpa_bwd_bf16_b4_h4_n4096_d128) a step is one sdpa_backward call
@@ -767,6 +769,13 @@ def main():
                                     "exp2_per_clock_per_cu": round(rate, 2), "exp_clock_ghz": round(ghz_e, 3),
                                     "hbm_copy_GBps": round(gbps, 1)}
         rec["pct_of_measured_mfma_ceiling"] = round(100 * value / tf, 2)
+        # the second ceiling of the softmax: one exp2 per visible score against the chip's measured v_exp_f32 rate
+        # (per CU per clock, at the clock it held under that probe, times the 256 CUs)
+        exps = w["B"] * w["h"] * _pairs(w) / (ms * 1e-3)
+        ceiling = rate * 256 * ghz_e * 1e9
+        rec["exp_throughput"] = {"exp_per_s": round(exps / 1e12, 3), "measured_ceiling_per_s": round(ceiling / 1e12, 3),
+                                 "unit": "1e12 exp2/s", "frac": round(exps / ceiling, 4),
+                                 "count": "one exp2 per visible (query, key) score"}
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, x, args.cpu_budget)
     print(json.dumps(rec), flush=True)

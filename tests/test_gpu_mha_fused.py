@@ -3,7 +3,8 @@ float64 oracle, through mha_forward and encoder_layer_forward.
 
 That path computes, per (batch entry, head), the head's Q/K/V projections and its attention in one workgroup (every
 key in LDS, the plain softmax over all of them). Swept here: sequence lengths around its 32-key blocks and its limit
-(1 .. 128, with 129 falling back to the separate kernels), d_model from one to sixteen heads, the causal mask, key
+(1 .. 128, with 129 falling back to the separate kernels), d_model from one to thirty-two heads and projections of
+h * 64 columns narrower or wider than d_model, the causal mask, key
 padding down to zero keys (encoder layer), and the same call twice (no state). Bars as everywhere for bf16:
 max-abs <= 2e-2, mean-abs <= 2e-3, normalised rms <= 1e-2 (the encoder layer's LayerNorm outputs are order 1 and use
 the encoder tests' bars).
@@ -39,7 +40,9 @@ def test_fused_mha_lengths(n, causal):
 
 
 @pytest.mark.parametrize("B,n,d_model,h", [(1, 128, 64, 1), (2, 77, 128, 2), (5, 40, 256, 4), (2, 128, 1024, 16),
-                                           (1, 3, 2048, 32)])
+                                           (1, 3, 2048, 32),
+                                           # h * 64 != d_model: projections narrower or wider than the model
+                                           (2, 100, 512, 4), (3, 50, 192, 8), (1, 128, 64, 3)])
 def test_fused_mha_widths(B, n, d_model, h):
     x = workloads.make_mha_inputs(B, n, n, d_model, h, 64, 64, "bf16", 7100 + d_model + n)
     xq = to_dev(x["Xq"])
