@@ -15,9 +15,10 @@
 // C^T = W^T X^T, exactly as in the projection GEMM, so the bf16 Q_i, K_i, V_i are the same numbers), rounded to bf16
 // into LDS over the ring's space, and the attention runs on them from there: with
 // every key in LDS the softmax is the plain one (row max over all keys, exp2, row sums on the matrix core from the
-// same bf16 weights that multiply V), no online rescaling. Eight waves share the projection (waves w and w + 4 split
-// each k-tile; each covers 64 rows of X against three 32-column blocks of the weights) and the attention (waves w
-// and w + 4 take the same 32 queries against the first and the second 64 keys, merged through LDS).
+// same bf16 weights that multiply V), no online rescaling. Eight waves share the projection (wave w forms rows
+// 32(w/2) .. +31 against three 32-column blocks of the weights over the whole of d_model, so no partial sums have to
+// meet) and the attention (waves w and w + 4 take the same 32 queries against the first and the second 64 keys,
+// merged through LDS).
 #include "attn_tile.h"
 #include "launch.h"
 
@@ -87,14 +88,14 @@ __global__ __launch_bounds__(64 * kFWaves, 1) void mha_self_fused_bf16(FusedMhaA
   // Projection operands, as in the projection GEMM. Second operand (X^T): row 32mb + li of X, k = 16ks + 8g .. +7
   // (logical chunk 2ks + g). First operand (W^T): two transposed reads give column 32nb + l%32 of a weight block at
   // k-rows 16ks + 8g + (0..3) and 16ks + 8g + 4 + (0..3).
-  // Waves w and w + 4 split each k-tile (k-steps 0-1 and 2-3: half the LDS operand reads per product of one wave
-  // per block) and each covers 64 rows of X against three 32-column blocks; their partial sums are added at the end.
-  const int kh = wave >> 2, r4 = wave & 3;
-  const int mbp = r4 >> 1;          // this wave's 64 rows of X: sub-tile mbp of a stage
-  const int cb0 = 3 * (r4 & 1);     // and its three 32-column blocks of [W^Q_i | W^K_i | W^V_i]
-  int aoff[2];
+  // Wave w covers 32 rows of X against three 32-column blocks, over every k-step of every k-tile. (Splitting the
+  // k-steps between waves w and w + 4, each on 64 rows, reads fewer operands from LDS per product but leaves two
+  // partial sums per output to meet in LDS: measured 6 % slower over the whole mha_forward call.)
+  const int rb = wave >> 1;          // this wave's 32 rows of X: 32rb .. 32rb + 31
+  const int cb0 = 3 * (wave & 1);    // and its three 32-column blocks of [W^Q_i | W^K_i | W^V_i]
+  int aoff[4];
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) aoff[kk] = li * kD + (((2 * (2 * kh + kk) + g) ^ swz(li)) << 3);
+  for (int ks = 0; ks < 4; ++ks) aoff[ks] = li * kD + (((2 * ks + g) ^ swz(li)) << 3);
   int toff[2][2];
   {
     const int jj = (lane & 15) >> 2;
@@ -107,12 +108,10 @@ __global__ __launch_bounds__(64 * kFWaves, 1) void mha_self_fused_bf16(FusedMhaA
         toff[nb][hi] = row * kD + ((lchunk ^ swz(row)) << 3) + 4 * (lane & 1);
       }
   }
-  // acc[mi][c]: register r = C[row 64mbp + 32mi + li][column 32(cb % 2) + 8(r/4) + 4g + r%4] of block cb = cb0 + c
-  f32x16 acc[2][3];
+  // acc[c]: register r = C[row 32rb + li][column 32(cb % 2) + 8(r/4) + 4g + r%4] of block cb = cb0 + c
+  f32x16 acc[3];
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int c = 0; c < 3; ++c) acc[mi][c] = f32x16{};
+  for (int c = 0; c < 3; ++c) acc[c] = f32x16{};
 
   const int nk = dm / kFTK;
 #pragma unroll
@@ -128,13 +127,11 @@ __global__ __launch_bounds__(64 * kFWaves, 1) void mha_self_fused_bf16(FusedMhaA
     lds_barrier();
     if (t + kFStages - 1 < nk) issue(t + kFStages - 1);
     const uint16_t* st = smem + (t % kFStages) * kFStageElems;
-    const uint16_t* Xs = st + mbp * kFSub;
+    const uint16_t* Xs = st + (rb >> 1) * kFSub + (rb & 1) * 32 * kD;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int ks = 2 * kh + kk;
-      bf16x8 bo[2], ao[3];
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi) bo[mi] = *reinterpret_cast<const bf16x8*>(Xs + mi * 32 * kD + aoff[kk]);
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8 ao[3];
+      const bf16x8 bo = *reinterpret_cast<const bf16x8*>(Xs + aoff[ks]);
 #pragma unroll
       for (int c = 0; c < 3; ++c) {
         const int cb = cb0 + c;
@@ -144,45 +141,28 @@ __global__ __launch_bounds__(64 * kFWaves, 1) void mha_self_fused_bf16(FusedMhaA
         ao[c] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
 #pragma unroll
-      for (int c = 0; c < 3; ++c)
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi) acc[mi][c] = mfma32x32x16(ao[c], bo[mi], acc[mi][c]);
+      for (int c = 0; c < 3; ++c) acc[c] = mfma32x32x16(ao[c], bo, acc[c]);
     }
   }
   lds_barrier();  // every wave is done with the ring before its space is reused
 
-  // The two k-halves meet in LDS: waves 4-7 store their partial sums (f32x4 pieces, lane-contiguous), waves 0-3 add
-  // them, round [Q_i | K_i | V_i] to bf16 and store it at qkv: row r of matrix m at qkv + m*128*64 + r*64, logical
-  // chunk c of the row at physical chunk c ^ swz(r) (a lane's four columns are half a chunk).
-  float* const red = reinterpret_cast<float*>(smem);           // 4 waves x 6 blocks x 16 registers x 64 lanes
-  uint16_t* const qkv = smem + 4 * 6 * 16 * 64 * 2;            // after the partial sums (96 KB)
-  static_assert(4 * 6 * 16 * 64 * 2 + 3 * kFMaxN * kD <= kFStages * kFStageElems, "partial sums and Q/K/V fit");
-  if (kh == 1) {
+  // [Q_i | K_i | V_i] rounded to bf16 at qkv: row r of matrix m at qkv + m*128*64 + r*64, logical chunk c of the row
+  // at physical chunk c ^ swz(r) (a lane's four columns are half a chunk). qkv starts past the merge buffer of the
+  // attention step below.
+  float* const red = reinterpret_cast<float*>(smem);
+  uint16_t* const qkv = smem + 4 * 6 * 16 * 64 * 2;
+  static_assert(4 * 6 * 16 * 64 * 2 + 3 * kFMaxN * kD <= kFStages * kFStageElems, "merge buffer and Q/K/V fit");
+  {
+    const int row = 32 * rb + li;
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+    for (int c = 0; c < 3; ++c) {
+      const int cb = cb0 + c, m = cb >> 1;
 #pragma unroll
-      for (int c = 0; c < 3; ++c)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          *reinterpret_cast<f32x4*>(red + (((r4 * 6 + 3 * mi + c) * 4 + q4) * 64 + lane) * 4) =
-              f32x4{acc[mi][c][4 * q4], acc[mi][c][4 * q4 + 1], acc[mi][c][4 * q4 + 2], acc[mi][c][4 * q4 + 3]};
-  }
-  lds_barrier();
-  if (kh == 0) {
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
-      const int row = 64 * mbp + 32 * mi + li;
-#pragma unroll
-      for (int c = 0; c < 3; ++c) {
-        const int cb = cb0 + c, m = cb >> 1;
-#pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          const f32x4 o = *reinterpret_cast<const f32x4*>(red + (((r4 * 6 + 3 * mi + c) * 4 + rg) * 64 + lane) * 4);
-          const int chunk = 4 * (cb & 1) + rg;
-          uint16_t* dst = qkv + m * kFMaxN * kD + row * kD + ((chunk ^ swz(row)) << 3) + 4 * g;
-          *reinterpret_cast<uint2*>(dst) = uint2{pack_bf16x2(acc[mi][c][4 * rg] + o[0], acc[mi][c][4 * rg + 1] + o[1]),
-                                                 pack_bf16x2(acc[mi][c][4 * rg + 2] + o[2], acc[mi][c][4 * rg + 3] + o[3])};
-        }
+      for (int rg = 0; rg < 4; ++rg) {
+        const int chunk = 4 * (cb & 1) + rg;
+        uint16_t* dst = qkv + m * kFMaxN * kD + row * kD + ((chunk ^ swz(row)) << 3) + 4 * g;
+        *reinterpret_cast<uint2*>(dst) = uint2{pack_bf16x2(acc[c][4 * rg], acc[c][4 * rg + 1]),
+                                               pack_bf16x2(acc[c][4 * rg + 2], acc[c][4 * rg + 3])};
       }
     }
   }
@@ -192,6 +172,7 @@ __global__ __launch_bounds__(64 * kFWaves, 1) void mha_self_fused_bf16(FusedMhaA
   // operand: lane supplies Q[q][32g + 8ks + j]) and keys in the registers. Waves w and w + 4 take queries
   // 32(w%4) .. +31 against keys 0-63 and 64-127 respectively; each forms its part with its own row max, and wave w
   // merges the two parts through LDS.
+  const int kh = wave >> 2, r4 = wave & 3;  // key half, query block
   const uint16_t* Qs = qkv;
   const uint16_t* Ks = qkv + kFMaxN * kD;
   const uint16_t* Vs = qkv + 2 * kFMaxN * kD;
