@@ -543,7 +543,7 @@ def bench_mha(args, w, x, m, dev):
 
 
 def bench_encoder(args, w, x, m, dev):
-    """Time encoder_layer_forward (seven launches per step); returns the JSON record."""
+    """Time encoder_layer_forward (six launches per step at this shape); returns the JSON record."""
     import numpy as np
     import torch
 

@@ -257,7 +257,7 @@ def sdpa_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.
                   dv: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
                   kv_len: torch.Tensor | None = None, window: int | None = None):
     """Gradients (dq, dk, dv) of attention given the forward's output `out`, its `lse` (from sdpa_forward_lse, or
-    sdpa_forward_padded with the same `kv_len`) and the upstream gradient `dout` [B,h,n_q,d], d in {32, 64}.
+    sdpa_forward_padded with the same `kv_len`) and the upstream gradient `dout` [B,h,n_q,d], d in {32, 64, 128}.
     For bf16 inputs `out` may be the float32 out_f32 of sdpa_forward_train (D = dO . O is then formed from the
     unrounded output). `workspace` (uint8, at least sdpa_backward_workspace_size bytes) may be passed in to avoid an
     allocation."""

@@ -3,12 +3,14 @@
 // sdpa_forward -> one fused attention launch (bf16 MFMA kernel or fp32 VALU kernel); sdpa_forward_lse also writes
 //                 the row log-sum-exp.
 // encoder_layer_forward -> projections, attention, W^O + residual, LayerNorm, FFN W1 + bias + ReLU, FFN W2 + bias +
-//                 residual, LayerNorm: seven launches, no host sync.
+//                 residual, LayerNorm: seven launches (six for short sequences at head width 64, where the
+//                 projections and the attention are one launch), no host sync.
 // sdpa_forward_window -> the same launch restricted to a band of keys around each query.
 // sdpa_forward_padded -> the same launch with per-batch key counts (key padding mask).
 // sdpa_backward -> three launches: the per-row pre-pass (D = dO . O and lse into the workspace), dK/dV, dQ.
 // mha_forward  -> Q/K/V projections (one grouped GEMM launch writing per-head layout into the workspace), the fused
-//                 attention writing the concatenated heads, and the W^O GEMM into `out`: three launches, no host sync.
+//                 attention writing the concatenated heads, and the W^O GEMM into `out`: three launches, no host sync
+//                 (two for short self-attention at head width 64: projections and attention in one launch).
 // Every argument error is returned before the first HIP call; nothing is enqueued in that case.
 #include <hip/hip_runtime.h>
 

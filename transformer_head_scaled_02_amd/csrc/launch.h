@@ -36,7 +36,7 @@ hipError_t launch_attn_fwd_f32(const AttnArgs& a, int d, hipStream_t stream);
 // (causal or windowed arguments: hipErrorInvalidValue, nothing launched)
 hipError_t launch_attn_fwd_pp_bf16(const AttnArgs& a, hipStream_t stream);
 
-// Backward pass of attention over [B, H] heads of width d (32 or 64), every tensor dense [B, H, n, d] in the element
+// Backward pass of attention over [B, H] heads of width d (32, 64 or 128), every tensor dense [B, H, n, d] in the element
 // type.
 // `aux` is the workspace: per head and per 64-row query tile, 256 floats = [log2(e)*lse of the 64 rows | D of the 64
 // rows | per row 8 bytes: -D as three bf16 parts and a zero], where D_i = dO_i . O_i; rows past n_q hold lse = +inf
@@ -64,7 +64,7 @@ constexpr int kAuxFloatsPerTile = 256;
 __device__ __forceinline__ int real_keys(const int* kv_len, int b, int n_k) {
   return kv_len == nullptr ? n_k : min(max(kv_len[b], 0), n_k);
 }
-// d: the head width, 32 or 64 (every other value: hipErrorInvalidValue, nothing launched)
+// d: the head width, 32, 64 or 128 (every other value: hipErrorInvalidValue, nothing launched)
 hipError_t launch_attn_bwd_pre(const BwdArgs& a, bool f32, int d, hipStream_t stream);  // fills `aux`
 hipError_t launch_attn_bwd_bf16(const BwdArgs& a, int d, hipStream_t stream);  // pre-pass, dK/dV, dQ
 hipError_t launch_attn_bwd_f32(const BwdArgs& a, int d, hipStream_t stream);
