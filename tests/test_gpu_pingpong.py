@@ -131,3 +131,15 @@ def test_pingpong_matches_across_block_boundaries():
     head = m.sdpa_forward(q[:, :, :512].contiguous(), k, v)
     torch.cuda.synchronize()
     assert torch.equal(full[:, :, :512], head)
+
+
+def test_pingpong_train_forward_float32_output():
+    # the training forward also writes the output before its bf16 rounding, [B, h, n_q, 64] float32: rounding it gives
+    # the bf16 output bit for bit, and it meets the oracle at least as closely
+    x, (q, k, v) = _case(2, 2, 700, 333, 4800)
+    out, o32, lse = m.sdpa_forward_train(q, k, v)
+    torch.cuda.synchronize()
+    assert o32.dtype == torch.float32 and o32.shape == out.shape
+    assert torch.equal(o32.to(torch.bfloat16), out)
+    ref = sdpa_ref(x["Q"].f64, x["K"].f64, x["V"].f64)
+    assert_bf16_parity(o32.double().cpu().numpy(), ref, "float32 output")
