@@ -3,8 +3,8 @@
 A step is one sdpa_forward call (scores, scale, mask, online softmax, weighted sum of V: the whole fused attention)
 over the long-sequence workload B=4, h=8, n_q=n_k=4096, d_k=d_v=64, bf16, unmasked, with Q/K/V ~ N(0,1) seeded and
 already resident in HBM. Metric: attention TFLOP/s = 4*B*h*n_q*n_k*d_k / time, against the bf16 dense MFMA peak.
-The line also carries the ceilings measured on the chip after the timed region (dense MFMA, v_exp_f32, copy
-bandwidth) and the softmax's exp2 throughput (one per visible score) against the measured exp ceiling.
+The line also carries the ceilings measured on the chip after the timed region (dense MFMA, v_exp_f32, LDS reads,
+copy bandwidth) and the softmax's exp2 throughput (one per visible score) against the measured exp ceiling.
 
 With a backward workload (--workload sdpa_bwd_bf16_b4_h8_n4096, sdpa_bwd_causal_bf16_b4_h8_n4096, or the head widths
 32 and 128: sdpa_bwd_bf16_b4_h16_n4096_d32, sdpa_bwd_bf16_b4_h4_n4096_d128) a step is one sdpa_backward call
@@ -764,9 +764,13 @@ def main():
         # (and the clock it holds under that load), the v_exp_f32 rate and device-to-device copy bandwidth
         tf, ghz = m.probe_mfma_bf16(iters=20000)
         rate, ghz_e = m.probe_exp_f32(iters=4000)
+        lds_row, _ = m.probe_lds_read(False, iters=20000)
+        lds_tr, _ = m.probe_lds_read(True, iters=20000)
         gbps = m.probe_hbm_copy(nbytes=1 << 30, reps=5)
         rec["measured_ceilings"] = {"mfma_bf16_tflops": round(tf, 1), "mfma_clock_ghz": round(ghz, 3),
                                     "exp2_per_clock_per_cu": round(rate, 2), "exp_clock_ghz": round(ghz_e, 3),
+                                    "lds_read_bytes_per_clock_per_cu": {"ds_read_b128": round(lds_row, 1),
+                                                                        "ds_read_b64_tr_b16": round(lds_tr, 1)},
                                     "hbm_copy_GBps": round(gbps, 1)}
         rec["pct_of_measured_mfma_ceiling"] = round(100 * value / tf, 2)
         # the second ceiling of the softmax: one exp2 per visible score against the chip's measured v_exp_f32 rate

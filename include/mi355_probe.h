@@ -7,6 +7,7 @@
  *     clock under matrix-core load depends on how many operand bits change), and consecutive products sharing one
  *     operand, the order the attention kernel uses;
  *   - probe_exp_f32: the rate of v_exp_f32 (the softmax's transcendental) with every CU busy;
+ *   - probe_lds_read: LDS read throughput with every CU busy, for the two read forms the attention kernels use;
  *   - probe_hbm_copy: device-to-device copy bandwidth (bytes read + bytes written per second).
  *
  * Conventions: pointers are caller-owned DEVICE pointers (16-byte aligned); `stream` is a hipStream_t (NULL: the
@@ -37,6 +38,12 @@ int probe_mfma_bf16(void* scratch, size_t scratch_bytes, int64_t iters, void* st
  *   exp_per_clock_per_cu: lane results per shader cycle per CU; clock_ghz as above */
 int probe_exp_f32(void* scratch, size_t scratch_bytes, int64_t iters, void* stream, double* exp_per_clock_per_cu,
                   double* clock_ghz);
+
+/* LDS read throughput: `iters` loop trips of 32 reads per wave (iters in [1, 1e6]), two 4-wave workgroups per CU, each
+ * reading its own 32 KB; transposed = 0: ds_read_b128 (16 bytes a lane), 1: ds_read_b64_tr_b16 (8 bytes a lane).
+ *   bytes_per_clock_per_cu: bytes delivered to lanes per shader cycle per CU; clock_ghz as above */
+int probe_lds_read(void* scratch, size_t scratch_bytes, int64_t iters, int transposed, void* stream,
+                   double* bytes_per_clock_per_cu, double* clock_ghz);
 
 /* Copy `bytes` (a multiple of 16, at most 2^34) from src to dst `reps` times (reps in [1, 1000]); src and dst must
  * not overlap. gbps: (bytes read + bytes written) per second, in GB/s (1e9 B/s). */

@@ -244,6 +244,15 @@ def test_probes_reject_bad_scratch_before_any_hip_call(lib, case):
     x, y = ctypes.c_double(), ctypes.c_double()
     assert lib.probe_mfma_bf16(scratch, nbytes, iters, None, ctypes.byref(x), ctypes.byref(y)) == INVALID
     assert lib.probe_exp_f32(scratch, nbytes, iters, None, ctypes.byref(x), ctypes.byref(y)) == INVALID
+    for tr in (0, 1):
+        assert lib.probe_lds_read(scratch, nbytes, iters, tr, None, ctypes.byref(x), ctypes.byref(y)) == INVALID
+
+
+def test_probe_lds_read_rejects_bad_form(lib):
+    import ctypes
+    x, y = ctypes.c_double(), ctypes.c_double()
+    assert lib.probe_lds_read(A, lib.probe_scratch_size(), 10, 2, None, ctypes.byref(x), ctypes.byref(y)) == INVALID
+    assert lib.probe_lds_read(A, lib.probe_scratch_size(), 10, 0, None, None, ctypes.byref(y)) == INVALID
 
 
 @pytest.mark.parametrize("kw", [dict(src=0), dict(nbytes=0), dict(nbytes=24), dict(reps=0), dict(reps=1001),

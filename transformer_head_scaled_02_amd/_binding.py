@@ -24,7 +24,7 @@ ATTN_F32, ATTN_BF16, ATTN_BF16_F32O = 0, 1, 2
 EXPORTED = ("sdpa_forward", "sdpa_forward_lse", "sdpa_forward_padded", "sdpa_forward_window", "sdpa_forward_train",
             "sdpa_backward", "sdpa_backward_workspace_size", "mha_forward", "mha_forward_noalloc",
             "encoder_layer_forward", "encoder_layer_workspace_size",
-            "mha_workspace_size", "attn_status_string", "attn_last_error", "probe_scratch_size", "probe_mfma_bf16", "probe_exp_f32", "probe_hbm_copy")
+            "mha_workspace_size", "attn_status_string", "attn_last_error", "probe_scratch_size", "probe_mfma_bf16", "probe_exp_f32", "probe_lds_read", "probe_hbm_copy")
 
 _lib = None
 
@@ -82,6 +82,8 @@ def load_library(path: Path | str | None = None) -> ctypes.CDLL:
     lib.probe_mfma_bf16.restype = ci
     lib.probe_exp_f32.argtypes = [vp, sz, i64, vp, dp, dp]
     lib.probe_exp_f32.restype = ci
+    lib.probe_lds_read.argtypes = [vp, sz, i64, ci, vp, dp, dp]
+    lib.probe_lds_read.restype = ci
     lib.probe_hbm_copy.argtypes = [vp, vp, sz, ci, vp, dp]
     lib.probe_hbm_copy.restype = ci
     if path is None:
@@ -459,6 +461,18 @@ def probe_exp_f32(iters: int = 4000, device="cuda") -> tuple[float, float]:
     rate, ghz = ctypes.c_double(), ctypes.c_double()
     _check(lib.probe_exp_f32(scratch.data_ptr(), scratch.numel(), iters, _stream_handle(dev), ctypes.byref(rate),
                              ctypes.byref(ghz)))
+    return rate.value, ghz.value
+
+
+def probe_lds_read(transposed: bool, iters: int = 20000, device="cuda") -> tuple[float, float]:
+    """LDS read throughput with every CU busy, ds_read_b128 (transposed=False) or ds_read_b64_tr_b16 (True):
+    (bytes per clock per CU, shader clock in GHz). Synchronises the stream."""
+    lib = load_library()
+    dev = torch.device(device)
+    scratch = _probe_scratch(dev)
+    rate, ghz = ctypes.c_double(), ctypes.c_double()
+    _check(lib.probe_lds_read(scratch.data_ptr(), scratch.numel(), iters, 1 if transposed else 0, _stream_handle(dev),
+                              ctypes.byref(rate), ctypes.byref(ghz)))
     return rate.value, ghz.value
 
 

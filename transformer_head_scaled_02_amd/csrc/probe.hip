@@ -1,5 +1,5 @@
-// Measurement kernels (microbenchmarks): matrix-core and v_exp_f32 throughput with every CU busy, and HBM copy
-// bandwidth. They give the ceilings the attention kernel is compared with on the chip it runs on (the published
+// Measurement kernels (microbenchmarks): matrix-core, v_exp_f32 and LDS read throughput with every CU busy, and HBM
+// copy bandwidth. They give the ceilings the attention kernel is compared with on the chip it runs on (the published
 // peak assumes the 2.4 GHz clock, which the chip does not hold under dense matrix-core load).
 #include <hip/hip_runtime.h>
 
@@ -86,6 +86,55 @@ __global__ __launch_bounds__(kProbeThreads, kProbeBlocksPerCU) void probe_exp_ke
 #pragma unroll
   for (int i = 0; i < 32; ++i) s += r[i];
   sink[gid] = s;
+  if ((threadIdx.x & 63) == 0) cycles[gid >> 6] = t1 - t0;
+}
+
+// LDS reads as the attention kernels issue them: row reads of 16 bytes a lane (ds_read_b128, the score operands) or
+// transposed reads of four 16-bit values from four rows (ds_read_b64_tr_b16, the V operands), 32 in flight per
+// wave, over a 32 KB buffer. Every address stays inside the buffer; the values only feed the sink.
+template <bool kTr>
+__global__ __launch_bounds__(kProbeThreads, kProbeBlocksPerCU) void probe_lds_kernel(float* sink,
+                                                                                   unsigned long long* cycles,
+                                                                                   int iters) {
+  constexpr int kElems = 16384;  // 32 KB of 16-bit values
+  __shared__ __attribute__((aligned(16))) uint16_t buf[kElems];
+  for (int i = threadIdx.x; i < kElems; i += kProbeThreads) buf[i] = (uint16_t)(mix32((uint32_t)i) & 0x3fffu);
+  __syncthreads();
+  const uint32_t gid = blockIdx.x * kProbeThreads + threadIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t base = (uint32_t)(uintptr_t)buf;
+  // per-lane element offset inside a 1 KB (row reads) or 512-byte (transposed reads) piece: a row read takes 8
+  // consecutive elements per lane; a transposed read takes row 4g + (lane%16)/4 (+8 for lanes 16..31 of each half)
+  // and 4 elements at column 8(2((lane/16)%2) + (lane%4)/2) + 4(lane%2) of a 64-column block, as the kernels do
+  const int g = lane >> 5, jj = (lane & 15) >> 2;
+  const uint32_t loff = kTr ? (uint32_t)((4 * g + jj) * 64 + 8 * (2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) +
+                                         4 * (lane & 1)) * 2u
+                            : (uint32_t)lane * 16u;
+  uint32_t acc = 0;
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < iters; ++it) {
+    // 32 reads, then one wait: piece (wave * 4 + j + it) mod 16 of the buffer (2 KB apart), all in bounds
+    uint32_t r[32][4];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const uint32_t addr = base + (uint32_t)(((wave * 4 + j + it) & 15) * 2048) + loff;
+      if constexpr (kTr) {
+        asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(*reinterpret_cast<uint64_t*>(&r[j][0])) : "v"(addr));
+        r[j][2] = r[j][3] = 0u;
+      } else {
+        asm volatile("ds_read_b128 %0, %1" : "=v"(*reinterpret_cast<uint4*>(&r[j][0])) : "v"(addr));
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    // (one word of each read passes through an empty volatile statement after the wait, so it is read only once it
+    // has landed; one XOR per read keeps the VALU out of the way of the LDS)
+#pragma unroll
+    for (int j = 0; j < 32; ++j) asm volatile("" : "+v"(r[j][0]));
+#pragma unroll
+    for (int j = 0; j < 32; ++j) acc ^= r[j][0];
+  }
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+  sink[gid] = (float)(acc & 0xffffu);
   if ((threadIdx.x & 63) == 0) cycles[gid >> 6] = t1 - t0;
 }
 
@@ -198,6 +247,33 @@ ATTN_EXPORT int probe_exp_f32(void* scratch, size_t scratch_bytes, int64_t iters
   if (rc != ATTN_OK) return rc;
   const double lanes = (double)waves * 64.0 * (double)iters * 32.0;
   *exp_per_clock_per_cu = lanes / cyc / cus;
+  *clock_ghz = cyc / (ms * 1e-3) / 1e9;
+  return ATTN_OK;
+}
+
+ATTN_EXPORT int probe_lds_read(void* scratch, size_t scratch_bytes, int64_t iters, int transposed, void* stream,
+                               double* bytes_per_clock_per_cu, double* clock_ghz) {
+  if (!bytes_per_clock_per_cu || !clock_ghz) return fail_status(ATTN_ERR_INVALID, "probe_lds_read: null result pointer");
+  if (transposed != 0 && transposed != 1) return fail_status(ATTN_ERR_INVALID, "probe_lds_read: transposed must be 0 or 1");
+  int rc = check_scratch(scratch, scratch_bytes, iters, "probe_lds_read");
+  if (rc != ATTN_OK) return rc;
+  int cus = 0;
+  if ((rc = cu_count(&cus)) != ATTN_OK) return rc;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  auto* cycles = static_cast<unsigned long long*>(scratch);
+  auto* sink = reinterpret_cast<float*>(static_cast<char*>(scratch) + kCycleBytes);
+  const int blocks = cus * kProbeBlocksPerCU, waves = blocks * (kProbeThreads / 64);
+  float ms = 0.f;
+  double cyc = 0.0;
+  rc = timed_probe([&] {
+    if (transposed)
+      hipLaunchKernelGGL(probe_lds_kernel<true>, dim3(blocks), dim3(kProbeThreads), 0, s, sink, cycles, (int)iters);
+    else
+      hipLaunchKernelGGL(probe_lds_kernel<false>, dim3(blocks), dim3(kProbeThreads), 0, s, sink, cycles, (int)iters);
+  }, s, cycles, waves, &ms, &cyc);
+  if (rc != ATTN_OK) return rc;
+  const double bytes = (double)waves * (double)iters * 32.0 * 64.0 * (transposed ? 8.0 : 16.0);
+  *bytes_per_clock_per_cu = bytes / cyc / cus;
   *clock_ghz = cyc / (ms * 1e-3) / 1e9;
   return ATTN_OK;
 }
