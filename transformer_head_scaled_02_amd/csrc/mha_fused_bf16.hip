@@ -85,7 +85,7 @@ __global__ __launch_bounds__(64 * kFWaves, 1) void mha_self_fused_bf16(FusedMhaA
     }
   };
 
-  // Projection operands, as in the projection GEMM. Second operand (X^T): row 32mb + li of X, k = 16ks + 8g .. +7
+  // Projection operands, as in the projection GEMM. Second operand (X^T): row 32rb + li of X, k = 16ks + 8g .. +7
   // (logical chunk 2ks + g). First operand (W^T): two transposed reads give column 32nb + l%32 of a weight block at
   // k-rows 16ks + 8g + (0..3) and 16ks + 8g + 4 + (0..3).
   // Wave w covers 32 rows of X against three 32-column blocks, over every k-step of every k-tile. (Splitting the
@@ -147,11 +147,12 @@ __global__ __launch_bounds__(64 * kFWaves, 1) void mha_self_fused_bf16(FusedMhaA
   lds_barrier();  // every wave is done with the ring before its space is reused
 
   // [Q_i | K_i | V_i] rounded to bf16 at qkv: row r of matrix m at qkv + m*128*64 + r*64, logical chunk c of the row
-  // at physical chunk c ^ swz(r) (a lane's four columns are half a chunk). qkv starts past the merge buffer of the
-  // attention step below.
+  // at physical chunk c ^ swz(r) (a lane's four columns are half a chunk). The ring's space is free now: qkv takes
+  // 48 KB from its 96 KB mark, and the attention step's merge buffer (4 x 34 x 64 floats) its start.
   float* const red = reinterpret_cast<float*>(smem);
   uint16_t* const qkv = smem + 4 * 6 * 16 * 64 * 2;
-  static_assert(4 * 6 * 16 * 64 * 2 + 3 * kFMaxN * kD <= kFStages * kFStageElems, "merge buffer and Q/K/V fit");
+  static_assert(4 * 34 * 64 * 2 <= 4 * 6 * 16 * 64 * 2, "the merge buffer ends before qkv");
+  static_assert(4 * 6 * 16 * 64 * 2 + 3 * kFMaxN * kD <= kFStages * kFStageElems, "Q/K/V fit in the ring's space");
   {
     const int row = 32 * rb + li;
 #pragma unroll
