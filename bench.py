@@ -350,9 +350,22 @@ def cpu_baseline(w, x, budget_s: float):
         done += 1
         assert np.isfinite(o).all()
     per_head = flops_metric(w) / (w["B"] * w["h"])
-    return {"value": per_head * done / t_total / 1e12, "unit": "TFLOP/s", "cores": threads, "host": host, "kind": "oracle",
-            "sample": f"{done} head evaluations over the workload's {len(heads)} heads ({w['n_q']}x{w['n_k']} "
-                      f"scores each, float64 NumPy), {t_total:.1f} s"}
+    rec = {"value": per_head * done / t_total / 1e12, "unit": "TFLOP/s", "cores": threads, "host": host, "kind": "oracle",
+           "sample": f"{done} head evaluations over the workload's {len(heads)} heads ({w['n_q']}x{w['n_k']} "
+                     f"scores each, float64 NumPy), {t_total:.1f} s"}
+    if w["n_q"] * w["n_k"] <= 4096 and w["B"] * w["h"] <= 64:
+        # tiny heads (the fp32 single-head case): the pure-Python literal definition as well, one thread
+        from oracle import sdpa_brute
+        reps, tb = 0, 0.0
+        while tb < min(2.0, budget_s):
+            b, hh = heads[reps % len(heads)]
+            t0 = time.perf_counter()
+            sdpa_brute(Q[b, hh], K[b, hh], V[b, hh], w["causal"])
+            tb += time.perf_counter() - t0
+            reps += 1
+        rec["brute_force"] = {"value": per_head * reps / tb / 1e12, "unit": "TFLOP/s", "cores": 1,
+                              "sample": f"{reps} head evaluations of the pure-Python definition, {tb:.1f} s"}
+    return rec
 
 
 def cpu_baseline_bwd(w, x, budget_s: float):
