@@ -76,8 +76,8 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_bf16_mfma(GemmBatch batch) {
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     const uint32_t chunk = (uint32_t)(((lane & 7) ^ swz(8 * c + lr)) << 4);
-    a_voff[c] = (uint32_t)(lr * K * 2) + chunk;
-    w_voff[c] = (uint32_t)(lr * N * 2) + chunk;
+    a_voff[c] = (uint32_t)lr * (uint32_t)K * 2u + chunk;
+    w_voff[c] = (uint32_t)lr * (uint32_t)N * 2u + chunk;
   }
   auto issue = [&](int t) __attribute__((always_inline)) {
     const int k0 = t * kTK;
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_bf16_mfma(GemmBatch batch) {
           asm volatile("" : "+v"(l8));
           const int row = 8 * gi + l8;
           const uint32_t chunk = (uint32_t)(((lane & 7) ^ swz(row)) << 4);
-          lds_dma16(A + (int64_t)m0 * K + k0, (uint32_t)(min(row, rows_left - 1) * K * 2) + chunk, dst);
+          lds_dma16(A + (int64_t)m0 * K + k0, (uint32_t)min(row, rows_left - 1) * (uint32_t)K * 2u + chunk, dst);
         }
       } else {
         // W k-rows 8c .. 8c+7 of sub-tile s (columns n0 + 64s ..); a missing second half re-reads the first (its
@@ -305,7 +305,9 @@ hipError_t launch_gemm_bf16(const GemmProblem* probs, int nprobs, hipStream_t st
   for (int i = 0; i < nprobs; ++i) {
     const GemmProblem& p = probs[i];
     if (p.M <= 0 || p.N <= 0 || p.K <= 0 || p.N % 64 || p.K % kTK) return hipErrorInvalidValue;
-    if ((int64_t)8 * p.K * 2 > 0xffffffffLL || (int64_t)8 * p.N * 2 > 0xffffffffLL) return hipErrorInvalidValue;
+    // the copies' per-lane byte offsets are 32-bit: up to 128 rows of A (a ragged tile's rows are addressed from its
+    // first row) and eight k-rows of W must stay below 4 GiB
+    if ((int64_t)128 * p.K * 2 > 0xffffffffLL || (int64_t)8 * p.N * 2 > 0xffffffffLL) return hipErrorInvalidValue;
     batch.p[i] = p;
     batch.tiles_n[i] = (p.N + kTN - 1) / kTN;
     batch.tile_start[i] = (int)total;

@@ -57,8 +57,8 @@ __global__ __launch_bounds__(64 * kFWaves, 1) void mha_self_fused_bf16(FusedMhaA
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     const uint32_t chunk = (uint32_t)(((lane & 7) ^ swz(8 * c + lr)) << 4);
-    x_voff[c] = (uint32_t)(lr * dm * 2) + chunk;
-    w_voff[c] = (uint32_t)(lr * N * 2) + chunk;
+    x_voff[c] = (uint32_t)lr * (uint32_t)dm * 2u + chunk;
+    w_voff[c] = (uint32_t)lr * (uint32_t)N * 2u + chunk;
   }
   auto issue = [&](int t) __attribute__((always_inline)) {
     const int k0 = t * kFTK;
@@ -75,7 +75,7 @@ __global__ __launch_bounds__(64 * kFWaves, 1) void mha_self_fused_bf16(FusedMhaA
           asm volatile("" : "+v"(l8));
           const int row = 8 * gi + l8;
           const uint32_t chunk = (uint32_t)(((lane & 7) ^ swz(row)) << 4);
-          lds_dma16(X + k0, (uint32_t)(min(row, n - 1) * dm * 2) + chunk, dst);
+          lds_dma16(X + k0, (uint32_t)min(row, n - 1) * (uint32_t)dm * 2u + chunk, dst);
         }
       } else {
         const int gw = gi - 16, m = gw >> 3, c = gw & 7;
@@ -297,8 +297,9 @@ __global__ __launch_bounds__(64 * kFWaves, 1) void mha_self_fused_bf16(FusedMhaA
 
 hipError_t launch_mha_self_fused_bf16(const FusedMhaArgs& a, hipStream_t stream) {
   if (a.n < 1 || a.n > kFMaxN || a.dm < kFTK || a.dm % kFTK || a.H < 1) return hipErrorInvalidValue;
-  // the copies' per-lane offsets are 32-bit: eight rows of X or of the weights must stay below 4 GiB
-  if ((int64_t)8 * a.dm * 2 > 0xffffffffLL || (int64_t)8 * a.H * kD * 2 > 0xffffffffLL) return hipErrorInvalidValue;
+  // the copies' per-lane byte offsets are 32-bit: the 128 rows of X (a short sequence's rows are addressed from row 0)
+  // and eight k-rows of the weights must stay below 4 GiB
+  if ((int64_t)kFMaxN * a.dm * 2 > 0xffffffffLL || (int64_t)8 * a.H * kD * 2 > 0xffffffffLL) return hipErrorInvalidValue;
   const int64_t nblocks = (int64_t)a.B * a.H;
   if (nblocks <= 0 || nblocks > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(mha_self_fused_bf16, dim3((unsigned)nblocks), dim3(64 * kFWaves), 0, stream, a);
