@@ -245,10 +245,14 @@ def test_mha_workspace_reuse_and_out_argument():
 @pytest.mark.gpu
 def test_probes_report_plausible_ceilings():
     """The measurement kernels run and land inside what the chip can do (published: 2516.6 TFLOP/s dense bf16,
-    8 TB/s HBM); the MFMA clock they report is the one the chip holds under that load."""
+    8 TB/s HBM, 64 exp lane results and a few hundred LDS bytes per clock per CU); the clock each reports is the one
+    the chip holds under that load."""
     tflops, ghz = m.probe_mfma_bf16(iters=2000)
     assert 200.0 < tflops < 2600.0 and 0.5 < ghz < 3.0
     rate, ghz_e = m.probe_exp_f32(iters=400)
     assert 0.5 < rate < 64.0 and 0.5 < ghz_e < 3.0
+    for transposed in (False, True):
+        lds, ghz_l = m.probe_lds_read(transposed, iters=2000)
+        assert 16.0 < lds < 512.0 and 0.5 < ghz_l < 3.0
     gbps = m.probe_hbm_copy(nbytes=256 << 20, reps=2)
     assert 500.0 < gbps < 8500.0
