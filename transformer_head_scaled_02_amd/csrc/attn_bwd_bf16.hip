@@ -17,7 +17,9 @@
 //     dP product (those parts against a column of ones) then yields dP - D straight from the matrix core, which
 //     saves a VALU subtraction per score in both gradient kernels (widths 32 and 64; at 128, where a wave's
 //     registers are already full, the subtraction measured faster and stays on the VALU).
-//  2. attn_bwd_dkdv: a workgroup of NW waves owns NW*32 keys of one head; each wave keeps the K and V rows of its 32
+//  2. attn_bwd_dkdv (widths 32 and 128, and the window at every width; width 64 otherwise runs the same arithmetic
+//     in attn_bwd_dkdv_pp_bf16, eight waves in ping-pong, described at that kernel):
+//     a workgroup of NW waves owns NW*32 keys of one head; each wave keeps the K and V rows of its 32
 //     keys in registers as MFMA B operands. 64-row query tiles (Q rows, dO rows and the tile's lse/D, 17 KB) stream
 //     through a 3-stage LDS ring by global_load_lds_dwordx4. Per tile and 32-row half, S = Q K^T and dP = dO V^T
 //     come out of v_mfma_f32_32x32x16_bf16 with the wave's keys in the lane index and queries in the accumulator
@@ -33,6 +35,8 @@
 // Causal: query tiles wholly before a wave's keys (dK/dV) and key tiles wholly after a wave's queries (dQ) are
 // skipped; the tiles that straddle the diagonal set the future scores to -inf before the exponential.
 #include <math.h>
+
+#include <type_traits>
 
 #include "attn_tile.h"
 #include "launch.h"
@@ -419,6 +423,330 @@ __global__ __launch_bounds__(64 * NW, D == 128 ? 1 : 2) void attn_bwd_dkdv_bf16(
   }
 }
 
+// dK and dV at width 64 with the eight waves of a workgroup in ping-pong, as in the forward's attn_fwd_pp_bf16:
+// waves w and w + 4 share a SIMD, and the two groups of four are held half a query tile apart by the barrier that
+// ends every slot, so that in every slot one wave of each SIMD feeds the matrix core while the other runs the
+// exponentials and the dS products on the VALU. Per query tile u a wave's work splits into
+//   M(u):  dV^T += dO^T P(u-1), dK^T += Q^T dS(u-1) (transposed reads of tile u-1), then S(u) = Q K^T and
+//          dP(u) - D = dO V^T (- D by the extra k-step) from row reads of tile u: 34 products;
+//   V(u):  P(u) = exp2(S c - log2(e) lse), dS(u) = P o (dP - D), both packed to bf16.
+// Slot schedule:   slot  0     1     2     3    ...  2n-1    2n
+//                  g0:   M(0)  V(0)  M(1)  V(1) ...  V(n-1)  M(n)
+//                  g1:   -     M(0)  V(0)  M(1) ...  M(n-1)  V(n-1) M(n)
+// Tile u is read in slots 2u .. 2u+3; the group in its V slot (whose vector-memory issue is otherwise idle) copies
+// the tiles: tile u + 3 in group 1's V(u) (slot 2u + 2), into the stage of tile u - 1, last read in slot 2u + 1.
+// Each wave owns 32 keys (the workgroup 256); the arithmetic per key is exactly that of attn_bwd_dkdv_bf16.
+// Unlike the forward, the matrix-core slot sets the pace here (the VALU slot ends well before its barrier), so the
+// matrix-core wave holds the higher issue priority.
+constexpr int kPPBwdStages = 4;
+
+__global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pp_bf16(BwdArgs a, int n_kblocks) {
+  constexpr int D = 64;
+  constexpr int kStageElems = 2 * kTileElems + kAuxElems;  // [Q | dO | lse, D]
+  constexpr int kBK = 32 * 8;                              // keys per workgroup
+  constexpr int kLPW = 4;                                  // Q/dO copies per copying wave per tile
+  __shared__ __attribute__((aligned(16))) uint16_t smem[kPPBwdStages * kStageElems];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, gw = wave & 3;
+  const int lane = tid & 63;
+  const int g = lane >> 5, li = lane & 31;
+  const int n_q = a.n_q, n_k = a.n_k;
+  const bool causal = a.causal != 0;
+  const int n_tiles = (n_q + kBN - 1) / kBN;
+
+  int kb, slot;  // causal: key block 0 sees the most query tiles, so it goes first
+  if (causal) {
+    causal_order(blockIdx.x, gridDim.x, n_kblocks, slot, kb);
+  } else {
+    const int blk = xcd_remap(blockIdx.x, gridDim.x);
+    kb = blk % n_kblocks;
+    slot = blk / n_kblocks;
+  }
+  int bh;
+  const int b = head_of_slot(slot, a.B, a.H, bh);
+  const int n_real = real_keys(a.kv_len, b, n_k);  // keys from n_real on are padding: gradient 0
+  const uint16_t* Qp = static_cast<const uint16_t*>(a.Q) + (int64_t)bh * n_q * D;
+  const uint16_t* dOp = static_cast<const uint16_t*>(a.dO) + (int64_t)bh * n_q * D;
+  const uint16_t* Kp = static_cast<const uint16_t*>(a.K) + (int64_t)bh * n_k * D;
+  const uint16_t* Vp = static_cast<const uint16_t*>(a.V) + (int64_t)bh * n_k * D;
+  const float* auxp = a.aux + (int64_t)bh * n_tiles * kAuxFloatsPerTile;
+
+  const int k_blk0 = kb * kBK;
+  const int kw0 = k_blk0 + 32 * wave;  // this wave's keys: kw0 .. kw0+31; lane's key kw0 + li
+  const int key = kw0 + li;
+
+  bf16x8 kf[4], vf[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int64_t off = (int64_t)key * D + 8 * (4 * g + ks);
+    kf[ks] = key < n_real ? *reinterpret_cast<const bf16x8*>(Kp + off) : bf16x8{};
+    vf[ks] = key < n_real ? *reinterpret_cast<const bf16x8*>(Vp + off) : bf16x8{};
+  }
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    settle(kf[ks]);
+    settle(vf[ks]);
+  }
+
+  // Query tiles t0 .. nt-1 (local index u = t - t0). Causal: the workgroup starts at the tile holding its first key,
+  // and tiles from t_nomask on need no mask for this wave.
+  const int t0 = causal ? k_blk0 / kBN : 0;
+  const int t_nomask = causal ? (kw0 + 31) / kBN + 1 : 0;
+  const int nt = k_blk0 < n_real ? n_tiles : 0;  // a workgroup of padding keys only writes zeros
+  const int nu = nt - t0;
+
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)smem;
+  const int lrow = lane / 8;
+  uint32_t ld_voff[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int row = 8 * c + lrow;
+    ld_voff[c] = (uint32_t)(row * D + (((lane % 8) ^ swz_d<D>(row)) << 3)) * 2u;
+  }
+  // group 1 copies: wave 4 + gw moves Q/dO pieces 4gw .. 4gw+3 of the tile, and wave 4 also the tile's lse/D block
+  auto issue = [&](int u) __attribute__((always_inline)) {
+    const int t = t0 + u;
+    const uint32_t stage = smem_lds + (uint32_t)((u % kPPBwdStages) * kStageElems * 2);
+    issue_rows<4, D>(Qp + (int64_t)t * kBN * D, dOp + (int64_t)t * kBN * D, n_q - t * kBN, stage, gw, lrow, ld_voff);
+    if (gw == 0) lds_dma16(auxp + (int64_t)t * kAuxFloatsPerTile, (uint32_t)lane * 16u, stage + kTileElems * 4u);
+  };
+
+  int roff[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) roff[ks] = row_off<D>(li, g, ks);
+  int toff[2][2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) toff[mb][hi] = tr_off<D>(lane, mb, hi);
+  const bf16x8 ones3 = ones3_operand(g);
+
+  f32x16 dv[2], dk[2];
+  bf16x8 pp[4], ps[4];  // P and dS in bf16, B operands for k-steps (16 query rows) 0..3 of the tile
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) dv[mb] = dk[mb] = f32x16{};
+
+  // M(u): the gradient products of tile u - 1, then S and dP - D of tile u (either part may be absent). The operand
+  // reads run ahead of the products: the update's transposed reads two k-steps ahead (double-buffered), and every
+  // S / dP operand of tile u issued while the update's last products run; the four S / dP accumulators are
+  // interleaved, so that no product waits for the one before it. A fence after each operand keeps the reads in the
+  // order the products use them (the compiler would group them by base register).
+  auto mslot = [&](int u, auto upd_c, auto sdp_c, f32x16(&s)[2], f32x16(&dp)[2]) __attribute__((always_inline)) {
+    constexpr bool upd = decltype(upd_c)::value, sdp = decltype(sdp_c)::value;
+    __builtin_amdgcn_s_setprio(3);
+    const uint16_t* stc = smem + (u % kPPBwdStages) * kStageElems;
+    const float* auxc = reinterpret_cast<const float*>(stc + 2 * kTileElems);
+    bf16x8 qr[2][2], dr[2][2];  // [k-step % 2][mq]: S / dP operands, two k-steps ahead of their products
+    uint2 nd[2];
+    auto read_ks = [&](int ks) __attribute__((always_inline)) {
+#pragma unroll
+      for (int mq = 0; mq < 2; ++mq) {
+        qr[ks & 1][mq] = *reinterpret_cast<const bf16x8*>(stc + mq * 32 * D + roff[ks]);
+        __builtin_amdgcn_sched_barrier(0);
+        dr[ks & 1][mq] = *reinterpret_cast<const bf16x8*>(stc + kTileElems + mq * 32 * D + roff[ks]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    auto read_sdp = [&]() __attribute__((always_inline)) {
+      read_ks(0);
+      read_ks(1);
+#pragma unroll
+      for (int mq = 0; mq < 2; ++mq) nd[mq] = *reinterpret_cast<const uint2*>(auxc + 2 * kBN + 2 * (32 * mq + li));
+    };
+    if constexpr (upd) {
+      const uint16_t* st = smem + ((u - 1) % kPPBwdStages) * kStageElems;
+      bf16x8 ot[2][2], qt[2][2];
+#pragma unroll
+      for (int kq = 0; kq < 2; ++kq)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          ot[kq][mb] = tr_operand<D>(st + kTileElems, kq, toff, mb);
+          __builtin_amdgcn_sched_barrier(0);
+          qt[kq][mb] = tr_operand<D>(st, kq, toff, mb);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+      for (int kq = 0; kq < 4; ++kq) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          dv[mb] = mfma32x32x16(ot[kq & 1][mb], pp[kq], dv[mb]);
+          dk[mb] = mfma32x32x16(qt[kq & 1][mb], ps[kq], dk[mb]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (kq + 2 < 4) {
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb) {
+            ot[kq & 1][mb] = tr_operand<D>(st + kTileElems, kq + 2, toff, mb);
+            __builtin_amdgcn_sched_barrier(0);
+            qt[kq & 1][mb] = tr_operand<D>(st, kq + 2, toff, mb);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        // the first S / dP operands go into the registers the update's k-steps 0 and 1 have released
+        if constexpr (sdp) {
+          if (kq == 2) read_ks(0);
+          if (kq == 3) {
+            read_ks(1);
+#pragma unroll
+            for (int mq = 0; mq < 2; ++mq)
+              nd[mq] = *reinterpret_cast<const uint2*>(auxc + 2 * kBN + 2 * (32 * mq + li));
+          }
+        }
+      }
+    } else if constexpr (sdp) {
+      read_sdp();
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (sdp) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int mq = 0; mq < 2; ++mq) {
+          s[mq] = mfma32x32x16(qr[ks & 1][mq], kf[ks], ks == 0 ? f32x16{} : s[mq]);
+          dp[mq] = mfma32x32x16(dr[ks & 1][mq], vf[ks], ks == 0 ? f32x16{} : dp[mq]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (ks + 2 < 4) read_ks(ks + 2);
+      }
+#pragma unroll
+      for (int mq = 0; mq < 2; ++mq)
+        dp[mq] = mfma32x32x16(__builtin_bit_cast(bf16x8, uint4{nd[mq].x, nd[mq].y, 0u, 0u}), ones3, dp[mq]);
+    }
+  };
+
+  // V(u): P and dS of tile u in bf16
+  auto vslot = [&](int u, f32x16(&s)[2], const f32x16(&dp)[2]) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(0);
+    const int t = t0 + u;
+    const uint16_t* st = smem + (u % kPPBwdStages) * kStageElems;
+    const float* aux = reinterpret_cast<const float*>(st + 2 * kTileElems);
+    const bool masked = t < t_nomask;  // (uniform) causal tiles that straddle the wave's keys
+#pragma unroll
+    for (int mq = 0; mq < 2; ++mq) {
+      // register r holds query row 32mq + 8(r/4) + 4g + r%4 of the tile: its log2(e) lse come in fours
+      f32x4 lq[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lq[i] = *reinterpret_cast<const f32x4*>(aux + 32 * mq + 8 * i + 4 * g);
+      if (masked) {
+        const int base = key - t * kBN - 32 * mq - 4 * g;  // key - row = base - (8(r/4) + r%4); allowed when <= 0
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (8 * (r >> 2) + (r & 3) < base) s[mq][r] = -INFINITY;
+      }
+      float p[16], ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        p[r] = fast_exp2(__builtin_fmaf(s[mq][r], scale_log2<D>(), -lq[r >> 2][r & 3]));
+        ds[r] = p[r] * dp[mq][r];
+      }
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        uint32_t wp[4], wd[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          wp[j] = pack_bf16x2(p[8 * hf + 2 * j], p[8 * hf + 2 * j + 1]);
+          wd[j] = pack_bf16x2(ds[8 * hf + 2 * j], ds[8 * hf + 2 * j + 1]);
+        }
+        pp[2 * mq + hf] = __builtin_bit_cast(bf16x8, (uint4){wp[0], wp[1], wp[2], wp[3]});
+        ps[2 * mq + hf] = __builtin_bit_cast(bf16x8, (uint4){wd[0], wd[1], wd[2], wd[3]});
+      }
+    }
+    // P and dS are only used by the next M slot: without this the compiler sinks their arithmetic past the slot's
+    // barrier into that slot, and the two waves of a SIMD would take turns again instead of overlapping
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      settle(pp[k]);
+      settle(ps[k]);
+    }
+  };
+
+  if (nu > 0) {  // (uniform over the workgroup)
+    // prologue: group 1 brings tiles 0..2 and waits for tile 0
+    if (grp == 1) {
+#pragma unroll
+      for (int u = 0; u < 3; ++u)
+        if (u < nu) issue(u);
+      if (gw == 0) wait_copies<kLPW + 1, 4>(min(2, nu - 1));
+      else wait_copies<kLPW, 4>(min(2, nu - 1));
+    }
+    lds_barrier();
+    // Group 1 enters one slot later (an extra barrier first) and group 0 leaves with an extra barrier, so every wave
+    // passes the same number of barriers. Before the barrier that ends its M slot 2u + 1, group 1 waits until its
+    // copies of tile u + 1 have landed (tile u + 2 may stay in flight).
+    auto after_m = [&](int u) __attribute__((always_inline)) {
+      if (grp == 1) {
+        const int ahead = min(1, nu - 2 - u);  // tiles after u + 1 still in flight: u + 2 if it exists
+        if (ahead >= 0) {
+          if (gw == 0) {
+            if (ahead >= 1) wait_vmcnt<kLPW + 1>();
+            else wait_vmcnt<0>();
+          } else {
+            if (ahead >= 1) wait_vmcnt<kLPW>();
+            else wait_vmcnt<0>();
+          }
+        }
+      }
+      lds_barrier();
+    };
+    auto after_v = [&](int u) __attribute__((always_inline)) {
+      if (grp == 1 && u + 3 < nu) issue(u + 3);
+      lds_barrier();
+    };
+    if (grp == 1) lds_barrier();  // slot 0 of group 1: nothing
+    const std::true_type yes;
+    const std::false_type no;
+    // Every wave runs every tile of the loop through one code path (a single copy of the slots keeps the register
+    // allocation inside 256): a causal tile wholly before a wave's keys has all its weights masked to exactly 0 and
+    // adds exactly 0 to dV and dK. S and dP live from a tile's M slot to its V slot only.
+    {
+      f32x16 s[2], dp[2];
+      mslot(0, no, yes, s, dp);
+      after_m(0);
+      vslot(0, s, dp);
+      after_v(0);
+    }
+    for (int u = 1; u < nu; ++u) {
+      f32x16 s[2], dp[2];
+      mslot(u, yes, yes, s, dp);
+      after_m(u);
+      vslot(u, s, dp);
+      after_v(u);
+    }
+    {
+      f32x16 s[2], dp[2];
+      mslot(nu, yes, no, s, dp);
+    }
+    lds_barrier();
+    if (grp == 0) lds_barrier();  // slot 2nu + 1 of group 0: nothing
+  }
+
+  // lane holds d = 32mb + 8(r/4) + 4g + r%4 of its key's dV and dK rows; padding keys get 0
+  if (key >= n_real) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) dv[mb] = dk[mb] = f32x16{};
+  }
+  if (key < n_k) {
+    uint16_t* dvrow = static_cast<uint16_t*>(a.dV) + ((int64_t)bh * n_k + key) * D;
+    uint16_t* dkrow = static_cast<uint16_t*>(a.dK) + ((int64_t)bh * n_k + key) * D;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int d = 32 * mb + 8 * rg + 4 * g;
+        const uint2 wv = {pack_bf16x2(dv[mb][4 * rg], dv[mb][4 * rg + 1]),
+                          pack_bf16x2(dv[mb][4 * rg + 2], dv[mb][4 * rg + 3])};
+        const uint2 wk = {pack_bf16x2(dk[mb][4 * rg] * inv_sqrt_d<D>(), dk[mb][4 * rg + 1] * inv_sqrt_d<D>()),
+                          pack_bf16x2(dk[mb][4 * rg + 2] * inv_sqrt_d<D>(), dk[mb][4 * rg + 3] * inv_sqrt_d<D>())};
+        *reinterpret_cast<uint2*>(dvrow + d) = wv;
+        *reinterpret_cast<uint2*>(dkrow + d) = wk;
+      }
+  }
+}
+
 // dQ: see the file comment (launch 3).
 template <int D, int NW, int kStages, bool WIN>
 __global__ __launch_bounds__(64 * NW, D == 128 ? 1 : 2) void attn_bwd_dq_bf16(BwdArgs a, int n_qblocks) {
@@ -635,15 +963,22 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
   const int n_kblocks = (a.n_k + 32 * NW - 1) / (32 * NW);
   const int n_qblocks = (a.n_q + 32 * NW - 1) / (32 * NW);
   const int64_t nb_kv = (int64_t)n_kblocks * a.B * a.H, nb_q = (int64_t)n_qblocks * a.B * a.H;
-  if (!grid_ok(nb_kv) || !grid_ok(nb_q)) return hipErrorInvalidValue;
+  // width 64 without a window: the eight-wave ping-pong dK/dV kernel, 256 keys a workgroup
+  const int n_kb_pp = (a.n_k + 255) / 256;
+  const int64_t nb_pp = (int64_t)n_kb_pp * a.B * a.H;
+  if (!grid_ok(nb_kv) || !grid_ok(nb_q) || !grid_ok(nb_pp)) return hipErrorInvalidValue;
   hipError_t e = launch_attn_bwd_pre(a, false, D, stream);
   if (e != hipSuccess) return e;
-  if (a.windowed)
+  if (a.windowed) {
     hipLaunchKernelGGL((attn_bwd_dkdv_bf16<D, NW, kStagesKV, true>), dim3((unsigned)nb_kv), dim3(64 * NW), 0, stream,
                        a, n_kblocks);
-  else
-    hipLaunchKernelGGL((attn_bwd_dkdv_bf16<D, NW, kStagesKV, false>), dim3((unsigned)nb_kv), dim3(64 * NW), 0, stream,
-                       a, n_kblocks);
+  } else {
+    if constexpr (D == 64)
+      hipLaunchKernelGGL(attn_bwd_dkdv_pp_bf16, dim3((unsigned)nb_pp), dim3(512), 0, stream, a, n_kb_pp);
+    else
+      hipLaunchKernelGGL((attn_bwd_dkdv_bf16<D, NW, kStagesKV, false>), dim3((unsigned)nb_kv), dim3(64 * NW), 0,
+                         stream, a, n_kblocks);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.windowed)
