@@ -432,8 +432,9 @@ def bench_backward(args, w, x, m, dev):
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": "sdpa_backward step (attn_bwd_pre + " + ("attn_bwd_dkdv_pp_bf16" if w["d_k"] == 64
-                                                                     else "attn_bwd_dkdv_bf16") + " + attn_bwd_dq_bf16)",
+                     "kernel": "sdpa_backward step (attn_bwd_pre + " + ("attn_bwd_dkdv_pp_bf16 + attn_bwd_dq_pp_bf16)"
+                                                                     if w["d_k"] == 64 else
+                                                                     "attn_bwd_dkdv_bf16 + attn_bwd_dq_bf16)"),
                      "algorithmic_hbm_bytes": hbm_bytes_bwd(w),
                      "algorithmic_hbm_GBps": round(hbm_bytes_bwd(w) / (ms * 1e-3) / 1e9, 1)},
         "wall_s_timed_region": round(wall, 4),

@@ -26,14 +26,17 @@
 //     registers; P and dS are formed on the VALU and packed to bf16, which is directly the B operand of
 //     dV^T += dO^T P and dK^T += Q^T dS, whose A operands are transposed LDS reads (ds_read_b64_tr_b16) of the dO
 //     and Q tiles. Four products per tile, no cross-wave reduction, no atomics.
-//  3. attn_bwd_dq: a workgroup of NW waves owns NW*32 queries; each wave keeps its Q and dO rows in registers as B
-//     operands and its rows' lse and D in lanes. K/V tiles stream through the ring; per tile S^T = K Q^T and
-//     dP^T = V dO^T (keys in registers, queries in lanes), dS^T on the VALU packed to bf16 as the B operand of
-//     dQ^T += K^T dS^T, whose A operand is a transposed read of the K tile. Three products per tile.
+//  3. attn_bwd_dq (widths 32 and 128, and the window at every width; width 64 otherwise runs the same arithmetic in
+//     attn_bwd_dq_pp_bf16, eight waves in ping-pong): a workgroup of NW waves owns NW*32 queries; each wave keeps its
+//     Q and dO rows in registers as B operands and its rows' lse and D in lanes. K/V tiles stream through the ring;
+//     per tile S^T = K Q^T and dP^T = V dO^T (keys in registers, queries in lanes), dS^T on the VALU packed to bf16
+//     as the B operand of dQ^T += K^T dS^T, whose A operand is a transposed read of the K tile. Three products per
+//     tile.
 // Splitting dQ from dK/dV costs one recomputation of S and dP (seven products per score instead of five) but needs
 // neither atomics nor a transpose of dS, and every output is written once, deterministically.
 // Causal: query tiles wholly before a wave's keys (dK/dV) and key tiles wholly after a wave's queries (dQ) are
-// skipped; the tiles that straddle the diagonal set the future scores to -inf before the exponential.
+// skipped (in the ping-pong kernels, whose eight waves step through the tiles together, such a tile is masked whole
+// and adds exactly 0); the tiles that straddle the diagonal set the future scores to -inf before the exponential.
 #include <math.h>
 
 #include <type_traits>
@@ -929,6 +932,268 @@ __global__ __launch_bounds__(64 * NW, D == 128 ? 1 : 2) void attn_bwd_dq_bf16(Bw
   }
 }
 
+// dQ at width 64 with the eight waves of a workgroup in ping-pong, as attn_bwd_dkdv_pp_bf16: waves w and w + 4 share
+// a SIMD and run half a key tile apart, so that in every slot one wave of each SIMD feeds the matrix core while the
+// other forms dS on the VALU. Per key tile u a wave's work splits into
+//   M(u):  dQ^T += K^T dS^T(u-1) (transposed reads of tile u-1), then S^T(u) = K Q^T and dP^T(u) - D = V dO^T (- D by
+//          the extra k-step) from row reads of tile u: 26 products;
+//   V(u):  P = exp2(S^T c - log2(e) lse) (masked where the tile needs it), dS^T = P o (dP^T - D), packed to bf16.
+// Slot schedule and copies as in attn_bwd_dkdv_pp_bf16, with K/V tiles (16 KB) in a four-stage ring. Each wave owns
+// 32 queries (the workgroup 256); the arithmetic per query is exactly that of attn_bwd_dq_bf16.
+__global__ __launch_bounds__(512, 1) void attn_bwd_dq_pp_bf16(BwdArgs a, int n_qblocks) {
+  constexpr int D = 64;
+  constexpr int kStageElems = 2 * kTileElems;  // [K | V]
+  constexpr int kBM = 32 * 8;                  // queries per workgroup
+  constexpr int kLPW = 4;                      // K/V copies per copying wave per tile
+  __shared__ __attribute__((aligned(16))) uint16_t smem[kPPBwdStages * kStageElems];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, gw = wave & 3;
+  const int lane = tid & 63;
+  const int g = lane >> 5, li = lane & 31;
+  const bool causal = a.causal != 0;
+  const int n_q = a.n_q;
+  const int n_tiles_q = (n_q + kBN - 1) / kBN;
+
+  int qb, slot;
+  if (causal) {
+    causal_order(blockIdx.x, gridDim.x, n_qblocks, slot, qb);
+    qb = n_qblocks - 1 - qb;  // heaviest query blocks first
+  } else {
+    const int blk = xcd_remap(blockIdx.x, gridDim.x);
+    qb = blk % n_qblocks;
+    slot = blk / n_qblocks;
+  }
+  int bh;
+  const int b = head_of_slot(slot, a.B, a.H, bh);
+  const int n_k = real_keys(a.kv_len, b, a.n_k);  // keys from n_k on (padding) are never read
+  const uint16_t* Qp = static_cast<const uint16_t*>(a.Q) + (int64_t)bh * n_q * D;
+  const uint16_t* dOp = static_cast<const uint16_t*>(a.dO) + (int64_t)bh * n_q * D;
+  const uint16_t* Kp = static_cast<const uint16_t*>(a.K) + (int64_t)bh * a.n_k * D;
+  const uint16_t* Vp = static_cast<const uint16_t*>(a.V) + (int64_t)bh * a.n_k * D;
+  const float* auxp = a.aux + (int64_t)bh * n_tiles_q * kAuxFloatsPerTile;
+
+  const int q_blk0 = qb * kBM;
+  const int qw0 = q_blk0 + 32 * wave;
+  const int q = qw0 + li;
+
+  // Q and dO rows as B operands of S^T = K Q^T and dP^T = V dO^T; zero past n_q
+  bf16x8 qf[4], df[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int64_t off = (int64_t)q * D + 8 * (4 * g + ks);
+    qf[ks] = q < n_q ? *reinterpret_cast<const bf16x8*>(Qp + off) : bf16x8{};
+    df[ks] = q < n_q ? *reinterpret_cast<const bf16x8*>(dOp + off) : bf16x8{};
+  }
+  float lse2 = INFINITY;  // rows past n_q: weights 0
+  uint2 nd = {0u, 0u};    // the query's -D as three bf16 parts (0 past n_q)
+  if (q < n_q) {
+    const float* at = auxp + (int64_t)(q / kBN) * kAuxFloatsPerTile;
+    lse2 = at[q % kBN];
+    nd = *reinterpret_cast<const uint2*>(at + 2 * kBN + 2 * (q % kBN));
+  }
+  const bf16x8 ones3 = ones3_operand(g);
+  const bf16x8 ndop = __builtin_bit_cast(bf16x8, uint4{nd.x, nd.y, 0u, 0u});
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    settle(qf[ks]);
+    settle(df[ks]);
+  }
+  settle_f(lse2);
+
+  // Key tiles 0 .. nt-1 (causal: up to the workgroup's last query). Tiles from t_mask on hold keys past some query of
+  // this wave (or past n_k) and are masked; a tile wholly after the wave's queries is masked entirely and adds 0.
+  int nt = (n_k + kBN - 1) / kBN;
+  if (causal) nt = min(nt, (q_blk0 + kBM - 1) / kBN + 1);
+  const int t_mask = min(causal ? qw0 / kBN : nt, n_k / kBN);
+  const int key_lim = (causal ? min(q, n_k - 1) : n_k - 1) - 4 * g;  // keys past it (from the lane's first) masked
+  const int nu = nt;
+
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)smem;
+  const int lrow = lane / 8;
+  uint32_t ld_voff[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int row = 8 * c + lrow;
+    ld_voff[c] = (uint32_t)(row * D + (((lane % 8) ^ swz_d<D>(row)) << 3)) * 2u;
+  }
+  // group 1 copies: wave 4 + gw moves K/V pieces 4gw .. 4gw+3 of the tile
+  auto issue = [&](int u) __attribute__((always_inline)) {
+    const uint32_t stage = smem_lds + (uint32_t)((u % kPPBwdStages) * kStageElems * 2);
+    issue_rows<4, D>(Kp + (int64_t)u * kBN * D, Vp + (int64_t)u * kBN * D, n_k - u * kBN, stage, gw, lrow, ld_voff);
+  };
+
+  int roff[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) roff[ks] = row_off<D>(li, g, ks);
+  int toff[2][2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) toff[mb][hi] = tr_off<D>(lane, mb, hi);
+
+  f32x16 dq[2];
+  bf16x8 pds[4];  // dS^T in bf16, B operands for k-steps (16 keys) 0..3 of the tile
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) dq[mb] = f32x16{};
+
+  // M(u): the dQ product of tile u - 1, then S^T and dP^T - D of tile u (either part may be absent), operand reads
+  // two k-steps ahead of their products and fenced in the order the products use them.
+  auto mslot = [&](int u, auto upd_c, auto sdp_c, f32x16(&s)[2], f32x16(&dp)[2]) __attribute__((always_inline)) {
+    constexpr bool upd = decltype(upd_c)::value, sdp = decltype(sdp_c)::value;
+    __builtin_amdgcn_s_setprio(3);
+    const uint16_t* stc = smem + (u % kPPBwdStages) * kStageElems;
+    bf16x8 kr[2][2], vr[2][2];  // [k-step % 2][kb]: S^T / dP^T operands
+    auto read_ks = [&](int ks) __attribute__((always_inline)) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        kr[ks & 1][kb] = *reinterpret_cast<const bf16x8*>(stc + kb * 32 * D + roff[ks]);
+        __builtin_amdgcn_sched_barrier(0);
+        vr[ks & 1][kb] = *reinterpret_cast<const bf16x8*>(stc + kTileElems + kb * 32 * D + roff[ks]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    if constexpr (upd) {
+      const uint16_t* st = smem + ((u - 1) % kPPBwdStages) * kStageElems;
+      bf16x8 kt[2][2];  // [k-step % 2][mb]: transposed K operands of the dQ product
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          kt[ks][mb] = tr_operand<D>(st, ks, toff, mb);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) dq[mb] = mfma32x32x16(kt[ks & 1][mb], pds[ks], dq[mb]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (ks + 2 < 4) {
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb) {
+            kt[ks & 1][mb] = tr_operand<D>(st, ks + 2, toff, mb);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        if constexpr (sdp) {
+          if (ks == 2) read_ks(0);
+          if (ks == 3) read_ks(1);
+        }
+      }
+    } else if constexpr (sdp) {
+      read_ks(0);
+      read_ks(1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (sdp) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          s[kb] = mfma32x32x16(kr[ks & 1][kb], qf[ks], ks == 0 ? f32x16{} : s[kb]);
+          dp[kb] = mfma32x32x16(vr[ks & 1][kb], df[ks], ks == 0 ? f32x16{} : dp[kb]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (ks + 2 < 4) read_ks(ks + 2);
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) dp[kb] = mfma32x32x16(ones3, ndop, dp[kb]);  // dP^T - D
+    }
+  };
+
+  // V(u): dS^T of tile u in bf16
+  auto vslot = [&](int u, f32x16(&s)[2], const f32x16(&dp)[2]) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(0);
+    if (u >= t_mask) {  // (uniform) register r of block kb holds key 32kb + 8(r/4) + 4g + r%4 of the tile
+      const int lim = key_lim - u * kBN;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = -INFINITY;
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int kb = ks >> 1, base = 8 * (ks & 1);
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float p0 = fast_exp2(__builtin_fmaf(s[kb][base + 2 * j], scale_log2<D>(), -lse2));
+        const float p1 = fast_exp2(__builtin_fmaf(s[kb][base + 2 * j + 1], scale_log2<D>(), -lse2));
+        w[j] = pack_bf16x2(p0 * dp[kb][base + 2 * j], p1 * dp[kb][base + 2 * j + 1]);
+      }
+      pds[ks] = __builtin_bit_cast(bf16x8, (uint4){w[0], w[1], w[2], w[3]});
+    }
+    // dS is only used by the next M slot: pinned here so that its arithmetic is not sunk past the slot's barrier
+#pragma unroll
+    for (int k = 0; k < 4; ++k) settle(pds[k]);
+  };
+
+  if (nu > 0) {  // (uniform over the workgroup; no real key: dQ = 0)
+    // prologue: group 1 brings tiles 0..2 and waits for tile 0
+    if (grp == 1) {
+#pragma unroll
+      for (int u = 0; u < 3; ++u)
+        if (u < nu) issue(u);
+      wait_copies<kLPW, 4>(min(2, nu - 1));
+    }
+    lds_barrier();
+    // Group 1 enters one slot later and group 0 leaves with an extra barrier, so every wave passes the same number
+    // of barriers. Before the barrier that ends its M slot 2u + 1, group 1 waits until its copies of tile u + 1 have
+    // landed (tile u + 2 may stay in flight).
+    auto after_m = [&](int u) __attribute__((always_inline)) {
+      if (grp == 1 && u + 1 < nu) {
+        if (u + 2 < nu) wait_vmcnt<kLPW>();
+        else wait_vmcnt<0>();
+      }
+      lds_barrier();
+    };
+    auto after_v = [&](int u) __attribute__((always_inline)) {
+      if (grp == 1 && u + 3 < nu) issue(u + 3);
+      lds_barrier();
+    };
+    if (grp == 1) lds_barrier();  // slot 0 of group 1: nothing
+    const std::true_type yes;
+    const std::false_type no;
+    {
+      f32x16 s[2], dp[2];
+      mslot(0, no, yes, s, dp);
+      after_m(0);
+      vslot(0, s, dp);
+      after_v(0);
+    }
+    for (int u = 1; u < nu; ++u) {
+      f32x16 s[2], dp[2];
+      mslot(u, yes, yes, s, dp);
+      after_m(u);
+      vslot(u, s, dp);
+      after_v(u);
+    }
+    {
+      f32x16 s[2], dp[2];
+      mslot(nu, yes, no, s, dp);
+    }
+    lds_barrier();
+    if (grp == 0) lds_barrier();  // slot 2nu + 1 of group 0: nothing
+  }
+
+  // dQ = dQ^T / sqrt(D); lane holds d = 32mb + 8(r/4) + 4g + r%4 of its query
+  if (q < n_q) {
+    uint16_t* row = static_cast<uint16_t*>(a.dQ) + ((int64_t)bh * n_q + q) * D;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const uint2 w = {pack_bf16x2(dq[mb][4 * rg] * inv_sqrt_d<D>(), dq[mb][4 * rg + 1] * inv_sqrt_d<D>()),
+                         pack_bf16x2(dq[mb][4 * rg + 2] * inv_sqrt_d<D>(), dq[mb][4 * rg + 3] * inv_sqrt_d<D>())};
+        *reinterpret_cast<uint2*>(row + 32 * mb + 8 * rg + 4 * g) = w;
+      }
+  }
+}
+
 bool grid_ok(int64_t n) { return n > 0 && n <= 0x7fffffff; }
 
 }  // namespace
@@ -964,9 +1229,9 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
   const int n_qblocks = (a.n_q + 32 * NW - 1) / (32 * NW);
   const int64_t nb_kv = (int64_t)n_kblocks * a.B * a.H, nb_q = (int64_t)n_qblocks * a.B * a.H;
   // width 64 without a window: the eight-wave ping-pong dK/dV kernel, 256 keys a workgroup
-  const int n_kb_pp = (a.n_k + 255) / 256;
-  const int64_t nb_pp = (int64_t)n_kb_pp * a.B * a.H;
-  if (!grid_ok(nb_kv) || !grid_ok(nb_q) || !grid_ok(nb_pp)) return hipErrorInvalidValue;
+  const int n_kb_pp = (a.n_k + 255) / 256, n_qb_pp = (a.n_q + 255) / 256;
+  const int64_t nb_pp = (int64_t)n_kb_pp * a.B * a.H, nbq_pp = (int64_t)n_qb_pp * a.B * a.H;
+  if (!grid_ok(nb_kv) || !grid_ok(nb_q) || !grid_ok(nb_pp) || !grid_ok(nbq_pp)) return hipErrorInvalidValue;
   hipError_t e = launch_attn_bwd_pre(a, false, D, stream);
   if (e != hipSuccess) return e;
   if (a.windowed) {
@@ -981,12 +1246,16 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.windowed)
+  if (a.windowed) {
     hipLaunchKernelGGL((attn_bwd_dq_bf16<D, NW, kStagesQ, true>), dim3((unsigned)nb_q), dim3(64 * NW), 0, stream, a,
                        n_qblocks);
-  else
-    hipLaunchKernelGGL((attn_bwd_dq_bf16<D, NW, kStagesQ, false>), dim3((unsigned)nb_q), dim3(64 * NW), 0, stream, a,
-                       n_qblocks);
+  } else {
+    if constexpr (D == 64)
+      hipLaunchKernelGGL(attn_bwd_dq_pp_bf16, dim3((unsigned)nbq_pp), dim3(512), 0, stream, a, n_qb_pp);
+    else
+      hipLaunchKernelGGL((attn_bwd_dq_bf16<D, NW, kStagesQ, false>), dim3((unsigned)nb_q), dim3(64 * NW), 0, stream,
+                         a, n_qblocks);
+  }
   return hipGetLastError();
 }
 
