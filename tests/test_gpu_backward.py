@@ -173,6 +173,31 @@ def test_causal_gradients_ignore_the_other_side(dtype, t):
     assert torch.equal(dk3[:, :, t:], dk[:, :, t:]) and torch.equal(dv3[:, :, t:], dv[:, :, t:])
 
 
+@pytest.mark.parametrize("t", [255, 256, 257, 384, 511, 512, 639])
+def test_causal_gradients_ignore_the_other_side_across_blocks(t):
+    # as above at n = 640, where the width-64 gradient kernels split the keys (dK/dV) and the queries (dQ) into blocks
+    # of 256 (256, 256, 128) and each block into two groups of 128: cuts at and around those boundaries
+    n = 640
+    x = workloads.make_sdpa_inputs(1, 2, n, n, 64, 64, "bf16", 6500 + t, dout=True)
+    _, _, (dq, dk, dv) = _run(x, True)
+    y = workloads.make_sdpa_inputs(1, 2, n, n, 64, 64, "bf16", 7500 + t, dout=True)
+    x2 = dict(x)
+    for name in ("K", "V"):
+        raw = x[name].raw.copy()
+        raw[..., t:, :] = y[name].raw[..., t:, :]
+        x2[name] = workloads.Quantised(raw=raw, f64=None, dtype="bf16")
+    _, _, (dq2, _, _) = _run(x2, True)
+    assert torch.equal(dq2[:, :, :t], dq[:, :, :t])
+    assert not torch.equal(dq2, dq)
+    x3 = dict(x)
+    for name in ("Q", "dO"):
+        raw = x[name].raw.copy()
+        raw[..., :t, :] = y[name].raw[..., :t, :]
+        x3[name] = workloads.Quantised(raw=raw, f64=None, dtype="bf16")
+    _, _, (_, dk3, dv3) = _run(x3, True)
+    assert torch.equal(dk3[:, :, t:], dk[:, :, t:]) and torch.equal(dv3[:, :, t:], dv[:, :, t:])
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_zero_queries_give_zero_key_gradient(dtype):
     # Q = 0: dK = dS^T Q / 8 is exactly 0, and every weight is 1/n_k so dV_j = (1/n_k) sum_i dO_i
